@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Throughput of the gated delta rule hot path on one MI355X (gfx950).
+
+    python bench.py [--steps K] [--warmup W] [--workload prefill_1k]
+
+Headline: chunked-prefill tokens/s of one Qwen3.5-9B Gated DeltaNet layer
+(16 query/key heads, 32 value heads, head dim 128, chunk 64; B=1, T=1024,
+bf16 q/k/v, fp32 g/beta/state).  One step = one gdn_prefill_chunked call
+(chunk table, prep, chunk scan) over one batch already resident in HBM.
+Several copies of the batch are rotated so that repeated steps do not run
+out of the 256 MB last-level cache.  The same run also measures the decode
+step (64 sequences, state updated in place, state sets rotated), the long
+32k prefill and the 16-sequence varlen prefill, each with its per-kernel
+durations from HIP events recorded on the library's launch stream; and the
+fp64 CPU oracle on a bounded sample of the headline workload.
+
+Prints ONE JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0       # dense bf16 matrix cores
+PEAK_FP32_MFMA_TFLOPS = 157.3   # dense fp32 matrix cores
+CACHE_DEFEAT_BYTES = 600e6      # rotate copies until the working set exceeds the 256 MB MALL twice over
+
+METRIC = "prefill tokens/s + decode tokens/s (Qwen3.5-9B GDN layer), % MFMA/HBM peak"
+
+
+def esize(dtype):
+    import torch
+    return 2 if dtype == torch.bfloat16 else 4
+
+
+def prefill_costs(w, lengths):
+    """Algorithmic bytes and flops per launch of each prefill kernel."""
+    es = esize(w.io_dtype)
+    T = sum(lengths)
+    N = len(lengths)
+    C, dk, dv, hqk, hv = w.chunk, w.dk, w.dv, w.hqk, w.hv
+    E = sum((L + C - 1) // C for L in lengths)
+    qk_bytes = 2 * T * hqk * dk * es
+    gb_bytes = 2 * T * hv * 4
+    ta_bytes = 2 * E * hv * C * C * es
+    s_in = N * hv * dk * dv * 4 if w.s0_std is not None else 0
+    s_out = N * hv * dk * dv * 4
+    prep = {
+        "bytes": qk_bytes + gb_bytes + ta_bytes,
+        # two lower-triangular Gram products per chunk and query/key head, plus the
+        # forward substitution (C^3/3 flops per chunk and value head)
+        "flops": E * hqk * 2 * (C * (C + 1) // 2) * dk * 2 + E * hv * (C ** 3) // 3,
+    }
+    scan = {
+        "bytes": qk_bytes + T * hv * dv * es + gb_bytes + ta_bytes + T * hv * dv * es + s_in + s_out,
+        # [Q;K] S, S update: 6 dk dv; T X and A D: 4 C dv  (per token and value head)
+        "flops": T * hv * (6 * dk * dv + 4 * C * dv),
+    }
+    io_bytes = qk_bytes + 2 * T * hv * dv * es + gb_bytes + s_in + s_out   # what a step must move at least
+    return {"prep": prep, "scan": scan, "io_bytes": io_bytes, "chunks": E}
+
+
+def decode_costs(w):
+    es = esize(w.io_dtype)
+    N = len(w.lengths)
+    state = 2 * N * w.hv * w.dk * w.dv * 4
+    other = 2 * N * w.hqk * w.dk * es + 2 * N * w.hv * w.dv * es + 2 * N * w.hv * 4
+    return {"bytes": state + other, "state_bytes": state, "flops": N * w.hv * 7 * w.dk * w.dv}
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _clone_inputs(d):
+    return {k: (v.clone() if hasattr(v, "clone") else v) for k, v in d.items()}
+
+
+def measure_prefill(name, steps, warmup, lengths=None):
+    import torch
+
+    import gated_deltanet_scan_amd as gdn
+    from gated_deltanet_scan_amd import synthetic
+    w = synthetic.workload(name)
+    lengths = lengths or w.lengths
+    x = synthetic.make_workload_inputs(w, lengths=lengths)
+    dev = torch.device("cuda:0")
+    base = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    costs = prefill_costs(w, lengths)
+    shape = gdn.make_shape(w.hqk, w.hv, w.dk, w.dv, w.chunk, 1 if w.io_dtype == torch.bfloat16 else 0, 1.0)
+    ws_bytes = gdn.workspace_bytes(shape, sum(lengths), len(lengths))
+    per_set = costs["io_bytes"] + ws_bytes
+    n_sets = int(min(16, max(1, math.ceil(CACHE_DEFEAT_BYTES / per_set))))
+    calls = []
+    for i in range(n_sets):
+        d = base if i == 0 else _clone_inputs(base)
+        calls.append(gdn.prepare_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+                                         d["initial_state"], chunk=w.chunk))
+    for i in range(warmup):
+        calls[i % n_sets]()
+    _sync()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        calls[i % n_sets]()
+    _sync()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / steps
+
+    # per-kernel durations: HIP events on the launch stream over a second timed pass
+    gdn.profile_enable(True)
+    for i in range(steps):
+        calls[i % n_sets]()
+    _sync()
+    kern = {}
+    for kid, kname in ((0, "chunk_table"), (1, "prep"), (2, "scan")):
+        n, tot = gdn.profile_collect(kid)
+        kern[kname] = {"launches": n, "avg_us": (tot / n * 1e3) if n else None}
+    gdn.profile_enable(False)
+    T = sum(lengths)
+    flops = costs["prep"]["flops"] + costs["scan"]["flops"]
+    peak = PEAK_BF16_TFLOPS if w.io_dtype == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
+    out = {
+        "workload": name, "tokens": T, "sequences": len(lengths), "ms_per_step": ms,
+        "tokens_per_s": T / (ms * 1e-3), "rotated_copies": n_sets,
+        "mfma_frac": flops / (ms * 1e-3) / (peak * 1e12),
+        "hbm_frac": costs["io_bytes"] / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "kernels_us": {k: v["avg_us"] for k, v in kern.items()},
+    }
+    for kname in ("prep", "scan"):
+        us = kern[kname]["avg_us"]
+        c = costs[kname]
+        if us:
+            out["kernels_us"][kname] = us
+            out[kname + "_gbs"] = c["bytes"] / (us * 1e-6) / 1e9
+            out[kname + "_tflops"] = c["flops"] / (us * 1e-6) / 1e12
+    out["_costs"] = costs
+    out["_peak_tflops"] = peak
+    return out
+
+
+def roofline_for(pre):
+    """Roofline object of the dominant prefill kernel (the one with the longest average launch)."""
+    kus = pre["kernels_us"]
+    name = max(("prep", "scan"), key=lambda k: kus.get(k) or 0.0)
+    us = kus[name]
+    c = pre["_costs"][name]
+    intensity = c["flops"] / c["bytes"]
+    ridge = pre["_peak_tflops"] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if intensity < ridge:
+        achieved = c["bytes"] / (us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = c["flops"] / (us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": pre["_peak_tflops"], "unit": "TFLOP/s",
+                "frac": achieved / pre["_peak_tflops"]}
+    roof.update({"traffic": None, "kernel": "gdn_%s_kernel" % ("prep" if name == "prep" else "chunk_scan"),
+                 "avg_us": us, "algorithmic_bytes": c["bytes"], "algorithmic_flops": c["flops"],
+                 "intensity_flop_per_byte": intensity})
+    return roof
+
+
+def measure_decode(name, steps, warmup):
+    import torch
+
+    import gated_deltanet_scan_amd as gdn
+    from gated_deltanet_scan_amd import synthetic
+    w = synthetic.workload(name)
+    x = synthetic.make_workload_inputs(w)
+    dev = torch.device("cuda:0")
+    base = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    costs = decode_costs(w)
+    n_sets = int(min(16, max(3, math.ceil(CACHE_DEFEAT_BYTES / costs["bytes"]))))
+    calls = []
+    for i in range(n_sets):
+        d = base if i == 0 else _clone_inputs(base)
+        calls.append(gdn.prepare_decode(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"]))
+    for i in range(warmup):
+        calls[i % n_sets]()
+    _sync()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        calls[i % n_sets]()
+    _sync()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gdn.profile_enable(True)
+    for i in range(steps):
+        calls[i % n_sets]()
+    _sync()
+    n, tot = gdn.profile_collect(3)
+    gdn.profile_enable(False)
+    us = tot / n * 1e3
+    achieved = costs["bytes"] / (us * 1e-6) / 1e9
+    N = len(w.lengths)
+    return {
+        "workload": name, "sequences": N, "ms_per_step": ms, "tokens_per_s": N / (ms * 1e-3),
+        "kernel_avg_us": us, "kernel_tokens_per_s": N / (us * 1e-6),
+        "state_gbs": costs["state_bytes"] / (us * 1e-6) / 1e9, "rotated_state_sets": n_sets,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "gdn_decode_kernel",
+                     "avg_us": us, "algorithmic_bytes": costs["bytes"]},
+    }
+
+
+def cpu_baseline(name, seconds):
+    import oracle
+    from gated_deltanet_scan_amd import synthetic
+    w = synthetic.workload(name)
+    x = synthetic.make_workload_inputs(w)
+    threads = oracle.default_threads()
+    T = w.total_tokens
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.gdn_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], x["initial_state"],
+                           threads=threads)
+        runs += 1
+        wall = time.perf_counter() - t0
+        if wall >= seconds or runs >= 1000:
+            break
+    return {"value": runs * T / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full passes of %s (%d tokens x %d value heads, fp64 sequential recurrence, "
+                      "%d threads over (sequence, head) items), %.1f s wall" % (runs, name, T, w.hv, threads,
+                                                                                 wall)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_1k")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the long and varlen prefill lines")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: the gated delta rule shards over heads and sequences with no "
+              "exchange, and this build runs and reports a single GPU (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import gated_deltanet_scan_amd as gdn
+    gdn.load_library()
+
+    print("[bench] prefill %s" % args.workload, file=sys.stderr, flush=True)
+    pre = measure_prefill(args.workload, args.steps, args.warmup)
+    print("[bench] decode_64", file=sys.stderr, flush=True)
+    dec = measure_decode("decode_64", max(args.steps, 20), args.warmup)
+    extra = {}
+    if not args.no_extra:
+        for name in ("prefill_32k", "varlen_16"):
+            if name == args.workload:
+                continue
+            print("[bench] prefill %s" % name, file=sys.stderr, flush=True)
+            r = measure_prefill(name, max(5, min(args.steps, 20)), 2)
+            extra[name] = {k: v for k, v in r.items() if not k.startswith("_")}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+
+    from gated_deltanet_scan_amd import synthetic
+    w = synthetic.workload(args.workload)
+    line = {
+        "metric": METRIC,
+        "value": pre["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.io_dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": "%s: Qwen3.5-9B GDN layer prefill, %d sequence(s), %d tokens, %d QK / %d V heads, "
+                               "dk=dv=%d, chunk %d, bf16 q/k/v, fp32 g/beta/state"
+                               % (args.workload, len(w.lengths), w.total_tokens, w.hqk, w.hv, w.dk, w.chunk),
+                   "global_batch": len(w.lengths), "seq_len": w.total_tokens},
+        "roofline": roofline_for(pre),
+        "cpu_baseline": cpu,
+        "prefill": {k: v for k, v in pre.items() if not k.startswith("_")},
+        "decode": dec,
+        "extra": extra,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

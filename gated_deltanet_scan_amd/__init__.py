@@ -1,0 +1,13 @@
+"""MI355X (gfx950) implementation of the gated delta rule scan.
+
+The computation lives in libgdn.so (hand-written HIP kernels behind the C ABI
+of include/gdn.h); this package holds its Python binding, the build script and
+the seeded synthetic-input generator.
+"""
+from .binding import (GdnError, Shape, decode_step, header_functions, library_path, load_library,
+                      make_shape, prefill_chunked, prepare_decode, prepare_prefill, profile_collect, profile_enable, state_snapshot, version,
+                      workspace_bytes)
+
+__all__ = ["GdnError", "Shape", "decode_step", "header_functions", "library_path", "load_library",
+           "make_shape", "prefill_chunked", "prepare_decode", "prepare_prefill", "profile_collect", "profile_enable", "state_snapshot", "version",
+           "workspace_bytes"]

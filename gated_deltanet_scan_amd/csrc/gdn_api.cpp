@@ -1,0 +1,329 @@
+// gdn_api.cpp -- the extern "C" entry points of libgdn: argument validation
+// on the host, workspace sizing and dispatch to the kernel launchers.  Every
+// check runs before anything is enqueued, so an invalid call touches no
+// device memory (and needs no device at all).
+#include "../../include/gdn.h"
+#include "gdn_internal.hpp"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdn_status fail(gdn_status st, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+gdn_status ok()
+{
+    g_last_error[0] = '\0';
+    return GDN_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t io_size(int32_t io_dtype) { return io_dtype == GDN_DTYPE_BF16 ? 2 : 4; }
+
+// [p, p + bytes) and [r, r + rbytes) share a byte.
+bool overlaps(const void *p, size_t bytes, const void *r, size_t rbytes)
+{
+    if (!p || !r || bytes == 0 || rbytes == 0)
+        return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(r);
+    return a < b + rbytes && b < a + bytes;
+}
+
+gdn_status check_shape(const gdn_shape *s)
+{
+    if (!s)
+        return fail(GDN_ERR_INVALID_ARG, "shape is NULL");
+    if (s->num_qk_heads < 1 || s->num_v_heads < 1)
+        return fail(GDN_ERR_INVALID_ARG, "head counts must be >= 1 (HQK=%d, HV=%d)", s->num_qk_heads,
+                    s->num_v_heads);
+    if (s->num_v_heads % s->num_qk_heads != 0)
+        return fail(GDN_ERR_INVALID_ARG, "HV=%d is not a multiple of HQK=%d", s->num_v_heads, s->num_qk_heads);
+    if (s->dk < 1 || s->dv < 1)
+        return fail(GDN_ERR_INVALID_ARG, "head dimensions must be >= 1 (dk=%d, dv=%d)", s->dk, s->dv);
+    if (s->io_dtype != GDN_DTYPE_F32 && s->io_dtype != GDN_DTYPE_BF16)
+        return fail(GDN_ERR_INVALID_ARG, "io_dtype %d is neither GDN_DTYPE_F32 nor GDN_DTYPE_BF16", s->io_dtype);
+    if (!std::isfinite(s->scale))
+        return fail(GDN_ERR_INVALID_ARG, "scale is not finite");
+    return GDN_OK;
+}
+
+}  // namespace
+
+namespace gdn {
+
+bool prefill_supported(int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype)
+{
+    if (dk != dv)
+        return false;
+    if (io_dtype == GDN_DTYPE_F32 && dk > 64)
+        return false;
+    if (chunk == 64)
+        return dk == 32 || dk == 64 || dk == 128;
+    if (chunk == 16)
+        return dk == 32 || dk == 64;
+    return false;
+}
+
+bool decode_supported(int32_t dk, int32_t dv, int32_t io_dtype)
+{
+    (void)io_dtype;
+    return dk == dv && (dk == 32 || dk == 64 || dk == 128);
+}
+
+PrefillWorkspace prefill_workspace(int32_t hv, int32_t chunk, int32_t io_dtype, int64_t total_tokens,
+                                   int32_t num_seqs)
+{
+    PrefillWorkspace w{0, 0, 0};
+    if (chunk <= 0 || total_tokens < 0 || num_seqs < 0 || hv <= 0)
+        return w;
+    const int64_t max_chunks = (total_tokens + chunk - 1) / chunk + num_seqs;
+    if (max_chunks > INT32_MAX)
+        return w;
+    w.max_chunks = (int32_t)max_chunks;
+    w.table_bytes = (((size_t)num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
+    const size_t mats = 2 * (size_t)max_chunks * (size_t)hv * (size_t)chunk * (size_t)chunk * io_size(io_dtype);
+    w.total_bytes = w.table_bytes + mats;
+    return w;
+}
+
+}  // namespace gdn
+
+extern "C" {
+
+size_t gdn_prefill_workspace_bytes(const gdn_shape *shape, int64_t total_tokens, int32_t num_seqs)
+{
+    if (check_shape(shape) != GDN_OK)
+        return 0;
+    if (!gdn::prefill_supported(shape->dk, shape->dv, shape->chunk, shape->io_dtype))
+        return 0;
+    return gdn::prefill_workspace(shape->num_v_heads, shape->chunk, shape->io_dtype, total_tokens, num_seqs)
+        .total_bytes;
+}
+
+gdn_status gdn_prefill_chunked(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const int32_t *cu_seqlens, int32_t num_seqs,
+                               int64_t total_tokens, const int32_t *cu_seqlens_host, const float *initial_state,
+                               float *final_state, void *o, void *workspace, size_t workspace_bytes, void *stream)
+{
+    gdn_status st = check_shape(shape);
+    if (st != GDN_OK)
+        return st;
+    const gdn_shape &s = *shape;
+    if (!gdn::prefill_supported(s.dk, s.dv, s.chunk, s.io_dtype))
+        return fail(GDN_ERR_UNSUPPORTED,
+                    "no prefill kernel for dk=%d dv=%d chunk=%d io_dtype=%d (dk == dv in {32,64,128}, "
+                    "chunk 64, or chunk 16 with dk <= 64; fp32 io needs dk <= 64)",
+                    s.dk, s.dv, s.chunk, s.io_dtype);
+    if (num_seqs < 0 || total_tokens < 0)
+        return fail(GDN_ERR_INVALID_ARG, "negative num_seqs (%d) or total_tokens (%lld)", num_seqs,
+                    (long long)total_tokens);
+    if (num_seqs == 0) {
+        if (total_tokens != 0)
+            return fail(GDN_ERR_INVALID_ARG, "total_tokens=%lld with no sequences", (long long)total_tokens);
+        return ok();
+    }
+    if ((int64_t)num_seqs * s.num_v_heads > INT32_MAX / 16)
+        return fail(GDN_ERR_INVALID_ARG, "num_seqs * HV too large");
+    if (!cu_seqlens || !final_state)
+        return fail(GDN_ERR_INVALID_ARG, "cu_seqlens and final_state are required");
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
+        return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta and o are required when total_tokens > 0");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(final_state, 16) ||
+        !aligned(initial_state, 16))
+        return fail(GDN_ERR_INVALID_ARG, "q, k, v, o and state pointers must be 16-byte aligned");
+    if (!aligned(g, 4) || !aligned(beta, 4) || !aligned(cu_seqlens, 4))
+        return fail(GDN_ERR_INVALID_ARG, "g, beta and cu_seqlens must be 4-byte aligned");
+    if (cu_seqlens_host) {
+        if (cu_seqlens_host[0] != 0)
+            return fail(GDN_ERR_INVALID_ARG, "cu_seqlens[0] = %d, expected 0", cu_seqlens_host[0]);
+        for (int32_t n = 0; n < num_seqs; ++n)
+            if (cu_seqlens_host[n + 1] < cu_seqlens_host[n])
+                return fail(GDN_ERR_INVALID_ARG, "cu_seqlens decreases at index %d", n + 1);
+        if (cu_seqlens_host[num_seqs] != total_tokens)
+            return fail(GDN_ERR_INVALID_ARG, "cu_seqlens[%d] = %d but total_tokens = %lld", num_seqs,
+                        cu_seqlens_host[num_seqs], (long long)total_tokens);
+    }
+    const gdn::PrefillWorkspace ws =
+        gdn::prefill_workspace(s.num_v_heads, s.chunk, s.io_dtype, total_tokens, num_seqs);
+    if (ws.total_bytes == 0)
+        return fail(GDN_ERR_INVALID_ARG, "batch too large for the chunk table");
+    if (!workspace || workspace_bytes < ws.total_bytes)
+        return fail(GDN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", ws.total_bytes,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256))
+        return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+
+    const size_t es = io_size(s.io_dtype);
+    const size_t qk_bytes = (size_t)total_tokens * s.num_qk_heads * s.dk * es;
+    const size_t v_bytes = (size_t)total_tokens * s.num_v_heads * s.dv * es;
+    const size_t gb_bytes = (size_t)total_tokens * s.num_v_heads * sizeof(float);
+    const size_t state_bytes = (size_t)num_seqs * s.num_v_heads * s.dk * s.dv * sizeof(float);
+    const void *inputs[] = {q, k, v, g, beta, initial_state, workspace};
+    const size_t in_bytes[] = {qk_bytes, qk_bytes, v_bytes, gb_bytes, gb_bytes, state_bytes, ws.total_bytes};
+    for (int i = 0; i < 7; ++i) {
+        if (overlaps(o, v_bytes, inputs[i], in_bytes[i]))
+            return fail(GDN_ERR_INVALID_ARG, "o overlaps an input or the workspace");
+        if (i != 5 && overlaps(final_state, state_bytes, inputs[i], in_bytes[i]))
+            return fail(GDN_ERR_INVALID_ARG, "final_state overlaps an input or the workspace");
+    }
+    if (overlaps(o, v_bytes, final_state, state_bytes))
+        return fail(GDN_ERR_INVALID_ARG, "o overlaps final_state");
+    if (initial_state && initial_state != final_state && overlaps(final_state, state_bytes, initial_state, state_bytes))
+        return fail(GDN_ERR_INVALID_ARG, "final_state partially overlaps initial_state (only exact aliasing is allowed)");
+
+    gdn::PrefillArgs p{};
+    p.hqk = s.num_qk_heads;
+    p.hv = s.num_v_heads;
+    p.dk = s.dk;
+    p.dv = s.dv;
+    p.chunk = s.chunk;
+    p.io_dtype = s.io_dtype;
+    p.scale = s.scale;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.cu_seqlens = cu_seqlens;
+    p.num_seqs = num_seqs;
+    p.total_tokens = total_tokens;
+    p.initial_state = initial_state;
+    p.final_state = final_state;
+    p.o = o;
+    p.workspace = workspace;
+    p.max_chunks = ws.max_chunks;
+    p.table_bytes = ws.table_bytes;
+    p.stream = stream;
+    const hipError_t err = gdn::launch_prefill(p);
+    if (err != hipSuccess)
+        return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+gdn_status gdn_decode_step(const gdn_shape *shape, const void *q, const void *k, const void *v, const float *g,
+                           const float *beta, float *state, void *o, int32_t num_seqs, void *stream)
+{
+    gdn_status st = check_shape(shape);
+    if (st != GDN_OK)
+        return st;
+    const gdn_shape &s = *shape;
+    if (!gdn::decode_supported(s.dk, s.dv, s.io_dtype))
+        return fail(GDN_ERR_UNSUPPORTED, "no decode kernel for dk=%d dv=%d (dk == dv in {32,64,128})", s.dk, s.dv);
+    if (num_seqs < 0)
+        return fail(GDN_ERR_INVALID_ARG, "negative num_seqs");
+    if (num_seqs == 0)
+        return ok();
+    if ((int64_t)num_seqs * s.num_v_heads > INT32_MAX)
+        return fail(GDN_ERR_INVALID_ARG, "num_seqs * HV too large");
+    if (!q || !k || !v || !g || !beta || !state || !o)
+        return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta, state and o are required");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16))
+        return fail(GDN_ERR_INVALID_ARG, "q, k, v, o and state must be 16-byte aligned");
+    if (!aligned(g, 4) || !aligned(beta, 4))
+        return fail(GDN_ERR_INVALID_ARG, "g and beta must be 4-byte aligned");
+    const size_t es = io_size(s.io_dtype);
+    const size_t state_bytes = (size_t)num_seqs * s.num_v_heads * s.dk * s.dv * sizeof(float);
+    const size_t o_bytes = (size_t)num_seqs * s.num_v_heads * s.dv * es;
+    const size_t qk_bytes = (size_t)num_seqs * s.num_qk_heads * s.dk * es;
+    const size_t gb_bytes = (size_t)num_seqs * s.num_v_heads * sizeof(float);
+    const void *others[] = {q, k, v, g, beta};
+    const size_t ob[] = {qk_bytes, qk_bytes, o_bytes, gb_bytes, gb_bytes};
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(state, state_bytes, others[i], ob[i]) || overlaps(o, o_bytes, others[i], ob[i]))
+            return fail(GDN_ERR_INVALID_ARG, "state or o overlaps an input");
+    if (overlaps(o, o_bytes, state, state_bytes))
+        return fail(GDN_ERR_INVALID_ARG, "o overlaps the state");
+
+    gdn::DecodeArgs p{};
+    p.hqk = s.num_qk_heads;
+    p.hv = s.num_v_heads;
+    p.dk = s.dk;
+    p.dv = s.dv;
+    p.io_dtype = s.io_dtype;
+    p.scale = s.scale;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.g = g;
+    p.beta = beta;
+    p.state = state;
+    p.o = o;
+    p.num_seqs = num_seqs;
+    p.stream = stream;
+    const hipError_t err = gdn::launch_decode(p);
+    if (err != hipSuccess)
+        return fail(GDN_ERR_HIP, "decode launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+gdn_status gdn_state_snapshot(const gdn_shape *shape, const float *src, const int32_t *src_rows,
+                              int32_t src_capacity, float *dst, const int32_t *dst_rows, int32_t dst_capacity,
+                              int32_t num_rows, void *stream)
+{
+    gdn_status st = check_shape(shape);
+    if (st != GDN_OK)
+        return st;
+    if (num_rows < 0 || src_capacity < 0 || dst_capacity < 0)
+        return fail(GDN_ERR_INVALID_ARG, "negative row count or capacity");
+    if (num_rows == 0)
+        return ok();
+    if (!src || !dst)
+        return fail(GDN_ERR_INVALID_ARG, "src and dst are required");
+    if (!aligned(src, 16) || !aligned(dst, 16) || !aligned(src_rows, 4) || !aligned(dst_rows, 4))
+        return fail(GDN_ERR_INVALID_ARG, "src/dst must be 16-byte aligned, row indices 4-byte aligned");
+    const int64_t row_floats = (int64_t)shape->num_v_heads * shape->dk * shape->dv;
+    if (row_floats % 4 != 0)
+        return fail(GDN_ERR_UNSUPPORTED, "HV * dk * dv must be a multiple of 4");
+    if (!src_rows && num_rows > src_capacity)
+        return fail(GDN_ERR_INVALID_ARG, "num_rows=%d exceeds src_capacity=%d", num_rows, src_capacity);
+    if (!dst_rows && num_rows > dst_capacity)
+        return fail(GDN_ERR_INVALID_ARG, "num_rows=%d exceeds dst_capacity=%d", num_rows, dst_capacity);
+    if (overlaps(src, (size_t)src_capacity * row_floats * 4, dst, (size_t)dst_capacity * row_floats * 4))
+        return fail(GDN_ERR_INVALID_ARG, "src and dst overlap");
+
+    gdn::SnapshotArgs p{};
+    p.src = src;
+    p.src_rows = src_rows;
+    p.src_capacity = src_capacity;
+    p.dst = dst;
+    p.dst_rows = dst_rows;
+    p.dst_capacity = dst_capacity;
+    p.num_rows = num_rows;
+    p.row_floats = row_floats;
+    p.stream = stream;
+    const hipError_t err = gdn::launch_snapshot(p);
+    if (err != hipSuccess)
+        return fail(GDN_ERR_HIP, "snapshot launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
+const char *gdn_status_string(gdn_status status)
+{
+    switch (status) {
+    case GDN_OK: return "GDN_OK";
+    case GDN_ERR_INVALID_ARG: return "GDN_ERR_INVALID_ARG";
+    case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED";
+    case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE";
+    case GDN_ERR_HIP: return "GDN_ERR_HIP";
+    }
+    return "GDN_ERR_UNKNOWN";
+}
+
+const char *gdn_last_error(void) { return g_last_error; }
+
+int32_t gdn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// gdn_device.hpp -- device-side building blocks shared by the libgdn kernels
+// (gfx950 only): element types, 16x16 matrix-core tiles and small helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;  // every kernel runs 4 waves per workgroup
+constexpr int kWaves = kThreads / kWave;
+
+// ---------------------------------------------------------------------------
+// Matrix-core tiles.  All products are built from 16x16 output tiles:
+//   acc[16x16] += A[16 x K] * B[K x 16]
+// with A given row-major (row stride lda elements) and B given TRANSPOSED,
+// i.e. as Bt[16 x K] row-major (row stride ldb), so that both operands are
+// read along contiguous K.  A lane contributes row (lane % 16) of A and row
+// (lane % 16) of Bt over the K-slice selected by (lane / 16); A and B use the
+// same K-slice per lane, so the contraction is complete whatever order the
+// hardware sums the slice in.  The result tile is held with lane l owning
+// column (l % 16) and rows 4 * (l / 16) + {0, 1, 2, 3}.
+// ---------------------------------------------------------------------------
+template <typename E>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+    static constexpr int kStep = 32;  // K per instruction
+    static constexpr int kPerLane = 8;
+    typedef bf16x8 frag;
+    __device__ static inline frag load(const bf16 *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+    __device__ static inline f32x4 mma(frag a, frag b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mma<float> {
+    static constexpr int kStep = 4;
+    static constexpr int kPerLane = 1;
+    typedef float frag;
+    __device__ static inline frag load(const float *p) { return *p; }
+    __device__ static inline f32x4 mma(frag a, frag b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+template <typename E, int K>
+__device__ inline f32x4 mma_tile(f32x4 acc, const E *A, int lda, const E *Bt, int ldb, int lane)
+{
+    const int r = lane & 15;
+    const int kk = (lane >> 4) * Mma<E>::kPerLane;
+    const E *a = A + r * lda + kk;
+    const E *b = Bt + r * ldb + kk;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += Mma<E>::kStep)
+        acc = Mma<E>::mma(Mma<E>::load(a + k0), Mma<E>::load(b + k0), acc);
+    return acc;
+}
+
+__device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// Row of the result tile held in accumulator slot i by this lane.
+__device__ inline int tile_row(int lane, int i) { return ((lane >> 4) << 2) + i; }
+__device__ inline int tile_col(int lane) { return lane & 15; }
+
+// Four consecutive elements of one column of a result tile, written to a
+// transposed LDS buffer (one 8- or 16-byte store).
+__device__ inline void store4(bf16 *p, float a, float b, float c, float d)
+{
+    *reinterpret_cast<bf16x4 *>(p) = bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+}
+__device__ inline void store4(float *p, float a, float b, float c, float d)
+{
+    *reinterpret_cast<f32x4 *>(p) = f32x4{a, b, c, d};
+}
+
+// 16-byte vectors of io elements.
+template <typename E>
+struct Vec16 {
+    static constexpr int n = 16 / sizeof(E);
+    typedef E type __attribute__((ext_vector_type(16 / sizeof(E))));
+};
+
+template <typename E>
+__device__ inline float to_f32(E x) { return (float)x; }
+
+// Padding (in elements) that keeps 16-byte alignment of LDS rows and spreads
+// consecutive rows over different banks.
+template <typename E>
+struct LdsPad {
+    static constexpr int value = 16 / sizeof(E);
+};
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ inline float wave_inclusive_sum(float x, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        float y = __shfl_up(x, d, kWave);
+        if (lane >= d)
+            x += y;
+    }
+    return x;
+}
+
+__device__ inline float wave_sum(float x)
+{
+#pragma unroll
+    for (int d = kWave / 2; d >= 1; d >>= 1)
+        x += __shfl_xor(x, d, kWave);
+    return x;
+}
+
+}  // namespace gdn

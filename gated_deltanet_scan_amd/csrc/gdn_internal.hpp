@@ -1,0 +1,67 @@
+// gdn_internal.hpp -- launch descriptors shared by the C ABI layer
+// (gdn_api.cpp) and the kernel translation units.  Host-side only.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+struct PrefillArgs {
+    int32_t hqk, hv, dk, dv, chunk, io_dtype;
+    float scale;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const int32_t *cu_seqlens;
+    int32_t num_seqs;
+    int64_t total_tokens;
+    const float *initial_state;
+    float *final_state;
+    void *o;
+    void *workspace;
+    int32_t max_chunks;    // upper bound on the number of chunks of the batch
+    size_t table_bytes;    // bytes of the chunk table at the start of the workspace
+    void *stream;
+};
+
+struct DecodeArgs {
+    int32_t hqk, hv, dk, dv, io_dtype;
+    float scale;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float *state;
+    void *o;
+    int32_t num_seqs;
+    void *stream;
+};
+
+struct SnapshotArgs {
+    const float *src;
+    const int32_t *src_rows;
+    int32_t src_capacity;
+    float *dst;
+    const int32_t *dst_rows;
+    int32_t dst_capacity;
+    int32_t num_rows;
+    int64_t row_floats;  // HV * dk * dv
+    void *stream;
+};
+
+// Workspace layout of the prefill: [chunk table | T matrices | A matrices].
+struct PrefillWorkspace {
+    int32_t max_chunks;
+    size_t table_bytes;
+    size_t total_bytes;
+};
+
+bool prefill_supported(int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype);
+bool decode_supported(int32_t dk, int32_t dv, int32_t io_dtype);
+PrefillWorkspace prefill_workspace(int32_t hv, int32_t chunk, int32_t io_dtype, int64_t total_tokens,
+                                   int32_t num_seqs);
+
+hipError_t launch_prefill(const PrefillArgs &p);
+hipError_t launch_decode(const DecodeArgs &p);
+hipError_t launch_snapshot(const SnapshotArgs &p);
+
+}  // namespace gdn

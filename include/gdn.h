@@ -1,0 +1,193 @@
+/*
+ * gdn.h -- C ABI of libgdn, the gfx950 (MI355X) implementation of the gated
+ * delta rule used by the Gated DeltaNet linear-attention layers of Qwen3.5.
+ *
+ * The rule (Qwen3.5-9B architecture page, section Gated DeltaNet; the same
+ * step written as a per-token Loop on the NPU page, section "How it works"):
+ *     S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,   a_t = exp(g_t)
+ *     o_t = scale * S_t^T q_t
+ * for each value head, with the state S (dk x dv) carried from token to
+ * token.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Memory.   Every tensor argument is a pointer to DEVICE memory owned by
+ *           the caller; the library never allocates, frees or keeps a
+ *           pointer after the call returns.  Scratch space is passed in
+ *           through `workspace`.  Tensors are dense and contiguous in the
+ *           layouts given below (last index fastest).  Pointers to q, k, v,
+ *           o and state tensors must be 16-byte aligned; g and beta 4-byte.
+ * Heads.    HQK query/key heads serve HV value heads, HV a multiple of
+ *           HQK; value head h reads query/key head floor(h * HQK / HV)
+ *           (contiguous grouped-query blocks).
+ * Dtypes.   q, k, v and o share one io dtype (fp32 or bf16).  g, beta and
+ *           every state are fp32.  Arithmetic is fp32 (bf16 operands of the
+ *           matrix cores accumulate in fp32); the state is never rounded
+ *           below fp32.
+ * Gate.     g is the log of the forget gate (a_t = exp(g_t)), one value per
+ *           token and value head.  PRECONDITION, not checked on the device:
+ *           g <= 0 and beta finite (the chunked form relies on every decay
+ *           exponent being <= 0).
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *           stream).  Every call only enqueues work on that stream and
+ *           returns; it never synchronises and never reads device memory
+ *           on the host.  Results are ready when the stream reaches them.
+ * Errors.   Calls return GDN_OK or an error code; nothing throws or aborts
+ *           across this boundary.  Argument errors are detected on the host
+ *           BEFORE any device work is enqueued, so a failing call leaves
+ *           every buffer untouched.  gdn_last_error() gives a message for
+ *           the calling thread's last failure.
+ * Sizes.    Supported head dimensions: dk == dv in {32, 64, 128}; chunk
+ *           length in {16, 64} (chunk 16 only with dk <= 64).  Anything else
+ *           returns GDN_ERR_UNSUPPORTED.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment, bad cu_seqlens (host copy) */
+    GDN_ERR_UNSUPPORTED = 2,  /* a valid request this build has no kernel for */
+    GDN_ERR_WORKSPACE = 3,    /* workspace missing or smaller than gdn_prefill_workspace_bytes() */
+    GDN_ERR_HIP = 4           /* the HIP runtime refused a launch; see gdn_last_error() */
+} gdn_status;
+
+typedef enum gdn_dtype {
+    GDN_DTYPE_F32 = 0,
+    GDN_DTYPE_BF16 = 1
+} gdn_dtype;
+
+typedef struct gdn_shape {
+    int32_t num_qk_heads; /* HQK >= 1 */
+    int32_t num_v_heads;  /* HV >= 1, HV % HQK == 0 */
+    int32_t dk;           /* key/query head dimension */
+    int32_t dv;           /* value head dimension */
+    int32_t chunk;        /* prefill chunk length C (16 or 64) */
+    int32_t io_dtype;     /* gdn_dtype of q, k, v, o */
+    float scale;          /* output multiplier, usually 1/sqrt(dk) */
+} gdn_shape;
+
+/*
+ * Bytes of device scratch that gdn_prefill_chunked needs for a packed batch
+ * of `total_tokens` tokens in `num_seqs` sequences.  Returns 0 for an
+ * unsupported or invalid shape.
+ */
+size_t gdn_prefill_workspace_bytes(const gdn_shape *shape, int64_t total_tokens, int32_t num_seqs);
+
+/*
+ * Chunked prefill over a packed batch of variable-length sequences.
+ *
+ * Defined by the chunkwise-parallel form on the NPU page (section "How it
+ * works"): within a chunk of C tokens, with G the cumulative sum of g,
+ *   N   = diag(beta) [exp(G_t - G_j) k_t.k_j]_{j<t}
+ *   D   = (I + N)^-1 diag(beta) (V - diag(exp G) K S0)
+ *   O   = diag(exp G) Q S0 + [exp(G_t - G_j) q_t.k_j]_{j<=t} D
+ *   S_T = exp(G_T) S0 + K^T diag(exp(G_T - G)) D
+ * and carried from chunk to chunk in order; (I + N)^-1 by forward
+ * substitution per chunk, decay exponents masked in log space before exp
+ * (Candle pull-request page, section Chunked GatedDeltaNet Scan).  The
+ * result equals the token-by-token recurrence up to rounding.
+ *
+ *   q, k           [total_tokens, HQK, dk]  io dtype
+ *   v              [total_tokens, HV, dv]   io dtype
+ *   g, beta        [total_tokens, HV]       fp32
+ *   cu_seqlens     [num_seqs + 1] int32, device: sequence n owns tokens
+ *                  cu_seqlens[n] .. cu_seqlens[n+1]-1; cu_seqlens[0] = 0,
+ *                  non-decreasing, cu_seqlens[num_seqs] = total_tokens.
+ *                  Zero-length sequences are allowed (their state passes
+ *                  through).
+ *   cu_seqlens_host  optional host copy of the same offsets; when given it
+ *                  is validated and the call fails with GDN_ERR_INVALID_ARG
+ *                  on a violation.  Without it, invalid device offsets give
+ *                  unspecified results but never out-of-bounds accesses.
+ *   initial_state  [num_seqs, HV, dk, dv] fp32, or NULL for zeros
+ *   final_state    [num_seqs, HV, dk, dv] fp32 out; MAY alias initial_state
+ *                  (in-place prefix reuse), must not overlap anything else
+ *   o              [total_tokens, HV, dv] io dtype out; must not overlap
+ *                  any input
+ *   workspace      device scratch of at least gdn_prefill_workspace_bytes()
+ *                  bytes, 256-byte aligned; contents on entry are ignored.
+ */
+gdn_status gdn_prefill_chunked(const gdn_shape *shape,
+                               const void *q, const void *k, const void *v,
+                               const float *g, const float *beta,
+                               const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                               const int32_t *cu_seqlens_host,
+                               const float *initial_state, float *final_state,
+                               void *o, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step: one new token for each of `num_seqs` independent
+ * sequences, state updated IN PLACE.  Defined by the one-token matrix form
+ * on the NPU page (section "How it works"): with d = exp(g) and
+ * delta = beta (v - d S^T k),  o = scale (d S^T q + (q.k) delta),
+ * S' = d S + k delta^T.  The state is read once and written once.
+ *
+ *   q, k    [num_seqs, HQK, dk]  io dtype
+ *   v       [num_seqs, HV, dv]   io dtype
+ *   g, beta [num_seqs, HV]       fp32
+ *   state   [num_seqs, HV, dk, dv] fp32, read and overwritten
+ *   o       [num_seqs, HV, dv]   io dtype out (must not overlap the state)
+ */
+gdn_status gdn_decode_step(const gdn_shape *shape,
+                           const void *q, const void *k, const void *v,
+                           const float *g, const float *beta,
+                           float *state, void *o, int32_t num_seqs, void *stream);
+
+/*
+ * State snapshot / restore: copies whole per-sequence states (all HV heads,
+ * dk x dv fp32 each) between two state buffers, so that a verify pass can
+ * be rolled back and re-fed (NPU page, "New in v2": the recurrent state
+ * cannot be rewound, so it is saved before a draft is checked).
+ *
+ * For i in [0, num_rows): dst[dst_rows ? dst_rows[i] : i] =
+ *                         src[src_rows ? src_rows[i] : i].
+ *   src, dst          [capacity, HV, dk, dv] fp32 device buffers; they must
+ *                     not overlap.
+ *   src_rows, dst_rows  optional device int32 index arrays of num_rows
+ *                     entries (gather / scatter).  Entries outside
+ *                     [0, src_capacity) resp. [0, dst_capacity) are skipped.
+ *                     Restore is the same call with the buffers swapped.
+ *   With both index arrays NULL, num_rows must not exceed either capacity.
+ */
+gdn_status gdn_state_snapshot(const gdn_shape *shape,
+                              const float *src, const int32_t *src_rows, int32_t src_capacity,
+                              float *dst, const int32_t *dst_rows, int32_t dst_capacity,
+                              int32_t num_rows, void *stream);
+
+/*
+ * Kernel timing for benchmarks (not needed for normal use).
+ * gdn_profile_enable(1) clears the record and starts bracketing every kernel
+ * the library launches, on any thread, with two HIP events recorded on that
+ * kernel's stream; gdn_profile_enable(0) stops recording new launches.
+ * gdn_profile_collect() waits for the recorded events of one kernel and
+ * returns how many launches were recorded and their summed duration in ms.
+ * Kernel identifiers: 0 chunk table, 1 prep (Gram products and solve),
+ * 2 chunk scan (state pass and outputs), 3 decode, 4 snapshot.
+ * The events are created on first use and kept until the process ends;
+ * no device memory is allocated.
+ */
+gdn_status gdn_profile_enable(int32_t enable);
+gdn_status gdn_profile_collect(int32_t kernel, int32_t *launches, double *total_ms);
+
+/* Static description of a status code. */
+const char *gdn_status_string(gdn_status status);
+
+/* Message of the calling thread's most recent failed call ("" if none). */
+const char *gdn_last_error(void);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,77 @@
+"""Shared helpers of the GPU parity tests: run the HIP path and the fp64 oracle on
+the same seeded inputs and compare them.
+
+Error metric: per tensor, max |x - x_ref| / max |x_ref| (max-norm relative
+error), taken separately for the outputs and the final states, and per
+sequence for packed batches.  Bars: 1e-4 for fp32 io; 2e-2 on outputs and
+1e-2 on final states for bf16 io (fp32 state).
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL = {torch.float32: (1e-4, 1e-4), torch.bfloat16: (2e-2, 1e-2)}
+
+
+def say(*args):
+    print("[gpu-case]", *args, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(x, ref):
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    den = np.max(np.abs(ref))
+    num = np.max(np.abs(x - ref))
+    if den == 0.0:
+        return float(num)
+    return float(num / den)
+
+
+def to_dev(inp, device="cuda"):
+    out = {}
+    for key, val in inp.items():
+        out[key] = val.to(device) if isinstance(val, torch.Tensor) else val
+    return out
+
+
+def gpu_prefill(inp, chunk, scale=None, initial_state="from_inputs", inplace=False):
+    import gated_deltanet_scan_amd as gdn
+    d = to_dev(inp)
+    s0 = d["initial_state"] if initial_state == "from_inputs" else initial_state
+    fs = None
+    if inplace:
+        fs = s0
+    o, S = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], s0,
+                               scale=scale, chunk=chunk, final_state=fs)
+    torch.cuda.synchronize()
+    return o, S
+
+
+def oracle_prefill(inp, scale=None, initial_state="from_inputs"):
+    s0 = inp["initial_state"] if initial_state == "from_inputs" else initial_state
+    return oracle.gdn_forward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["cu_seqlens"], s0,
+                              scale=scale)
+
+
+def check_prefill(o, S, o_ref, S_ref, cu, io_dtype, label=""):
+    tol_o, tol_s = TOL[io_dtype]
+    o = o.double().cpu().numpy()
+    S = S.double().cpu().numpy()
+    assert np.all(np.isfinite(o)), label + ": non-finite output"
+    assert np.all(np.isfinite(S)), label + ": non-finite state"
+    cu = [int(x) for x in cu]
+    worst_o = worst_s = 0.0
+    for n in range(len(cu) - 1):
+        a, b = cu[n], cu[n + 1]
+        eo = rel_err(o[a:b], o_ref[a:b]) if b > a else 0.0
+        es = rel_err(S[n], S_ref[n])
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+        assert eo <= tol_o, "%s seq %d: output rel err %.3e > %.1e" % (label, n, eo, tol_o)
+        assert es <= tol_s, "%s seq %d: state rel err %.3e > %.1e" % (label, n, es, tol_s)
+    return worst_o, worst_s

@@ -1,0 +1,150 @@
+"""The C ABI on the host: the library loads, exports every function include/gdn.h
+declares, sizes its workspace, and rejects bad arguments before any device work.
+
+No call here reaches a kernel launch: every call carries at least one
+argument that the host-side validation refuses, and the fake device pointers
+are never dereferenced.
+"""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+import gated_deltanet_scan_amd as gdn
+from gated_deltanet_scan_amd import binding
+
+F32, BF16 = binding.GDN_DTYPE_F32, binding.GDN_DTYPE_BF16
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.library_path()):
+        from gated_deltanet_scan_amd import build
+        build.build()
+    return gdn.load_library()
+
+
+def shape(hqk=16, hv=32, d=128, chunk=64, io=BF16, scale=0.088):
+    return gdn.make_shape(hqk, hv, d, d, chunk, io, scale)
+
+
+# distinct, 256-byte aligned fake device addresses far apart (never dereferenced)
+def fake(i):
+    return ctypes.c_void_p(0x7f0000000000 + i * (1 << 34))
+
+
+def prefill(lib, sh, T=128, N=1, cu_host=None, ws_bytes=None, ws=None, q=None, g=None, s0=None, fs=None, o=None):
+    cu = np.array([0, T] if N == 1 else np.linspace(0, T, N + 1).astype(np.int32), dtype=np.int32) \
+        if cu_host is None else np.asarray(cu_host, dtype=np.int32)
+    need = lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), T, N)
+    return lib.gdn_prefill_chunked(
+        ctypes.byref(sh), q if q is not None else fake(1), fake(2), fake(3), g if g is not None else fake(4),
+        fake(5), fake(6), N, T, cu.ctypes.data_as(ctypes.c_void_p), s0 if s0 is not None else fake(7),
+        fs if fs is not None else fake(8), o if o is not None else fake(9), ws if ws is not None else fake(10),
+        need if ws_bytes is None else ws_bytes, None)
+
+
+def test_every_declared_function_is_exported(lib):
+    names = gdn.header_functions()
+    assert set(names) >= {"gdn_prefill_chunked", "gdn_decode_step", "gdn_state_snapshot",
+                          "gdn_prefill_workspace_bytes", "gdn_status_string", "gdn_last_error", "gdn_version"}
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.gdn_status_string(0) == b"GDN_OK"
+    assert lib.gdn_status_string(3) == b"GDN_ERR_WORKSPACE"
+    assert lib.gdn_version() >= 100
+
+
+def test_workspace_size(lib):
+    sh = shape()
+    T, N = 1000, 3
+    max_chunks = -(-T // 64) + N
+    expect = 256 + 2 * max_chunks * 32 * 64 * 64 * 2
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), T, N) == expect
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(shape(d=96)), T, N) == 0     # unsupported
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(shape(hqk=3)), T, N) == 0    # 32 % 3 != 0
+    assert lib.gdn_prefill_workspace_bytes(None, T, N) == 0
+
+
+def test_prefill_rejects_bad_shapes(lib):
+    assert lib.gdn_prefill_chunked(None, *([None] * 5), None, 1, 1, None, None, None, None, None, 0, None) == 1
+    assert prefill(lib, shape(hqk=3)) == binding.GDN_ERR_INVALID_ARG
+    assert b"multiple" in lib.gdn_last_error()
+    assert prefill(lib, shape(d=96)) == binding.GDN_ERR_UNSUPPORTED
+    assert prefill(lib, shape(chunk=32)) == binding.GDN_ERR_UNSUPPORTED
+    assert prefill(lib, shape(d=128, chunk=16)) == binding.GDN_ERR_UNSUPPORTED
+    assert prefill(lib, shape(d=128, io=F32)) == binding.GDN_ERR_UNSUPPORTED
+    assert prefill(lib, shape(io=7)) == binding.GDN_ERR_INVALID_ARG
+    assert prefill(lib, shape(scale=float("nan"))) == binding.GDN_ERR_INVALID_ARG
+
+
+def test_prefill_rejects_bad_cu_seqlens(lib):
+    sh = shape()
+    assert prefill(lib, sh, T=100, N=2, cu_host=[1, 50, 100]) == binding.GDN_ERR_INVALID_ARG
+    assert prefill(lib, sh, T=100, N=2, cu_host=[0, 60, 50]) == binding.GDN_ERR_INVALID_ARG
+    assert b"decreases" in lib.gdn_last_error()
+    assert prefill(lib, sh, T=100, N=2, cu_host=[0, 50, 99]) == binding.GDN_ERR_INVALID_ARG
+
+
+def test_prefill_rejects_workspace_and_alignment(lib):
+    sh = shape()
+    assert prefill(lib, sh, ws_bytes=1024) == binding.GDN_ERR_WORKSPACE
+    assert prefill(lib, sh, ws=ctypes.c_void_p(0x7f0000000000 + 10 * (1 << 34) + 64)) == \
+        binding.GDN_ERR_INVALID_ARG
+    assert prefill(lib, sh, q=ctypes.c_void_p(0x7f0000000000 + (1 << 34) + 2)) == binding.GDN_ERR_INVALID_ARG
+    assert prefill(lib, sh, g=ctypes.c_void_p(0x7f0000000000 + 4 * (1 << 34) + 2)) == binding.GDN_ERR_INVALID_ARG
+
+
+def test_prefill_rejects_overlaps(lib):
+    sh = shape()
+    # o placed on top of q
+    assert prefill(lib, sh, o=fake(1)) == binding.GDN_ERR_INVALID_ARG
+    # final state partially overlapping the initial state (exact aliasing is fine, partial is not)
+    s0 = fake(7)
+    fs_partial = ctypes.c_void_p(s0.value + 4096)
+    assert prefill(lib, sh, s0=s0, fs=fs_partial) == binding.GDN_ERR_INVALID_ARG
+    assert b"partially" in lib.gdn_last_error()
+
+
+def test_prefill_with_no_sequences_is_a_no_op(lib):
+    sh = shape()
+    assert lib.gdn_prefill_chunked(ctypes.byref(sh), None, None, None, None, None, None, 0, 0, None, None, None,
+                                   None, None, 0, None) == binding.GDN_OK
+    assert lib.gdn_prefill_chunked(ctypes.byref(sh), None, None, None, None, None, None, 0, 5, None, None, None,
+                                   None, None, 0, None) == binding.GDN_ERR_INVALID_ARG
+
+
+def test_decode_rejects_bad_arguments(lib):
+    sh = shape()
+    args = [fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), fake(7)]
+    assert lib.gdn_decode_step(ctypes.byref(shape(d=96)), *args, 4, None) == binding.GDN_ERR_UNSUPPORTED
+    assert lib.gdn_decode_step(ctypes.byref(sh), *args, -1, None) == binding.GDN_ERR_INVALID_ARG
+    bad = list(args)
+    bad[5] = None
+    assert lib.gdn_decode_step(ctypes.byref(sh), *bad, 4, None) == binding.GDN_ERR_INVALID_ARG
+    bad = list(args)
+    bad[6] = ctypes.c_void_p(fake(6).value + 8)   # o on top of the state
+    assert lib.gdn_decode_step(ctypes.byref(sh), *bad, 4, None) == binding.GDN_ERR_INVALID_ARG
+    assert lib.gdn_decode_step(ctypes.byref(sh), *args, 0, None) == binding.GDN_OK
+
+
+def test_snapshot_rejects_bad_arguments(lib):
+    sh = shape()
+    assert lib.gdn_state_snapshot(ctypes.byref(sh), fake(1), None, 4, fake(2), None, 4, 5, None) == \
+        binding.GDN_ERR_INVALID_ARG   # more rows than capacity
+    assert lib.gdn_state_snapshot(ctypes.byref(sh), fake(1), None, 4, ctypes.c_void_p(fake(1).value + 16), None,
+                                  4, 2, None) == binding.GDN_ERR_INVALID_ARG   # overlap
+    assert lib.gdn_state_snapshot(ctypes.byref(sh), None, None, 4, fake(2), None, 4, 2, None) == \
+        binding.GDN_ERR_INVALID_ARG
+    assert lib.gdn_state_snapshot(ctypes.byref(sh), fake(1), None, 4, fake(2), None, 4, 0, None) == binding.GDN_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 1, 32)
+    with pytest.raises(ValueError):
+        gdn.prefill_chunked(x, x, torch.zeros(4, 2, 32), torch.zeros(4, 2), torch.zeros(4, 2))

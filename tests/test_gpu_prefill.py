@@ -1,0 +1,142 @@
+"""GPU parity of the chunked prefill (gdn_prefill_chunked) against the fp64 oracle.
+
+Cases: the five workloads at their full sizes (the tiny fp32 one, 1k prefill,
+32k prefill, the 16-sequence varlen batch), lengths below, at and above the
+chunk, multi-chunk ragged tails, zero-length sequences, every supported head
+size and chunk length in both io dtypes, the strong-decay (-6.72) segment,
+a weak-decay long-memory stress, in-place prefix reuse and run-to-run
+determinism.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gated_deltanet_scan_amd import synthetic as S
+from gpu_helpers import check_prefill, gpu_prefill, oracle_prefill, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(lengths, hqk, hv, d, io, seed, g_law="uniform", s0_std=0.05, strong=False):
+    return S.make_inputs(lengths, hqk, hv, d, d, io, seed=seed, g_law=g_law, s0_std=s0_std,
+                         strong_segment=strong)
+
+
+def _run(inp, chunk, io, label, scale=None):
+    say(label, "T=%d" % int(inp["cu_seqlens"][-1]), "N=%d" % (len(inp["cu_seqlens"]) - 1),
+        "q", tuple(inp["q"].shape), "v", tuple(inp["v"].shape), "chunk", chunk, io)
+    o, St = gpu_prefill(inp, chunk, scale=scale)
+    o_ref, S_ref = oracle_prefill(inp, scale=scale)
+    eo, es = check_prefill(o, St, o_ref, S_ref, inp["cu_seqlens"], io, label)
+    say(label, "max rel err: o %.3e  S %.3e" % (eo, es))
+    return eo, es
+
+
+def test_tiny_fp32_workload():
+    w = S.workload("tiny_fp32")
+    _run(S.make_workload_inputs(w), w.chunk, w.io_dtype, "tiny_fp32")
+
+
+def test_prefill_1k_workload():
+    w = S.workload("prefill_1k")
+    _run(S.make_workload_inputs(w), w.chunk, w.io_dtype, "prefill_1k")
+
+
+def test_prefill_32k_workload():
+    w = S.workload("prefill_32k")
+    _run(S.make_workload_inputs(w), w.chunk, w.io_dtype, "prefill_32k")
+
+
+def test_varlen_16_workload():
+    w = S.workload("varlen_16")
+    _run(S.make_workload_inputs(w), w.chunk, w.io_dtype, "varlen_16")
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 127, 128, 129])
+@pytest.mark.parametrize("io,d,chunk", [(torch.float32, 32, 16), (torch.bfloat16, 128, 64)])
+def test_lengths_around_the_chunk(T, io, d, chunk):
+    _run(_case([T], 1, 2, d, io, seed=100 + T), chunk, io, "len%d_d%d_c%d" % (T, d, chunk))
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d,chunk", [(32, 16), (64, 16), (32, 64), (64, 64), (128, 64)])
+def test_every_kernel_instance(io, d, chunk):
+    if io == torch.float32 and d > 64:
+        pytest.skip("fp32 io is built for dk <= 64")
+    lengths = [3 * chunk + 5, chunk, 1, 2 * chunk - 1]
+    _run(_case(lengths, 2, 4, d, io, seed=7 * d + chunk), chunk, io, "inst_d%d_c%d" % (d, chunk))
+
+
+def test_zero_length_sequences_pass_state_through():
+    lengths = [0, 70, 0, 0, 5, 0]
+    inp = _case(lengths, 2, 4, 128, torch.bfloat16, seed=21)
+    _run(inp, 64, torch.bfloat16, "zero_lengths")
+    o, St = gpu_prefill(inp, 64)
+    s0 = inp["initial_state"]
+    for n in (0, 2, 3, 5):
+        assert torch.equal(St[n].cpu(), s0[n]), "empty sequence %d changed its state" % n
+
+
+def test_zero_initial_state_and_gqa_groups_of_four():
+    inp = _case([150, 90], 2, 8, 64, torch.bfloat16, seed=22, s0_std=None)
+    _run(inp, 64, torch.bfloat16, "gqa4_zero_s0")
+
+
+def test_strong_decay_segment_stays_finite():
+    """Tokens 64..127 of head 0 decay by exactly -6.72 per step: the upper-triangle exponent
+    would overflow fp32 without log-space masking."""
+    inp = _case([256], 1, 2, 128, torch.bfloat16, seed=23, strong=True)
+    assert float(inp["g"][100, 0]) == np.float32(-6.72)
+    _run(inp, 64, torch.bfloat16, "strong_decay")
+
+
+def test_weak_decay_long_memory():
+    """g ~ -U(0, 0.02): the state remembers thousands of tokens, so rounding can accumulate
+    across many chunks."""
+    inp = _case([4096], 1, 2, 128, torch.bfloat16, seed=24, g_law="weak")
+    _run(inp, 64, torch.bfloat16, "weak_decay")
+
+
+def test_scale_argument():
+    inp = _case([100], 1, 2, 64, torch.float32, seed=25)
+    _run(inp, 64, torch.float32, "scale_0.3", scale=0.3)
+
+
+def test_in_place_prefix_reuse_matches_two_calls():
+    """Prefill [0, a) then [a, T) from the carried state (final_state aliasing initial_state)
+    matches the oracle on [0, T)."""
+    inp = _case([300], 2, 4, 128, torch.bfloat16, seed=26)
+    a = 130
+    part1 = {k: (v[:a].contiguous() if k in ("q", "k", "v", "g", "beta") else v) for k, v in inp.items()}
+    part1["cu_seqlens"] = torch.tensor([0, a], dtype=torch.int32)
+    part2 = {k: (v[a:].contiguous() if k in ("q", "k", "v", "g", "beta") else v) for k, v in inp.items()}
+    part2["cu_seqlens"] = torch.tensor([0, 300 - a], dtype=torch.int32)
+    import gated_deltanet_scan_amd as gdn
+    state = inp["initial_state"].cuda().clone()
+    outs = []
+    for part in (part1, part2):
+        say("prefix_reuse part", tuple(part["q"].shape))
+        d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in part.items()}
+        o, st = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], state,
+                                    final_state=state)
+        assert st.data_ptr() == state.data_ptr()
+        outs.append(o)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(inp)
+    check_prefill(torch.cat(outs), state, o_ref, S_ref, inp["cu_seqlens"], torch.bfloat16, "prefix_reuse")
+
+
+def test_run_to_run_bitwise_determinism():
+    inp = _case([700, 33], 2, 4, 128, torch.bfloat16, seed=27)
+    o1, s1 = gpu_prefill(inp, 64)
+    o2, s2 = gpu_prefill(inp, 64)
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_chunk_length_does_not_change_the_answer():
+    """The chunked form is exact, so chunk 16 and chunk 64 agree with each other to rounding."""
+    inp = _case([257], 1, 2, 32, torch.float32, seed=28)
+    o16, s16 = gpu_prefill(inp, 16)
+    o64, s64 = gpu_prefill(inp, 64)
+    assert rel_err(o16.double().cpu(), o64.double().cpu()) < 1e-4
+    assert rel_err(s16.double().cpu(), s64.double().cpu()) < 1e-4
