@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gdn {
 
 typedef __bf16 bf16;
@@ -54,16 +56,43 @@ struct Mma<float> {
     }
 };
 
+// bf16 with K = 16 per instruction, for contractions whose length is not a
+// multiple of 32 (the chunk index when C = 16).
+struct MmaBf16K16 {
+    static constexpr int kStep = 16;
+    static constexpr int kPerLane = 4;
+    typedef bf16x4 frag;
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    __device__ static inline frag load(const bf16 *p) { return *reinterpret_cast<const bf16x4 *>(p); }
+    __device__ static inline f32x4 mma(frag a, frag b, f32x4 c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b),
+                                                         c, 0, 0, 0);
+    }
+};
+
+// Instruction used for a contraction of length K.
+template <typename E, int K>
+struct MmaFor {
+    typedef Mma<E> type;
+};
+template <int K>
+struct MmaFor<bf16, K> {
+    typedef typename std::conditional<K % 32 == 0, Mma<bf16>, MmaBf16K16>::type type;
+};
+
 template <typename E, int K>
 __device__ inline f32x4 mma_tile(f32x4 acc, const E *A, int lda, const E *Bt, int ldb, int lane)
 {
+    typedef typename MmaFor<E, K>::type M;
+    static_assert(K % M::kStep == 0, "contraction length must be a whole number of instructions");
     const int r = lane & 15;
-    const int kk = (lane >> 4) * Mma<E>::kPerLane;
+    const int kk = (lane >> 4) * M::kPerLane;
     const E *a = A + r * lda + kk;
     const E *b = Bt + r * ldb + kk;
 #pragma unroll
-    for (int k0 = 0; k0 < K; k0 += Mma<E>::kStep)
-        acc = Mma<E>::mma(Mma<E>::load(a + k0), Mma<E>::load(b + k0), acc);
+    for (int k0 = 0; k0 < K; k0 += M::kStep)
+        acc = M::mma(M::load(a + k0), M::load(b + k0), acc);
     return acc;
 }
 

@@ -40,7 +40,7 @@ void prof_begin(int32_t kernel, hipStream_t stream)
     }
     Rec &r = g_recs[g_used++];
     r.kernel = kernel;
-    hipEventRecord(r.start, stream);
+    (void)hipEventRecord(r.start, stream);
     g_open = &r;
 }
 
@@ -49,7 +49,7 @@ void prof_end(hipStream_t stream)
     if (!g_open)
         return;
     std::lock_guard<std::mutex> lk(g_mu);
-    hipEventRecord(g_open->stop, stream);
+    (void)hipEventRecord(g_open->stop, stream);
     g_open = nullptr;
 }
 
