@@ -102,7 +102,8 @@ def measure_prefill(name, steps, warmup, lengths=None):
     calls = []
     for i in range(n_sets):
         d = base if i == 0 else _clone_inputs(base)
-        calls.append(gdn.prepare_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"],
+        # host copy of the offsets: the library validates them and plans its segments
+        calls.append(gdn.prepare_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], x["cu_seqlens"],
                                          d["initial_state"], chunk=w.chunk))
     for i in range(warmup):
         calls[i % n_sets]()

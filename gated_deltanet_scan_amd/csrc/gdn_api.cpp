@@ -5,6 +5,7 @@
 #include "../../include/gdn.h"
 #include "gdn_internal.hpp"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -94,9 +95,31 @@ PrefillWorkspace prefill_workspace(int32_t hv, int32_t chunk, int32_t io_dtype, 
         return w;
     w.max_chunks = (int32_t)max_chunks;
     w.table_bytes = (((size_t)num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
+    // per chunk slot and value head: T and A (C x C io elements each) and the decay
+    // record exp(G), exp(G_last - G), beta (3 C floats)
     const size_t mats = 2 * (size_t)max_chunks * (size_t)hv * (size_t)chunk * (size_t)chunk * io_size(io_dtype);
-    w.total_bytes = w.table_bytes + mats;
+    const size_t recs = (size_t)max_chunks * (size_t)hv * 3 * (size_t)chunk * sizeof(float);
+    w.total_bytes = w.table_bytes + mats + recs;
     return w;
+}
+
+// Segments keep the T and A matrices plus the q and k rows of one segment
+// (about this many bytes) resident in the last-level cache between the prep
+// and the scan kernels.
+constexpr size_t kSegmentBytes = 128u << 20;
+
+int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype,
+                            int32_t num_seqs, int32_t max_seq_chunks, int32_t slot_capacity)
+{
+    if (num_seqs <= 0 || max_seq_chunks <= 0)
+        return 0;
+    const size_t es = io_size(io_dtype);
+    const size_t per_slot = (size_t)hv * 2 * chunk * chunk * es + (size_t)chunk * 2 * hqk * dk * es;
+    int64_t m = (int64_t)(kSegmentBytes / per_slot) / num_seqs;
+    m = std::max<int64_t>(m, 1);
+    m = std::min<int64_t>(m, max_seq_chunks);
+    m = std::min<int64_t>(m, slot_capacity / num_seqs);
+    return (int32_t)std::max<int64_t>(m, 0);
 }
 
 }  // namespace gdn
@@ -206,6 +229,20 @@ gdn_status gdn_prefill_chunked(const gdn_shape *shape, const void *q, const void
     p.workspace = workspace;
     p.max_chunks = ws.max_chunks;
     p.table_bytes = ws.table_bytes;
+    p.seg_len = 0;
+    p.max_seq_chunks = 0;
+    if (cu_seqlens_host) {
+        int64_t longest = 0;
+        for (int32_t n = 0; n < num_seqs; ++n)
+            longest = std::max<int64_t>(longest, cu_seqlens_host[n + 1] - cu_seqlens_host[n]);
+        p.max_seq_chunks = (int32_t)((longest + s.chunk - 1) / s.chunk);
+        p.seg_len = gdn::prefill_segment_len(s.num_qk_heads, s.num_v_heads, s.dk, s.chunk, s.io_dtype, num_seqs,
+                                             p.max_seq_chunks, ws.max_chunks);
+        if (p.max_seq_chunks == 0) {   // every sequence empty: one launch passes the states through
+            p.seg_len = 1;
+            p.max_seq_chunks = 1;
+        }
+    }
     p.stream = stream;
     const hipError_t err = gdn::launch_prefill(p);
     if (err != hipSuccess)

@@ -20,8 +20,10 @@ struct PrefillArgs {
     float *final_state;
     void *o;
     void *workspace;
-    int32_t max_chunks;    // upper bound on the number of chunks of the batch
+    int32_t max_chunks;    // chunk slots the workspace holds (upper bound on the chunks of the batch)
     size_t table_bytes;    // bytes of the chunk table at the start of the workspace
+    int32_t seg_len;       // > 0: segment mode, local chunks per sequence per segment (0: global mode)
+    int32_t max_seq_chunks;  // segment mode: chunks of the longest sequence
     void *stream;
 };
 
@@ -59,6 +61,10 @@ bool prefill_supported(int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype);
 bool decode_supported(int32_t dk, int32_t dv, int32_t io_dtype);
 PrefillWorkspace prefill_workspace(int32_t hv, int32_t chunk, int32_t io_dtype, int64_t total_tokens,
                                    int32_t num_seqs);
+// Segment length (local chunks per sequence) for a batch whose longest sequence has
+// max_seq_chunks chunks; 0 selects the single-launch global mode.
+int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype,
+                            int32_t num_seqs, int32_t max_seq_chunks, int32_t slot_capacity);
 
 hipError_t launch_prefill(const PrefillArgs &p);
 hipError_t launch_decode(const DecodeArgs &p);

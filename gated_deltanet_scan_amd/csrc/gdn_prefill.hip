@@ -8,21 +8,28 @@
 //   O   = diag(exp G) Q S0 + [exp(G_t - G_j) q_t.k_j]_{j<=t} D
 //   S_T = exp(G_T) S0 + K^T diag(exp(G_T - G)) D
 // Everything that does not depend on the state (the Gram products, the
-// decay matrix, the solve of (I + N), the decayed query-key matrix) is done
-// for all chunks at once by the prep kernel; the scan kernel then walks the
-// chunks of each sequence in order with the state slice held on chip
-// ("state propagated sequentially between chunks, intra-chunk work as
-// batched products": Candle pull-request page, section Chunked GatedDeltaNet
-// Scan).  Three kernels per call:
+// decay matrix, the inverse of I + N, the decayed query-key matrix) is done
+// for many chunks at once by the prep kernel; the scan kernel then walks the
+// chunks of each sequence in order with the state slice held on chip (the
+// state is carried from chunk to chunk in order, the work inside a chunk is
+// batched products: Candle pull-request page, section Chunked GatedDeltaNet
+// Scan).  Kernels:
 //   gdn_chunk_table_kernel  chunk offsets of every sequence (integer scan)
 //   gdn_prep_kernel         per (chunk, query/key head): K K^T and Q K^T on
 //                           the matrix cores; per value head of the group:
 //                           G, log-space-masked exp(G_t - G_j), N, the unit
-//                           lower-triangular inverse T = (I + N)^-1 by
-//                           forward substitution, A = decayed Q K^T
+//                           lower-triangular T = (I + N)^-1, A = decayed Q K^T
 //   gdn_chunk_scan_kernel   per (sequence, value head, dv-slice): for each
 //                           chunk, [Q;K] S, X = diag(beta)(V - diag(exp G) K S),
 //                           D = T X, O = diag(exp G) Q S + A D, S update.
+//
+// Where the chunks' T and A live.  Global mode: one slot per chunk of the
+// batch, slot = chunk_start[n] + c.  Segment mode (the host knows the
+// sequence lengths): the launch is split into segments of M local chunk
+// indices [s0, s0 + M) of every sequence, slot = n * M + (c - s0); prep and
+// scan run per segment, the state is carried in final_state between
+// segments, and a segment's T, A, q and k stay in the last-level cache
+// between the two kernels.
 #include "gdn_device.hpp"
 #include "gdn_internal.hpp"
 #include "gdn_profile.hpp"
@@ -95,100 +102,138 @@ __device__ inline void seq_range(const int32_t *cu, int n, int64_t total_tokens,
     b = min<int64_t>(max<int64_t>(cu[n + 1], a), total_tokens);
 }
 
-// ---------------------------------------------------------------------------
-// Prep kernel.  Grid (max_chunks, HQK); entries past the real chunk count
-// exit at once.  Writes, for every value head h of the group and chunk e,
-//   tmat[e][h] = (I + N)^-1   (C x C, row-major, unit lower triangular)
-//   amat[e][h] = [exp(G_t - G_j) q_t.k_j]_{j<=t}  (C x C, zero above)
-// ---------------------------------------------------------------------------
-template <int C>
-__device__ inline void solve_unit_lower_column(const float *Nm, int ldf, int col, float (&x)[C])
+// Placement of chunk slots in the workspace (see the file header).
+struct SlotMap {
+    const int32_t *chunk_start;  // global mode: per-sequence first slot; NULL in segment mode
+    int32_t seg_first;           // first local chunk index of this launch
+    int32_t seg_len;             // local chunks per sequence in this launch
+};
+
+// Number of chunks of sequence n (consistent with the clamping of the chunk table).
+__device__ inline int seq_chunks(const SlotMap &m, const int32_t *cu, int n, int64_t total_tokens, int chunk)
 {
-    // Column `col` of (I + N)^-1: x_t = [t == col] - sum_{j<t} N[t][j] x_j.
-#pragma unroll
-    for (int t = 0; t < C; ++t) {
-        float s = (t == col) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < t; ++j)
-            s -= Nm[t * ldf + j] * x[j];
-        x[t] = s;
-    }
+    if (m.chunk_start)
+        return m.chunk_start[n + 1] - m.chunk_start[n];
+    int64_t a, b;
+    seq_range(cu, n, total_tokens, a, b);
+    return (int)((b - a + chunk - 1) / chunk);
 }
 
+__device__ inline size_t slot_of(const SlotMap &m, int n, int c)
+{
+    if (m.chunk_start)
+        return (size_t)m.chunk_start[n] + c;
+    return (size_t)n * m.seg_len + (c - m.seg_first);
+}
+
+// ---------------------------------------------------------------------------
+// Prep kernel.  One workgroup per (chunk slot, query/key head); writes, for
+// every value head h of the group,
+//   tmat[slot][h] = (I + N)^-1   (C x C, row-major, unit lower triangular)
+//   amat[slot][h] = [exp(G_t - G_j) q_t.k_j]_{j<=t}  (C x C, zero above)
+//
+// The inverse is formed in 16 x 16 blocks: the diagonal blocks D_b by
+// forward substitution (one lane per column), then the blocks below the
+// diagonal, one block-diagonal at a time, by
+//   T_{b,b'} = -D_b * sum_{b' <= m < b} N_{b,m} T_{m,b'}
+// which is the exact block-doubling identity (D + C)^-1 = D^-1 - D^-1 C D^-1
+// of the NPU page applied to the block-triangular split, in fp32 on the
+// matrix cores.
+// ---------------------------------------------------------------------------
 template <typename E, int C, int DK>
 __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const float *__restrict__ g,
-    const float *__restrict__ beta, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_start, int32_t num_seqs, int64_t total_tokens, int32_t hqk,
-    int32_t hv, E *__restrict__ tmat, E *__restrict__ amat)
+    const float *__restrict__ beta, const int32_t *__restrict__ cu, SlotMap map, int32_t num_seqs,
+    int64_t total_tokens, int32_t hqk, int32_t hv, E *__restrict__ tmat, E *__restrict__ amat,
+    float *__restrict__ dec)
 {
     constexpr int PAD = LdsPad<E>::value;
     constexpr int LDK = DK + PAD;
-    constexpr int LDF = C + 4;
-    constexpr int RT = C / 16;
-    constexpr int HB = 2;  // value heads per pass
+    constexpr int LDF = C + 4;      // fp32 C x C rows
+    constexpr int RT = C / 16;      // 16-row blocks
+    constexpr int HB = 2;           // value heads per pass
     constexpr int IN_BYTES = 2 * C * LDK * (int)sizeof(E);
-    constexpr int N_BYTES = HB * C * LDF * (int)sizeof(float);
-    constexpr int U_BYTES = IN_BYTES > N_BYTES ? IN_BYTES : N_BYTES;
+    constexpr int F_BYTES = HB * C * LDF * (int)sizeof(float);
+    constexpr int U1 = IN_BYTES > F_BYTES ? IN_BYTES : F_BYTES;   // Ks,Qs  then N of HB heads
+    constexpr int U2 = 2 * C * LDF * (int)sizeof(float);           // KK,QK  then T of HB heads
+    static_assert(U2 >= F_BYTES, "T of HB heads must fit where the Gram products were");
     constexpr int VN = Vec16<E>::n;
     typedef typename Vec16<E>::type V16;
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem_u[U_BYTES];
-    __shared__ __attribute__((aligned(16))) float KK[C * LDF];
-    __shared__ __attribute__((aligned(16))) float QK[C * LDF];
+    __shared__ __attribute__((aligned(16))) unsigned char smem_a[U1];
+    __shared__ __attribute__((aligned(16))) unsigned char smem_b[U2];
+    __shared__ __attribute__((aligned(16))) float Yw[kWaves][16][17];
     __shared__ float Gs[HB][C];
     __shared__ float Bs[HB][C];
-    E *Ks = reinterpret_cast<E *>(smem_u);
+    E *Ks = reinterpret_cast<E *>(smem_a);
     E *Qs = Ks + C * LDK;
-    float *Nm = reinterpret_cast<float *>(smem_u);  // reused once the Gram products are done
+    float *Nm = reinterpret_cast<float *>(smem_a);   // [HB][C][LDF], after the Gram products
+    float *KK = reinterpret_cast<float *>(smem_b);
+    float *QK = KK + C * LDF;
+    float *Tf = reinterpret_cast<float *>(smem_b);   // [HB][C][LDF], after N and A are built
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int32_t e = blockIdx.x;
     const int hq = blockIdx.y;
-    if (e >= chunk_start[num_seqs])
-        return;
-    const int n = find_sequence(chunk_start, num_seqs, e);
+    int n, c;
+    size_t slot;
+    if (map.chunk_start) {
+        const int32_t e = blockIdx.x;
+        if (e >= map.chunk_start[num_seqs])
+            return;
+        n = find_sequence(map.chunk_start, num_seqs, e);
+        c = e - map.chunk_start[n];
+        slot = e;
+    } else {
+        n = blockIdx.x / map.seg_len;
+        c = map.seg_first + (int)(blockIdx.x - n * map.seg_len);
+        if (n >= num_seqs || c >= seq_chunks(map, cu, n, total_tokens, C))
+            return;
+        slot = blockIdx.x;
+    }
     int64_t a, b;
     seq_range(cu, n, total_tokens, a, b);
-    const int64_t t0 = a + (int64_t)(e - chunk_start[n]) * C;
+    const int64_t t0 = a + (int64_t)c * C;
     const int len = (int)min<int64_t>(C, b - t0);
 
-    // Q and K rows of this query/key head; rows past the end are zero.
-    for (int i = tid; i < C * DK / VN; i += kThreads) {
-        const int r = i / (DK / VN), c0 = (i % (DK / VN)) * VN;
-        V16 kv = (V16)(E)0.f, qv = (V16)(E)0.f;
-        if (r < len) {
-            const size_t off = ((size_t)(t0 + r) * hqk + hq) * DK + c0;
-            kv = *reinterpret_cast<const V16 *>(k + off);
-            qv = *reinterpret_cast<const V16 *>(q + off);
+    // Q and K rows of this query/key head (rows past the end are zero), then K K^T and
+    // Q K^T, lower block triangle only (tile row >= tile column).  The T of one pass
+    // overwrites the Gram products, so every pass after the first stages them again.
+    auto stage_gram = [&]() {
+        for (int i = tid; i < C * DK / VN; i += kThreads) {
+            const int r = i / (DK / VN), c0 = (i % (DK / VN)) * VN;
+            V16 kv = (V16)(E)0.f, qv = (V16)(E)0.f;
+            if (r < len) {
+                const size_t off = ((size_t)(t0 + r) * hqk + hq) * DK + c0;
+                kv = *reinterpret_cast<const V16 *>(k + off);
+                qv = *reinterpret_cast<const V16 *>(q + off);
+            }
+            *reinterpret_cast<V16 *>(Ks + r * LDK + c0) = kv;
+            *reinterpret_cast<V16 *>(Qs + r * LDK + c0) = qv;
         }
-        *reinterpret_cast<V16 *>(Ks + r * LDK + c0) = kv;
-        *reinterpret_cast<V16 *>(Qs + r * LDK + c0) = qv;
-    }
-    __syncthreads();
-
-    // K K^T and Q K^T, lower block triangle only (tile row >= tile column).
-    constexpr int NT = RT * (RT + 1) / 2;
-    for (int it = wave; it < 2 * NT; it += kWaves) {
-        const int which = it / NT;
-        const int t = it % NT;
-        int tr = 0;
-        while ((tr + 1) * (tr + 2) / 2 <= t)
-            ++tr;
-        const int tc = t - tr * (tr + 1) / 2;
-        const E *A = (which ? Qs : Ks) + tr * 16 * LDK;
-        const E *Bt = Ks + tc * 16 * LDK;
-        const f32x4 acc = mma_tile<E, DK>(zero4(), A, LDK, Bt, LDK, lane);
-        float *dst = which ? QK : KK;
+        __syncthreads();
+        constexpr int NT = RT * (RT + 1) / 2;
+        for (int it = wave; it < 2 * NT; it += kWaves) {
+            const int which = it / NT;
+            const int t = it % NT;
+            int tr = 0;
+            while ((tr + 1) * (tr + 2) / 2 <= t)
+                ++tr;
+            const int tc = t - tr * (tr + 1) / 2;
+            const E *A = (which ? Qs : Ks) + tr * 16 * LDK;
+            const E *Bt = Ks + tc * 16 * LDK;
+            const f32x4 acc = mma_tile<E, DK>(zero4(), A, LDK, Bt, LDK, lane);
+            float *dst = which ? QK : KK;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dst[(tr * 16 + tile_row(lane, i)) * LDF + tc * 16 + tile_col(lane)] = acc[i];
-    }
-    __syncthreads();
+            for (int i = 0; i < 4; ++i)
+                dst[(tr * 16 + tile_row(lane, i)) * LDF + tc * 16 + tile_col(lane)] = acc[i];
+        }
+        __syncthreads();
+    };
 
     const int group = hv / hqk;
     for (int hb = 0; hb < group; hb += HB) {
         const int nh = min(HB, group - hb);
+        stage_gram();
         // G = in-chunk inclusive cumulative sum of g; padding tokens carry g = 0, beta = 0.
         if (wave < nh) {
             const int h = hq * group + hb + wave;
@@ -198,33 +243,116 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
                 bv = beta[(size_t)(t0 + lane) * hv + h];
             }
             const float G = wave_inclusive_sum(gv, lane);
+            // lanes >= len carry g = 0, so lane C-1 holds G at the last real token
+            const float Glast = __shfl(G, C - 1, kWave);
             if (lane < C) {
                 Gs[wave][lane] = G;
                 Bs[wave][lane] = bv;
+                // decay record of the chunk for the scan: exp(G_t), exp(G_last - G_t), beta_t
+                float *rec = dec + (slot * hv + h) * 3 * C;
+                rec[lane] = expf(G);
+                rec[C + lane] = expf(Glast - G);
+                rec[2 * C + lane] = bv;
             }
         }
         __syncthreads();
         // exp(G_t - G_j) only for j <= t, where the exponent is <= 0 (log-space mask).
-        for (int idx = tid; idx < nh * C * C; idx += kThreads) {
-            const int hh = idx / (C * C);
-            const int rem = idx - hh * C * C;
-            const int t = rem / C, j = rem - (rem / C) * C;
+        // One thread per VN consecutive entries of a row: one 16-byte store of A.
+        for (int idx = tid; idx < nh * C * C / VN; idx += kThreads) {
+            const int hh = idx / (C * C / VN);
+            const int rem = (idx - hh * (C * C / VN)) * VN;
+            const int t = rem / C, j0 = rem - (rem / C) * C;
             const int h = hq * group + hb + hh;
-            float ed = 0.f;
-            if (j <= t)
-                ed = __expf(Gs[hh][t] - Gs[hh][j]);
-            Nm[(hh * C + t) * LDF + j] = (j < t) ? Bs[hh][t] * ed * KK[t * LDF + j] : 0.f;
-            amat[((size_t)e * hv + h) * C * C + rem] = (E)(ed * QK[t * LDF + j]);
+            const float gt = Gs[hh][t], bt = Bs[hh][t];
+            V16 av;
+#pragma unroll
+            for (int e = 0; e < VN; ++e) {
+                const int j = j0 + e;
+                const float ed = (j <= t) ? __expf(gt - Gs[hh][j]) : 0.f;
+                Nm[(hh * C + t) * LDF + j] = (j < t) ? bt * ed * KK[t * LDF + j] : 0.f;
+                av[e] = (E)(ed * QK[t * LDF + j]);
+            }
+            *reinterpret_cast<V16 *>(amat + (slot * hv + h) * C * C + rem) = av;
+        }
+        __syncthreads();   // KK, QK are dead from here: their space holds T
+
+        // Diagonal blocks D_b: one wave per head, lane = (block b, column j).
+        if (wave < nh) {
+            const int bb = lane >> 4, j = lane & 15;
+            if (bb < RT) {
+                const float *Nb = Nm + (wave * C + bb * 16) * LDF + bb * 16;
+                float *Tb = Tf + (wave * C + bb * 16) * LDF + bb * 16;
+                float x[16];
+#pragma unroll
+                for (int t = 0; t < 16; ++t) {
+                    float s = (t == j) ? 1.f : 0.f;
+#pragma unroll
+                    for (int u = 0; u < t; ++u)
+                        s -= Nb[t * LDF + u] * x[u];
+                    x[t] = s;
+                }
+#pragma unroll
+                for (int t = 0; t < 16; ++t)
+                    Tb[t * LDF + j] = x[t];
+            }
         }
         __syncthreads();
-        if (wave < nh && lane < C) {
-            const int h = hq * group + hb + wave;
-            float x[C];
-            solve_unit_lower_column<C>(Nm + wave * C * LDF, LDF, lane, x);
-            E *out = tmat + ((size_t)e * hv + h) * C * C + lane;
+
+        // Blocks below the diagonal, one block-diagonal (distance d) at a time.
+        for (int d = 1; d < RT; ++d) {
+            const int nblk = nh * (RT - d);
+            // Y = sum_m N_{b,m} T_{m,b'}   (b = b' + d), one wave per block
+            for (int base = 0; base < nblk; base += kWaves) {
+                const int blk = base + wave;
+                if (blk < nblk) {
+                    const int hh = blk / (RT - d), bp = blk % (RT - d), bq = bp + d;
+                    const float *Nh = Nm + hh * C * LDF;
+                    const float *Th = Tf + hh * C * LDF;
+                    f32x4 acc = zero4();
+                    for (int m = bp; m < bq; ++m) {
 #pragma unroll
-            for (int t = 0; t < C; ++t)
-                out[t * C] = (E)x[t];
+                        for (int k4 = 0; k4 < 16; k4 += 4) {
+                            const float av = Nh[(bq * 16 + (lane & 15)) * LDF + m * 16 + k4 + (lane >> 4)];
+                            const float bv = Th[(m * 16 + k4 + (lane >> 4)) * LDF + bp * 16 + (lane & 15)];
+                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Yw[wave][tile_row(lane, i)][tile_col(lane)] = acc[i];
+                }
+                __syncthreads();
+                if (blk < nblk) {
+                    const int hh = blk / (RT - d), bp = blk % (RT - d), bq = bp + d;
+                    float *Th = Tf + hh * C * LDF;
+                    f32x4 acc = zero4();
+#pragma unroll
+                    for (int k4 = 0; k4 < 16; k4 += 4) {
+                        const float av = Th[(bq * 16 + (lane & 15)) * LDF + bq * 16 + k4 + (lane >> 4)];
+                        const float bv = Yw[wave][k4 + (lane >> 4)][lane & 15];
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Th[(bq * 16 + tile_row(lane, i)) * LDF + bp * 16 + tile_col(lane)] = -acc[i];
+                }
+                __syncthreads();
+            }
+        }
+
+        // T to global, zero above the diagonal blocks.
+        for (int idx = tid; idx < nh * C * C / VN; idx += kThreads) {
+            const int hh = idx / (C * C / VN);
+            const int rem = (idx - hh * (C * C / VN)) * VN;
+            const int t = rem / C, j0 = rem - (rem / C) * C;
+            const int h = hq * group + hb + hh;
+            V16 tv;
+#pragma unroll
+            for (int e = 0; e < VN; ++e) {
+                const int j = j0 + e;
+                tv[e] = (E)(((j >> 4) <= (t >> 4)) ? Tf[(hh * C + t) * LDF + j] : 0.f);
+            }
+            *reinterpret_cast<V16 *>(tmat + (slot * hv + h) * C * C + rem) = tv;
         }
         __syncthreads();
     }
@@ -238,41 +366,118 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
 // accumulators of the S-update tiles for the whole sequence; a bf16 (or
 // fp32) copy transposed in LDS feeds the [Q;K] S product of the next chunk.
 //
+// The S update contracts over the chunk index, so it needs K^T as a matrix
+// operand: with bf16 it is read from the row-major K tile with the LDS
+// transpose read (ds_read_b64_tr_b16: in every group of 16 lanes, input lane
+// 4e + q reads 4 consecutive elements of row e, and output lane j receives
+// column j of the 4 rows); with fp32 a transposed copy of K is kept in LDS.
+//
 // Block index -> work: the 8 XCDs take workgroups round-robin, so the dv
 // slices of one (sequence, head) are placed on one XCD (shared Q, K, T, A
 // reads then hit the same L2).
 // ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// LDS row stride (elements) of the key-dimension tiles.  In dwords it is a multiple
+// of 4 with an odd quotient, so 16 rows read with 16-byte accesses hit 16 distinct
+// bank groups; for bf16 it is also 12, 28, 36 or 52 modulo 64, so the transpose
+// reads (4 consecutive rows, 32 bytes of each) touch disjoint banks.
+template <typename E>
+constexpr int key_row_stride(int dk)
+{
+    const int dw = dk * (int)sizeof(E) / 4;
+    for (int s = (dw + 3) / 4 * 4;; s += 4) {
+        if ((s / 4) % 2 == 1) {
+            if (sizeof(E) == 4)
+                return s;
+            const int m = s % 64;
+            if (m == 12 || m == 28 || m == 36 || m == 52)
+                return s * 4 / (int)sizeof(E);
+        }
+    }
+}
+
+template <typename E, int C, int DK>
+struct KtOperand;
+
+// bf16: fragments of K^T straight from the row-major K tile (LDS transpose read).
+template <int C, int DK>
+struct KtOperand<bf16, C, DK> {
+    static constexpr bool kNeedsCopy = false;
+    typedef typename MmaFor<bf16, C>::type M;
+    // A-fragment of K^T for output rows m0..m0+15 (key index), contraction
+    // slice starting at chunk row k0.
+    __device__ static inline typename M::frag load(const bf16 *Ks, int ldk, const bf16 *, int, int m0, int k0,
+                                                   int lane)
+    {
+        const int g = lane >> 4, s = lane & 15, e = s >> 2, qd = s & 3;
+        if constexpr (M::kPerLane == 8) {
+            const bf16 *p0 = Ks + (k0 + 8 * g + e) * ldk + m0 + 4 * qd;
+            const bf16 *p1 = p0 + 4 * ldk;
+            s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(p0));
+            s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(p1));
+            typedef short s16x8 __attribute__((ext_vector_type(8)));
+            s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8, v);
+        } else {
+            const bf16 *p0 = Ks + (k0 + 4 * g + e) * ldk + m0 + 4 * qd;
+            s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(p0));
+            return __builtin_bit_cast(bf16x4, lo);
+        }
+    }
+};
+
+// fp32: a transposed copy Kt[key][chunk row] is written when the chunk is staged.
+template <int C, int DK>
+struct KtOperand<float, C, DK> {
+    static constexpr bool kNeedsCopy = true;
+    typedef Mma<float> M;
+    __device__ static inline float load(const float *, int, const float *Kt, int ldc, int m0, int k0, int lane)
+    {
+        return Kt[(m0 + (lane & 15)) * ldc + k0 + (lane >> 4)];
+    }
+};
+
 template <typename E, int C, int DK, int DVS>
 __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
-    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_start, int32_t num_seqs, int64_t total_tokens, int32_t hqk,
-    int32_t hv, int32_t dv, const E *__restrict__ tmat, const E *__restrict__ amat,
-    const float *initial_state, float *final_state, E *__restrict__ o, float scale)
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v, const int32_t *__restrict__ cu,
+    SlotMap map, int32_t num_seqs, int64_t total_tokens, int32_t hqk, int32_t hv, int32_t dv,
+    const E *__restrict__ tmat,
+    const E *__restrict__ amat, const float *__restrict__ dec, const float *state_in, float *state_out,
+    E *__restrict__ o, float scale)
 {
     constexpr int PAD = LdsPad<E>::value;
-    constexpr int LDK = DK + PAD;
+    constexpr int LDK = key_row_stride<E>(DK);
     constexpr int LDC = C + PAD;
+    constexpr int LDV = DVS + PAD;
     constexpr int RT = C / 16, CT = DVS / 16, SR = DK / 16;
-    constexpr int NO = (RT * CT + kWaves - 1) / kWaves;
-    constexpr int NS = (SR * CT + kWaves - 1) / kWaves;
+    constexpr int SR_PER = (SR + kWaves - 1) / kWaves;
     constexpr int VN = Vec16<E>::n;
     typedef typename Vec16<E>::type V16;
+    typedef KtOperand<E, C, DK> KT;
+    typedef typename MmaFor<E, C>::type MC;
+    typedef typename MmaFor<E, DK>::type MK;
     constexpr int QK_VECS = C * DK / VN, QK_PER = (QK_VECS + kThreads - 1) / kThreads;
     constexpr int CC_VECS = C * C / VN, CC_PER = (CC_VECS + kThreads - 1) / kThreads;
     constexpr int V_VECS = C * DVS / VN, V_PER = (V_VECS + kThreads - 1) / kThreads;
+    constexpr int KT_ROWS = KT::kNeedsCopy ? DK : 1;
     static_assert(C <= kWave, "one lane per token of a chunk");
+    static_assert(DVS % 16 == 0 && DK % 16 == 0 && C % 16 == 0, "16x16 tiles");
 
     __shared__ __attribute__((aligned(16))) E Ks[C * LDK];
     __shared__ __attribute__((aligned(16))) E Qs[C * LDK];
-    __shared__ __attribute__((aligned(16))) E Kt[DK * LDC];
+    __shared__ __attribute__((aligned(16))) E Kt[KT_ROWS * LDC];
     __shared__ __attribute__((aligned(16))) E Ts[C * LDC];
     __shared__ __attribute__((aligned(16))) E As[C * LDC];
-    __shared__ __attribute__((aligned(16))) E Vs[C * DVS];
+    __shared__ __attribute__((aligned(16))) E Vs[C * LDV];
     __shared__ __attribute__((aligned(16))) E Xt[DVS * LDC];
     __shared__ __attribute__((aligned(16))) E Dt[DVS * LDC];
     __shared__ __attribute__((aligned(16))) E LDt[DVS * LDC];
     __shared__ __attribute__((aligned(16))) E St[DVS * LDK];
+    __shared__ __attribute__((aligned(16))) E Os[C * LDV];
     __shared__ float Gam[C], Lam[C], Bet[C];
     __shared__ float GamL;
 
@@ -289,93 +494,116 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
     const int hq = h / (hv / hqk);
     int64_t a, b;
     seq_range(cu, n, total_tokens, a, b);
-    const int32_t cs0 = chunk_start[n];
-    const int nchunks = chunk_start[n + 1] - cs0;
+    const int nch = seq_chunks(map, cu, n, total_tokens, C);
+    const int c_begin = map.seg_first;
+    const int c_end = min(nch, map.seg_first + map.seg_len);
     const size_t state_base = (size_t)(n * hv + h) * DK * dv + (size_t)s * DVS;
-
-    // ---- state slice into accumulators, bf16 copy into St ----
-    f32x4 sacc[NS];
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-        const int st = wave + u * kWaves;
-        sacc[u] = zero4();
-        if (st < SR * CT) {
-            const int sr = st / CT, ct = st % CT;
-            if (initial_state) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sacc[u][i] = initial_state[state_base + (size_t)(sr * 16 + tile_row(lane, i)) * dv +
-                                               ct * 16 + tile_col(lane)];
+    if (c_begin >= c_end) {
+        // No chunk of this sequence in this launch.  The first launch still owes the
+        // sequence its final state (initial state passed through, or zeros).
+        if (c_begin == 0 && state_in != state_out) {
+            for (int i = tid; i < DK * DVS; i += kThreads) {
+                const size_t off = state_base + (size_t)(i / DVS) * dv + (i % DVS);
+                state_out[off] = state_in ? state_in[off] : 0.f;
             }
-            store4(St + (ct * 16 + tile_col(lane)) * LDK + sr * 16 + tile_row(lane, 0), sacc[u][0],
-                   sacc[u][1], sacc[u][2], sacc[u][3]);
+        }
+        return;
+    }
+
+    // ---- state slice into accumulators (wave w owns key-row tiles w, w+4, ...) ----
+    f32x4 sacc[SR_PER][CT];
+#pragma unroll
+    for (int u = 0; u < SR_PER; ++u) {
+        const int sr = wave + u * kWaves;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            sacc[u][ct] = zero4();
+            if (sr < SR) {
+                if (state_in) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        sacc[u][ct][i] = state_in[state_base + (size_t)(sr * 16 + tile_row(lane, i)) * dv +
+                                                  ct * 16 + tile_col(lane)];
+                }
+                store4(St + (ct * 16 + tile_col(lane)) * LDK + sr * 16 + tile_row(lane, 0), sacc[u][ct][0],
+                       sacc[u][ct][1], sacc[u][ct][2], sacc[u][ct][3]);
+            }
         }
     }
 
     // ---- chunk inputs: global -> registers (prefetch) -> LDS ----
-    V16 rq[QK_PER], rk[QK_PER], rtm[CC_PER], ram[CC_PER], rv[V_PER];
-    float rg = 0.f, rb = 0.f;
-    int64_t pre_t0 = a;
-    int pre_len = 0;
+    // Narrow slices keep two register sets in flight, so the loads of a chunk get two
+    // steps to arrive; wide slices keep one (register budget).  Rows past the end of
+    // the sequence are loaded from its last row and replaced by zeros (no branches).
+    constexpr bool kTwoSets = DVS <= 32;
+    struct Staged {
+        V16 q[QK_PER], k[QK_PER], t[CC_PER], a[CC_PER], v[V_PER];
+        float gam, lam, bet;
+        int64_t t0;
+        int len;
+    };
+    Staged R0, R1;
+    const V16 zv = (V16)(E)0.f;
 
-    auto load_chunk = [&](int c) {
+    auto load_chunk = [&](Staged &R, int c) {
         const int64_t t0 = a + (int64_t)c * C;
         const int len = (int)min<int64_t>(C, b - t0);
-        pre_t0 = t0;
-        pre_len = len;
-        const size_t ent = ((size_t)(cs0 + c) * hv + h) * C * C;
+        R.t0 = t0;
+        R.len = len;
+        const size_t slot = slot_of(map, n, c);
+        const size_t ent = (slot * hv + h) * C * C;
 #pragma unroll
         for (int u = 0; u < QK_PER; ++u) {
             const int i = tid + u * kThreads;
-            rq[u] = (V16)(E)0.f;
-            rk[u] = (V16)(E)0.f;
             if (i < QK_VECS) {
                 const int r = i / (DK / VN), c0 = (i % (DK / VN)) * VN;
-                if (r < len) {
-                    const size_t off = ((size_t)(t0 + r) * hqk + hq) * DK + c0;
-                    rq[u] = *reinterpret_cast<const V16 *>(q + off);
-                    rk[u] = *reinterpret_cast<const V16 *>(k + off);
-                }
+                const size_t off = ((size_t)(t0 + min(r, len - 1)) * hqk + hq) * DK + c0;
+                // raw rows here; rows past the end are zeroed when staged, so that the
+                // loads stay in flight until then
+                R.q[u] = *reinterpret_cast<const V16 *>(q + off);
+                R.k[u] = *reinterpret_cast<const V16 *>(k + off);
             }
         }
 #pragma unroll
         for (int u = 0; u < CC_PER; ++u) {
             const int i = tid + u * kThreads;
             if (i < CC_VECS) {
-                rtm[u] = *reinterpret_cast<const V16 *>(tmat + ent + (size_t)i * VN);
-                ram[u] = *reinterpret_cast<const V16 *>(amat + ent + (size_t)i * VN);
+                R.t[u] = *reinterpret_cast<const V16 *>(tmat + ent + (size_t)i * VN);
+                R.a[u] = *reinterpret_cast<const V16 *>(amat + ent + (size_t)i * VN);
             }
         }
 #pragma unroll
         for (int u = 0; u < V_PER; ++u) {
             const int i = tid + u * kThreads;
-            rv[u] = (V16)(E)0.f;
             if (i < V_VECS) {
                 const int r = i / (DVS / VN), c0 = (i % (DVS / VN)) * VN;
-                if (r < len)
-                    rv[u] = *reinterpret_cast<const V16 *>(v + ((size_t)(t0 + r) * hv + h) * dv +
-                                                           (size_t)s * DVS + c0);
+                R.v[u] = *reinterpret_cast<const V16 *>(v + ((size_t)(t0 + min(r, len - 1)) * hv + h) * dv +
+                                                        (size_t)s * DVS + c0);
             }
         }
-        rg = 0.f;
-        rb = 0.f;
-        if (wave == 0 && lane < len) {
-            rg = g[(size_t)(t0 + lane) * hv + h];
-            rb = beta[(size_t)(t0 + lane) * hv + h];
+        if (wave == 0 && lane < C) {
+            const float *rec = dec + (slot * hv + h) * 3 * C;
+            R.gam = rec[lane];
+            R.lam = rec[C + lane];
+            R.bet = rec[2 * C + lane];
         }
     };
 
-    auto store_chunk = [&]() {
+    auto store_chunk = [&](const Staged &R) {
 #pragma unroll
         for (int u = 0; u < QK_PER; ++u) {
             const int i = tid + u * kThreads;
             if (i < QK_VECS) {
                 const int r = i / (DK / VN), c0 = (i % (DK / VN)) * VN;
-                *reinterpret_cast<V16 *>(Qs + r * LDK + c0) = rq[u];
-                *reinterpret_cast<V16 *>(Ks + r * LDK + c0) = rk[u];
+                const V16 qv = r < R.len ? R.q[u] : zv;
+                const V16 kv = r < R.len ? R.k[u] : zv;
+                *reinterpret_cast<V16 *>(Qs + r * LDK + c0) = qv;
+                *reinterpret_cast<V16 *>(Ks + r * LDK + c0) = kv;
+                if constexpr (KT::kNeedsCopy) {
 #pragma unroll
-                for (int j = 0; j < VN; ++j)
-                    Kt[(c0 + j) * LDC + r] = rk[u][j];
+                    for (int j = 0; j < VN; ++j)
+                        Kt[(c0 + j) * LDC + r] = kv[j];
+                }
             }
         }
 #pragma unroll
@@ -383,125 +611,219 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
             const int i = tid + u * kThreads;
             if (i < CC_VECS) {
                 const int r = (i * VN) / C, c0 = (i * VN) % C;
-                *reinterpret_cast<V16 *>(Ts + r * LDC + c0) = rtm[u];
-                *reinterpret_cast<V16 *>(As + r * LDC + c0) = ram[u];
+                *reinterpret_cast<V16 *>(Ts + r * LDC + c0) = R.t[u];
+                *reinterpret_cast<V16 *>(As + r * LDC + c0) = R.a[u];
             }
         }
 #pragma unroll
         for (int u = 0; u < V_PER; ++u) {
             const int i = tid + u * kThreads;
-            if (i < V_VECS)
-                *reinterpret_cast<V16 *>(Vs + i * VN) = rv[u];
-        }
-        if (wave == 0) {
-            const float G = wave_inclusive_sum(rg, lane);   // lanes >= len add 0
-            const float Glast = __shfl(G, kWave - 1, kWave);
-            if (lane < C) {
-                Gam[lane] = expf(G);
-                Lam[lane] = expf(Glast - G);
-                Bet[lane] = rb;
+            if (i < V_VECS) {
+                const int r = i / (DVS / VN), c0 = (i % (DVS / VN)) * VN;
+                *reinterpret_cast<V16 *>(Vs + r * LDV + c0) = r < R.len ? R.v[u] : zv;
             }
-            if (lane == 0)
-                GamL = expf(Glast);
+        }
+        if (wave == 0 && lane < C) {
+            Gam[lane] = R.gam;
+            Lam[lane] = R.lam;
+            Bet[lane] = R.bet;
+            if (lane == C - 1)
+                GamL = R.gam;   // exp(G_last)
         }
     };
 
-    if (nchunks > 0) {
-        load_chunk(0);
-        store_chunk();
-    }
-    __syncthreads();
-
-    for (int c = 0; c < nchunks; ++c) {
-        const int64_t t0 = pre_t0;
-        const int len = pre_len;
-        if (c + 1 < nchunks)
-            load_chunk(c + 1);
-
-        // P1: Q S and K S; X = diag(beta)(V - diag(exp G) K S) -> Xt (transposed)
-        f32x4 oacc[NO];
+    // One chunk step on the chunk staged in LDS; ends with its outputs written.
+    // prefetch(): issues the global loads of a later chunk; called once the products
+    // of P1 are under way so that the loads do not delay them.
+    auto step = [&](int64_t t0, int len, auto &&prefetch) {
+        // P1: Q S and K S for row tile rt (all column tiles); X = diag(beta)(V - diag(exp G) K S)
+        //     goes to Xt (transposed); diag(exp G) Q S stays in oacc for P3.
+        constexpr int RT_PER = (RT + kWaves - 1) / kWaves;
+        f32x4 oacc[RT_PER][CT];
+        f32x4 kacc[RT_PER][CT];
 #pragma unroll
-        for (int u = 0; u < NO; ++u) {
-            const int it = wave + u * kWaves;
-            oacc[u] = zero4();
-            if (it < RT * CT) {
-                const int rt = it / CT, ct = it % CT;
-                const f32x4 qs = mma_tile<E, DK>(zero4(), Qs + rt * 16 * LDK, LDK, St + ct * 16 * LDK, LDK, lane);
-                const f32x4 ks = mma_tile<E, DK>(zero4(), Ks + rt * 16 * LDK, LDK, St + ct * 16 * LDK, LDK, lane);
-                const int col = ct * 16 + tile_col(lane);
-                float x[4];
+        for (int u = 0; u < RT_PER; ++u) {
+            const int rt = wave + u * kWaves;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = rt * 16 + tile_row(lane, i);
-                    x[i] = Bet[r] * (to_f32(Vs[r * DVS + col]) - Gam[r] * ks[i]);
-                    oacc[u][i] = Gam[r] * qs[i];
+            for (int ct = 0; ct < CT; ++ct) {
+                oacc[u][ct] = zero4();
+                kacc[u][ct] = zero4();
+            }
+            if (rt < RT) {
+                const int r = lane & 15, kk = (lane >> 4) * MK::kPerLane;
+#pragma unroll
+                for (int k0 = 0; k0 < DK; k0 += MK::kStep) {
+                    const typename MK::frag aq = MK::load(Qs + (rt * 16 + r) * LDK + k0 + kk);
+                    const typename MK::frag ak = MK::load(Ks + (rt * 16 + r) * LDK + k0 + kk);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) {
+                        const typename MK::frag bs = MK::load(St + (ct * 16 + r) * LDK + k0 + kk);
+                        oacc[u][ct] = MK::mma(aq, bs, oacc[u][ct]);
+                        kacc[u][ct] = MK::mma(ak, bs, kacc[u][ct]);
+                    }
                 }
-                store4(Xt + col * LDC + rt * 16 + tile_row(lane, 0), x[0], x[1], x[2], x[3]);
+            }
+        }
+        prefetch();
+#pragma unroll
+        for (int u = 0; u < RT_PER; ++u) {
+            const int rt = wave + u * kWaves;
+            if (rt < RT) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const int col = ct * 16 + tile_col(lane);
+                    float x[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int rr = rt * 16 + tile_row(lane, i);
+                        x[i] = Bet[rr] * (to_f32(Vs[rr * LDV + col]) - Gam[rr] * kacc[u][ct][i]);
+                        oacc[u][ct][i] *= Gam[rr];
+                    }
+                    store4(Xt + col * LDC + rt * 16 + tile_row(lane, 0), x[0], x[1], x[2], x[3]);
+                }
             }
         }
         __syncthreads();
 
         // P2: D = T X -> Dt and (diag(lambda) D) -> LDt, both transposed
 #pragma unroll
-        for (int u = 0; u < NO; ++u) {
-            const int it = wave + u * kWaves;
-            if (it < RT * CT) {
-                const int rt = it / CT, ct = it % CT;
-                const f32x4 d = mma_tile<E, C>(zero4(), Ts + rt * 16 * LDC, LDC, Xt + ct * 16 * LDC, LDC, lane);
-                const int col = ct * 16 + tile_col(lane);
+        for (int u = 0; u < RT_PER; ++u) {
+            const int rt = wave + u * kWaves;
+            if (rt < RT) {
+                f32x4 dacc[CT];
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    dacc[ct] = zero4();
+                const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
+#pragma unroll
+                for (int k0 = 0; k0 < C; k0 += MC::kStep) {
+                    const typename MC::frag at = MC::load(Ts + (rt * 16 + r) * LDC + k0 + kk);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+                        dacc[ct] = MC::mma(at, MC::load(Xt + (ct * 16 + r) * LDC + k0 + kk), dacc[ct]);
+                }
                 const int r0 = rt * 16 + tile_row(lane, 0);
-                store4(Dt + col * LDC + r0, d[0], d[1], d[2], d[3]);
-                store4(LDt + col * LDC + r0, Lam[r0] * d[0], Lam[r0 + 1] * d[1], Lam[r0 + 2] * d[2],
-                       Lam[r0 + 3] * d[3]);
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    const int col = ct * 16 + tile_col(lane);
+                    store4(Dt + col * LDC + r0, dacc[ct][0], dacc[ct][1], dacc[ct][2], dacc[ct][3]);
+                    store4(LDt + col * LDC + r0, Lam[r0] * dacc[ct][0], Lam[r0 + 1] * dacc[ct][1],
+                           Lam[r0 + 2] * dacc[ct][2], Lam[r0 + 3] * dacc[ct][3]);
+                }
             }
         }
         __syncthreads();
 
-        // P3: O = diag(exp G) Q S + A D, scaled, to global
+        // P3: O = diag(exp G) Q S + A D, scaled, staged in Os
 #pragma unroll
-        for (int u = 0; u < NO; ++u) {
-            const int it = wave + u * kWaves;
-            if (it < RT * CT) {
-                const int rt = it / CT, ct = it % CT;
-                oacc[u] = mma_tile<E, C>(oacc[u], As + rt * 16 * LDC, LDC, Dt + ct * 16 * LDC, LDC, lane);
-                const int col = s * DVS + ct * 16 + tile_col(lane);
+        for (int u = 0; u < RT_PER; ++u) {
+            const int rt = wave + u * kWaves;
+            if (rt < RT) {
+                const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = rt * 16 + tile_row(lane, i);
-                    if (r < len)
-                        o[((size_t)(t0 + r) * hv + h) * dv + col] = (E)(scale * oacc[u][i]);
+                for (int k0 = 0; k0 < C; k0 += MC::kStep) {
+                    const typename MC::frag aa = MC::load(As + (rt * 16 + r) * LDC + k0 + kk);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+                        oacc[u][ct] = MC::mma(aa, MC::load(Dt + (ct * 16 + r) * LDC + k0 + kk), oacc[u][ct]);
                 }
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        Os[(rt * 16 + tile_row(lane, i)) * LDV + ct * 16 + tile_col(lane)] =
+                            (E)(scale * oacc[u][ct][i]);
             }
         }
         // P4: S <- exp(G_last) S + K^T diag(lambda) D; refresh the transposed copy
+        const float gl = GamL;
 #pragma unroll
-        for (int u = 0; u < NS; ++u) {
-            const int st = wave + u * kWaves;
-            if (st < SR * CT) {
-                const int sr = st / CT, ct = st % CT;
-                f32x4 acc = sacc[u] * GamL;
-                acc = mma_tile<E, C>(acc, Kt + sr * 16 * LDC, LDC, LDt + ct * 16 * LDC, LDC, lane);
-                sacc[u] = acc;
-                store4(St + (ct * 16 + tile_col(lane)) * LDK + sr * 16 + tile_row(lane, 0), acc[0], acc[1],
-                       acc[2], acc[3]);
+        for (int u = 0; u < SR_PER; ++u) {
+            const int sr = wave + u * kWaves;
+            if (sr < SR) {
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    sacc[u][ct] = sacc[u][ct] * gl;
+                const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
+#pragma unroll
+                for (int k0 = 0; k0 < C; k0 += MC::kStep) {
+                    const typename MC::frag akt = KT::load(Ks, LDK, Kt, LDC, sr * 16, k0, lane);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct)
+                        sacc[u][ct] = MC::mma(akt, MC::load(LDt + (ct * 16 + r) * LDC + k0 + kk), sacc[u][ct]);
+                }
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    store4(St + (ct * 16 + tile_col(lane)) * LDK + sr * 16 + tile_row(lane, 0), sacc[u][ct][0],
+                           sacc[u][ct][1], sacc[u][ct][2], sacc[u][ct][3]);
             }
         }
         __syncthreads();
-        if (c + 1 < nchunks)
-            store_chunk();
-        __syncthreads();
+
+        // Outputs of this chunk: coalesced 16-byte rows to global.
+        constexpr int O_VECS = C * DVS / VN;
+        for (int i = tid; i < O_VECS; i += kThreads) {
+            const int r = i / (DVS / VN), c0 = (i % (DVS / VN)) * VN;
+            if (r < len)
+                *reinterpret_cast<V16 *>(o + ((size_t)(t0 + r) * hv + h) * dv + (size_t)s * DVS + c0) =
+                    *reinterpret_cast<const V16 *>(Os + r * LDV + c0);
+        }
+    };
+
+    load_chunk(R0, c_begin);
+    if (kTwoSets && c_begin + 1 < c_end)
+        load_chunk(R1, c_begin + 1);
+    store_chunk(R0);
+    __syncthreads();
+
+    if constexpr (kTwoSets) {
+        // chunk c is in LDS and R1 holds chunk c + 1 at the top of every iteration
+        for (int c = c_begin; c < c_end; c += 2) {
+            const int64_t t0a = R0.t0;
+            const int lena = R0.len;
+            step(t0a, lena, [&] {
+                if (c + 2 < c_end)
+                    load_chunk(R0, c + 2);
+            });
+            if (c + 1 >= c_end)
+                break;
+            store_chunk(R1);
+            __syncthreads();
+            const int64_t t0b = R1.t0;
+            const int lenb = R1.len;
+            step(t0b, lenb, [&] {
+                if (c + 3 < c_end)
+                    load_chunk(R1, c + 3);
+            });
+            if (c + 2 < c_end)
+                store_chunk(R0);
+            __syncthreads();
+        }
+    } else {
+        for (int c = c_begin; c < c_end; ++c) {
+            const int64_t t0 = R0.t0;
+            const int len = R0.len;
+            step(t0, len, [&] {
+                if (c + 1 < c_end)
+                    load_chunk(R0, c + 1);
+            });
+            if (c + 1 < c_end)
+                store_chunk(R0);
+            __syncthreads();
+        }
     }
 
     // ---- final state ----
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-        const int st = wave + u * kWaves;
-        if (st < SR * CT) {
-            const int sr = st / CT, ct = st % CT;
+    for (int u = 0; u < SR_PER; ++u) {
+        const int sr = wave + u * kWaves;
+        if (sr < SR) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                final_state[state_base + (size_t)(sr * 16 + tile_row(lane, i)) * dv + ct * 16 + tile_col(lane)] =
-                    sacc[u][i];
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    state_out[state_base + (size_t)(sr * 16 + tile_row(lane, i)) * dv + ct * 16 +
+                              tile_col(lane)] = sacc[u][ct][i];
         }
     }
 }
@@ -509,38 +831,85 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
 // ---------------------------------------------------------------------------
 // Launch.
 // ---------------------------------------------------------------------------
-template <typename E, int C, int DK>
-static hipError_t launch_prefill_t(const PrefillArgs &p)
-{
-    constexpr int DVS = 16;
-    int32_t *chunk_start = reinterpret_cast<int32_t *>(p.workspace);
-    E *tmat = reinterpret_cast<E *>(static_cast<char *>(p.workspace) + p.table_bytes);
-    E *amat = tmat + (size_t)p.max_chunks * p.hv * C * C;
-    hipStream_t st = static_cast<hipStream_t>(p.stream);
 
-    prof_begin(PROF_CHUNK_TABLE, st);
-    hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(kThreads), 0, st, p.cu_seqlens,
-                       p.num_seqs, p.total_tokens, (int32_t)C, p.max_chunks, chunk_start);
-    prof_end(st);
-    if (p.max_chunks > 0) {
-        prof_begin(PROF_PREP, st);
-        hipLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), dim3(p.max_chunks, p.hqk), dim3(kThreads), 0, st,
-                           static_cast<const E *>(p.q), static_cast<const E *>(p.k), p.g, p.beta,
-                           p.cu_seqlens, chunk_start, p.num_seqs, p.total_tokens, p.hqk, p.hv, tmat, amat);
-        prof_end(st);
-    }
+// Widest dv slice that still gives the chip at least two workgroups per CU.
+static int pick_dvs(int64_t pairs, int dv, int widest)
+{
+    const int64_t want = 512;
+    if (widest >= 64 && dv % 64 == 0 && pairs * (dv / 64) >= want)
+        return 64;
+    if (dv % 32 == 0 && pairs * (dv / 32) >= want)
+        return 32;
+    return 16;
+}
+
+template <typename E, int C, int DK, int DVS>
+static void launch_scan(const PrefillArgs &p, const SlotMap &map, const E *tmat, const E *amat, const float *dec,
+                        const float *sin, float *sout, hipStream_t st)
+{
     const int nv = p.dv / DVS;
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
     const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
-    if (blocks > 0) {
-        prof_begin(PROF_SCAN, st);
-        hipLaunchKernelGGL((gdn_chunk_scan_kernel<E, C, DK, DVS>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
-                           static_cast<const E *>(p.q), static_cast<const E *>(p.k),
-                           static_cast<const E *>(p.v), p.g, p.beta, p.cu_seqlens, chunk_start, p.num_seqs,
-                           p.total_tokens, p.hqk, p.hv, p.dv, tmat, amat, p.initial_state, p.final_state,
-                           static_cast<E *>(p.o), p.scale);
+    prof_begin(PROF_SCAN, st);
+    hipLaunchKernelGGL((gdn_chunk_scan_kernel<E, C, DK, DVS>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
+                       static_cast<const E *>(p.q), static_cast<const E *>(p.k), static_cast<const E *>(p.v),
+                       p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv, p.dv, tmat, amat, dec, sin, sout,
+                       static_cast<E *>(p.o), p.scale);
+    prof_end(st);
+}
+
+template <typename E, int C, int DK>
+static hipError_t launch_prefill_t(const PrefillArgs &p)
+{
+    hipStream_t st = static_cast<hipStream_t>(p.stream);
+    // workspace: [chunk table | T matrices | A matrices | decay records]
+    int32_t *chunk_start = reinterpret_cast<int32_t *>(p.workspace);
+    E *tmat = reinterpret_cast<E *>(static_cast<char *>(p.workspace) + p.table_bytes);
+    E *amat = tmat + (size_t)p.max_chunks * p.hv * C * C;
+    float *dec = reinterpret_cast<float *>(amat + (size_t)p.max_chunks * p.hv * C * C);
+    const int64_t pairs = (int64_t)p.num_seqs * p.hv;
+    // 64-column slices only where their LDS footprint fits (bf16 operands).
+    constexpr bool kWide = DK >= 64 && sizeof(E) == 2;
+    const int dvs = pick_dvs(pairs, p.dv, kWide ? 64 : 32);
+
+    auto scan = [&](const SlotMap &map, const float *sin, float *sout) {
+        if constexpr (kWide) {
+            if (dvs == 64) {
+                launch_scan<E, C, DK, 64>(p, map, tmat, amat, dec, sin, sout, st);
+                return;
+            }
+        }
+        if (dvs == 32)
+            launch_scan<E, C, DK, 32>(p, map, tmat, amat, dec, sin, sout, st);
+        else
+            launch_scan<E, C, DK, 16>(p, map, tmat, amat, dec, sin, sout, st);
+    };
+    auto prep = [&](const SlotMap &map, int64_t slots) {
+        prof_begin(PROF_PREP, st);
+        hipLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), dim3((unsigned)slots, p.hqk), dim3(kThreads), 0, st,
+                           static_cast<const E *>(p.q), static_cast<const E *>(p.k), p.g, p.beta, p.cu_seqlens, map,
+                           p.num_seqs, p.total_tokens, p.hqk, p.hv, tmat, amat, dec);
         prof_end(st);
+    };
+
+    if (p.seg_len > 0) {
+        // Segment mode: local chunks [s0, s0 + seg_len) of every sequence per step.
+        for (int32_t s0 = 0; s0 < p.max_seq_chunks; s0 += p.seg_len) {
+            const SlotMap map{nullptr, s0, p.seg_len};
+            prep(map, (int64_t)p.num_seqs * p.seg_len);
+            scan(map, s0 == 0 ? p.initial_state : p.final_state, p.final_state);
+        }
+        return hipGetLastError();
     }
+
+    prof_begin(PROF_CHUNK_TABLE, st);
+    hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(kThreads), 0, st, p.cu_seqlens, p.num_seqs,
+                       p.total_tokens, (int32_t)C, p.max_chunks, chunk_start);
+    prof_end(st);
+    const SlotMap map{chunk_start, 0, INT32_MAX};
+    if (p.max_chunks > 0)
+        prep(map, p.max_chunks);
+    scan(map, p.initial_state, p.final_state);
     return hipGetLastError();
 }
 

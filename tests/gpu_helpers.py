@@ -40,14 +40,17 @@ def to_dev(inp, device="cuda"):
     return out
 
 
-def gpu_prefill(inp, chunk, scale=None, initial_state="from_inputs", inplace=False):
+def gpu_prefill(inp, chunk, scale=None, initial_state="from_inputs", inplace=False, host_offsets=True):
+    """Run gdn_prefill_chunked.  host_offsets=True hands the library a host copy of cu_seqlens
+    (segmented launch); False passes device offsets only (single launch over a chunk table)."""
     import gated_deltanet_scan_amd as gdn
     d = to_dev(inp)
     s0 = d["initial_state"] if initial_state == "from_inputs" else initial_state
     fs = None
     if inplace:
         fs = s0
-    o, S = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], s0,
+    cu = inp["cu_seqlens"].cpu() if host_offsets else d["cu_seqlens"]
+    o, S = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, s0,
                                scale=scale, chunk=chunk, final_state=fs)
     torch.cuda.synchronize()
     return o, S

@@ -22,10 +22,11 @@ def _case(lengths, hqk, hv, d, io, seed, g_law="uniform", s0_std=0.05, strong=Fa
                          strong_segment=strong)
 
 
-def _run(inp, chunk, io, label, scale=None):
+def _run(inp, chunk, io, label, scale=None, host_offsets=True):
     say(label, "T=%d" % int(inp["cu_seqlens"][-1]), "N=%d" % (len(inp["cu_seqlens"]) - 1),
-        "q", tuple(inp["q"].shape), "v", tuple(inp["v"].shape), "chunk", chunk, io)
-    o, St = gpu_prefill(inp, chunk, scale=scale)
+        "q", tuple(inp["q"].shape), "v", tuple(inp["v"].shape), "chunk", chunk, io,
+        "host offsets" if host_offsets else "device offsets")
+    o, St = gpu_prefill(inp, chunk, scale=scale, host_offsets=host_offsets)
     o_ref, S_ref = oracle_prefill(inp, scale=scale)
     eo, es = check_prefill(o, St, o_ref, S_ref, inp["cu_seqlens"], io, label)
     say(label, "max rel err: o %.3e  S %.3e" % (eo, es))
@@ -42,14 +43,16 @@ def test_prefill_1k_workload():
     _run(S.make_workload_inputs(w), w.chunk, w.io_dtype, "prefill_1k")
 
 
-def test_prefill_32k_workload():
+@pytest.mark.parametrize("host_offsets", [True, False])
+def test_prefill_32k_workload(host_offsets):
     w = S.workload("prefill_32k")
-    _run(S.make_workload_inputs(w), w.chunk, w.io_dtype, "prefill_32k")
+    _run(S.make_workload_inputs(w), w.chunk, w.io_dtype, "prefill_32k", host_offsets=host_offsets)
 
 
-def test_varlen_16_workload():
+@pytest.mark.parametrize("host_offsets", [True, False])
+def test_varlen_16_workload(host_offsets):
     w = S.workload("varlen_16")
-    _run(S.make_workload_inputs(w), w.chunk, w.io_dtype, "varlen_16")
+    _run(S.make_workload_inputs(w), w.chunk, w.io_dtype, "varlen_16", host_offsets=host_offsets)
 
 
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 127, 128, 129])
@@ -58,13 +61,31 @@ def test_lengths_around_the_chunk(T, io, d, chunk):
     _run(_case([T], 1, 2, d, io, seed=100 + T), chunk, io, "len%d_d%d_c%d" % (T, d, chunk))
 
 
+@pytest.mark.parametrize("host_offsets", [True, False])
 @pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("d,chunk", [(32, 16), (64, 16), (32, 64), (64, 64), (128, 64)])
-def test_every_kernel_instance(io, d, chunk):
+def test_every_kernel_instance(io, d, chunk, host_offsets):
     if io == torch.float32 and d > 64:
         pytest.skip("fp32 io is built for dk <= 64")
     lengths = [3 * chunk + 5, chunk, 1, 2 * chunk - 1]
-    _run(_case(lengths, 2, 4, d, io, seed=7 * d + chunk), chunk, io, "inst_d%d_c%d" % (d, chunk))
+    _run(_case(lengths, 2, 4, d, io, seed=7 * d + chunk), chunk, io, "inst_d%d_c%d" % (d, chunk),
+         host_offsets=host_offsets)
+
+
+@pytest.mark.parametrize("nseq", [40, 160])
+def test_wide_slices_many_sequences(nseq):
+    """Enough (sequence, head) pairs that the scan takes 32- and 64-column dv slices."""
+    gen = torch.Generator().manual_seed(nseq)
+    lengths = [int(x) for x in torch.randint(0, 200, (nseq,), generator=gen)]
+    for host_offsets in (True, False):
+        _run(_case(lengths, 2, 4, 128, torch.bfloat16, seed=500 + nseq), 64, torch.bfloat16,
+             "wide_n%d" % nseq, host_offsets=host_offsets)
+
+
+def test_long_sequence_spans_several_segments():
+    """With host offsets the launch is cut into segments of local chunks; 20000 tokens of one
+    sequence with 32 value heads span several of them (state carried in final_state)."""
+    _run(_case([20000, 300], 16, 32, 128, torch.bfloat16, seed=29), 64, torch.bfloat16, "segments")
 
 
 def test_zero_length_sequences_pass_state_through():
