@@ -366,122 +366,164 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
 // accumulators of the S-update tiles for the whole sequence; a bf16 (or
 // fp32) copy transposed in LDS feeds the [Q;K] S product of the next chunk.
 //
+// Chunk inputs (Q, K, T, A, the V slice and the decay record) are copied
+// from global memory straight into one of two LDS stage buffers by the
+// direct-to-LDS loads (lane i of a load lands at base + 16 i), one chunk
+// ahead of the chunk being computed, so no registers or LDS store
+// instructions are spent on staging.  Staged rows are not padded: within a
+// row the 16-byte chunks are permuted (Swz) so that the 16-row operand
+// reads and the 4-row transpose reads hit distinct LDS banks.  Rows past the
+// end of a sequence are loaded from its last row: every term they feed is
+// multiplied by beta = 0, by a zero column of A or by a unit row of T.
+//
 // The S update contracts over the chunk index, so it needs K^T as a matrix
 // operand: with bf16 it is read from the row-major K tile with the LDS
 // transpose read (ds_read_b64_tr_b16: in every group of 16 lanes, input lane
 // 4e + q reads 4 consecutive elements of row e, and output lane j receives
-// column j of the 4 rows); with fp32 a transposed copy of K is kept in LDS.
+// column j of the 4 rows); with fp32 every lane reads its single element.
 //
 // Block index -> work: the 8 XCDs take workgroups round-robin, so the dv
 // slices of one (sequence, head) are placed on one XCD (shared Q, K, T, A
 // reads then hit the same L2).
 // ---------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
 
-// LDS row stride (elements) of the key-dimension tiles.  In dwords it is a multiple
-// of 4 with an odd quotient, so 16 rows read with 16-byte accesses hit 16 distinct
-// bank groups; for bf16 it is also 12, 28, 36 or 52 modulo 64, so the transpose
-// reads (4 consecutive rows, 32 bytes of each) touch disjoint banks.
+// Byte layout of a staged tile with rows of RB bytes: row r holds its 16-byte
+// chunk j at position j ^ perm(r).  perm is injective over 16 consecutive rows
+// of one 256-byte bank line and moves 4 consecutive rows by even amounts, so
+// both read patterns above are conflict-free.
+template <int RB>
+struct Swz {
+    static_assert(RB % 16 == 0 && RB <= 256, "rows of 16..256 bytes");
+    static constexpr int NCH = RB / 16;
+    static constexpr int RPL = 256 / RB;   // rows per 256-byte bank line
+    __device__ static inline int perm(int r)
+    {
+        if constexpr (NCH < 4) {
+            return 0;
+        } else {
+            const int u = r / RPL;
+            return ((u & (NCH / 2 - 1)) << 1) | ((u / (NCH / 2)) & 1);
+        }
+    }
+    __device__ static inline int off(int r, int b) { return r * RB + ((((b >> 4) ^ perm(r)) << 4) | (b & 15)); }
+};
+
+// LDS row stride (elements) of the padded key-dimension tile St.  In dwords it
+// is a multiple of 4 with an odd quotient, so 16 rows read with 16-byte
+// accesses hit 16 distinct bank groups.
 template <typename E>
 constexpr int key_row_stride(int dk)
 {
     const int dw = dk * (int)sizeof(E) / 4;
-    for (int s = (dw + 3) / 4 * 4;; s += 4) {
-        if ((s / 4) % 2 == 1) {
-            if (sizeof(E) == 4)
-                return s;
-            const int m = s % 64;
-            if (m == 12 || m == 28 || m == 36 || m == 52)
-                return s * 4 / (int)sizeof(E);
-        }
-    }
+    for (int s = (dw + 3) / 4 * 4;; s += 4)
+        if ((s / 4) % 2 == 1)
+            return s * 4 / (int)sizeof(E);
 }
 
 template <typename E, int C, int DK>
 struct KtOperand;
 
-// bf16: fragments of K^T straight from the row-major K tile (LDS transpose read).
+// bf16: fragments of K^T straight from the staged K tile (LDS transpose read).
 template <int C, int DK>
 struct KtOperand<bf16, C, DK> {
-    static constexpr bool kNeedsCopy = false;
     typedef typename MmaFor<bf16, C>::type M;
-    // A-fragment of K^T for output rows m0..m0+15 (key index), contraction
-    // slice starting at chunk row k0.
-    __device__ static inline typename M::frag load(const bf16 *Ks, int ldk, const bf16 *, int, int m0, int k0,
-                                                   int lane)
+    typedef Swz<DK * 2> S;
+    // A-fragment of K^T for output rows m0..m0+15 (key index), contraction slice
+    // starting at chunk row k0.
+    __device__ static inline typename M::frag load(const unsigned char *Kb, int m0, int k0, int lane)
     {
         const int g = lane >> 4, s = lane & 15, e = s >> 2, qd = s & 3;
+        const int b = 2 * (m0 + 4 * qd);
         if constexpr (M::kPerLane == 8) {
-            const bf16 *p0 = Ks + (k0 + 8 * g + e) * ldk + m0 + 4 * qd;
-            const bf16 *p1 = p0 + 4 * ldk;
+            const int r0 = k0 + 8 * g + e;
             s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(p0));
+                (__attribute__((address_space(3))) s16x4 *)(Kb + S::off(r0, b)));
             s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(p1));
+                (__attribute__((address_space(3))) s16x4 *)(Kb + S::off(r0 + 4, b)));
             typedef short s16x8 __attribute__((ext_vector_type(8)));
             s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             return __builtin_bit_cast(bf16x8, v);
         } else {
-            const bf16 *p0 = Ks + (k0 + 4 * g + e) * ldk + m0 + 4 * qd;
             s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(p0));
+                (__attribute__((address_space(3))) s16x4 *)(Kb + S::off(k0 + 4 * g + e, b)));
             return __builtin_bit_cast(bf16x4, lo);
         }
     }
 };
 
-// fp32: a transposed copy Kt[key][chunk row] is written when the chunk is staged.
+// fp32: every lane reads its element K[k0 + lane/16][m0 + lane%16].
 template <int C, int DK>
 struct KtOperand<float, C, DK> {
-    static constexpr bool kNeedsCopy = true;
     typedef Mma<float> M;
-    __device__ static inline float load(const float *, int, const float *Kt, int ldc, int m0, int k0, int lane)
+    typedef Swz<DK * 4> S;
+    __device__ static inline float load(const unsigned char *Kb, int m0, int k0, int lane)
     {
-        return Kt[(m0 + (lane & 15)) * ldc + k0 + (lane >> 4)];
+        return *reinterpret_cast<const float *>(Kb + S::off(k0 + (lane >> 4), 4 * (m0 + (lane & 15))));
     }
 };
 
+// Operand fragment (K-slice of one row) of a staged tile.
+template <typename M, typename S, typename E>
+__device__ inline typename M::frag staged_frag(const unsigned char *base, int row, int col)
+{
+    return M::load(reinterpret_cast<const E *>(base + S::off(row, col * (int)sizeof(E))));
+}
+
+constexpr int kScanThreads = 2 * kThreads;   // 4 compute waves + 4 loader waves
+
 template <typename E, int C, int DK, int DVS>
-__global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
+__global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v, const int32_t *__restrict__ cu,
     SlotMap map, int32_t num_seqs, int64_t total_tokens, int32_t hqk, int32_t hv, int32_t dv,
-    const E *__restrict__ tmat,
-    const E *__restrict__ amat, const float *__restrict__ dec, const float *state_in, float *state_out,
-    E *__restrict__ o, float scale)
+    const E *__restrict__ tmat, const E *__restrict__ amat, const float *__restrict__ dec, const float *state_in,
+    float *state_out, E *__restrict__ o, float scale)
 {
+    constexpr int ES = (int)sizeof(E);
     constexpr int PAD = LdsPad<E>::value;
     constexpr int LDK = key_row_stride<E>(DK);
     constexpr int LDC = C + PAD;
     constexpr int LDV = DVS + PAD;
     constexpr int RT = C / 16, CT = DVS / 16, SR = DK / 16;
     constexpr int SR_PER = (SR + kWaves - 1) / kWaves;
+    constexpr int RT_PER = (RT + kWaves - 1) / kWaves;
     constexpr int VN = Vec16<E>::n;
     typedef typename Vec16<E>::type V16;
     typedef KtOperand<E, C, DK> KT;
     typedef typename MmaFor<E, C>::type MC;
     typedef typename MmaFor<E, DK>::type MK;
-    constexpr int QK_VECS = C * DK / VN, QK_PER = (QK_VECS + kThreads - 1) / kThreads;
-    constexpr int CC_VECS = C * C / VN, CC_PER = (CC_VECS + kThreads - 1) / kThreads;
-    constexpr int V_VECS = C * DVS / VN, V_PER = (V_VECS + kThreads - 1) / kThreads;
-    constexpr int KT_ROWS = KT::kNeedsCopy ? DK : 1;
+    typedef Swz<DK * ES> SK;
+    typedef Swz<C * ES> SC;
+    typedef Swz<DVS * ES> SV;
     static_assert(C <= kWave, "one lane per token of a chunk");
     static_assert(DVS % 16 == 0 && DK % 16 == 0 && C % 16 == 0, "16x16 tiles");
 
-    __shared__ __attribute__((aligned(16))) E Ks[C * LDK];
-    __shared__ __attribute__((aligned(16))) E Qs[C * LDK];
-    __shared__ __attribute__((aligned(16))) E Kt[KT_ROWS * LDC];
-    __shared__ __attribute__((aligned(16))) E Ts[C * LDC];
-    __shared__ __attribute__((aligned(16))) E As[C * LDC];
-    __shared__ __attribute__((aligned(16))) E Vs[C * LDV];
+    // stage buffer layout (bytes) and the 1 KB direct-load jobs that fill it
+    constexpr int OFF_Q = 0;
+    constexpr int OFF_K = OFF_Q + C * DK * ES;
+    constexpr int OFF_T = OFF_K + C * DK * ES;
+    constexpr int OFF_A = OFF_T + C * C * ES;
+    constexpr int OFF_V = OFF_A + C * C * ES;
+    constexpr int OFF_D = OFF_V + C * DVS * ES;
+    constexpr int STAGE = OFF_D + 3 * C * 4;
+    constexpr int NJ_QK = (C * DK * ES / 16 + 63) / 64;
+    constexpr int NJ_TA = (C * C * ES / 16 + 63) / 64;
+    constexpr int NJ_V = (C * DVS * ES / 16 + 63) / 64;
+    constexpr int NJ_D = (3 * C * 4 / 16 + 63) / 64;
+    constexpr int NJ = 2 * NJ_QK + 2 * NJ_TA + NJ_V + NJ_D;
+
+    __shared__ __attribute__((aligned(1024))) unsigned char stage_mem[2 * STAGE];
     __shared__ __attribute__((aligned(16))) E Xt[DVS * LDC];
     __shared__ __attribute__((aligned(16))) E Dt[DVS * LDC];
     __shared__ __attribute__((aligned(16))) E LDt[DVS * LDC];
     __shared__ __attribute__((aligned(16))) E St[DVS * LDK];
     __shared__ __attribute__((aligned(16))) E Os[C * LDV];
-    __shared__ float Gam[C], Lam[C], Bet[C];
-    __shared__ float GamL;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const bool loader = wave >= kWaves;              // waves 4..7 stage chunks, 0..3 compute
+    const int lw = wave - kWaves;                    // loader index
     const int nv = dv / DVS;
     const int pairs = num_seqs * hv;
     const int bid = blockIdx.x;
@@ -502,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
         // No chunk of this sequence in this launch.  The first launch still owes the
         // sequence its final state (initial state passed through, or zeros).
         if (c_begin == 0 && state_in != state_out) {
-            for (int i = tid; i < DK * DVS; i += kThreads) {
+            for (int i = tid; i < DK * DVS; i += kScanThreads) {
                 const size_t off = state_base + (size_t)(i / DVS) * dv + (i % DVS);
                 state_out[off] = state_in ? state_in[off] : 0.f;
             }
@@ -510,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
         return;
     }
 
-    // ---- state slice into accumulators (wave w owns key-row tiles w, w+4, ...) ----
+    // ---- state slice into accumulators (compute wave w owns key-row tiles w, w+4, ...) ----
     f32x4 sacc[SR_PER][CT];
 #pragma unroll
     for (int u = 0; u < SR_PER; ++u) {
@@ -518,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             sacc[u][ct] = zero4();
-            if (sr < SR) {
+            if (!loader && sr < SR) {
                 if (state_in) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -531,114 +573,102 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
         }
     }
 
-    // ---- chunk inputs: global -> registers (prefetch) -> LDS ----
-    // Narrow slices keep two register sets in flight, so the loads of a chunk get two
-    // steps to arrive; wide slices keep one (register budget).  Rows past the end of
-    // the sequence are loaded from its last row and replaced by zeros (no branches).
-    constexpr bool kTwoSets = DVS <= 32;
-    struct Staged {
-        V16 q[QK_PER], k[QK_PER], t[CC_PER], a[CC_PER], v[V_PER];
-        float gam, lam, bet;
-        int64_t t0;
-        int len;
-    };
-    Staged R0, R1;
-    const V16 zv = (V16)(E)0.f;
-
-    auto load_chunk = [&](Staged &R, int c) {
+    // ---- loaders: chunk c into registers (issue_loads), then into a stage buffer ----
+    // Loader lw owns jobs lw, lw + 4, ... of 64 16-byte chunks each; lane l of a job
+    // moves physical chunk 64 * idx + l of its tile.
+    constexpr int NJ_PER = (NJ + kWaves - 1) / kWaves;
+    V16 lbuf[NJ_PER];
+    int ldst[NJ_PER];
+    // The job list of each loader is fixed at compile time (one branch per loader), and
+    // every load is unconditional: a lane past the end of a tile reloads the tile's last
+    // chunk and only its LDS store is skipped.  This keeps all loads of a step in flight
+    // together instead of behind per-job waits.
+    auto issue_jobs = [&](auto lwc, int c) __attribute__((always_inline)) {
+        constexpr int LW = decltype(lwc)::value;
         const int64_t t0 = a + (int64_t)c * C;
-        const int len = (int)min<int64_t>(C, b - t0);
-        R.t0 = t0;
-        R.len = len;
+        const int last = (int)min<int64_t>(C, b - t0) - 1;   // >= 0 for every chunk of the sequence
         const size_t slot = slot_of(map, n, c);
         const size_t ent = (slot * hv + h) * C * C;
 #pragma unroll
-        for (int u = 0; u < QK_PER; ++u) {
-            const int i = tid + u * kThreads;
-            if (i < QK_VECS) {
-                const int r = i / (DK / VN), c0 = (i % (DK / VN)) * VN;
-                const size_t off = ((size_t)(t0 + min(r, len - 1)) * hqk + hq) * DK + c0;
-                // raw rows here; rows past the end are zeroed when staged, so that the
-                // loads stay in flight until then
-                R.q[u] = *reinterpret_cast<const V16 *>(q + off);
-                R.k[u] = *reinterpret_cast<const V16 *>(k + off);
+        for (int u = 0; u < NJ_PER; ++u) {
+            const int job = LW + u * kWaves;
+            const E *src;
+            int dst, valid;
+            if (job < 2 * NJ_QK) {
+                const int which = job / NJ_QK, idx = job % NJ_QK;
+                const int P = idx * 64 + lane;                     // physical chunk of the tile
+                const int r = P / (DK * ES / 16), pos = P % (DK * ES / 16);
+                const int j = pos ^ SK::perm(r);
+                src = (which ? k : q) + ((size_t)(t0 + min(r, last)) * hqk + hq) * DK + j * VN;
+                dst = (which ? OFF_K : OFF_Q) + P * 16;
+                valid = 1;
+            } else if (job < 2 * NJ_QK + 2 * NJ_TA) {
+                constexpr int NCK = C * C * ES / 16;
+                const int jj = job - 2 * NJ_QK;
+                const int which = jj / NJ_TA, idx = jj % NJ_TA;
+                const int P = idx * 64 + lane;
+                valid = P < NCK;
+                const int Pl = min(P, NCK - 1);
+                const int r = Pl / (C * ES / 16), pos = Pl % (C * ES / 16);
+                const int j = pos ^ SC::perm(r);
+                src = (which ? amat : tmat) + ent + (size_t)r * C + j * VN;
+                dst = (which ? OFF_A : OFF_T) + P * 16;
+            } else if (job < 2 * NJ_QK + 2 * NJ_TA + NJ_V) {
+                constexpr int NCK = C * DVS * ES / 16;
+                const int P = (job - 2 * NJ_QK - 2 * NJ_TA) * 64 + lane;
+                valid = P < NCK;
+                const int Pl = min(P, NCK - 1);
+                const int r = Pl / (DVS * ES / 16), pos = Pl % (DVS * ES / 16);
+                const int j = pos ^ SV::perm(r);
+                src = v + ((size_t)(t0 + min(r, last)) * hv + h) * dv + (size_t)s * DVS + j * VN;
+                dst = OFF_V + P * 16;
+            } else {
+                constexpr int NCK = 3 * C * 4 / 16;
+                const int P = job < NJ ? (job - 2 * NJ_QK - 2 * NJ_TA - NJ_V) * 64 + lane : NCK;
+                valid = P < NCK;
+                src = reinterpret_cast<const E *>(dec + (slot * hv + h) * 3 * C + min(P, NCK - 1) * 4);
+                dst = OFF_D + P * 16;
             }
+            ldst[u] = valid ? dst : -1;
+            lbuf[u] = *reinterpret_cast<const V16 *>(src);
         }
+    };
+    auto issue_loads = [&](int c) __attribute__((always_inline)) {
+        switch (lw) {
+        case 0: issue_jobs(std::integral_constant<int, 0>{}, c); break;
+        case 1: issue_jobs(std::integral_constant<int, 1>{}, c); break;
+        case 2: issue_jobs(std::integral_constant<int, 2>{}, c); break;
+        default: issue_jobs(std::integral_constant<int, 3>{}, c); break;
+        }
+    };
+    auto write_stage = [&](int buf) __attribute__((always_inline)) {
+        unsigned char *stg = stage_mem + buf * STAGE;
 #pragma unroll
-        for (int u = 0; u < CC_PER; ++u) {
-            const int i = tid + u * kThreads;
-            if (i < CC_VECS) {
-                R.t[u] = *reinterpret_cast<const V16 *>(tmat + ent + (size_t)i * VN);
-                R.a[u] = *reinterpret_cast<const V16 *>(amat + ent + (size_t)i * VN);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < V_PER; ++u) {
-            const int i = tid + u * kThreads;
-            if (i < V_VECS) {
-                const int r = i / (DVS / VN), c0 = (i % (DVS / VN)) * VN;
-                R.v[u] = *reinterpret_cast<const V16 *>(v + ((size_t)(t0 + min(r, len - 1)) * hv + h) * dv +
-                                                        (size_t)s * DVS + c0);
-            }
-        }
-        if (wave == 0 && lane < C) {
-            const float *rec = dec + (slot * hv + h) * 3 * C;
-            R.gam = rec[lane];
-            R.lam = rec[C + lane];
-            R.bet = rec[2 * C + lane];
+        for (int u = 0; u < NJ_PER; ++u)
+            if (ldst[u] >= 0)
+                *reinterpret_cast<V16 *>(stg + ldst[u]) = lbuf[u];
+    };
+    // Outputs of a finished chunk (staged in Os by the compute waves): coalesced
+    // 16-byte rows to global, written by the loaders.
+    auto flush = [&](int64_t t0, int len) __attribute__((always_inline)) {
+        constexpr int O_VECS = C * DVS / VN;
+        for (int i = tid - kThreads; i < O_VECS; i += kThreads) {
+            const int r = i / (DVS / VN), c0 = (i % (DVS / VN)) * VN;
+            if (r < len)
+                *reinterpret_cast<V16 *>(o + ((size_t)(t0 + r) * hv + h) * dv + (size_t)s * DVS + c0) =
+                    *reinterpret_cast<const V16 *>(Os + r * LDV + c0);
         }
     };
 
-    auto store_chunk = [&](const Staged &R) {
-#pragma unroll
-        for (int u = 0; u < QK_PER; ++u) {
-            const int i = tid + u * kThreads;
-            if (i < QK_VECS) {
-                const int r = i / (DK / VN), c0 = (i % (DK / VN)) * VN;
-                const V16 qv = r < R.len ? R.q[u] : zv;
-                const V16 kv = r < R.len ? R.k[u] : zv;
-                *reinterpret_cast<V16 *>(Qs + r * LDK + c0) = qv;
-                *reinterpret_cast<V16 *>(Ks + r * LDK + c0) = kv;
-                if constexpr (KT::kNeedsCopy) {
-#pragma unroll
-                    for (int j = 0; j < VN; ++j)
-                        Kt[(c0 + j) * LDC + r] = kv[j];
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < CC_PER; ++u) {
-            const int i = tid + u * kThreads;
-            if (i < CC_VECS) {
-                const int r = (i * VN) / C, c0 = (i * VN) % C;
-                *reinterpret_cast<V16 *>(Ts + r * LDC + c0) = R.t[u];
-                *reinterpret_cast<V16 *>(As + r * LDC + c0) = R.a[u];
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < V_PER; ++u) {
-            const int i = tid + u * kThreads;
-            if (i < V_VECS) {
-                const int r = i / (DVS / VN), c0 = (i % (DVS / VN)) * VN;
-                *reinterpret_cast<V16 *>(Vs + r * LDV + c0) = r < R.len ? R.v[u] : zv;
-            }
-        }
-        if (wave == 0 && lane < C) {
-            Gam[lane] = R.gam;
-            Lam[lane] = R.lam;
-            Bet[lane] = R.bet;
-            if (lane == C - 1)
-                GamL = R.gam;   // exp(G_last)
-        }
-    };
+    // ---- compute waves: one chunk step on stage buffer `cur` (barriers B1 and B2 inside) ----
+    auto step = [&](int cur) __attribute__((always_inline)) {
+        const unsigned char *stg = stage_mem + cur * STAGE;
+        const float *Gam = reinterpret_cast<const float *>(stg + OFF_D);
+        const float *Lam = Gam + C;
+        const float *Bet = Gam + 2 * C;
 
-    // One chunk step on the chunk staged in LDS; ends with its outputs written.
-    // prefetch(): issues the global loads of a later chunk; called once the products
-    // of P1 are under way so that the loads do not delay them.
-    auto step = [&](int64_t t0, int len, auto &&prefetch) {
         // P1: Q S and K S for row tile rt (all column tiles); X = diag(beta)(V - diag(exp G) K S)
         //     goes to Xt (transposed); diag(exp G) Q S stays in oacc for P3.
-        constexpr int RT_PER = (RT + kWaves - 1) / kWaves;
         f32x4 oacc[RT_PER][CT];
         f32x4 kacc[RT_PER][CT];
 #pragma unroll
@@ -653,8 +683,8 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
                 const int r = lane & 15, kk = (lane >> 4) * MK::kPerLane;
 #pragma unroll
                 for (int k0 = 0; k0 < DK; k0 += MK::kStep) {
-                    const typename MK::frag aq = MK::load(Qs + (rt * 16 + r) * LDK + k0 + kk);
-                    const typename MK::frag ak = MK::load(Ks + (rt * 16 + r) * LDK + k0 + kk);
+                    const auto aq = staged_frag<MK, SK, E>(stg + OFF_Q, rt * 16 + r, k0 + kk);
+                    const auto ak = staged_frag<MK, SK, E>(stg + OFF_K, rt * 16 + r, k0 + kk);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) {
                         const typename MK::frag bs = MK::load(St + (ct * 16 + r) * LDK + k0 + kk);
@@ -662,13 +692,6 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
                         kacc[u][ct] = MK::mma(ak, bs, kacc[u][ct]);
                     }
                 }
-            }
-        }
-        prefetch();
-#pragma unroll
-        for (int u = 0; u < RT_PER; ++u) {
-            const int rt = wave + u * kWaves;
-            if (rt < RT) {
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
                     const int col = ct * 16 + tile_col(lane);
@@ -676,14 +699,15 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int rr = rt * 16 + tile_row(lane, i);
-                        x[i] = Bet[rr] * (to_f32(Vs[rr * LDV + col]) - Gam[rr] * kacc[u][ct][i]);
+                        const E vv = *reinterpret_cast<const E *>(stg + OFF_V + SV::off(rr, col * ES));
+                        x[i] = Bet[rr] * (to_f32(vv) - Gam[rr] * kacc[u][ct][i]);
                         oacc[u][ct][i] *= Gam[rr];
                     }
                     store4(Xt + col * LDC + rt * 16 + tile_row(lane, 0), x[0], x[1], x[2], x[3]);
                 }
             }
         }
-        __syncthreads();
+        __syncthreads();   // B1
 
         // P2: D = T X -> Dt and (diag(lambda) D) -> LDt, both transposed
 #pragma unroll
@@ -697,7 +721,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
                 const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
 #pragma unroll
                 for (int k0 = 0; k0 < C; k0 += MC::kStep) {
-                    const typename MC::frag at = MC::load(Ts + (rt * 16 + r) * LDC + k0 + kk);
+                    const auto at = staged_frag<MC, SC, E>(stg + OFF_T, rt * 16 + r, k0 + kk);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
                         dacc[ct] = MC::mma(at, MC::load(Xt + (ct * 16 + r) * LDC + k0 + kk), dacc[ct]);
@@ -712,7 +736,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
                 }
             }
         }
-        __syncthreads();
+        __syncthreads();   // B2
 
         // P3: O = diag(exp G) Q S + A D, scaled, staged in Os
 #pragma unroll
@@ -722,7 +746,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
                 const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
 #pragma unroll
                 for (int k0 = 0; k0 < C; k0 += MC::kStep) {
-                    const typename MC::frag aa = MC::load(As + (rt * 16 + r) * LDC + k0 + kk);
+                    const auto aa = staged_frag<MC, SC, E>(stg + OFF_A, rt * 16 + r, k0 + kk);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
                         oacc[u][ct] = MC::mma(aa, MC::load(Dt + (ct * 16 + r) * LDC + k0 + kk), oacc[u][ct]);
@@ -736,7 +760,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
             }
         }
         // P4: S <- exp(G_last) S + K^T diag(lambda) D; refresh the transposed copy
-        const float gl = GamL;
+        const float gl = Gam[C - 1];   // exp(G_last): G is flat past the last real token
 #pragma unroll
         for (int u = 0; u < SR_PER; ++u) {
             const int sr = wave + u * kWaves;
@@ -747,7 +771,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
                 const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
 #pragma unroll
                 for (int k0 = 0; k0 < C; k0 += MC::kStep) {
-                    const typename MC::frag akt = KT::load(Ks, LDK, Kt, LDC, sr * 16, k0, lane);
+                    const typename MC::frag akt = KT::load(stg + OFF_K, sr * 16, k0, lane);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
                         sacc[u][ct] = MC::mma(akt, MC::load(LDt + (ct * 16 + r) * LDC + k0 + kk), sacc[u][ct]);
@@ -758,72 +782,48 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_scan_kernel(
                            sacc[u][ct][1], sacc[u][ct][2], sacc[u][ct][3]);
             }
         }
-        __syncthreads();
-
-        // Outputs of this chunk: coalesced 16-byte rows to global.
-        constexpr int O_VECS = C * DVS / VN;
-        for (int i = tid; i < O_VECS; i += kThreads) {
-            const int r = i / (DVS / VN), c0 = (i % (DVS / VN)) * VN;
-            if (r < len)
-                *reinterpret_cast<V16 *>(o + ((size_t)(t0 + r) * hv + h) * dv + (size_t)s * DVS + c0) =
-                    *reinterpret_cast<const V16 *>(Os + r * LDV + c0);
-        }
     };
 
-    load_chunk(R0, c_begin);
-    if (kTwoSets && c_begin + 1 < c_end)
-        load_chunk(R1, c_begin + 1);
-    store_chunk(R0);
-    __syncthreads();
-
-    if constexpr (kTwoSets) {
-        // chunk c is in LDS and R1 holds chunk c + 1 at the top of every iteration
-        for (int c = c_begin; c < c_end; c += 2) {
-            const int64_t t0a = R0.t0;
-            const int lena = R0.len;
-            step(t0a, lena, [&] {
-                if (c + 2 < c_end)
-                    load_chunk(R0, c + 2);
-            });
-            if (c + 1 >= c_end)
-                break;
-            store_chunk(R1);
-            __syncthreads();
-            const int64_t t0b = R1.t0;
-            const int lenb = R1.len;
-            step(t0b, lenb, [&] {
-                if (c + 3 < c_end)
-                    load_chunk(R1, c + 3);
-            });
-            if (c + 2 < c_end)
-                store_chunk(R0);
-            __syncthreads();
-        }
-    } else {
-        for (int c = c_begin; c < c_end; ++c) {
-            const int64_t t0 = R0.t0;
-            const int len = R0.len;
-            step(t0, len, [&] {
-                if (c + 1 < c_end)
-                    load_chunk(R0, c + 1);
-            });
-            if (c + 1 < c_end)
-                store_chunk(R0);
-            __syncthreads();
-        }
+    // ---- pipeline: while the compute waves work on chunk c (stage c & 1), the loaders
+    //      flush the outputs of chunk c - 1 and stage chunk c + 1 into the other buffer ----
+    if (loader) {
+        issue_loads(c_begin);
+        write_stage(c_begin & 1);
     }
-
-    // ---- final state ----
+    __syncthreads();
+    for (int c = c_begin; c < c_end; ++c) {
+        if (loader) {
+            if (c > c_begin) {
+                const int64_t pt0 = a + (int64_t)(c - 1) * C;
+                flush(pt0, (int)min<int64_t>(C, b - pt0));
+            }
+            if (c + 1 < c_end)
+                issue_loads(c + 1);
+            __syncthreads();   // B1
+            __syncthreads();   // B2
+            if (c + 1 < c_end)
+                write_stage((c + 1) & 1);
+        } else {
+            step(c & 1);
+        }
+        __syncthreads();       // end of step: St, Os and the next stage are complete
+    }
+    if (loader) {
+        const int64_t pt0 = a + (int64_t)(c_end - 1) * C;
+        flush(pt0, (int)min<int64_t>(C, b - pt0));
+    } else {
+        // ---- final state ----
 #pragma unroll
-    for (int u = 0; u < SR_PER; ++u) {
-        const int sr = wave + u * kWaves;
-        if (sr < SR) {
+        for (int u = 0; u < SR_PER; ++u) {
+            const int sr = wave + u * kWaves;
+            if (sr < SR) {
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
+                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    state_out[state_base + (size_t)(sr * 16 + tile_row(lane, i)) * dv + ct * 16 +
-                              tile_col(lane)] = sacc[u][ct][i];
+                    for (int i = 0; i < 4; ++i)
+                        state_out[state_base + (size_t)(sr * 16 + tile_row(lane, i)) * dv + ct * 16 +
+                                  tile_col(lane)] = sacc[u][ct][i];
+            }
         }
     }
 }
@@ -851,7 +851,7 @@ static void launch_scan(const PrefillArgs &p, const SlotMap &map, const E *tmat,
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
     const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
     prof_begin(PROF_SCAN, st);
-    hipLaunchKernelGGL((gdn_chunk_scan_kernel<E, C, DK, DVS>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((gdn_chunk_scan_kernel<E, C, DK, DVS>), dim3((unsigned)blocks), dim3(kScanThreads), 0, st,
                        static_cast<const E *>(p.q), static_cast<const E *>(p.k), static_cast<const E *>(p.v),
                        p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv, p.dv, tmat, amat, dec, sin, sout,
                        static_cast<E *>(p.o), p.scale);
@@ -868,21 +868,19 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
     E *amat = tmat + (size_t)p.max_chunks * p.hv * C * C;
     float *dec = reinterpret_cast<float *>(amat + (size_t)p.max_chunks * p.hv * C * C);
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
-    // 64-column slices only where their LDS footprint fits (bf16 operands).
-    constexpr bool kWide = DK >= 64 && sizeof(E) == 2;
-    const int dvs = pick_dvs(pairs, p.dv, kWide ? 64 : 32);
+    // Two stage buffers of a chunk leave room for slices of at most 32 columns (bf16)
+    // or 16 columns (fp32).
+    constexpr bool kWide = sizeof(E) == 2;
+    const int dvs = pick_dvs(pairs, p.dv, kWide ? 32 : 16);
 
     auto scan = [&](const SlotMap &map, const float *sin, float *sout) {
         if constexpr (kWide) {
-            if (dvs == 64) {
-                launch_scan<E, C, DK, 64>(p, map, tmat, amat, dec, sin, sout, st);
+            if (dvs == 32) {
+                launch_scan<E, C, DK, 32>(p, map, tmat, amat, dec, sin, sout, st);
                 return;
             }
         }
-        if (dvs == 32)
-            launch_scan<E, C, DK, 32>(p, map, tmat, amat, dec, sin, sout, st);
-        else
-            launch_scan<E, C, DK, 16>(p, map, tmat, amat, dec, sin, sout, st);
+        launch_scan<E, C, DK, 16>(p, map, tmat, amat, dec, sin, sout, st);
     };
     auto prep = [&](const SlotMap &map, int64_t slots) {
         prof_begin(PROF_PREP, st);
