@@ -34,6 +34,43 @@ CACHE_DEFEAT_BYTES = 600e6      # rotate copies until the working set exceeds th
 
 METRIC = "prefill tokens/s + decode tokens/s (Qwen3.5-9B GDN layer), % MFMA/HBM peak"
 
+# HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and WRITE_SIZE, each
+# scaled by what the counter reads for a plain copy of known size).  A figure is used only
+# while the kernel's sources still hash to the digest stored beside it.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+KERNEL_SOURCES = {
+    "gdn_chunk_scan_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
+    "gdn_prep_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
+    "gdn_decode_kernel": ("gated_deltanet_scan_amd/csrc/gdn_decode.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
+}
+
+
+def sources_digest(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter summary, or
+    None when there is none or the kernel's sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    want = sources_digest(kernel)
+    for line in lines:
+        if not line.startswith("traffic:"):
+            continue
+        kv = dict(tok.split("=", 1) for tok in line[len("traffic:"):].split())
+        if kv.get("kernel") == kernel and kv.get("workload") == workload and kv.get("sources") == want:
+            return float(kv["bytes_per_launch"])
+    return None
+
 
 def esize(dtype):
     import torch
@@ -41,7 +78,11 @@ def esize(dtype):
 
 
 def prefill_costs(w, lengths):
-    """Algorithmic bytes and flops per launch of each prefill kernel."""
+    """Algorithmic bytes and flops per launch of each prefill kernel.
+
+    Bytes are what the kernel must move between HBM and the chip at least: its inputs
+    read once and its outputs written once.  Flops count the dense contractions only
+    (a multiply-add is two flops): per real token for the scan, per chunk for the prep."""
     es = esize(w.io_dtype)
     T = sum(lengths)
     N = len(lengths)
@@ -123,7 +164,8 @@ def measure_prefill(name, steps, warmup, lengths=None):
     kern = {}
     for kid, kname in ((0, "chunk_table"), (1, "prep"), (2, "scan")):
         n, tot = gdn.profile_collect(kid)
-        kern[kname] = {"launches": n, "avg_us": (tot / n * 1e3) if n else None}
+        kern[kname] = {"launches_per_step": n / steps, "avg_us": (tot / n * 1e3) if n else None,
+                       "per_step_us": tot * 1e3 / steps}
     gdn.profile_enable(False)
     T = sum(lengths)
     flops = costs["prep"]["flops"] + costs["scan"]["flops"]
@@ -133,13 +175,14 @@ def measure_prefill(name, steps, warmup, lengths=None):
         "tokens_per_s": T / (ms * 1e-3), "rotated_copies": n_sets,
         "mfma_frac": flops / (ms * 1e-3) / (peak * 1e12),
         "hbm_frac": costs["io_bytes"] / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9),
-        "kernels_us": {k: v["avg_us"] for k, v in kern.items()},
+        "kernels": kern,
     }
+    # whole-step costs over the kernel's summed launch time (a long or batched prefill is
+    # cut into several launches of each kernel)
     for kname in ("prep", "scan"):
-        us = kern[kname]["avg_us"]
+        us = kern[kname]["per_step_us"]
         c = costs[kname]
         if us:
-            out["kernels_us"][kname] = us
             out[kname + "_gbs"] = c["bytes"] / (us * 1e-6) / 1e9
             out[kname + "_tflops"] = c["flops"] / (us * 1e-6) / 1e12
     out["_costs"] = costs
@@ -149,10 +192,12 @@ def measure_prefill(name, steps, warmup, lengths=None):
 
 def roofline_for(pre):
     """Roofline object of the dominant prefill kernel (the one with the longest average launch)."""
-    kus = pre["kernels_us"]
-    name = max(("prep", "scan"), key=lambda k: kus.get(k) or 0.0)
-    us = kus[name]
-    c = pre["_costs"][name]
+    kern = pre["kernels"]
+    name = max(("prep", "scan"), key=lambda k: kern[k]["per_step_us"] or 0.0)
+    launches = kern[name]["launches_per_step"]
+    us = kern[name]["avg_us"]
+    # algorithmic cost of one launch: the step's cost over its launches of this kernel
+    c = {k: v / launches for k, v in pre["_costs"][name].items()}
     intensity = c["flops"] / c["bytes"]
     ridge = pre["_peak_tflops"] * 1e12 / (PEAK_HBM_GBS * 1e9)
     if intensity < ridge:
@@ -163,7 +208,8 @@ def roofline_for(pre):
         achieved = c["flops"] / (us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": pre["_peak_tflops"], "unit": "TFLOP/s",
                 "frac": achieved / pre["_peak_tflops"]}
-    roof.update({"traffic": None, "kernel": "gdn_%s_kernel" % ("prep" if name == "prep" else "chunk_scan"),
+    kernel = "gdn_prep_kernel" if name == "prep" else "gdn_chunk_scan_kernel"
+    roof.update({"traffic": measured_traffic(kernel, pre["workload"]), "kernel": kernel,
                  "avg_us": us, "algorithmic_bytes": c["bytes"], "algorithmic_flops": c["flops"],
                  "intensity_flop_per_byte": intensity})
     return roof
@@ -206,7 +252,8 @@ def measure_decode(name, steps, warmup):
         "kernel_avg_us": us, "kernel_tokens_per_s": N / (us * 1e-6),
         "state_gbs": costs["state_bytes"] / (us * 1e-6) / 1e9, "rotated_state_sets": n_sets,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "gdn_decode_kernel",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic("gdn_decode_kernel", name),
+                     "kernel": "gdn_decode_kernel",
                      "avg_us": us, "algorithmic_bytes": costs["bytes"]},
     }
 
@@ -242,10 +289,16 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the long and varlen prefill lines")
+    ap.add_argument("--profile-prefill", action="store_true",
+                    help="run only the headline prefill loop (for rocprofv3 kernel traces and counters)")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="run only the decode loop (for rocprofv3 kernel traces and counters)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run only a plain device copy of MIB MiB, 10 times (scale for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the gated delta rule shards over heads and sequences with no "
-              "exchange, and this build runs and reports a single GPU (got --gpus %d)" % args.gpus,
+              "exchange; more than one GPU is not measured here (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
@@ -253,11 +306,27 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            torch.neg(src, out=dst)     # one elementwise kernel: reads n bytes, writes n bytes
+        _sync()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 10}))
+        return
     import gated_deltanet_scan_amd as gdn
     gdn.load_library()
 
+    if args.profile_decode:
+        dec = measure_decode("decode_64", args.steps, args.warmup)
+        print(json.dumps(dec))
+        return
     print("[bench] prefill %s" % args.workload, file=sys.stderr, flush=True)
     pre = measure_prefill(args.workload, args.steps, args.warmup)
+    if args.profile_prefill:
+        print(json.dumps({k: v for k, v in pre.items() if not k.startswith("_")}))
+        return
     print("[bench] decode_64", file=sys.stderr, flush=True)
     dec = measure_decode("decode_64", max(args.steps, 20), args.warmup)
     extra = {}
