@@ -263,8 +263,8 @@ gdn_status gdn_decode_step(const gdn_shape *shape, const void *q, const void *k,
         return fail(GDN_ERR_INVALID_ARG, "negative num_seqs");
     if (num_seqs == 0)
         return ok();
-    if ((int64_t)num_seqs * s.num_v_heads > INT32_MAX)
-        return fail(GDN_ERR_INVALID_ARG, "num_seqs * HV too large");
+    if ((int64_t)num_seqs * s.num_v_heads > (int64_t(1) << 24))
+        return fail(GDN_ERR_INVALID_ARG, "num_seqs * HV too large (at most 2^24 states per call)");
     if (!q || !k || !v || !g || !beta || !state || !o)
         return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta, state and o are required");
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(state, 16))

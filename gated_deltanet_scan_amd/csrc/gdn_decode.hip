@@ -14,97 +14,119 @@
 
 namespace gdn {
 
-// One workgroup per (sequence, value head).  Thread t owns 4 consecutive
-// columns (one 16-byte vector per row, lanes along dv so every row is read
-// and written as whole coalesced segments) of RPT rows spaced RG apart; the
-// reductions over dk go through LDS in a fixed order (deterministic).
+// Each wave owns one 32-column slice of one (sequence, value head) state, all
+// dk rows: lane (rg, cg) = (lane / 8, lane % 8) holds columns 4 cg .. 4 cg + 3
+// of the RPL consecutive rows rg * RPL .. rg * RPL + RPL - 1.  Every load and
+// store instruction of the wave covers 8 whole 128-byte row segments.  The
+// sums over dk are a register sum over the lane's rows followed by a
+// butterfly over the 8 row groups (fixed order: deterministic).  Waves never
+// wait for each other: no LDS and no barrier.
+constexpr int kDecodeCols = 32;
+
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float *__restrict__ state,
-    E *__restrict__ o, int32_t hqk, int32_t hv, float scale)
+    E *__restrict__ o, int32_t hqk, int32_t hv, int64_t waves, float scale)
 {
-    constexpr int C4 = D / 4;           // 16-byte column groups per row
-    constexpr int RG = kThreads / C4;   // row groups
-    constexpr int RPT = D / RG;         // rows per thread
-    static_assert(RG * C4 == kThreads && RPT * RG == D, "thread layout");
+    constexpr int NS = D / kDecodeCols;   // column slices per state
+    constexpr int RG = 8;                 // row groups per wave
+    constexpr int RPL = D / RG;           // rows per lane
+    constexpr int VN = 16 / (int)sizeof(E);
+    static_assert(D % kDecodeCols == 0, "lane layout");
+    typedef typename Vec16<E>::type V16;
 
-    __shared__ float qs[D], ks[D];
-    __shared__ __attribute__((aligned(16))) float pa[RG * D];
-    __shared__ __attribute__((aligned(16))) float pb[RG * D];
-    __shared__ __attribute__((aligned(16))) float dl[D];
-    __shared__ float qk_s;
-
-    const int pair = blockIdx.x;  // n * hv + h
-    const int n = pair / hv, h = pair - (pair / hv) * hv;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t w = (int64_t)blockIdx.x * kWaves + threadIdx.x / kWave;
+    if (w >= waves)
+        return;
+    const int64_t pair = w / NS;            // n * hv + h
+    const int slice = (int)(w - pair * NS);
+    const int n = (int)(pair / hv), h = (int)(pair - (int64_t)n * hv);
     const int hq = h / (hv / hqk);
-    const int tid = threadIdx.x, cg = tid % C4, rg = tid / C4;
-    float *S = state + (size_t)pair * D * D;
+    const int rg = lane / 8, cg = lane % 8;
+    const int col = slice * kDecodeCols + 4 * cg;
+    float *S = state + (size_t)pair * D * D + (size_t)(rg * RPL) * D + col;
 
-    f32x4 s[RPT];
+    f32x4 s[RPL];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-        s[i] = *reinterpret_cast<const f32x4 *>(S + (size_t)(rg + RG * i) * D + 4 * cg);
-    if (tid < D) {
-        qs[tid] = to_f32(q[((size_t)n * hqk + hq) * D + tid]);
-        ks[tid] = to_f32(k[((size_t)n * hqk + hq) * D + tid]);
+    for (int i = 0; i < RPL; ++i)
+        s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)i * D));
+
+    // this lane's rows of k and q
+    float kr[RPL], qr[RPL];
+    const E *kp = k + ((size_t)n * hqk + hq) * D + rg * RPL;
+    const E *qp = q + ((size_t)n * hqk + hq) * D + rg * RPL;
+    if constexpr (RPL % VN == 0) {
+#pragma unroll
+        for (int c = 0; c < RPL / VN; ++c) {
+            const V16 kv = *reinterpret_cast<const V16 *>(kp + c * VN);
+            const V16 qv = *reinterpret_cast<const V16 *>(qp + c * VN);
+#pragma unroll
+            for (int e = 0; e < VN; ++e) {
+                kr[c * VN + e] = to_f32(kv[e]);
+                qr[c * VN + e] = to_f32(qv[e]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            kr[i] = to_f32(kp[i]);
+            qr[i] = to_f32(qp[i]);
+        }
     }
     const float alpha = expf(g[pair]);
     const float bt = beta[pair];
-    __syncthreads();
-
-    f32x4 pa4 = zero4(), pb4 = zero4();
+    float vv[4];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + RG * i;
-        pa4 += ks[r] * s[i];
-        pb4 += qs[r] * s[i];
-    }
-    *reinterpret_cast<f32x4 *>(pa + rg * D + 4 * cg) = pa4;
-    *reinterpret_cast<f32x4 *>(pb + rg * D + 4 * cg) = pb4;
-    if (tid < kWave) {
-        float x = 0.f;
-        for (int i = tid; i < D; i += kWave)
-            x += qs[i] * ks[i];
-        x = wave_sum(x);
-        if (tid == 0)
-            qk_s = x;
-    }
-    __syncthreads();
+    for (int e = 0; e < 4; ++e)
+        vv[e] = to_f32(v[(size_t)pair * D + col + e]);
 
-    if (tid < D) {
-        float A = 0.f, B = 0.f;
+    f32x4 a4 = zero4(), b4 = zero4();
+    float qk = 0.f;
 #pragma unroll
-        for (int r = 0; r < RG; ++r) {
-            A += pa[r * D + tid];
-            B += pb[r * D + tid];
+    for (int i = 0; i < RPL; ++i) {
+        a4 += kr[i] * s[i];
+        b4 += qr[i] * s[i];
+        qk += qr[i] * kr[i];
+    }
+    // butterfly over the row groups (lane bits 3..5)
+#pragma unroll
+    for (int m = 8; m < kWave; m <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a4[e] += __shfl_xor(a4[e], m, kWave);
+            b4[e] += __shfl_xor(b4[e], m, kWave);
         }
-        const float d = bt * (to_f32(v[(size_t)pair * D + tid]) - alpha * A);
-        dl[tid] = d;
-        o[(size_t)pair * D + tid] = (E)(scale * (alpha * B + qk_s * d));
+        qk += __shfl_xor(qk, m, kWave);
     }
-    __syncthreads();
-
-    const f32x4 d4 = *reinterpret_cast<const f32x4 *>(dl + 4 * cg);
+    f32x4 d4;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + RG * i;
-        *reinterpret_cast<f32x4 *>(S + (size_t)r * D + 4 * cg) = alpha * s[i] + ks[r] * d4;
+    for (int e = 0; e < 4; ++e)
+        d4[e] = bt * (vv[e] - alpha * a4[e]);
+    if (rg == 0) {
+        E *op = o + (size_t)pair * D + col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            op[e] = (E)(scale * (alpha * b4[e] + qk * d4[e]));
     }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+        __builtin_nontemporal_store(alpha * s[i] + kr[i] * d4, reinterpret_cast<f32x4 *>(S + (size_t)i * D));
 }
 
 template <typename E, int D>
 static hipError_t launch_decode_t(const DecodeArgs &p)
 {
-    const int64_t blocks = (int64_t)p.num_seqs * p.hv;
+    const int64_t waves = (int64_t)p.num_seqs * p.hv * (D / kDecodeCols);
+    const int64_t blocks = (waves + kWaves - 1) / kWaves;
     if (blocks > 0) {
         hipStream_t st = static_cast<hipStream_t>(p.stream);
-        prof_begin(PROF_DECODE, st);
-        hipLaunchKernelGGL((gdn_decode_kernel<E, D>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
-                           static_cast<const E *>(p.q), static_cast<const E *>(p.k),
-                           static_cast<const E *>(p.v), p.g, p.beta, p.state, static_cast<E *>(p.o), p.hqk,
-                           p.hv, p.scale);
-        prof_end(st);
+        const ProfEvents ev = prof_events(PROF_DECODE);
+        hipExtLaunchKernelGGL((gdn_decode_kernel<E, D>), dim3((unsigned)blocks), dim3(kThreads), 0, st, ev.start,
+                              ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k),
+                              static_cast<const E *>(p.v), p.g, p.beta, p.state, static_cast<E *>(p.o), p.hqk, p.hv,
+                              waves, p.scale);
     }
     return hipGetLastError();
 }
@@ -162,10 +184,10 @@ hipError_t launch_snapshot(const SnapshotArgs &p)
     const int64_t parts = (row_vec4 + per_block - 1) / per_block;
     if (p.num_rows > 0 && parts > 0) {
         hipStream_t st = static_cast<hipStream_t>(p.stream);
-        prof_begin(PROF_SNAPSHOT, st);
-        hipLaunchKernelGGL(gdn_snapshot_kernel, dim3((unsigned)p.num_rows, (unsigned)parts), dim3(kThreads), 0,
-                           st, p.src, p.src_rows, p.src_capacity, p.dst, p.dst_rows, p.dst_capacity, row_vec4);
-        prof_end(st);
+        const ProfEvents ev = prof_events(PROF_SNAPSHOT);
+        hipExtLaunchKernelGGL(gdn_snapshot_kernel, dim3((unsigned)p.num_rows, (unsigned)parts), dim3(kThreads), 0,
+                              st, ev.start, ev.stop, 0, p.src, p.src_rows, p.src_capacity, p.dst, p.dst_rows,
+                              p.dst_capacity, row_vec4);
     }
     return hipGetLastError();
 }

@@ -2,6 +2,7 @@
 // (gfx950 only): element types, 16x16 matrix-core tiles and small helpers.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -850,12 +850,11 @@ static void launch_scan(const PrefillArgs &p, const SlotMap &map, const E *tmat,
     const int nv = p.dv / DVS;
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
     const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
-    prof_begin(PROF_SCAN, st);
-    hipLaunchKernelGGL((gdn_chunk_scan_kernel<E, C, DK, DVS>), dim3((unsigned)blocks), dim3(kScanThreads), 0, st,
-                       static_cast<const E *>(p.q), static_cast<const E *>(p.k), static_cast<const E *>(p.v),
-                       p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv, p.dv, tmat, amat, dec, sin, sout,
-                       static_cast<E *>(p.o), p.scale);
-    prof_end(st);
+    const ProfEvents ev = prof_events(PROF_SCAN);
+    hipExtLaunchKernelGGL((gdn_chunk_scan_kernel<E, C, DK, DVS>), dim3((unsigned)blocks), dim3(kScanThreads), 0, st,
+                          ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k),
+                          static_cast<const E *>(p.v), p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv,
+                          p.dv, tmat, amat, dec, sin, sout, static_cast<E *>(p.o), p.scale);
 }
 
 template <typename E, int C, int DK>
@@ -883,11 +882,10 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
         launch_scan<E, C, DK, 16>(p, map, tmat, amat, dec, sin, sout, st);
     };
     auto prep = [&](const SlotMap &map, int64_t slots) {
-        prof_begin(PROF_PREP, st);
-        hipLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), dim3((unsigned)slots, p.hqk), dim3(kThreads), 0, st,
-                           static_cast<const E *>(p.q), static_cast<const E *>(p.k), p.g, p.beta, p.cu_seqlens, map,
-                           p.num_seqs, p.total_tokens, p.hqk, p.hv, tmat, amat, dec);
-        prof_end(st);
+        const ProfEvents ev = prof_events(PROF_PREP);
+        hipExtLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), dim3((unsigned)slots, p.hqk), dim3(kThreads), 0, st,
+                              ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k), p.g,
+                              p.beta, p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv, tmat, amat, dec);
     };
 
     if (p.seg_len > 0) {
@@ -900,10 +898,11 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
         return hipGetLastError();
     }
 
-    prof_begin(PROF_CHUNK_TABLE, st);
-    hipLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(kThreads), 0, st, p.cu_seqlens, p.num_seqs,
-                       p.total_tokens, (int32_t)C, p.max_chunks, chunk_start);
-    prof_end(st);
+    {
+        const ProfEvents ev = prof_events(PROF_CHUNK_TABLE);
+        hipExtLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
+                              p.cu_seqlens, p.num_seqs, p.total_tokens, (int32_t)C, p.max_chunks, chunk_start);
+    }
     const SlotMap map{chunk_start, 0, INT32_MAX};
     if (p.max_chunks > 0)
         prep(map, p.max_chunks);

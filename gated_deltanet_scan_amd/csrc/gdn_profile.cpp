@@ -1,9 +1,11 @@
 // gdn_profile.cpp -- optional per-kernel timing with HIP events.
 //
-// While enabled, every kernel the library launches is bracketed by two HIP
-// events recorded on the launch stream.  gdn_profile_collect() waits for the
-// recorded events and sums the elapsed time per kernel.  Disabled (the
-// default), the hooks cost one relaxed atomic load per launch.
+// While enabled, every kernel the library launches is given a start and a stop
+// event through hipExtLaunchKernelGGL, which records the kernel's own start
+// and completion on its stream (no separate marker commands around it).
+// gdn_profile_collect() waits for the events and sums the elapsed time per
+// kernel.  Disabled (the default), the hook costs one relaxed atomic load per
+// launch.
 #include "../../include/gdn.h"
 #include "gdn_profile.hpp"
 
@@ -23,34 +25,27 @@ std::atomic<bool> g_on{false};
 std::mutex g_mu;
 std::vector<Rec> g_recs;
 size_t g_used = 0;
-thread_local Rec *g_open = nullptr;
 
 }  // namespace
 
-void prof_begin(int32_t kernel, hipStream_t stream)
+ProfEvents prof_events(int32_t kernel)
 {
     if (!g_on.load(std::memory_order_relaxed))
-        return;
+        return ProfEvents{nullptr, nullptr};
     std::lock_guard<std::mutex> lk(g_mu);
     if (g_used == g_recs.size()) {
         Rec r;
-        if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess)
-            return;
+        if (hipEventCreate(&r.start) != hipSuccess)
+            return ProfEvents{nullptr, nullptr};
+        if (hipEventCreate(&r.stop) != hipSuccess) {
+            (void)hipEventDestroy(r.start);
+            return ProfEvents{nullptr, nullptr};
+        }
         g_recs.push_back(r);
     }
     Rec &r = g_recs[g_used++];
     r.kernel = kernel;
-    (void)hipEventRecord(r.start, stream);
-    g_open = &r;
-}
-
-void prof_end(hipStream_t stream)
-{
-    if (!g_open)
-        return;
-    std::lock_guard<std::mutex> lk(g_mu);
-    (void)hipEventRecord(g_open->stop, stream);
-    g_open = nullptr;
+    return ProfEvents{r.start, r.stop};
 }
 
 }  // namespace gdn

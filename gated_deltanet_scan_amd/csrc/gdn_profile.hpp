@@ -15,7 +15,12 @@ enum ProfKernel : int32_t {
     PROF_SNAPSHOT = 4,
 };
 
-void prof_begin(int32_t kernel, hipStream_t stream);
-void prof_end(hipStream_t stream);
+// Start and stop events for one launch of `kernel`: both null while timing is
+// off.  The launch sites pass them to hipExtLaunchKernelGGL, which stamps the
+// kernel's own start and end (dispatch to completion) into them.
+struct ProfEvents {
+    hipEvent_t start, stop;
+};
+ProfEvents prof_events(int32_t kernel);
 
 }  // namespace gdn

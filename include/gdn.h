@@ -164,9 +164,11 @@ gdn_status gdn_state_snapshot(const gdn_shape *shape,
 
 /*
  * Kernel timing for benchmarks (not needed for normal use).
- * gdn_profile_enable(1) clears the record and starts bracketing every kernel
- * the library launches, on any thread, with two HIP events recorded on that
- * kernel's stream; gdn_profile_enable(0) stops recording new launches.
+ * gdn_profile_enable(1) clears the record and starts timing every kernel the
+ * library launches, on any thread: each launch carries a start and a stop HIP
+ * event (hipExtLaunchKernelGGL) that record the kernel's own start and
+ * completion on its stream; gdn_profile_enable(0) stops recording new
+ * launches.
  * gdn_profile_collect() waits for the recorded events of one kernel and
  * returns how many launches were recorded and their summed duration in ms.
  * Kernel identifiers: 0 chunk table, 1 prep (Gram products and solve),
