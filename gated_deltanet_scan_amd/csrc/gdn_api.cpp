@@ -96,9 +96,9 @@ PrefillWorkspace prefill_workspace(int32_t hv, int32_t chunk, int32_t io_dtype, 
     w.max_chunks = (int32_t)max_chunks;
     w.table_bytes = (((size_t)num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
     // per chunk slot and value head: T and A (C x C io elements each) and the decay
-    // record exp(G), exp(G_last - G), beta (3 C floats)
+    // record scale exp(G), exp(G_last - G), beta, beta exp(G) (4 C floats)
     const size_t mats = 2 * (size_t)max_chunks * (size_t)hv * (size_t)chunk * (size_t)chunk * io_size(io_dtype);
-    const size_t recs = (size_t)max_chunks * (size_t)hv * 3 * (size_t)chunk * sizeof(float);
+    const size_t recs = (size_t)max_chunks * (size_t)hv * 4 * (size_t)chunk * sizeof(float);
     w.total_bytes = w.table_bytes + mats + recs;
     return w;
 }

@@ -7,6 +7,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 namespace gdn {
 
@@ -141,6 +142,18 @@ __device__ inline float wave_inclusive_sum(float x, int lane)
             x += y;
     }
     return x;
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 (compile-time loop).
+template <typename F, int... Is>
+__device__ inline void static_for_impl(F &&f, std::integer_sequence<int, Is...>)
+{
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 __device__ inline float wave_sum(float x)

@@ -19,6 +19,7 @@
 //                           the matrix cores; per value head of the group:
 //                           G, log-space-masked exp(G_t - G_j), N, the unit
 //                           lower-triangular T = (I + N)^-1, A = decayed Q K^T
+//                           times the output scale
 //   gdn_chunk_scan_kernel   per (sequence, value head, dv-slice): for each
 //                           chunk, [Q;K] S, X = diag(beta)(V - diag(exp G) K S),
 //                           D = T X, O = diag(exp G) Q S + A D, S update.
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, SlotMap map, int32_t num_seqs,
     int64_t total_tokens, int32_t hqk, int32_t hv, E *__restrict__ tmat, E *__restrict__ amat,
-    float *__restrict__ dec)
+    float *__restrict__ dec, float scale)
 {
     constexpr int PAD = LdsPad<E>::value;
     constexpr int LDK = DK + PAD;
@@ -248,11 +249,14 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
             if (lane < C) {
                 Gs[wave][lane] = G;
                 Bs[wave][lane] = bv;
-                // decay record of the chunk for the scan: exp(G_t), exp(G_last - G_t), beta_t
-                float *rec = dec + (slot * hv + h) * 3 * C;
-                rec[lane] = expf(G);
+                // decay record of the chunk for the scan: scale exp(G_t), exp(G_last - G_t),
+                // beta_t, beta_t exp(G_t)
+                float *rec = dec + (slot * hv + h) * 4 * C;
+                const float eg = expf(G);
+                rec[lane] = scale * eg;
                 rec[C + lane] = expf(Glast - G);
                 rec[2 * C + lane] = bv;
+                rec[3 * C + lane] = bv * eg;
             }
         }
         __syncthreads();
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
                 const int j = j0 + e;
                 const float ed = (j <= t) ? __expf(gt - Gs[hh][j]) : 0.f;
                 Nm[(hh * C + t) * LDF + j] = (j < t) ? bt * ed * KK[t * LDF + j] : 0.f;
-                av[e] = (E)(ed * QK[t * LDF + j]);
+                av[e] = (E)(scale * ed * QK[t * LDF + j]);
             }
             *reinterpret_cast<V16 *>(amat + (slot * hv + h) * C * C + rem) = av;
         }
@@ -359,36 +363,40 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Scan kernel.  One workgroup per (sequence, value head, dv-slice of DVS
-// columns).  The dv columns of S evolve independently (each column of the
-// state only ever meets the same column of v), so slices need no exchange;
-// the key dimension is never split.  The fp32 state slice lives in the
-// accumulators of the S-update tiles for the whole sequence; a bf16 (or
-// fp32) copy transposed in LDS feeds the [Q;K] S product of the next chunk.
+// Scan kernel.  One workgroup per (sequence, value head, dv-slice of DVS =
+// 16 NW columns), NW waves; wave w owns the 16 columns 16 w .. 16 w + 15 of
+// the slice.  The dv columns of S evolve independently (each column of the
+// state only ever meets the same column of v), so the waves never exchange
+// data: each runs the whole chunk step on its own columns, with its fp32
+// state columns held in matrix-core accumulators for the whole sequence.
+// Per chunk the wave computes, on its columns,
+//   [Q;K] S,  X = diag(beta)(V - diag(exp G) K S),  D = T X,
+//   O = scale (diag(exp G) Q S + A D),  S <- exp(G_last) S + K^T diag(lambda) D
+// entirely in registers (see Chain below): nothing but the staged chunk
+// inputs goes through LDS, and the only barrier per chunk is the one that
+// hands over the next chunk's stage buffer.
 //
-// Chunk inputs (Q, K, T, A, the V slice and the decay record) are copied
-// from global memory straight into one of two LDS stage buffers by the
-// direct-to-LDS loads (lane i of a load lands at base + 16 i), one chunk
-// ahead of the chunk being computed, so no registers or LDS store
-// instructions are spent on staging.  Staged rows are not padded: within a
-// row the 16-byte chunks are permuted (Swz) so that the 16-row operand
-// reads and the 4-row transpose reads hit distinct LDS banks.  Rows past the
-// end of a sequence are loaded from its last row: every term they feed is
-// multiplied by beta = 0, by a zero column of A or by a unit row of T.
+// Staging: while computing chunk c from one of two LDS stage buffers, the
+// waves load chunk c + 1 (Q, K, T, A, the V slice, the decay record) into
+// registers and store it into the other buffer after their compute.  Rows
+// past the end of a sequence are loaded from its last row: every term they
+// feed is multiplied by beta = 0 (their rows of X and D are zero) or by a
+// zero column of A.  Within a staged row the 16-byte chunks are permuted
+// (Swz) so that the 16-row operand reads and the 4-row transpose reads hit
+// distinct LDS banks.
 //
 // The S update contracts over the chunk index, so it needs K^T as a matrix
 // operand: with bf16 it is read from the row-major K tile with the LDS
 // transpose read (ds_read_b64_tr_b16: in every group of 16 lanes, input lane
-// 4e + q reads 4 consecutive elements of row e, and output lane j receives
-// column j of the 4 rows); with fp32 every lane reads its single element.
+// 4 e + q reads 4 consecutive elements of row e, and output lane j receives
+// element j % 4 of input lane j / 4's read for each of the 4 rows); with fp32
+// every lane reads its single element.
 //
 // Block index -> work: the 8 XCDs take workgroups round-robin, so the dv
 // slices of one (sequence, head) are placed on one XCD (shared Q, K, T, A
 // reads then hit the same L2).
 // ---------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(1))) void global_void;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Byte layout of a staged tile with rows of RB bytes: row r holds its 16-byte
 // chunk j at position j ^ perm(r).  perm is injective over 16 consecutive rows
@@ -411,6 +419,555 @@ struct Swz {
     __device__ static inline int off(int r, int b) { return r * RB + ((((b >> 4) ^ perm(r)) << 4) | (b & 15)); }
 };
 
+// Tiles read in the row order of the 32-wide chain below: a 16-lane operand
+// read takes rows r0 + 8 a + b (a, b < 4, r0 a multiple of 4), and the
+// transpose read of K takes rows 8 g + e (e < 4) in 16-byte chunks 4 a + q
+// (q < 4).  These chunk permutations keep both patterns free of LDS bank
+// conflicts (for 256-, 128- and 64-byte rows).
+template <int RB>
+struct SwzChain {
+    static_assert(RB == 64 || RB == 128 || RB == 256, "rows of 64, 128 or 256 bytes");
+    __device__ static inline int perm(int r)
+    {
+        if constexpr (RB == 256)
+            return ((r & 3) << 2) | ((r >> 3) & 3);
+        else if constexpr (RB == 128)
+            return (((r >> 1) & 1) << 2) | ((r >> 3) & 3);
+        else
+            return (r >> 3) & 3;
+    }
+    __device__ static inline int off(int r, int b) { return r * RB + ((((b >> 4) ^ perm(r)) << 4) | (b & 15)); }
+};
+
+// ---------------------------------------------------------------------------
+// Register-resident chains of products.  Three products of the chunk step
+// take their B operand from the accumulator tiles of an earlier product:
+// [Q;K] S (S from the S update), T X and A D (X and D from the products
+// before them), K^T (lambda D).  An accumulator tile gives lane l column
+// l % 16 and rows 4 (l / 16) + {0..3}; a B fragment wants column l % 16 and
+// kPerLane contraction indices per lane group.  Chain<M> (M = the consuming
+// instruction) makes the two agree without moving data:
+//   row(t, r)     the matrix row that the PRODUCER computes in row r of its
+//                 output tile t (it reads that row of its own A operand);
+//   b_frag(t, s)  the consumer's B fragment of contraction step s, taken from
+//                 the accumulator tiles as they stand;
+//   a_col(s, l)   first contraction index of lane l's A fragment at step s.
+// ---------------------------------------------------------------------------
+template <typename M>
+struct Chain;
+
+// 16x16x32 bf16: tiles 2s and 2s+1 hold, in lane group g, the contraction
+// indices 32 s + 8 g + {0..3} and 32 s + 8 g + {4..7}.
+template <>
+struct Chain<Mma<bf16>> {
+    __device__ static inline int row(int t, int r) { return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3); }
+    __device__ static inline int a_col(int s, int lane) { return 32 * s + 8 * (lane >> 4); }
+    __device__ static inline bf16x8 b_frag(const f32x4 *t, int s)
+    {
+        const f32x4 a = t[2 * s], b = t[2 * s + 1];
+        return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3], (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+    }
+};
+
+// 16x16x16 bf16: tile s holds the indices 16 s + 4 g + {0..3} as it stands.
+template <>
+struct Chain<MmaBf16K16> {
+    __device__ static inline int row(int t, int r) { return 16 * t + r; }
+    __device__ static inline int a_col(int s, int lane) { return 16 * s + 4 * (lane >> 4); }
+    __device__ static inline bf16x4 b_frag(const f32x4 *t, int s)
+    {
+        const f32x4 a = t[s];
+        return bf16x4{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+    }
+};
+
+// 16x16x4 fp32: step s = 4 t + i uses slot i of tile t, i.e. in lane group g
+// the index 16 t + 4 g + i.
+template <>
+struct Chain<Mma<float>> {
+    __device__ static inline int row(int t, int r) { return 16 * t + r; }
+    __device__ static inline int a_col(int s, int lane) { return 16 * (s >> 2) + 4 * (lane >> 4) + (s & 3); }
+    __device__ static inline float b_frag(const f32x4 *t, int s) { return t[s >> 2][s & 3]; }
+};
+
+// A operand fragment (kPerLane consecutive elements of one row) of a staged tile.
+template <typename M, typename S, typename E>
+__device__ inline typename M::frag staged_frag(const unsigned char *base, int row, int col)
+{
+    return M::load(reinterpret_cast<const E *>(base + S::off(row, col * (int)sizeof(E))));
+}
+
+// A operand of the S update: K^T, output rows = key indices in the order
+// Chain<MK>::row(sr, .), contraction over chunk rows in the order of
+// Chain<MC> (MK, MC: the instructions of the key and chunk contractions).
+template <typename E, typename MC, typename MK, typename S>
+struct KtOperand;
+
+template <typename MC, typename MK, typename S>
+struct KtOperand<bf16, MC, MK, S> {
+    __device__ static inline typename MC::frag load(const unsigned char *Kb, int sr, int s, int lane)
+    {
+        const int g = lane >> 4, e = (lane >> 2) & 3, qd = lane & 3;
+        // input lane (e, qd) reads 4 consecutive key indices: output lanes 4 qd .. 4 qd + 3
+        // receive them, i.e. rows Chain<MK>::row(sr, 4 qd + {0..3}) of the output tile
+        const int b = 2 * Chain<MK>::row(sr, 4 * qd);
+        if constexpr (MC::kPerLane == 8) {
+            const int r0 = 32 * s + 8 * g + e;
+            s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(Kb + S::off(r0, b)));
+            s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(Kb + S::off(r0 + 4, b)));
+            typedef short s16x8 __attribute__((ext_vector_type(8)));
+            s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8, v);
+        } else {
+            s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(Kb + S::off(16 * s + 4 * g + e, b)));
+            return __builtin_bit_cast(bf16x4, lo);
+        }
+    }
+};
+
+template <typename MC, typename MK, typename S>
+struct KtOperand<float, MC, MK, S> {
+    __device__ static inline float load(const unsigned char *Kb, int sr, int s, int lane)
+    {
+        const int c = Chain<MC>::a_col(s, lane);
+        return *reinterpret_cast<const float *>(Kb + S::off(c, 4 * Chain<MK>::row(sr, lane & 15)));
+    }
+};
+
+__device__ inline void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename E, int C, int DK, int NW>
+__global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v, const int32_t *__restrict__ cu,
+    SlotMap map, int32_t num_seqs, int64_t total_tokens, int32_t hqk, int32_t hv, int32_t dv,
+    const E *__restrict__ tmat, const E *__restrict__ amat, const float *__restrict__ dec, const float *state_in,
+    float *state_out, E *__restrict__ o, float scale)
+{
+    constexpr int DVS = 16 * NW;
+    constexpr int NT = NW * kWave;
+    constexpr int ES = (int)sizeof(E);
+    constexpr int RT = C / 16, SR = DK / 16;
+    constexpr int VN = Vec16<E>::n;
+    typedef typename Vec16<E>::type V16;
+    typedef typename MmaFor<E, C>::type MC;     // contractions over the chunk rows
+    typedef typename MmaFor<E, DK>::type MK;    // contractions over the key index
+    typedef Chain<MC> CC;
+    typedef Chain<MK> CK;
+    // Q and A are read in natural row order; K and T in the row order of CC (and K
+    // also by the transpose read).
+    constexpr bool kChain32 = MC::kPerLane == 8;
+    typedef Swz<DK * ES> SQ;
+    typedef typename std::conditional<kChain32, SwzChain<DK * ES>, Swz<DK * ES>>::type SK;
+    typedef typename std::conditional<kChain32, SwzChain<C * ES>, Swz<C * ES>>::type ST;
+    typedef Swz<C * ES> SA;
+    typedef Swz<DVS * ES> SV;
+    typedef KtOperand<E, MC, MK, SK> KT;
+    constexpr int NSK = DK / MK::kStep;   // steps along the key index
+    constexpr int NSC = C / MC::kStep;    // steps along the chunk rows
+    static_assert(C <= kWave, "one lane per token of a chunk");
+    static_assert(DK % 32 == 0 || sizeof(E) == 4, "bf16 key contractions use 32-wide steps");
+
+    // stage buffer layout (bytes) and its 1 KB load jobs (64 lanes x 16 bytes)
+    constexpr int OFF_Q = 0;
+    constexpr int OFF_K = OFF_Q + C * DK * ES;
+    constexpr int OFF_T = OFF_K + C * DK * ES;
+    constexpr int OFF_A = OFF_T + C * C * ES;
+    constexpr int OFF_V = OFF_A + C * C * ES;
+    constexpr int OFF_D = OFF_V + C * DVS * ES;
+    constexpr int STAGE = OFF_D + 4 * C * 4;
+    constexpr int NCK_QK = C * DK * ES / 16;   // 16-byte chunks per tile
+    constexpr int NCK_TA = C * C * ES / 16;
+    constexpr int NCK_V = C * DVS * ES / 16;
+    constexpr int NCK_D = 4 * C * 4 / 16;
+    constexpr int NJ_QK = (NCK_QK + 63) / 64;
+    constexpr int NJ_TA = (NCK_TA + 63) / 64;
+    constexpr int NJ_V = (NCK_V + 63) / 64;
+    constexpr int NJ_D = (NCK_D + 63) / 64;
+    constexpr int J_T = 2 * NJ_QK, J_V = J_T + 2 * NJ_TA, J_D = J_V + NJ_V;
+    constexpr int NJ = J_D + NJ_D;
+    constexpr int NJ_PER = (NJ + NW - 1) / NW;
+
+    __shared__ __attribute__((aligned(1024))) unsigned char stage_mem[2 * STAGE];
+    __shared__ __attribute__((aligned(16))) E Os[NW][C * 16];   // each wave's output columns
+
+    // the stage buffers as LDS addresses (the direct loads write LDS by address)
+    __attribute__((address_space(3))) unsigned char *const lds_stage =
+        (__attribute__((address_space(3))) unsigned char *)stage_mem;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int r16 = lane & 15, g4 = 4 * (lane >> 4);
+    const int nv = dv / DVS;
+    const int pairs = num_seqs * hv;
+    const int bid = blockIdx.x;
+    const int j8 = bid >> 3;
+    const int pair = (j8 / nv) * 8 + (bid & 7);
+    const int s = j8 % nv;
+    if (pair >= pairs)
+        return;
+    const int n = pair / hv, h = pair - (pair / hv) * hv;
+    const int hq = h / (hv / hqk);
+    int64_t a, b;
+    seq_range(cu, n, total_tokens, a, b);
+    const int nch = seq_chunks(map, cu, n, total_tokens, C);
+    const int c_begin = map.seg_first;
+    const int c_end = min(nch, map.seg_first + map.seg_len);
+    const int col = s * DVS + 16 * w + r16;            // this lane's state / output column
+    const size_t state_base = (size_t)(n * hv + h) * DK * dv;
+    if (c_begin >= c_end) {
+        // No chunk of this sequence in this launch.  The first launch still owes the
+        // sequence its final state (initial state passed through, or zeros).
+        if (c_begin == 0 && state_in != state_out) {
+            for (int i = tid; i < DK * DVS; i += NT) {
+                const size_t off = state_base + (size_t)(i / DVS) * dv + s * DVS + (i % DVS);
+                state_out[off] = state_in ? state_in[off] : 0.f;
+            }
+        }
+        return;
+    }
+
+    // ---- state columns into accumulators: tile sr, slot i holds key row CK::row(sr, g4 + i) ----
+    f32x4 sacc[SR];
+#pragma unroll
+    for (int sr = 0; sr < SR; ++sr) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            sacc[sr][i] = state_in ? state_in[state_base + (size_t)CK::row(sr, g4 + i) * dv + col] : 0.f;
+    }
+    typename MK::frag sb[NSK];   // B fragments of S for [Q;K] S
+#pragma unroll
+    for (int st = 0; st < NSK; ++st)
+        sb[st] = CK::b_frag(sacc, st);
+
+    // ---- staging ----
+    // Job J (of NJ) moves 1 KB of the stage with one direct-to-LDS load: lane i writes
+    // the 16 bytes at 16 i of the job's block.  Wave w runs jobs w, w + NW, ...; which
+    // tile and rows a job covers is fixed at compile time, so each lane's source offset
+    // (elements from the chunk's first row, for a full chunk) is computed once.
+    const int qk_row = hqk * DK, v_row = hv * dv;
+    auto job_row = [&](auto jc) __attribute__((always_inline)) -> int {   // source row of this lane
+        constexpr int J = decltype(jc)::value;
+        if constexpr (J < J_T) {
+            return (((J % NJ_QK) * 64 + lane) / (DK * ES / 16));
+        } else if constexpr (J < J_V) {
+            return min(((J - J_T) % NJ_TA) * 64 + lane, NCK_TA - 1) / (C * ES / 16);
+        } else if constexpr (J < J_D) {
+            return min((J - J_V) * 64 + lane, NCK_V - 1) / (DVS * ES / 16);
+        } else {
+            return 0;
+        }
+    };
+    // element offset of this lane's 16 bytes from the tile's origin, given its source row
+    auto job_off = [&](auto jc, int row) __attribute__((always_inline)) -> int {
+        constexpr int J = decltype(jc)::value;
+        if constexpr (J < J_T) {
+            const int P = (J % NJ_QK) * 64 + lane;
+            const int r = P / (DK * ES / 16), pos = P % (DK * ES / 16);
+            const int j = pos ^ (J >= NJ_QK ? SK::perm(r) : SQ::perm(r));
+            return row * qk_row + j * VN;
+        } else if constexpr (J < J_V) {
+            const int P = min(((J - J_T) % NJ_TA) * 64 + lane, NCK_TA - 1);
+            const int r = P / (C * ES / 16), pos = P % (C * ES / 16);
+            const int j = pos ^ ((J - J_T) >= NJ_TA ? SA::perm(r) : ST::perm(r));
+            return r * C + j * VN;
+        } else if constexpr (J < J_D) {
+            const int P = min((J - J_V) * 64 + lane, NCK_V - 1);
+            const int r = P / (DVS * ES / 16), pos = P % (DVS * ES / 16);
+            const int j = pos ^ SV::perm(r);
+            return row * v_row + j * VN;
+        } else {
+            return min((J - J_D) * 64 + lane, NCK_D - 1) * 4;   // floats
+        }
+    };
+    int loff[NJ_PER];   // per-lane source offsets of this wave's jobs, full chunks
+    auto init_offsets = [&](auto wc) __attribute__((always_inline)) {
+        constexpr int W = decltype(wc)::value;
+        static_for<NJ_PER>([&](auto uc) {
+            constexpr int J = W + decltype(uc)::value * NW;
+            if constexpr (J < NJ)
+                loff[decltype(uc)::value] = job_off(std::integral_constant<int, J>{},
+                                                    job_row(std::integral_constant<int, J>{}));
+        });
+    };
+    // Stage chunk c into buffer BUF.  `last` is the index of the chunk's last real row;
+    // rows past it are loaded from it.
+    auto issue_jobs = [&](auto wc, auto bufc, int c) __attribute__((always_inline)) {
+        constexpr int W = decltype(wc)::value;
+        __attribute__((address_space(3))) unsigned char *stg = lds_stage + decltype(bufc)::value * STAGE;
+        const int64_t t0 = a + (int64_t)c * C;
+        const int last = (int)min<int64_t>(C, b - t0) - 1;
+        const size_t slot = slot_of(map, n, c);
+        const E *qb = q + ((size_t)t0 * hqk + hq) * DK;
+        const E *kb = k + ((size_t)t0 * hqk + hq) * DK;
+        const E *vb = v + ((size_t)t0 * hv + h) * dv + (size_t)s * DVS;
+        const E *tb = tmat + (slot * hv + h) * C * C;
+        const E *ab = amat + (slot * hv + h) * C * C;
+        const E *db = reinterpret_cast<const E *>(dec + (slot * hv + h) * 4 * C);
+        const bool full = last == C - 1;
+        static_for<NJ_PER>([&](auto uc) {
+            constexpr int U = decltype(uc)::value;
+            constexpr int J = W + U * NW;
+            if constexpr (J < NJ) {
+                constexpr std::integral_constant<int, J> jc{};
+                const E *base;
+                int off = loff[U];
+                if constexpr (J < J_T) {
+                    base = J >= NJ_QK ? kb : qb;
+                    if (!full)
+                        off = job_off(jc, min(job_row(jc), last));
+                } else if constexpr (J < J_V) {
+                    base = (J - J_T) >= NJ_TA ? ab : tb;
+                } else if constexpr (J < J_D) {
+                    base = vb;
+                    if (!full)
+                        off = job_off(jc, min(job_row(jc), last));
+                } else {
+                    base = db;
+                    off *= (int)(sizeof(float) / sizeof(E));
+                }
+                // lanes of the job that carry data, and the job's block in the stage
+                constexpr int NCK = J < J_T ? NCK_QK : J < J_V ? NCK_TA : J < J_D ? NCK_V : NCK_D;
+                constexpr int IDX = J < J_T ? J % NJ_QK : J < J_V ? (J - J_T) % NJ_TA : J < J_D ? J - J_V : J - J_D;
+                constexpr int NL = NCK - IDX * 64 < 64 ? NCK - IDX * 64 : 64;
+                constexpr int BLK = (J < J_T ? (J >= NJ_QK ? OFF_K : OFF_Q)
+                                             : J < J_V ? ((J - J_T) >= NJ_TA ? OFF_A : OFF_T)
+                                                       : J < J_D ? OFF_V : OFF_D) + IDX * 1024;
+                if (NL == 64 || lane < NL)
+                    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
+                                                     (__attribute__((address_space(3))) void *)(stg + BLK), 16, 0, 0);
+            }
+        });
+    };
+    auto by_wave = [&](auto fn) __attribute__((always_inline)) {
+        if constexpr (NW == 2) {
+            if (w == 0) fn(std::integral_constant<int, 0>{});
+            else fn(std::integral_constant<int, 1>{});
+        } else {
+            static_assert(NW == 4, "2 or 4 waves");
+            switch (w) {
+            case 0: fn(std::integral_constant<int, 0>{}); break;
+            case 1: fn(std::integral_constant<int, 1>{}); break;
+            case 2: fn(std::integral_constant<int, 2>{}); break;
+            default: fn(std::integral_constant<int, 3>{}); break;
+            }
+        }
+    };
+    by_wave([&](auto wc) { init_offsets(wc); });
+    auto issue_stage = [&](auto bufc, int c) __attribute__((always_inline)) {
+        by_wave([&](auto wc) { issue_jobs(wc, bufc, c); });
+    };
+    // The direct loads are not tracked by the compiler's LDS dependences: wait for
+    // them (and this wave's stores) explicitly before the barrier that publishes them.
+    auto stage_done = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    const float inv_scale = 1.f / scale;
+
+    // ---- one chunk step of this wave's 16 columns on stage buffer BUF ----
+    // Operand fragments are read from LDS one group of products ahead of their
+    // use; the scheduling barriers keep the compiler from sinking each read next
+    // to its product, where every product would wait out a full LDS latency.
+    E *os = Os[w];
+    auto step = [&](auto bufc, int64_t t0, int len) __attribute__((always_inline)) {
+        const unsigned char *stg = stage_mem + decltype(bufc)::value * STAGE;
+        const float *Gs = reinterpret_cast<const float *>(stg + OFF_D);   // scale exp(G)
+        const float *Lam = Gs + C;                                         // exp(G_last - G)
+        const float *Bet = Gs + 2 * C;                                     // beta
+        const float *BGam = Gs + 3 * C;                                    // beta exp(G)
+        typedef typename MK::frag FK;
+        typedef typename MC::frag FC;
+
+        // [Q;K] S.  Q rows in natural order (O tiles are only stored); K rows in the
+        // order of CC, since X = f(K S) is the B operand of T X.
+        FK fq[2][RT], fk[2][RT];
+        auto load_qk = [&](int bsel, int st) __attribute__((always_inline)) {
+            const int kc = CK::a_col(st, lane);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                fq[bsel][rt] = staged_frag<MK, SQ, E>(stg + OFF_Q, 16 * rt + r16, kc);
+                fk[bsel][rt] = staged_frag<MK, SK, E>(stg + OFF_K, CC::row(rt, r16), kc);
+            }
+        };
+        load_qk(0, 0);
+        // X = beta V - beta exp(G) (K S) on this lane's rows
+        float xp[RT][4];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int c = CC::row(rt, g4 + i);
+                xp[rt][i] = Bet[c] * to_f32(*reinterpret_cast<const E *>(stg + OFF_V + SV::off(c, (16 * w + r16) * ES)));
+            }
+        }
+        f32x4 qacc[RT], xacc[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            qacc[rt] = zero4();
+            xacc[rt] = zero4();
+        }
+#pragma unroll
+        for (int st = 0; st < NSK; ++st) {
+            if (st + 1 < NSK)
+                load_qk((st + 1) & 1, st + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                qacc[rt] = MK::mma(fq[st & 1][rt], sb[st], qacc[rt]);
+                xacc[rt] = MK::mma(fk[st & 1][rt], sb[st], xacc[rt]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // T fragments (rows in the order of CC: D feeds A D and the S update)
+        FC ft[NSC][RT];
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                ft[st][rt] = staged_frag<MC, ST, E>(stg + OFF_T, CC::row(rt, r16), CC::a_col(st, lane));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xacc[rt][i] = xp[rt][i] - BGam[CC::row(rt, g4 + i)] * xacc[rt][i];
+        FC xb[NSC];
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+            xb[st] = CC::b_frag(xacc, st);
+
+        // K^T fragments of the S update
+        FC fkt[SR][NSC];
+#pragma unroll
+        for (int sr = 0; sr < SR; ++sr)
+#pragma unroll
+            for (int st = 0; st < NSC; ++st)
+                fkt[sr][st] = KT::load(stg + OFF_K, sr, st, lane);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // D = T X
+        f32x4 dacc[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            dacc[rt] = zero4();
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                dacc[rt] = MC::mma(ft[st][rt], xb[st], dacc[rt]);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // A fragments of the output product (A carries the output scale)
+        FC fa[NSC][RT];
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                fa[st][rt] = staged_frag<MC, SA, E>(stg + OFF_A, 16 * rt + r16, CC::a_col(st, lane));
+        __builtin_amdgcn_sched_barrier(0);
+
+        FC db[NSC], lb[NSC];
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+            db[st] = CC::b_frag(dacc, st);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dacc[rt][i] *= Lam[CC::row(rt, g4 + i)];
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+            lb[st] = CC::b_frag(dacc, st);
+
+        // S <- exp(G_last) S + K^T (diag(lambda) D)
+        const float gl = Gs[C - 1] * inv_scale;   // exp(G_last): G is flat past the last real token
+#pragma unroll
+        for (int sr = 0; sr < SR; ++sr) {
+            sacc[sr] = sacc[sr] * gl;
+#pragma unroll
+            for (int st = 0; st < NSC; ++st)
+                sacc[sr] = MC::mma(fkt[sr][st], lb[st], sacc[sr]);
+        }
+#pragma unroll
+        for (int st = 0; st < NSK; ++st)
+            sb[st] = CK::b_frag(sacc, st);
+
+        // O = scale diag(exp G) Q S + (scale A) D, natural row order
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                qacc[rt][i] *= Gs[16 * rt + g4 + i];
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                qacc[rt] = MC::mma(fa[st][rt], db[st], qacc[rt]);
+        // this wave's 16 output columns: through its own LDS rows to 16-byte stores
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                os[(16 * rt + g4 + i) * 16 + r16] = (E)qacc[rt][i];
+        wave_lds_sync();
+        constexpr int RV = 16 / VN;   // 16-byte vectors per row of 16 columns
+        for (int idx = lane; idx < C * RV; idx += kWave) {
+            const int r = idx / RV, cv = (idx % RV) * VN;
+            if (r < len)
+                *reinterpret_cast<V16 *>(o + ((size_t)(t0 + r) * hv + h) * dv + (size_t)s * DVS + 16 * w + cv) =
+                    *reinterpret_cast<const V16 *>(os + r * 16 + cv);
+        }
+        wave_lds_sync();
+    };
+
+    // ---- pipeline: one barrier per chunk; chunk c_begin + 2 m uses buffer 0, the
+    //      next one buffer 1 (the loop is unrolled by two so that both buffers'
+    //      addresses are compile-time offsets) ----
+    const std::integral_constant<int, 0> buf0;
+    const std::integral_constant<int, 1> buf1;
+    issue_stage(buf0, c_begin);
+    stage_done();
+    for (int c = c_begin;;) {
+        if (c + 1 < c_end)
+            issue_stage(buf1, c + 1);
+        int64_t t0 = a + (int64_t)c * C;
+        step(buf0, t0, (int)min<int64_t>(C, b - t0));
+        stage_done();
+        if (++c >= c_end)
+            break;
+        if (c + 1 < c_end)
+            issue_stage(buf0, c + 1);
+        t0 = a + (int64_t)c * C;
+        step(buf1, t0, (int)min<int64_t>(C, b - t0));
+        stage_done();
+        if (++c >= c_end)
+            break;
+    }
+
+    // ---- final state ----
+#pragma unroll
+    for (int sr = 0; sr < SR; ++sr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            state_out[state_base + (size_t)CK::row(sr, g4 + i) * dv + col] = sacc[sr][i];
+}
+
+// ---------------------------------------------------------------------------
+// Scan kernel for few (sequence, head) pairs (bf16 io, chunk 64): one chunk
+// step is spread over 4 compute waves by chunk rows (and key rows for the S
+// update), exchanging X, D and the transposed bf16 copy of S through LDS; 4
+// loader waves stage the next chunk and write out the previous chunk's
+// outputs.  With few pairs the chip has more CUs than workgroups and the
+// chain of chunk steps is latency-bound, which this split shortens.  (Wide
+// batches use gdn_chunk_scan_bf16_kernel.)
+// ---------------------------------------------------------------------------
 // LDS row stride (elements) of the padded key-dimension tile St.  In dwords it
 // is a multiple of 4 with an odd quotient, so 16 rows read with 16-byte
 // accesses hit 16 distinct bank groups.
@@ -423,59 +980,10 @@ constexpr int key_row_stride(int dk)
             return s * 4 / (int)sizeof(E);
 }
 
-template <typename E, int C, int DK>
-struct KtOperand;
-
-// bf16: fragments of K^T straight from the staged K tile (LDS transpose read).
-template <int C, int DK>
-struct KtOperand<bf16, C, DK> {
-    typedef typename MmaFor<bf16, C>::type M;
-    typedef Swz<DK * 2> S;
-    // A-fragment of K^T for output rows m0..m0+15 (key index), contraction slice
-    // starting at chunk row k0.
-    __device__ static inline typename M::frag load(const unsigned char *Kb, int m0, int k0, int lane)
-    {
-        const int g = lane >> 4, s = lane & 15, e = s >> 2, qd = s & 3;
-        const int b = 2 * (m0 + 4 * qd);
-        if constexpr (M::kPerLane == 8) {
-            const int r0 = k0 + 8 * g + e;
-            s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(Kb + S::off(r0, b)));
-            s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(Kb + S::off(r0 + 4, b)));
-            typedef short s16x8 __attribute__((ext_vector_type(8)));
-            s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            return __builtin_bit_cast(bf16x8, v);
-        } else {
-            s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(Kb + S::off(k0 + 4 * g + e, b)));
-            return __builtin_bit_cast(bf16x4, lo);
-        }
-    }
-};
-
-// fp32: every lane reads its element K[k0 + lane/16][m0 + lane%16].
-template <int C, int DK>
-struct KtOperand<float, C, DK> {
-    typedef Mma<float> M;
-    typedef Swz<DK * 4> S;
-    __device__ static inline float load(const unsigned char *Kb, int m0, int k0, int lane)
-    {
-        return *reinterpret_cast<const float *>(Kb + S::off(k0 + (lane >> 4), 4 * (m0 + (lane & 15))));
-    }
-};
-
-// Operand fragment (K-slice of one row) of a staged tile.
-template <typename M, typename S, typename E>
-__device__ inline typename M::frag staged_frag(const unsigned char *base, int row, int col)
-{
-    return M::load(reinterpret_cast<const E *>(base + S::off(row, col * (int)sizeof(E))));
-}
-
 constexpr int kScanThreads = 2 * kThreads;   // 4 compute waves + 4 loader waves
 
 template <typename E, int C, int DK, int DVS>
-__global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
+__global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v, const int32_t *__restrict__ cu,
     SlotMap map, int32_t num_seqs, int64_t total_tokens, int32_t hqk, int32_t hv, int32_t dv,
     const E *__restrict__ tmat, const E *__restrict__ amat, const float *__restrict__ dec, const float *state_in,
@@ -491,12 +999,12 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
     constexpr int RT_PER = (RT + kWaves - 1) / kWaves;
     constexpr int VN = Vec16<E>::n;
     typedef typename Vec16<E>::type V16;
-    typedef KtOperand<E, C, DK> KT;
     typedef typename MmaFor<E, C>::type MC;
     typedef typename MmaFor<E, DK>::type MK;
     typedef Swz<DK * ES> SK;
     typedef Swz<C * ES> SC;
     typedef Swz<DVS * ES> SV;
+    typedef KtOperand<E, MC, MmaBf16K16, SK> KT;   // natural row order of the key index
     static_assert(C <= kWave, "one lane per token of a chunk");
     static_assert(DVS % 16 == 0 && DK % 16 == 0 && C % 16 == 0, "16x16 tiles");
 
@@ -507,11 +1015,11 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
     constexpr int OFF_A = OFF_T + C * C * ES;
     constexpr int OFF_V = OFF_A + C * C * ES;
     constexpr int OFF_D = OFF_V + C * DVS * ES;
-    constexpr int STAGE = OFF_D + 3 * C * 4;
+    constexpr int STAGE = OFF_D + 4 * C * 4;
     constexpr int NJ_QK = (C * DK * ES / 16 + 63) / 64;
     constexpr int NJ_TA = (C * C * ES / 16 + 63) / 64;
     constexpr int NJ_V = (C * DVS * ES / 16 + 63) / 64;
-    constexpr int NJ_D = (3 * C * 4 / 16 + 63) / 64;
+    constexpr int NJ_D = (4 * C * 4 / 16 + 63) / 64;
     constexpr int NJ = 2 * NJ_QK + 2 * NJ_TA + NJ_V + NJ_D;
 
     __shared__ __attribute__((aligned(1024))) unsigned char stage_mem[2 * STAGE];
@@ -551,6 +1059,8 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
         }
         return;
     }
+
+    const float inv_scale = 1.f / scale;
 
     // ---- state slice into accumulators (compute wave w owns key-row tiles w, w+4, ...) ----
     f32x4 sacc[SR_PER][CT];
@@ -623,10 +1133,10 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
                 src = v + ((size_t)(t0 + min(r, last)) * hv + h) * dv + (size_t)s * DVS + j * VN;
                 dst = OFF_V + P * 16;
             } else {
-                constexpr int NCK = 3 * C * 4 / 16;
+                constexpr int NCK = 4 * C * 4 / 16;
                 const int P = job < NJ ? (job - 2 * NJ_QK - 2 * NJ_TA - NJ_V) * 64 + lane : NCK;
                 valid = P < NCK;
-                src = reinterpret_cast<const E *>(dec + (slot * hv + h) * 3 * C + min(P, NCK - 1) * 4);
+                src = reinterpret_cast<const E *>(dec + (slot * hv + h) * 4 * C + min(P, NCK - 1) * 4);
                 dst = OFF_D + P * 16;
             }
             ldst[u] = valid ? dst : -1;
@@ -663,9 +1173,10 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
     // ---- compute waves: one chunk step on stage buffer `cur` (barriers B1 and B2 inside) ----
     auto step = [&](int cur) __attribute__((always_inline)) {
         const unsigned char *stg = stage_mem + cur * STAGE;
-        const float *Gam = reinterpret_cast<const float *>(stg + OFF_D);
-        const float *Lam = Gam + C;
-        const float *Bet = Gam + 2 * C;
+        const float *Gs = reinterpret_cast<const float *>(stg + OFF_D);   // scale exp(G)
+        const float *Lam = Gs + C;                                         // exp(G_last - G)
+        const float *Bet = Gs + 2 * C;                                     // beta
+        const float *BGam = Gs + 3 * C;                                    // beta exp(G)
 
         // P1: Q S and K S for row tile rt (all column tiles); X = diag(beta)(V - diag(exp G) K S)
         //     goes to Xt (transposed); diag(exp G) Q S stays in oacc for P3.
@@ -700,8 +1211,8 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
                     for (int i = 0; i < 4; ++i) {
                         const int rr = rt * 16 + tile_row(lane, i);
                         const E vv = *reinterpret_cast<const E *>(stg + OFF_V + SV::off(rr, col * ES));
-                        x[i] = Bet[rr] * (to_f32(vv) - Gam[rr] * kacc[u][ct][i]);
-                        oacc[u][ct][i] *= Gam[rr];
+                        x[i] = Bet[rr] * to_f32(vv) - BGam[rr] * kacc[u][ct][i];
+                        oacc[u][ct][i] *= Gs[rr];
                     }
                     store4(Xt + col * LDC + rt * 16 + tile_row(lane, 0), x[0], x[1], x[2], x[3]);
                 }
@@ -738,7 +1249,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
         }
         __syncthreads();   // B2
 
-        // P3: O = diag(exp G) Q S + A D, scaled, staged in Os
+        // P3: O = scale diag(exp G) Q S + (scale A) D, staged in Os
 #pragma unroll
         for (int u = 0; u < RT_PER; ++u) {
             const int rt = wave + u * kWaves;
@@ -756,11 +1267,11 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         Os[(rt * 16 + tile_row(lane, i)) * LDV + ct * 16 + tile_col(lane)] =
-                            (E)(scale * oacc[u][ct][i]);
+                            (E)oacc[u][ct][i];
             }
         }
         // P4: S <- exp(G_last) S + K^T diag(lambda) D; refresh the transposed copy
-        const float gl = Gam[C - 1];   // exp(G_last): G is flat past the last real token
+        const float gl = Gs[C - 1] * inv_scale;   // exp(G_last): G is flat past the last real token
 #pragma unroll
         for (int u = 0; u < SR_PER; ++u) {
             const int sr = wave + u * kWaves;
@@ -771,7 +1282,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
                 const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
 #pragma unroll
                 for (int k0 = 0; k0 < C; k0 += MC::kStep) {
-                    const typename MC::frag akt = KT::load(stg + OFF_K, sr * 16, k0, lane);
+                    const typename MC::frag akt = KT::load(stg + OFF_K, sr, k0 / MC::kStep, lane);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
                         sacc[u][ct] = MC::mma(akt, MC::load(LDt + (ct * 16 + r) * LDC + k0 + kk), sacc[u][ct]);
@@ -829,32 +1340,523 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Scan kernel for bf16 io and chunk 64 (the Qwen3.5 shapes): the same chunk
+// step as gdn_chunk_scan_kernel above, with the chunk's matrix operands staged
+// in FRAGMENT ORDER.  Every operand tile is a sequence of 1 KB units of 16
+// rows x 32 contraction indices; in a unit, the 16 bytes at position p belong
+// to matrix-core lane m(p): row m % 16 of the unit's rows, contraction indices
+// 8 (m / 16) .. +7.  One direct-to-LDS load fills one unit (lane i of the load
+// fetches the 16 bytes of position i), and one LDS read of 16 bytes at 16 l
+// gives lane l its operand fragment: neither side computes addresses beyond a
+// per-lane constant and instruction offsets, and a unit read covers 1 KB of
+// distinct banks.
+//   Q, A units (rt, kb): rows 16 rt + r (natural order), m(p) = p.
+//   T units (rt, kb):    rows Chain row(rt, r), m(p) = p.
+//   K units (rt, kb):    rows Chain row(rt, r); m(p) = r + 16 g with g = p / 16,
+//                        r = (p % 16) ^ 4 g, which keeps both the fragment read
+//                        and the transpose read of K^T conflict-free.
+//   V (the dv slice):    row-major; the 16-byte chunks of a row are permuted
+//                        (XOR with 2 (r % 4) for 256-byte rows, 2 ((r / 2) % 2)
+//                        for 128-byte rows) so that the transpose read of 4
+//                        consecutive rows of one column block is conflict-free.
+//   decay record:        [scale exp(G) | exp(G_last - G) | beta | beta exp(G)].
+// Each wave owns CT tiles of 16 state columns: every operand fragment read
+// from LDS then feeds CT matrix instructions.  The output is computed
+// transposed (O^T = (Q S)^T ... with S^T and D^T as the A operands, whose
+// registers are the B fragments as they stand), so that each lane holds 4
+// consecutive columns of one token row and stores them as one 8-byte write.
+// ---------------------------------------------------------------------------
+template <int DK, int NW, int CT>
+__global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const int32_t *__restrict__ cu, SlotMap map, int32_t num_seqs, int64_t total_tokens, int32_t hqk, int32_t hv,
+    int32_t dv, const bf16 *__restrict__ tmat, const bf16 *__restrict__ amat, const float *__restrict__ dec,
+    const float *state_in, float *state_out, bf16 *__restrict__ o, float scale)
+{
+    constexpr int C = 64;
+    constexpr int WC = 16 * CT;                   // columns per wave
+    constexpr int DVS = WC * NW;                  // columns per workgroup
+    constexpr int NT = NW * kWave;
+    constexpr int RT = C / 16, SR = DK / 16;
+    constexpr int NSK = DK / 32, NSC = C / 32;
+    typedef Mma<bf16> M;
+    typedef Chain<M> CH;
+    static_assert(DK % 32 == 0, "32-wide contraction steps");
+
+    // stage layout (bytes): 1 KB units
+    constexpr int NU_QK = RT * NSK, NU_TA = RT * NSC;
+    constexpr int VRB = DVS * 2;                   // bytes per row of the V slice
+    constexpr int NU_V = C * VRB / 1024;
+    constexpr int OFF_Q = 0;
+    constexpr int OFF_K = OFF_Q + NU_QK * 1024;
+    constexpr int OFF_T = OFF_K + NU_QK * 1024;
+    constexpr int OFF_A = OFF_T + NU_TA * 1024;
+    constexpr int OFF_V = OFF_A + NU_TA * 1024;
+    constexpr int OFF_D = OFF_V + NU_V * 1024;
+    constexpr int STAGE = OFF_D + 1024;
+    static_assert(C * VRB % 1024 == 0 && 4 * C * 4 == 1024, "whole units");
+    static_assert(VRB == 64 || VRB == 128 || VRB == 256, "V slice rows of 64, 128 or 256 bytes");
+
+    // The two stage buffers are separate objects, so that the compiler can tell the
+    // direct loads into one from the reads of the other (a single array would make
+    // every read of the current chunk wait for the loads of the next).
+    __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
+    auto stage_ptr = [&](auto bufc) __attribute__((always_inline)) -> unsigned char * {
+        return decltype(bufc)::value ? stage1 : stage0;
+    };
+    auto stage_lds = [&](auto bufc) __attribute__((always_inline)) {
+        return (__attribute__((address_space(3))) unsigned char *)(decltype(bufc)::value ? stage1 : stage0);
+    };
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int r16 = lane & 15, G = lane >> 4, g4 = 4 * G;
+    const int nv = dv / DVS;
+    const int pairs = num_seqs * hv;
+    const int bid = blockIdx.x;
+    const int j8 = bid >> 3;
+    const int pair = (j8 / nv) * 8 + (bid & 7);
+    const int s = j8 % nv;
+    if (pair >= pairs)
+        return;
+    const int n = pair / hv, h = pair - (pair / hv) * hv;
+    const int hq = h / (hv / hqk);
+    int64_t a, b;
+    seq_range(cu, n, total_tokens, a, b);
+    const int nch = seq_chunks(map, cu, n, total_tokens, C);
+    const int c_begin = map.seg_first;
+    const int c_end = min(nch, map.seg_first + map.seg_len);
+    const int col0 = s * DVS + WC * w;                  // first state / output column of this wave
+    const size_t state_base = (size_t)(n * hv + h) * DK * dv;
+    if (c_begin >= c_end) {
+        if (c_begin == 0 && state_in != state_out) {
+            for (int i = tid; i < DK * DVS; i += NT) {
+                const size_t off = state_base + (size_t)(i / DVS) * dv + s * DVS + (i % DVS);
+                state_out[off] = state_in ? state_in[off] : 0.f;
+            }
+        }
+        return;
+    }
+
+    // ---- state columns in accumulators: tile (sr, ct), slot i holds key row
+    //      CH::row(sr, g4 + i), column col0 + 16 ct + l % 16 ----
+    f32x4 sacc[SR][CT];
+#pragma unroll
+    for (int sr = 0; sr < SR; ++sr)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sacc[sr][ct][i] = state_in ? state_in[state_base + (size_t)CH::row(sr, g4 + i) * dv + col0 + 16 * ct +
+                                                      r16]
+                                           : 0.f;
+    bf16x8 sb[NSK][CT];
+    auto pack_s = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            f32x4 t[SR];
+#pragma unroll
+            for (int sr = 0; sr < SR; ++sr)
+                t[sr] = sacc[sr][ct];
+#pragma unroll
+            for (int st = 0; st < NSK; ++st)
+                sb[st][ct] = CH::b_frag(t, st);
+        }
+    };
+    pack_s();
+
+    // ---- staging ----
+    // chunk c of the sequence sits in workspace slot slot0 + c (in either launch mode)
+    const size_t slot0 = slot_of(map, n, 0);
+    // The stage is filled in rounds of NW units: in round R every wave loads one unit of
+    // the same tile (unit (R - first round of the tile) NW + w), so all waves run the same
+    // code and each lane's source offsets are computed once.  Rounds: Q, K, T, A, the V
+    // slice, then the decay record (wave 0 only).
+    constexpr int R_Q = NU_QK / NW, R_T = NU_TA / NW, R_V = NU_V / NW;
+    static_assert(NU_QK % NW == 0 && NU_TA % NW == 0 && NU_V % NW == 0, "whole rounds");
+    constexpr int RK0 = R_Q, RT0 = 2 * R_Q, RA0 = RT0 + R_T, RV0 = RA0 + R_T, RD0 = RV0 + R_V;
+    constexpr int NR = RD0 + 1;
+    const int qk_row = hqk * DK, v_row = hv * dv;
+    // (row in the chunk, element column, stage offset of the unit) of this lane's 16
+    // bytes in round R
+    auto round_src = [&](auto rc, int &row, int &ecol, int &blk) __attribute__((always_inline)) {
+        constexpr int R = decltype(rc)::value;
+        if constexpr (R < RT0) {                       // Q or K unit (rt, kb)
+            const int u = (R < RK0 ? R : R - RK0) * NW + w;
+            const int rt = u / NSK, kb = u % NSK;
+            row = R < RK0 ? 16 * rt + r16 : CH::row(rt, r16 ^ g4);
+            ecol = 32 * kb + 8 * G;
+            blk = (R < RK0 ? OFF_Q : OFF_K) + u * 1024;
+        } else if constexpr (R < RV0) {                // T or A unit (rt, kb)
+            const int u = (R < RA0 ? R - RT0 : R - RA0) * NW + w;
+            const int rt = u / NSC, kb = u % NSC;
+            row = R < RA0 ? CH::row(rt, r16) : 16 * rt + r16;
+            ecol = 32 * kb + 8 * G;
+            blk = (R < RA0 ? OFF_T : OFF_A) + u * 1024;
+        } else if constexpr (R < RD0) {                // 1 KB of rows of the V slice
+            const int u = (R - RV0) * NW + w;
+            const int P = u * 64 + lane;                  // physical 16-byte chunk
+            row = P / (VRB / 16);
+            int j = P % (VRB / 16);
+            if constexpr (VRB == 256)
+                j ^= 2 * (row & 3);
+            else if constexpr (VRB == 128)
+                j ^= 2 * ((row >> 1) & 1);
+            ecol = j * 8;
+            blk = OFF_V + u * 1024;
+        } else {                                       // decay record, 4 floats per lane
+            row = 0;
+            ecol = lane * 4;
+            blk = OFF_D;
+        }
+    };
+    // byte offset of this lane's 16 bytes from the chunk's base of the tile
+    auto round_bytes = [&](auto rc, int row, int ecol) __attribute__((always_inline)) -> uint32_t {
+        constexpr int R = decltype(rc)::value;
+        if constexpr (R < RT0)
+            return (uint32_t)(row * qk_row + ecol) * 2u;
+        else if constexpr (R < RV0)
+            return (uint32_t)(row * C + ecol) * 2u;
+        else if constexpr (R < RD0)
+            return (uint32_t)(row * v_row + ecol) * 2u;
+        else
+            return (uint32_t)ecol * 4u;
+    };
+    uint32_t loff[NR];
+    int lblk[NR];
+    static_for<NR>([&](auto rc) __attribute__((always_inline)) {
+        int row, ecol, blk;
+        round_src(rc, row, ecol, blk);
+        loff[decltype(rc)::value] = round_bytes(rc, row, ecol);
+        lblk[decltype(rc)::value] = blk;
+    });
+    auto issue_stage = [&](auto bufc, int c) __attribute__((always_inline)) {
+        __attribute__((address_space(3))) unsigned char *stg = stage_lds(bufc);
+        const int64_t t0 = a + (int64_t)c * C;
+        const int last = (int)min<int64_t>(C, b - t0) - 1;
+        const size_t slot = slot0 + c;
+        // wave-uniform bases: the loads take them as a scalar base plus a 32-bit lane offset
+        const char *qb = reinterpret_cast<const char *>(q + ((size_t)t0 * hqk + hq) * DK);
+        const char *kb = reinterpret_cast<const char *>(k + ((size_t)t0 * hqk + hq) * DK);
+        const char *vb = reinterpret_cast<const char *>(v + ((size_t)t0 * hv + h) * dv + (size_t)s * DVS);
+        const char *tb = reinterpret_cast<const char *>(tmat + (slot * hv + h) * C * C);
+        const char *ab = reinterpret_cast<const char *>(amat + (slot * hv + h) * C * C);
+        const char *db = reinterpret_cast<const char *>(dec + (slot * hv + h) * 4 * C);
+        const bool full = last == C - 1;
+        static_for<NR>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int R = decltype(rc)::value;
+            uint32_t off = loff[R];
+            if constexpr (R < RT0 || (R >= RV0 && R < RD0)) {
+                if (!full) {   // ragged last chunk: rows past its end repeat its last row
+                    int row, ecol, blk;
+                    round_src(rc, row, ecol, blk);
+                    off = round_bytes(rc, min(row, last), ecol);
+                }
+            }
+            const char *base = R < RK0 ? qb : R < RT0 ? kb : R < RA0 ? tb : R < RV0 ? ab : R < RD0 ? vb : db;
+            if (R < RD0 || w == 0)
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
+                                                 (__attribute__((address_space(3))) void *)(stg + lblk[R]), 16, 0,
+                                                 0);
+        });
+    };
+    auto stage_done = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    const float inv_scale = 1.f / scale;
+
+    // per-lane LDS byte offsets (everything else is an instruction offset)
+    const int lin = 16 * lane;                                   // Q, T, A units
+    const int kperm = 16 * (16 * G + (r16 ^ g4));                 // K units, fragment read
+    const int e = (lane >> 2) & 3, qd = lane & 3;
+    const int ktr = 16 * (16 * qd + 4 * (G ^ qd) + e);            // K units, transpose read
+    // V slice, transpose read of column block ct of this wave: rows 8 G + e (+ the
+    // tile's first row), logical chunk 2 (CT w + ct) + qd / 2, physical = logical ^ X(row)
+    auto vtr = [&](int ct) __attribute__((always_inline)) -> int {
+        int chunk = 2 * (CT * w + ct) + (qd >> 1);
+        if constexpr (VRB == 256)
+            chunk ^= 2 * e;
+        else if constexpr (VRB == 128)
+            chunk ^= 2 * (e >> 1);
+        return (8 * G + e) * VRB + 16 * chunk + 8 * (qd & 1);
+    };
+    int vtro[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+        vtro[ct] = vtr(ct);
+
+    // ---- one chunk step of this wave's WC columns on stage buffer BUF ----
+    auto step = [&](auto bufc, int64_t t0, int len) __attribute__((always_inline)) {
+        const unsigned char *stg = stage_ptr(bufc);
+        auto frag = [&](int off) __attribute__((always_inline)) {
+            return *reinterpret_cast<const bf16x8 *>(stg + off);
+        };
+        auto rec4 = [&](int arr, int row0) __attribute__((always_inline)) {
+            return *reinterpret_cast<const f32x4 *>(stg + OFF_D + 4 * (arr * C + row0));
+        };
+        auto tr4 = [&](int off) __attribute__((always_inline)) {
+            return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(stage_lds(bufc) + off));
+        };
+
+        // [Q;K] S: (Q S)^T with S^T as the A operand; K S with K rows in the order of CH
+        bf16x8 fq[2][RT], fk[2][RT];
+        auto load_qk = [&](int bsel, int st) __attribute__((always_inline)) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                fq[bsel][rt] = frag(OFF_Q + (rt * NSK + st) * 1024 + lin);
+                fk[bsel][rt] = frag(OFF_K + (rt * NSK + st) * 1024 + kperm);
+            }
+        };
+        load_qk(0, 0);
+        // beta v on this lane's rows CH::row(rt, g4 + i) (the bit cast is of the whole
+        // vector: a bit cast of one element of a vector reads element 0)
+        f32x4 xp[RT][CT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const f32x4 bt = rec4(2, CH::row(rt, g4));
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const bf16x4 vv = __builtin_bit_cast(bf16x4, tr4(OFF_V + CH::row(rt, 0) * VRB + vtro[ct]));
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xp[rt][ct][i] = bt[i] * (float)vv[i];
+            }
+        }
+        f32x4 qacc[RT][CT], xacc[RT][CT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                qacc[rt][ct] = zero4();
+                xacc[rt][ct] = zero4();
+            }
+#pragma unroll
+        for (int st = 0; st < NSK; ++st) {
+            if (st + 1 < NSK)
+                load_qk((st + 1) & 1, st + 1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct) {
+                    qacc[rt][ct] = M::mma(sb[st][ct], fq[st & 1][rt], qacc[rt][ct]);
+                    xacc[rt][ct] = M::mma(fk[st & 1][rt], sb[st][ct], xacc[rt][ct]);
+                }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+
+        // T fragments, then X = beta v - beta exp(G) (K S)
+        bf16x8 ft[NSC][RT];
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                ft[st][rt] = frag(OFF_T + (rt * NSC + st) * 1024 + lin);
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 xb[NSC][CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            f32x4 t[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                t[rt] = xp[rt][ct] - rec4(3, CH::row(rt, g4)) * xacc[rt][ct];
+#pragma unroll
+            for (int st = 0; st < NSC; ++st)
+                xb[st][ct] = CH::b_frag(t, st);
+        }
+
+        // K^T fragments of the S update: rows CH::row(sr, .) of the key index, chunk rows
+        // 32 st + 8 G + {0..7} (units rt = 2 st and 2 st + 1)
+        bf16x8 fkt[SR][NSC];
+#pragma unroll
+        for (int sr = 0; sr < SR; ++sr)
+#pragma unroll
+            for (int st = 0; st < NSC; ++st) {
+                const int base = OFF_K + (sr >> 1) * 1024 + ktr + 8 * (sr & 1);
+                const s16x4 lo = tr4(base + (2 * st) * NSK * 1024);
+                const s16x4 hi = tr4(base + (2 * st + 1) * NSK * 1024);
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                fkt[sr][st] = __builtin_bit_cast(bf16x8, vv);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // D = T X
+        f32x4 dacc[RT][CT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                dacc[rt][ct] = zero4();
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    dacc[rt][ct] = M::mma(ft[st][rt], xb[st][ct], dacc[rt][ct]);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // A fragments (A carries the output scale)
+        bf16x8 fa[NSC][RT];
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                fa[st][rt] = frag(OFF_A + (rt * NSC + st) * 1024 + lin);
+        __builtin_amdgcn_sched_barrier(0);
+
+        bf16x8 db[NSC][CT], lb[NSC][CT];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            f32x4 t[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                t[rt] = dacc[rt][ct];
+#pragma unroll
+            for (int st = 0; st < NSC; ++st)
+                db[st][ct] = CH::b_frag(t, st);
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                t[rt] *= rec4(1, CH::row(rt, g4));
+#pragma unroll
+            for (int st = 0; st < NSC; ++st)
+                lb[st][ct] = CH::b_frag(t, st);
+        }
+
+        // S <- exp(G_last) S + K^T (diag(lambda) D)
+        const float gl = *reinterpret_cast<const float *>(stg + OFF_D + 4 * (C - 1)) * inv_scale;
+#pragma unroll
+        for (int sr = 0; sr < SR; ++sr)
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                sacc[sr][ct] = sacc[sr][ct] * gl;
+#pragma unroll
+                for (int st = 0; st < NSC; ++st)
+                    sacc[sr][ct] = M::mma(fkt[sr][st], lb[st][ct], sacc[sr][ct]);
+            }
+        pack_s();
+
+        // O^T = scale (Q S)^T diag(exp G) + D^T (scale A)^T: lane l holds token row
+        // 16 rt + l % 16 and the four columns 16 ct + 4 (l / 16) .. +3 of this wave's
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const float gs = *reinterpret_cast<const float *>(stg + OFF_D + 4 * (16 * rt + r16));
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+                qacc[rt][ct] *= gs;
+        }
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    qacc[rt][ct] = M::mma(db[st][ct], fa[st][rt], qacc[rt][ct]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int r = 16 * rt + r16;
+            if (r < len) {
+                bf16 *orow = o + ((size_t)(t0 + r) * hv + h) * dv + col0 + g4;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+                    *reinterpret_cast<bf16x4 *>(orow + 16 * ct) =
+                        bf16x4{(bf16)qacc[rt][ct][0], (bf16)qacc[rt][ct][1], (bf16)qacc[rt][ct][2],
+                               (bf16)qacc[rt][ct][3]};
+            }
+        }
+    };
+
+    // ---- pipeline: one barrier per chunk; buffers alternate from buffer 0 ----
+    const std::integral_constant<int, 0> buf0;
+    const std::integral_constant<int, 1> buf1;
+    issue_stage(buf0, c_begin);
+    stage_done();
+    for (int c = c_begin;;) {
+        if (c + 1 < c_end)
+            issue_stage(buf1, c + 1);
+        int64_t t0 = a + (int64_t)c * C;
+        step(buf0, t0, (int)min<int64_t>(C, b - t0));
+        stage_done();
+        if (++c >= c_end)
+            break;
+        if (c + 1 < c_end)
+            issue_stage(buf0, c + 1);
+        t0 = a + (int64_t)c * C;
+        step(buf1, t0, (int)min<int64_t>(C, b - t0));
+        stage_done();
+        if (++c >= c_end)
+            break;
+    }
+
+    // ---- final state ----
+#pragma unroll
+    for (int sr = 0; sr < SR; ++sr)
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                state_out[state_base + (size_t)CH::row(sr, g4 + i) * dv + col0 + 16 * ct + r16] = sacc[sr][ct][i];
+}
+
+// ---------------------------------------------------------------------------
 // Launch.
 // ---------------------------------------------------------------------------
 
-// Widest dv slice that still gives the chip at least two workgroups per CU.
-static int pick_dvs(int64_t pairs, int dv, int widest)
+// Waves per scan workgroup (16 state columns each): four (64 columns) for bf16
+// io, two when dv = 32 and for fp32 io (whose two stage buffers then still
+// fit in LDS).
+template <typename E>
+static int pick_waves(int dv)
 {
-    const int64_t want = 512;
-    if (widest >= 64 && dv % 64 == 0 && pairs * (dv / 64) >= want)
-        return 64;
-    if (dv % 32 == 0 && pairs * (dv / 32) >= want)
-        return 32;
-    return 16;
+    if (sizeof(E) == 2 && dv % 64 == 0)
+        return 4;
+    return 2;
 }
 
-template <typename E, int C, int DK, int DVS>
+template <typename E, int C, int DK, int NW>
 static void launch_scan(const PrefillArgs &p, const SlotMap &map, const E *tmat, const E *amat, const float *dec,
                         const float *sin, float *sout, hipStream_t st)
+{
+    const int nv = p.dv / (16 * NW);
+    const int64_t pairs = (int64_t)p.num_seqs * p.hv;
+    const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
+    const ProfEvents ev = prof_events(PROF_SCAN);
+    hipExtLaunchKernelGGL((gdn_chunk_scan_kernel<E, C, DK, NW>), dim3((unsigned)blocks), dim3(NW * kWave), 0, st,
+                          ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k),
+                          static_cast<const E *>(p.v), p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv,
+                          p.dv, tmat, amat, dec, sin, sout, static_cast<E *>(p.o), p.scale);
+}
+
+template <int DK, int DVS>
+static void launch_scan_rows(const PrefillArgs &p, const SlotMap &map, const bf16 *tmat, const bf16 *amat,
+                             const float *dec, const float *sin, float *sout, hipStream_t st)
 {
     const int nv = p.dv / DVS;
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
     const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
     const ProfEvents ev = prof_events(PROF_SCAN);
-    hipExtLaunchKernelGGL((gdn_chunk_scan_kernel<E, C, DK, DVS>), dim3((unsigned)blocks), dim3(kScanThreads), 0, st,
-                          ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k),
-                          static_cast<const E *>(p.v), p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv,
-                          p.dv, tmat, amat, dec, sin, sout, static_cast<E *>(p.o), p.scale);
+    hipExtLaunchKernelGGL((gdn_chunk_scan_rows_kernel<bf16, 64, DK, DVS>), dim3((unsigned)blocks),
+                          dim3(kScanThreads), 0, st, ev.start, ev.stop, 0, static_cast<const bf16 *>(p.q),
+                          static_cast<const bf16 *>(p.k), static_cast<const bf16 *>(p.v), p.cu_seqlens, map,
+                          p.num_seqs, p.total_tokens, p.hqk, p.hv, p.dv, tmat, amat, dec, sin, sout,
+                          static_cast<bf16 *>(p.o), p.scale);
+}
+
+template <int DK, int NW, int CT>
+static void launch_scan_bf16(const PrefillArgs &p, const SlotMap &map, const bf16 *tmat, const bf16 *amat,
+                             const float *dec, const float *sin, float *sout, hipStream_t st)
+{
+    const int nv = p.dv / (16 * CT * NW);
+    const int64_t pairs = (int64_t)p.num_seqs * p.hv;
+    const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
+    const ProfEvents ev = prof_events(PROF_SCAN);
+    hipExtLaunchKernelGGL((gdn_chunk_scan_bf16_kernel<DK, NW, CT>), dim3((unsigned)blocks), dim3(NW * kWave), 0,
+                          st, ev.start, ev.stop, 0, static_cast<const bf16 *>(p.q), static_cast<const bf16 *>(p.k),
+                          static_cast<const bf16 *>(p.v), p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv,
+                          p.dv, tmat, amat, dec, sin, sout, static_cast<bf16 *>(p.o), p.scale);
 }
 
 template <typename E, int C, int DK>
@@ -866,26 +1868,33 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
     E *tmat = reinterpret_cast<E *>(static_cast<char *>(p.workspace) + p.table_bytes);
     E *amat = tmat + (size_t)p.max_chunks * p.hv * C * C;
     float *dec = reinterpret_cast<float *>(amat + (size_t)p.max_chunks * p.hv * C * C);
-    const int64_t pairs = (int64_t)p.num_seqs * p.hv;
-    // Two stage buffers of a chunk leave room for slices of at most 32 columns (bf16)
-    // or 16 columns (fp32).
-    constexpr bool kWide = sizeof(E) == 2;
-    const int dvs = pick_dvs(pairs, p.dv, kWide ? 32 : 16);
+    const int nw = pick_waves<E>(p.dv);
 
     auto scan = [&](const SlotMap &map, const float *sin, float *sout) {
-        if constexpr (kWide) {
-            if (dvs == 32) {
-                launch_scan<E, C, DK, 32>(p, map, tmat, amat, dec, sin, sout, st);
-                return;
+        if constexpr (std::is_same<E, bf16>::value && C == 64) {
+            // 32 columns per wave; a whole 128-column head per workgroup when the batch
+            // has enough (sequence, head) pairs to fill the chip, else 64 columns
+            // Few (sequence, head) pairs: the chain of chunk steps is latency-bound, so a
+            // step is spread over the rows of 4 waves (16-column slices).  Many pairs:
+            // whole 128-column heads with each wave owning 32 columns.
+            const int64_t pairs = (int64_t)p.num_seqs * p.hv;
+            if constexpr (DK == 128) {
+                if (pairs >= 256) {
+                    launch_scan_bf16<DK, 4, 2>(p, map, tmat, amat, dec, sin, sout, st);
+                    return;
+                }
             }
+            launch_scan_rows<DK, 16>(p, map, tmat, amat, dec, sin, sout, st);
+        } else {
+            launch_scan<E, C, DK, 2>(p, map, tmat, amat, dec, sin, sout, st);
         }
-        launch_scan<E, C, DK, 16>(p, map, tmat, amat, dec, sin, sout, st);
     };
     auto prep = [&](const SlotMap &map, int64_t slots) {
         const ProfEvents ev = prof_events(PROF_PREP);
         hipExtLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), dim3((unsigned)slots, p.hqk), dim3(kThreads), 0, st,
                               ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k), p.g,
-                              p.beta, p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv, tmat, amat, dec);
+                              p.beta, p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv, tmat, amat, dec,
+                              p.scale);
     };
 
     if (p.seg_len > 0) {

@@ -63,7 +63,7 @@ def test_workspace_size(lib):
     sh = shape()
     T, N = 1000, 3
     max_chunks = -(-T // 64) + N
-    expect = 256 + 2 * max_chunks * 32 * 64 * 64 * 2 + max_chunks * 32 * 3 * 64 * 4
+    expect = 256 + 2 * max_chunks * 32 * 64 * 64 * 2 + max_chunks * 32 * 4 * 64 * 4
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), T, N) == expect
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(shape(d=96)), T, N) == 0     # unsupported
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(shape(hqk=3)), T, N) == 0    # 32 % 3 != 0
