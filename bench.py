@@ -39,6 +39,8 @@ METRIC = "prefill tokens/s + decode tokens/s (Qwen3.5-9B GDN layer), % MFMA/HBM 
 # while the kernel's sources still hash to the digest stored beside it.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 KERNEL_SOURCES = {
+    "gdn_chunk_scan_rows_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
+    "gdn_chunk_scan_bf16_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_chunk_scan_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_prep_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_decode_kernel": ("gated_deltanet_scan_amd/csrc/gdn_decode.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
@@ -90,7 +92,7 @@ def prefill_costs(w, lengths):
     E = sum((L + C - 1) // C for L in lengths)
     qk_bytes = 2 * T * hqk * dk * es
     gb_bytes = 2 * T * hv * 4
-    ta_bytes = 2 * E * hv * C * C * es
+    ta_bytes = 2 * E * hv * C * C * es + E * hv * 4 * C * 4     # T, A and the decay record
     s_in = N * hv * dk * dv * 4 if w.s0_std is not None else 0
     s_out = N * hv * dk * dv * 4
     prep = {
@@ -176,6 +178,7 @@ def measure_prefill(name, steps, warmup, lengths=None):
         "mfma_frac": flops / (ms * 1e-3) / (peak * 1e12),
         "hbm_frac": costs["io_bytes"] / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "kernels": kern,
+        "scan_kernel": scan_kernel_name(w, lengths),
     }
     # whole-step costs over the kernel's summed launch time (a long or batched prefill is
     # cut into several launches of each kernel)
@@ -188,6 +191,17 @@ def measure_prefill(name, steps, warmup, lengths=None):
     out["_costs"] = costs
     out["_peak_tflops"] = peak
     return out
+
+
+def scan_kernel_name(w, lengths):
+    """Which scan kernel the library runs for this batch (bf16 io, chunk 64: whole-head
+    workgroups for wide batches of 128-dim heads, the row-split kernel otherwise)."""
+    import torch
+    if w.io_dtype == torch.bfloat16 and w.chunk == 64:
+        if w.dv == 128 and len(lengths) * w.hv >= 256:
+            return "gdn_chunk_scan_bf16_kernel"
+        return "gdn_chunk_scan_rows_kernel"
+    return "gdn_chunk_scan_kernel"
 
 
 def roofline_for(pre):
@@ -208,7 +222,7 @@ def roofline_for(pre):
         achieved = c["flops"] / (us * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": pre["_peak_tflops"], "unit": "TFLOP/s",
                 "frac": achieved / pre["_peak_tflops"]}
-    kernel = "gdn_prep_kernel" if name == "prep" else "gdn_chunk_scan_kernel"
+    kernel = "gdn_prep_kernel" if name == "prep" else pre["scan_kernel"]
     roof.update({"traffic": measured_traffic(kernel, pre["workload"]), "kernel": kernel,
                  "avg_us": us, "algorithmic_bytes": c["bytes"], "algorithmic_flops": c["flops"],
                  "intensity_flop_per_byte": intensity})
