@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
     __shared__ __attribute__((aligned(16))) unsigned char smem_a[U1];
     __shared__ __attribute__((aligned(16))) unsigned char smem_b[U2];
     __shared__ __attribute__((aligned(16))) float Yw[kWaves][16][17];
-    __shared__ float Gs[HB][C];
+    __shared__ __attribute__((aligned(16))) float Gs[HB][C];
     __shared__ float Bs[HB][C];
     E *Ks = reinterpret_cast<E *>(smem_a);
     E *Qs = Ks + C * LDK;
@@ -270,11 +270,20 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
             const float gt = Gs[hh][t], bt = Bs[hh][t];
             V16 av;
 #pragma unroll
-            for (int e = 0; e < VN; ++e) {
-                const int j = j0 + e;
-                const float ed = (j <= t) ? __expf(gt - Gs[hh][j]) : 0.f;
-                Nm[(hh * C + t) * LDF + j] = (j < t) ? bt * ed * KK[t * LDF + j] : 0.f;
-                av[e] = (E)(scale * ed * QK[t * LDF + j]);
+            for (int e4 = 0; e4 < VN; e4 += 4) {
+                // four consecutive entries at a time (16-byte LDS accesses)
+                const f32x4 gj = *reinterpret_cast<const f32x4 *>(&Gs[hh][j0 + e4]);
+                const f32x4 kk = *reinterpret_cast<const f32x4 *>(KK + t * LDF + j0 + e4);
+                const f32x4 qk = *reinterpret_cast<const f32x4 *>(QK + t * LDF + j0 + e4);
+                f32x4 nv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = j0 + e4 + e;
+                    const float ed = (j <= t) ? __expf(gt - gj[e]) : 0.f;
+                    nv[e] = (j < t) ? bt * ed * kk[e] : 0.f;
+                    av[e4 + e] = (E)(scale * ed * qk[e]);
+                }
+                *reinterpret_cast<f32x4 *>(Nm + (hh * C + t) * LDF + j0 + e4) = nv;
             }
             *reinterpret_cast<V16 *>(amat + (slot * hv + h) * C * C + rem) = av;
         }
@@ -352,9 +361,11 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
             const int h = hq * group + hb + hh;
             V16 tv;
 #pragma unroll
-            for (int e = 0; e < VN; ++e) {
-                const int j = j0 + e;
-                tv[e] = (E)(((j >> 4) <= (t >> 4)) ? Tf[(hh * C + t) * LDF + j] : 0.f);
+            for (int e4 = 0; e4 < VN; e4 += 4) {
+                const f32x4 tf = *reinterpret_cast<const f32x4 *>(Tf + (hh * C + t) * LDF + j0 + e4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    tv[e4 + e] = (E)((((j0 + e4 + e) >> 4) <= (t >> 4)) ? tf[e] : 0.f);
             }
             *reinterpret_cast<V16 *>(tmat + (slot * hv + h) * C * C + rem) = tv;
         }
