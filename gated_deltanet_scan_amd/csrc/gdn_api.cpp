@@ -104,9 +104,12 @@ PrefillWorkspace prefill_workspace(int32_t hv, int32_t chunk, int32_t io_dtype, 
 }
 
 // Segments keep the T and A matrices plus the q and k rows of one segment
-// (about this many bytes) resident in the last-level cache between the prep
-// and the scan kernels.
+// (about kSegmentBytes) resident in the last-level cache between the prep and
+// the scan kernels.  Every segment reads and writes the whole batch's states
+// once more, so a batch of many sequences gets segments of at least
+// kStateReuse times its state bytes.
 constexpr size_t kSegmentBytes = 128u << 20;
+constexpr size_t kStateReuse = 32;
 
 int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype,
                             int32_t num_seqs, int32_t max_seq_chunks, int32_t slot_capacity)
@@ -115,7 +118,9 @@ int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, 
         return 0;
     const size_t es = io_size(io_dtype);
     const size_t per_slot = (size_t)hv * 2 * chunk * chunk * es + (size_t)chunk * 2 * hqk * dk * es;
-    int64_t m = (int64_t)(kSegmentBytes / per_slot) / num_seqs;
+    const size_t state_bytes = (size_t)num_seqs * hv * dk * dk * sizeof(float);   // dk == dv
+    const size_t seg_bytes = std::max(kSegmentBytes, kStateReuse * state_bytes);
+    int64_t m = (int64_t)(seg_bytes / per_slot) / num_seqs;
     m = std::max<int64_t>(m, 1);
     m = std::min<int64_t>(m, max_seq_chunks);
     m = std::min<int64_t>(m, slot_capacity / num_seqs);
