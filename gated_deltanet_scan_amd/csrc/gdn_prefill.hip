@@ -1461,8 +1461,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
                 sacc[sr][ct][i] = state_in ? state_in[state_base + (size_t)CH::row(sr, g4 + i) * dv + col0 + 16 * ct +
                                                       r16]
                                            : 0.f;
-    bf16x8 sb[NSK][CT];
-    auto pack_s = [&]() __attribute__((always_inline)) {
+    auto pack_s = [&](bf16x8 (&sb)[NSK][CT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             f32x4 t[SR];
@@ -1474,7 +1473,6 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
                 sb[st][ct] = CH::b_frag(t, st);
         }
     };
-    pack_s();
 
     // ---- staging ----
     // chunk c of the sequence sits in workspace slot slot0 + c (in either launch mode)
@@ -1612,29 +1610,8 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
         };
 
         // [Q;K] S: (Q S)^T with S^T as the A operand; K S with K rows in the order of CH
-        bf16x8 fq[2][RT], fk[2][RT];
-        auto load_qk = [&](int bsel, int st) __attribute__((always_inline)) {
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-                fq[bsel][rt] = frag(OFF_Q + (rt * NSK + st) * 1024 + lin);
-                fk[bsel][rt] = frag(OFF_K + (rt * NSK + st) * 1024 + kperm);
-            }
-        };
-        load_qk(0, 0);
-        // beta v on this lane's rows CH::row(rt, g4 + i) (the bit cast is of the whole
-        // vector: a bit cast of one element of a vector reads element 0)
-        f32x4 xp[RT][CT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const f32x4 bt = rec4(2, CH::row(rt, g4));
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                const bf16x4 vv = __builtin_bit_cast(bf16x4, tr4(OFF_V + CH::row(rt, 0) * VRB + vtro[ct]));
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    xp[rt][ct][i] = bt[i] * (float)vv[i];
-            }
-        }
+        bf16x8 sb[NSK][CT];
+        pack_s(sb);
         f32x4 qacc[RT][CT], xacc[RT][CT];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
@@ -1645,17 +1622,19 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
             }
 #pragma unroll
         for (int st = 0; st < NSK; ++st) {
-            if (st + 1 < NSK)
-                load_qk((st + 1) & 1, st + 1);
-            __builtin_amdgcn_sched_barrier(0);
+            bf16x8 fq[RT], fk[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                fq[rt] = frag(OFF_Q + (rt * NSK + st) * 1024 + lin);
+                fk[rt] = frag(OFF_K + (rt * NSK + st) * 1024 + kperm);
+            }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) {
-                    qacc[rt][ct] = M::mma(sb[st][ct], fq[st & 1][rt], qacc[rt][ct]);
-                    xacc[rt][ct] = M::mma(fk[st & 1][rt], sb[st][ct], xacc[rt][ct]);
+                    qacc[rt][ct] = M::mma(sb[st][ct], fq[rt], qacc[rt][ct]);
+                    xacc[rt][ct] = M::mma(fk[rt], sb[st][ct], xacc[rt][ct]);
                 }
-            __builtin_amdgcn_sched_barrier(0);
         }
 
         // T fragments, then X = beta v - beta exp(G) (K S)
@@ -1666,33 +1645,22 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
             for (int rt = 0; rt < RT; ++rt)
                 ft[st][rt] = frag(OFF_T + (rt * NSC + st) * 1024 + lin);
         __builtin_amdgcn_sched_barrier(0);
+        // beta v on this lane's rows CH::row(rt, g4 + i) (the bit cast is of the whole
+        // vector: a bit cast of one element of a vector reads element 0)
         bf16x8 xb[NSC][CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             f32x4 t[RT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                t[rt] = xp[rt][ct] - rec4(3, CH::row(rt, g4)) * xacc[rt][ct];
+            for (int rt = 0; rt < RT; ++rt) {
+                const bf16x4 vv = __builtin_bit_cast(bf16x4, tr4(OFF_V + CH::row(rt, 0) * VRB + vtro[ct]));
+                const f32x4 vf = {(float)vv[0], (float)vv[1], (float)vv[2], (float)vv[3]};
+                t[rt] = rec4(2, CH::row(rt, g4)) * vf - rec4(3, CH::row(rt, g4)) * xacc[rt][ct];
+            }
 #pragma unroll
             for (int st = 0; st < NSC; ++st)
                 xb[st][ct] = CH::b_frag(t, st);
         }
-
-        // K^T fragments of the S update: rows CH::row(sr, .) of the key index, chunk rows
-        // 32 st + 8 G + {0..7} (units rt = 2 st and 2 st + 1)
-        bf16x8 fkt[SR][NSC];
-#pragma unroll
-        for (int sr = 0; sr < SR; ++sr)
-#pragma unroll
-            for (int st = 0; st < NSC; ++st) {
-                const int base = OFF_K + (sr >> 1) * 1024 + ktr + 8 * (sr & 1);
-                const s16x4 lo = tr4(base + (2 * st) * NSK * 1024);
-                const s16x4 hi = tr4(base + (2 * st + 1) * NSK * 1024);
-                typedef short s16x8 __attribute__((ext_vector_type(8)));
-                const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                fkt[sr][st] = __builtin_bit_cast(bf16x8, vv);
-            }
-        __builtin_amdgcn_sched_barrier(0);
 
         // D = T X
         f32x4 dacc[RT][CT];
@@ -1710,14 +1678,6 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
                     dacc[rt][ct] = M::mma(ft[st][rt], xb[st][ct], dacc[rt][ct]);
         __builtin_amdgcn_sched_barrier(0);
 
-        // A fragments (A carries the output scale)
-        bf16x8 fa[NSC][RT];
-#pragma unroll
-        for (int st = 0; st < NSC; ++st)
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                fa[st][rt] = frag(OFF_A + (rt * NSC + st) * 1024 + lin);
-        __builtin_amdgcn_sched_barrier(0);
 
         bf16x8 db[NSC][CT], lb[NSC][CT];
 #pragma unroll
@@ -1737,18 +1697,44 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
                 lb[st][ct] = CH::b_frag(t, st);
         }
 
-        // S <- exp(G_last) S + K^T (diag(lambda) D)
-        const float gl = *reinterpret_cast<const float *>(stg + OFF_D + 4 * (C - 1)) * inv_scale;
+        // S <- exp(G_last) S + K^T (diag(lambda) D).  K^T fragments: rows CH::row(sr, .) of
+        // the key index, chunk rows 32 st + 8 G + {0..7} (units rt = 2 st and 2 st + 1),
+        // read one key tile ahead of their products.
+        auto load_kt = [&](int sr, bf16x8 (&f)[NSC]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int sr = 0; sr < SR; ++sr)
+            for (int st = 0; st < NSC; ++st) {
+                const int base = OFF_K + (sr >> 1) * 1024 + ktr + 8 * (sr & 1);
+                const s16x4 lo = tr4(base + (2 * st) * NSK * 1024);
+                const s16x4 hi = tr4(base + (2 * st + 1) * NSK * 1024);
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                f[st] = __builtin_bit_cast(bf16x8, vv);
+            }
+        };
+        const float gl = *reinterpret_cast<const float *>(stg + OFF_D + 4 * (C - 1)) * inv_scale;
+        bf16x8 fkt[2][NSC];
+        load_kt(0, fkt[0]);
+#pragma unroll
+        for (int sr = 0; sr < SR; ++sr) {
+            if (sr + 1 < SR)
+                load_kt(sr + 1, fkt[(sr + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 sacc[sr][ct] = sacc[sr][ct] * gl;
 #pragma unroll
                 for (int st = 0; st < NSC; ++st)
-                    sacc[sr][ct] = M::mma(fkt[sr][st], lb[st][ct], sacc[sr][ct]);
+                    sacc[sr][ct] = M::mma(fkt[sr & 1][st], lb[st][ct], sacc[sr][ct]);
             }
-        pack_s();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // A fragments (A carries the output scale)
+        bf16x8 fa[NSC][RT];
+#pragma unroll
+        for (int st = 0; st < NSC; ++st)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                fa[st][rt] = frag(OFF_A + (rt * NSC + st) * 1024 + lin);
 
         // O^T = scale (Q S)^T diag(exp G) + D^T (scale A)^T: lane l holds token row
         // 16 rt + l % 16 and the four columns 16 ct + 4 (l / 16) .. +3 of this wave's
