@@ -1019,7 +1019,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     static_assert(C <= kWave, "one lane per token of a chunk");
     static_assert(DVS % 16 == 0 && DK % 16 == 0 && C % 16 == 0, "16x16 tiles");
 
-    // stage buffer layout (bytes) and the 1 KB direct-load jobs that fill it
+    // stage buffer layout (bytes) and the 1 KB direct-to-LDS load jobs that fill it
     constexpr int OFF_Q = 0;
     constexpr int OFF_K = OFF_Q + C * DK * ES;
     constexpr int OFF_T = OFF_K + C * DK * ES;
@@ -1027,11 +1027,17 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     constexpr int OFF_V = OFF_A + C * C * ES;
     constexpr int OFF_D = OFF_V + C * DVS * ES;
     constexpr int STAGE = OFF_D + 4 * C * 4;
-    constexpr int NJ_QK = (C * DK * ES / 16 + 63) / 64;
-    constexpr int NJ_TA = (C * C * ES / 16 + 63) / 64;
-    constexpr int NJ_V = (C * DVS * ES / 16 + 63) / 64;
-    constexpr int NJ_D = (4 * C * 4 / 16 + 63) / 64;
-    constexpr int NJ = 2 * NJ_QK + 2 * NJ_TA + NJ_V + NJ_D;
+    constexpr int NCK_QK = C * DK * ES / 16;   // 16-byte chunks per tile
+    constexpr int NCK_TA = C * C * ES / 16;
+    constexpr int NCK_V = C * DVS * ES / 16;
+    constexpr int NCK_D = 4 * C * 4 / 16;
+    constexpr int NJ_QK = (NCK_QK + 63) / 64;
+    constexpr int NJ_TA = (NCK_TA + 63) / 64;
+    constexpr int NJ_V = (NCK_V + 63) / 64;
+    constexpr int NJ_D = (NCK_D + 63) / 64;
+    constexpr int J_T = 2 * NJ_QK, J_V = J_T + 2 * NJ_TA, J_D = J_V + NJ_V;
+    constexpr int NJ = J_D + NJ_D;
+    static_assert(STAGE % 16 == 0 && OFF_D % 16 == 0, "16-byte aligned stage blocks");
 
     __shared__ __attribute__((aligned(1024))) unsigned char stage_mem[2 * STAGE];
     __shared__ __attribute__((aligned(16))) E Xt[DVS * LDC];
@@ -1040,6 +1046,9 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     __shared__ __attribute__((aligned(16))) E St[DVS * LDK];
     __shared__ __attribute__((aligned(16))) E Os[C * LDV];
 
+    // the stage buffers as LDS addresses (the direct loads write LDS by address)
+    __attribute__((address_space(3))) unsigned char *const lds_stage =
+        (__attribute__((address_space(3))) unsigned char *)stage_mem;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const bool loader = wave >= kWaves;              // waves 4..7 stage chunks, 0..3 compute
     const int lw = wave - kWaves;                    // loader index
@@ -1094,80 +1103,91 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         }
     }
 
-    // ---- loaders: chunk c into registers (issue_loads), then into a stage buffer ----
-    // Loader lw owns jobs lw, lw + 4, ... of 64 16-byte chunks each; lane l of a job
-    // moves physical chunk 64 * idx + l of its tile.
+    // ---- loaders: chunk c straight into stage buffer c & 1 (direct-to-LDS loads) ----
+    // Job J (of NJ) moves 1 KB of the stage with one load: lane i writes the 16 bytes at
+    // 16 i of the job's block.  Loader lw runs jobs lw, lw + 4, ...; which tile and rows a
+    // job covers is fixed at compile time (one code path per loader), and all loads of a
+    // chunk are in flight together without holding registers.
     constexpr int NJ_PER = (NJ + kWaves - 1) / kWaves;
-    V16 lbuf[NJ_PER];
-    int ldst[NJ_PER];
-    // The job list of each loader is fixed at compile time (one branch per loader), and
-    // every load is unconditional: a lane past the end of a tile reloads the tile's last
-    // chunk and only its LDS store is skipped.  This keeps all loads of a step in flight
-    // together instead of behind per-job waits.
-    auto issue_jobs = [&](auto lwc, int c) __attribute__((always_inline)) {
-        constexpr int LW = decltype(lwc)::value;
+    const int qk_row = hqk * DK, v_row = hv * dv;
+    const size_t slot_begin = slot_of(map, n, c_begin);   // chunk c sits in slot slot_begin + c - c_begin
+    auto job_row = [&](auto jc) __attribute__((always_inline)) -> int {   // source row of this lane
+        constexpr int J = decltype(jc)::value;
+        if constexpr (J < J_T)
+            return min((J % NJ_QK) * 64 + lane, NCK_QK - 1) / (DK * ES / 16);
+        else if constexpr (J >= J_V && J < J_D)
+            return min((J - J_V) * 64 + lane, NCK_V - 1) / (DVS * ES / 16);
+        else
+            return 0;
+    };
+    // element offset of this lane's 16 bytes from the tile's origin, given its source row
+    auto job_off = [&](auto jc, int row) __attribute__((always_inline)) -> int {
+        constexpr int J = decltype(jc)::value;
+        if constexpr (J < J_T) {
+            const int P = min((J % NJ_QK) * 64 + lane, NCK_QK - 1);
+            const int r = P / (DK * ES / 16), pos = P % (DK * ES / 16);
+            return row * qk_row + (pos ^ SK::perm(r)) * VN;
+        } else if constexpr (J < J_V) {
+            const int P = min(((J - J_T) % NJ_TA) * 64 + lane, NCK_TA - 1);
+            const int r = P / (C * ES / 16), pos = P % (C * ES / 16);
+            return r * C + (pos ^ SC::perm(r)) * VN;
+        } else if constexpr (J < J_D) {
+            const int P = min((J - J_V) * 64 + lane, NCK_V - 1);
+            const int r = P / (DVS * ES / 16), pos = P % (DVS * ES / 16);
+            return row * v_row + (pos ^ SV::perm(r)) * VN;
+        } else {
+            return min((J - J_D) * 64 + lane, NCK_D - 1) * 4;   // floats
+        }
+    };
+    // Stage chunk c.  Rows past the chunk's last real row are loaded from it.
+    auto issue_jobs = [&](auto wc, int c) __attribute__((always_inline)) {
+        constexpr int W = decltype(wc)::value;
+        __attribute__((address_space(3))) unsigned char *stg = lds_stage + (c & 1) * STAGE;
         const int64_t t0 = a + (int64_t)c * C;
         const int last = (int)min<int64_t>(C, b - t0) - 1;   // >= 0 for every chunk of the sequence
-        const size_t slot = slot_of(map, n, c);
-        const size_t ent = (slot * hv + h) * C * C;
-#pragma unroll
-        for (int u = 0; u < NJ_PER; ++u) {
-            const int job = LW + u * kWaves;
-            const E *src;
-            int dst, valid;
-            if (job < 2 * NJ_QK) {
-                const int which = job / NJ_QK, idx = job % NJ_QK;
-                const int P = idx * 64 + lane;                     // physical chunk of the tile
-                const int r = P / (DK * ES / 16), pos = P % (DK * ES / 16);
-                const int j = pos ^ SK::perm(r);
-                src = (which ? k : q) + ((size_t)(t0 + min(r, last)) * hqk + hq) * DK + j * VN;
-                dst = (which ? OFF_K : OFF_Q) + P * 16;
-                valid = 1;
-            } else if (job < 2 * NJ_QK + 2 * NJ_TA) {
-                constexpr int NCK = C * C * ES / 16;
-                const int jj = job - 2 * NJ_QK;
-                const int which = jj / NJ_TA, idx = jj % NJ_TA;
-                const int P = idx * 64 + lane;
-                valid = P < NCK;
-                const int Pl = min(P, NCK - 1);
-                const int r = Pl / (C * ES / 16), pos = Pl % (C * ES / 16);
-                const int j = pos ^ SC::perm(r);
-                src = (which ? amat : tmat) + ent + (size_t)r * C + j * VN;
-                dst = (which ? OFF_A : OFF_T) + P * 16;
-            } else if (job < 2 * NJ_QK + 2 * NJ_TA + NJ_V) {
-                constexpr int NCK = C * DVS * ES / 16;
-                const int P = (job - 2 * NJ_QK - 2 * NJ_TA) * 64 + lane;
-                valid = P < NCK;
-                const int Pl = min(P, NCK - 1);
-                const int r = Pl / (DVS * ES / 16), pos = Pl % (DVS * ES / 16);
-                const int j = pos ^ SV::perm(r);
-                src = v + ((size_t)(t0 + min(r, last)) * hv + h) * dv + (size_t)s * DVS + j * VN;
-                dst = OFF_V + P * 16;
-            } else {
-                constexpr int NCK = 4 * C * 4 / 16;
-                const int P = job < NJ ? (job - 2 * NJ_QK - 2 * NJ_TA - NJ_V) * 64 + lane : NCK;
-                valid = P < NCK;
-                src = reinterpret_cast<const E *>(dec + (slot * hv + h) * 4 * C + min(P, NCK - 1) * 4);
-                dst = OFF_D + P * 16;
+        const size_t slot = slot_begin + (size_t)(c - c_begin);
+        const E *qb = q + ((size_t)t0 * hqk + hq) * DK;
+        const E *kb = k + ((size_t)t0 * hqk + hq) * DK;
+        const E *vb = v + ((size_t)t0 * hv + h) * dv + (size_t)s * DVS;
+        const E *tb = tmat + (slot * hv + h) * C * C;
+        const E *ab = amat + (slot * hv + h) * C * C;
+        const E *db = reinterpret_cast<const E *>(dec + (slot * hv + h) * 4 * C);
+        static_for<NJ_PER>([&](auto uc) {
+            constexpr int J = W + decltype(uc)::value * kWaves;
+            if constexpr (J < NJ) {
+                constexpr std::integral_constant<int, J> jc{};
+                const E *base;
+                int off = job_off(jc, min(job_row(jc), last));
+                if constexpr (J < J_T)
+                    base = J >= NJ_QK ? kb : qb;
+                else if constexpr (J < J_V)
+                    base = (J - J_T) >= NJ_TA ? ab : tb;
+                else if constexpr (J < J_D)
+                    base = vb;
+                else {
+                    base = db;
+                    off *= (int)(sizeof(float) / sizeof(E));
+                }
+                // lanes of the job that carry data, and the job's block in the stage
+                constexpr int NCK = J < J_T ? NCK_QK : J < J_V ? NCK_TA : J < J_D ? NCK_V : NCK_D;
+                constexpr int IDX = J < J_T ? J % NJ_QK : J < J_V ? (J - J_T) % NJ_TA : J < J_D ? J - J_V : J - J_D;
+                constexpr int NL = NCK - IDX * 64 < 64 ? NCK - IDX * 64 : 64;
+                constexpr int BLK = (J < J_T ? (J >= NJ_QK ? OFF_K : OFF_Q)
+                                             : J < J_V ? ((J - J_T) >= NJ_TA ? OFF_A : OFF_T)
+                                                       : J < J_D ? OFF_V : OFF_D) + IDX * 1024;
+                if (NL == 64 || lane < NL)
+                    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
+                                                     (__attribute__((address_space(3))) void *)(stg + BLK), 16, 0, 0);
             }
-            ldst[u] = valid ? dst : -1;
-            lbuf[u] = *reinterpret_cast<const V16 *>(src);
-        }
+        });
     };
-    auto issue_loads = [&](int c) __attribute__((always_inline)) {
+    auto by_loader = [&](auto fn) __attribute__((always_inline)) {
         switch (lw) {
-        case 0: issue_jobs(std::integral_constant<int, 0>{}, c); break;
-        case 1: issue_jobs(std::integral_constant<int, 1>{}, c); break;
-        case 2: issue_jobs(std::integral_constant<int, 2>{}, c); break;
-        default: issue_jobs(std::integral_constant<int, 3>{}, c); break;
+        case 0: fn(std::integral_constant<int, 0>{}); break;
+        case 1: fn(std::integral_constant<int, 1>{}); break;
+        case 2: fn(std::integral_constant<int, 2>{}); break;
+        default: fn(std::integral_constant<int, 3>{}); break;
         }
-    };
-    auto write_stage = [&](int buf) __attribute__((always_inline)) {
-        unsigned char *stg = stage_mem + buf * STAGE;
-#pragma unroll
-        for (int u = 0; u < NJ_PER; ++u)
-            if (ldst[u] >= 0)
-                *reinterpret_cast<V16 *>(stg + ldst[u]) = lbuf[u];
     };
     // Outputs of a finished chunk (staged in Os by the compute waves): coalesced
     // 16-byte rows to global, written by the loaders.
@@ -1307,11 +1327,13 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     };
 
     // ---- pipeline: while the compute waves work on chunk c (stage c & 1), the loaders
-    //      flush the outputs of chunk c - 1 and stage chunk c + 1 into the other buffer ----
+    //      flush the outputs of chunk c - 1 and stage chunk c + 1 into the other buffer.
+    //      The direct loads are not tracked by the compiler's LDS dependences: each loader
+    //      waits for its own loads before the barrier that publishes the stage. ----
     if (loader) {
-        issue_loads(c_begin);
-        write_stage(c_begin & 1);
+        by_loader([&](auto wc) { issue_jobs(wc, c_begin); });
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     for (int c = c_begin; c < c_end; ++c) {
         if (loader) {
@@ -1320,11 +1342,12 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
                 flush(pt0, (int)min<int64_t>(C, b - pt0));
             }
             if (c + 1 < c_end)
-                issue_loads(c + 1);
-            __syncthreads();   // B1
-            __syncthreads();   // B2
-            if (c + 1 < c_end)
-                write_stage((c + 1) & 1);
+                by_loader([&](auto wc) { issue_jobs(wc, c + 1); });
+            // B1 and B2 of the compute waves: the loaders publish nothing there, so they
+            // take the bare barrier (a fenced one would first wait for all their loads)
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_s_barrier();
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         } else {
             step(c & 1);
         }
