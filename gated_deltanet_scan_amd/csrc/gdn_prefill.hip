@@ -127,11 +127,51 @@ __device__ inline size_t slot_of(const SlotMap &m, int n, int c)
     return (size_t)n * m.seg_len + (c - m.seg_first);
 }
 
+// Byte layout of a staged tile with rows of RB bytes: row r holds its 16-byte
+// chunk j at position j ^ perm(r).  perm is injective over 16 consecutive rows
+// of one 256-byte bank line and moves 4 consecutive rows by even amounts, so
+// that 16-row operand reads (16 bytes per lane) and 4-row transpose reads hit
+// distinct LDS banks.
+template <int RB>
+struct Swz {
+    static_assert(RB % 16 == 0 && RB <= 256, "rows of 16..256 bytes");
+    static constexpr int NCH = RB / 16;
+    static constexpr int RPL = 256 / RB;   // rows per 256-byte bank line
+    __device__ static inline int perm(int r)
+    {
+        if constexpr (NCH < 4) {
+            return 0;
+        } else {
+            const int u = r / RPL;
+            return ((u & (NCH / 2 - 1)) << 1) | ((u / (NCH / 2)) & 1);
+        }
+    }
+    __device__ static inline int off(int r, int b) { return r * RB + ((((b >> 4) ^ perm(r)) << 4) | (b & 15)); }
+};
+
+// A operand fragment (kPerLane consecutive elements of one row) of a staged tile.
+template <typename M, typename S, typename E>
+__device__ inline typename M::frag staged_frag(const unsigned char *base, int row, int col)
+{
+    return M::load(reinterpret_cast<const E *>(base + S::off(row, col * (int)sizeof(E))));
+}
+
 // ---------------------------------------------------------------------------
 // Prep kernel.  One workgroup per (chunk slot, query/key head); writes, for
 // every value head h of the group,
 //   tmat[slot][h] = (I + N)^-1   (C x C, row-major, unit lower triangular)
-//   amat[slot][h] = [exp(G_t - G_j) q_t.k_j]_{j<=t}  (C x C, zero above)
+//   amat[slot][h] = scale [exp(G_t - G_j) q_t.k_j]_{j<=t}  (C x C, zero above)
+//   dec[slot][h]  = [scale exp(G) | exp(G_last - G) | beta | beta exp(G)]
+//
+// All global reads are issued first: the chunk's q and k rows go straight
+// into LDS (direct-to-LDS loads, rows in the Swz chunk order; rows past the
+// end of the sequence repeat its last row, their products are masked), and
+// g, beta are read while they are in flight, so the in-chunk cumulative sum
+// G and the decay record are done under the latency of the big loads.  The
+// Gram products K K^T and Q K^T are formed tile by tile on the matrix cores
+// in transposed orientation (a lane holds one row t and four consecutive
+// columns j), and the log-space mask and decay are applied to the tile in
+// registers: N goes to LDS for the solve, A straight to global memory.
 //
 // The inverse is formed in 16 x 16 blocks: the diagonal blocks D_b by
 // forward substitution (one lane per column), then the blocks below the
@@ -148,30 +188,31 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
     int64_t total_tokens, int32_t hqk, int32_t hv, E *__restrict__ tmat, E *__restrict__ amat,
     float *__restrict__ dec, float scale)
 {
-    constexpr int PAD = LdsPad<E>::value;
-    constexpr int LDK = DK + PAD;
+    constexpr int ES = (int)sizeof(E);
     constexpr int LDF = C + 4;      // fp32 C x C rows
     constexpr int RT = C / 16;      // 16-row blocks
     constexpr int HB = 2;           // value heads per pass
-    constexpr int IN_BYTES = 2 * C * LDK * (int)sizeof(E);
-    constexpr int F_BYTES = HB * C * LDF * (int)sizeof(float);
-    constexpr int U1 = IN_BYTES > F_BYTES ? IN_BYTES : F_BYTES;   // Ks,Qs  then N of HB heads
-    constexpr int U2 = 2 * C * LDF * (int)sizeof(float);           // KK,QK  then T of HB heads
-    static_assert(U2 >= F_BYTES, "T of HB heads must fit where the Gram products were");
     constexpr int VN = Vec16<E>::n;
     typedef typename Vec16<E>::type V16;
+    typedef typename MmaFor<E, DK>::type MK;
+    typedef Swz<DK * ES> SK;
+    constexpr int TILE = C * DK * ES;                 // bytes of the staged q (or k) rows
+    constexpr int F_BYTES = HB * C * LDF * (int)sizeof(float);
+    constexpr int U1 = 2 * TILE > F_BYTES ? 2 * TILE : F_BYTES;   // k, q rows, then T of HB heads
+    constexpr int NCK = TILE / 16;                    // 16-byte chunks of a staged tile
+    constexpr int NJ1 = (NCK + 63) / 64;              // 64-lane load jobs per tile
+    constexpr int NJ_PER = (2 * NJ1 + kWaves - 1) / kWaves;
+    static_assert(DK * ES >= 16 && DK * ES <= 256, "staged rows of 16 .. 256 bytes");
+    static_assert(C <= kWave, "one lane per token of a chunk");
 
-    __shared__ __attribute__((aligned(16))) unsigned char smem_a[U1];
-    __shared__ __attribute__((aligned(16))) unsigned char smem_b[U2];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem_qk[U1];
+    __shared__ __attribute__((aligned(16))) float Nm[HB * C * LDF];
     __shared__ __attribute__((aligned(16))) float Yw[kWaves][16][17];
-    __shared__ __attribute__((aligned(16))) float Gs[HB][C];
-    __shared__ float Bs[HB][C];
-    E *Ks = reinterpret_cast<E *>(smem_a);
-    E *Qs = Ks + C * LDK;
-    float *Nm = reinterpret_cast<float *>(smem_a);   // [HB][C][LDF], after the Gram products
-    float *KK = reinterpret_cast<float *>(smem_b);
-    float *QK = KK + C * LDF;
-    float *Tf = reinterpret_cast<float *>(smem_b);   // [HB][C][LDF], after N and A are built
+    const unsigned char *Ks = smem_qk;                  // staged k rows
+    const unsigned char *Qs = smem_qk + TILE;           // staged q rows
+    float *Tf = reinterpret_cast<float *>(smem_qk);     // [HB][C][LDF], after the Gram products
+    __attribute__((address_space(3))) unsigned char *const lds_qk =
+        (__attribute__((address_space(3))) unsigned char *)smem_qk;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int hq = blockIdx.y;
@@ -194,102 +235,129 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
     int64_t a, b;
     seq_range(cu, n, total_tokens, a, b);
     const int64_t t0 = a + (int64_t)c * C;
-    const int len = (int)min<int64_t>(C, b - t0);
+    const int len = (int)min<int64_t>(C, b - t0);   // >= 1
 
-    // Q and K rows of this query/key head (rows past the end are zero), then K K^T and
-    // Q K^T, lower block triangle only (tile row >= tile column).  The T of one pass
-    // overwrites the Gram products, so every pass after the first stages them again.
-    auto stage_gram = [&]() {
-        for (int i = tid; i < C * DK / VN; i += kThreads) {
-            const int r = i / (DK / VN), c0 = (i % (DK / VN)) * VN;
-            V16 kv = (V16)(E)0.f, qv = (V16)(E)0.f;
-            if (r < len) {
-                const size_t off = ((size_t)(t0 + r) * hqk + hq) * DK + c0;
-                kv = *reinterpret_cast<const V16 *>(k + off);
-                qv = *reinterpret_cast<const V16 *>(q + off);
-            }
-            *reinterpret_cast<V16 *>(Ks + r * LDK + c0) = kv;
-            *reinterpret_cast<V16 *>(Qs + r * LDK + c0) = qv;
-        }
-        __syncthreads();
-        constexpr int NT = RT * (RT + 1) / 2;
-        for (int it = wave; it < 2 * NT; it += kWaves) {
-            const int which = it / NT;
-            const int t = it % NT;
-            int tr = 0;
-            while ((tr + 1) * (tr + 2) / 2 <= t)
-                ++tr;
-            const int tc = t - tr * (tr + 1) / 2;
-            const E *A = (which ? Qs : Ks) + tr * 16 * LDK;
-            const E *Bt = Ks + tc * 16 * LDK;
-            const f32x4 acc = mma_tile<E, DK>(zero4(), A, LDK, Bt, LDK, lane);
-            float *dst = which ? QK : KK;
+    // q and k rows of the chunk into LDS.  Job J moves 1 KB: lane i writes the 16 bytes
+    // at 16 i of the job's block, the source chunk is the Swz image of that position.
+    auto issue_qk = [&]() __attribute__((always_inline)) {
+        const E *kb = k + ((size_t)t0 * hqk + hq) * DK;
+        const E *qb = q + ((size_t)t0 * hqk + hq) * DK;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dst[(tr * 16 + tile_row(lane, i)) * LDF + tc * 16 + tile_col(lane)] = acc[i];
+        for (int u = 0; u < NJ_PER; ++u) {
+            const int J = wave + u * kWaves;
+            if (J < 2 * NJ1) {
+                const int idx = J % NJ1;
+                const int P = min(idx * 64 + lane, NCK - 1);
+                const int r = P / (DK * ES / 16), pos = P % (DK * ES / 16);
+                const E *src = (J >= NJ1 ? qb : kb) + (size_t)min(r, len - 1) * hqk * DK + (pos ^ SK::perm(r)) * VN;
+                if (idx * 64 + lane < NCK)
+                    __builtin_amdgcn_global_load_lds(
+                        (const __attribute__((address_space(1))) void *)src,
+                        (__attribute__((address_space(3))) void *)(lds_qk + (J >= NJ1 ? TILE : 0) + idx * 1024), 16, 0, 0);
+            }
         }
-        __syncthreads();
     };
 
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
     const int group = hv / hqk;
     for (int hb = 0; hb < group; hb += HB) {
         const int nh = min(HB, group - hb);
-        stage_gram();
-        // G = in-chunk inclusive cumulative sum of g; padding tokens carry g = 0, beta = 0.
-        if (wave < nh) {
-            const int h = hq * group + hb + wave;
-            float gv = 0.f, bv = 0.f;
-            if (lane < len) {
-                gv = g[(size_t)(t0 + lane) * hv + h];
-                bv = beta[(size_t)(t0 + lane) * hv + h];
-            }
-            const float G = wave_inclusive_sum(gv, lane);
-            // lanes >= len carry g = 0, so lane C-1 holds G at the last real token
-            const float Glast = __shfl(G, C - 1, kWave);
-            if (lane < C) {
-                Gs[wave][lane] = G;
-                Bs[wave][lane] = bv;
-                // decay record of the chunk for the scan: scale exp(G_t), exp(G_last - G_t),
-                // beta_t, beta_t exp(G_t)
-                float *rec = dec + (slot * hv + h) * 4 * C;
-                const float eg = expf(G);
-                rec[lane] = scale * eg;
-                rec[C + lane] = expf(Glast - G);
-                rec[2 * C + lane] = bv;
-                rec[3 * C + lane] = bv * eg;
+        // g and beta of the pass's value heads, one token per lane, in every wave (issued
+        // before the q, k rows); padding tokens carry g = 0, beta = 0
+        float gv[HB], bv[HB];
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh) {
+            gv[hh] = 0.f;
+            bv[hh] = 0.f;
+            if (hh < nh && lane < len) {
+                const int h = hq * group + hb + hh;
+                gv[hh] = g[(size_t)(t0 + lane) * hv + h];
+                bv[hh] = beta[(size_t)(t0 + lane) * hv + h];
             }
         }
+        issue_qk();
+        // the direct loads are not tracked by the compiler's LDS dependences
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        // exp(G_t - G_j) only for j <= t, where the exponent is <= 0 (log-space mask).
-        // One thread per VN consecutive entries of a row: one 16-byte store of A.
-        for (int idx = tid; idx < nh * C * C / VN; idx += kThreads) {
-            const int hh = idx / (C * C / VN);
-            const int rem = (idx - hh * (C * C / VN)) * VN;
-            const int t = rem / C, j0 = rem - (rem / C) * C;
-            const int h = hq * group + hb + hh;
-            const float gt = Gs[hh][t], bt = Bs[hh][t];
-            V16 av;
-#pragma unroll
-            for (int e4 = 0; e4 < VN; e4 += 4) {
-                // four consecutive entries at a time (16-byte LDS accesses)
-                const f32x4 gj = *reinterpret_cast<const f32x4 *>(&Gs[hh][j0 + e4]);
-                const f32x4 kk = *reinterpret_cast<const f32x4 *>(KK + t * LDF + j0 + e4);
-                const f32x4 qk = *reinterpret_cast<const f32x4 *>(QK + t * LDF + j0 + e4);
-                f32x4 nv;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = j0 + e4 + e;
-                    const float ed = (j <= t) ? __expf(gt - gj[e]) : 0.f;
-                    nv[e] = (j < t) ? bt * ed * kk[e] : 0.f;
-                    av[e4 + e] = (E)(scale * ed * qk[e]);
-                }
-                *reinterpret_cast<f32x4 *>(Nm + (hh * C + t) * LDF + j0 + e4) = nv;
-            }
-            *reinterpret_cast<V16 *>(amat + (slot * hv + h) * C * C + rem) = av;
-        }
-        __syncthreads();   // KK, QK are dead from here: their space holds T
 
-        // Diagonal blocks D_b: one wave per head, lane = (block b, column j).
+        // G = in-chunk inclusive cumulative sum of g (lanes >= len carry g = 0, so lane
+        // C - 1 holds G at the last real token), and the decay record of the chunk
+        float Gr[HB];
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh)
+            Gr[hh] = wave_inclusive_sum(gv[hh], lane);
+        if (wv < nh && lane < C) {
+            const int h = hq * group + hb + wv;
+            const float G = wv == 0 ? Gr[0] : Gr[HB - 1];
+            const float Glast = __shfl(G, C - 1, kWave);
+            float *rec = dec + (slot * hv + h) * 4 * C;
+            const float eg = expf(G);
+            rec[lane] = scale * eg;
+            rec[C + lane] = expf(Glast - G);
+            rec[2 * C + lane] = wv == 0 ? bv[0] : bv[HB - 1];
+            rec[3 * C + lane] = (wv == 0 ? bv[0] : bv[HB - 1]) * eg;
+        }
+
+        // Gram tiles, transposed: the tiles of block row tr (rows t) and block column tc
+        // (columns j) are computed as K_j . K_t and K_j . Q_t, so lane l holds row
+        // t = 16 tr + l % 16 and columns j = 16 tc + 4 (l / 16) + {0..3}.  The lower-triangle
+        // tiles (tc <= tr) give N (to LDS; the solve reads nothing above the diagonal) and A
+        // (to global memory); A tiles above the diagonal are stored as zeros.  The tiles are
+        // dealt to the waves round-robin at compile time.
+        const int r16 = lane & 15, kq = (lane >> 4) * MK::kPerLane;
+        static_for<RT * RT>([&](auto pc) {
+            constexpr int P = decltype(pc)::value;
+            constexpr int tr = P / RT, tc = P % RT;
+            constexpr bool lower = tc <= tr;
+            constexpr int idx = lower ? tr * (tr + 1) / 2 + tc : (tr * RT + tc) + 2;   // deal index
+            if (idx % kWaves != wv)
+                return;
+            const int t = tr * 16 + r16;
+            const int j0 = tc * 16 + 4 * (lane >> 4);
+            if constexpr (lower) {
+                constexpr int NS = DK / MK::kStep;
+                typename MK::frag fj[NS], fkt[NS], fqt[NS];
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    fj[st] = staged_frag<MK, SK, E>(Ks, tc * 16 + r16, st * MK::kStep + kq);
+                    fkt[st] = staged_frag<MK, SK, E>(Ks, tr * 16 + r16, st * MK::kStep + kq);
+                    fqt[st] = staged_frag<MK, SK, E>(Qs, tr * 16 + r16, st * MK::kStep + kq);
+                }
+                f32x4 kk = zero4(), qk = zero4();
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    kk = MK::mma(fj[st], fkt[st], kk);
+                    qk = MK::mma(fj[st], fqt[st], qk);
+                }
+#pragma unroll
+                for (int hh = 0; hh < HB; ++hh) {
+                    if (hh >= nh)
+                        break;
+                    const int h = hq * group + hb + hh;
+                    const float gt = __shfl(Gr[hh], t, kWave), bt = __shfl(bv[hh], t, kWave);
+                    f32x4 nv, av;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        // exp(G_t - G_j) only for j <= t, where the exponent is <= 0 (log-space mask)
+                        const int j = j0 + e;
+                        const float gj = __shfl(Gr[hh], j, kWave);
+                        const float ed = (j <= t) ? __expf(gt - gj) : 0.f;
+                        nv[e] = (j < t) ? bt * ed * kk[e] : 0.f;
+                        av[e] = (t < len) ? scale * ed * qk[e] : 0.f;
+                    }
+                    *reinterpret_cast<f32x4 *>(Nm + (hh * C + t) * LDF + j0) = nv;
+                    store4(amat + (slot * hv + h) * C * C + t * C + j0, av[0], av[1], av[2], av[3]);
+                }
+            } else {
+#pragma unroll
+                for (int hh = 0; hh < HB; ++hh)
+                    if (hh < nh)
+                        store4(amat + (slot * hv + hq * group + hb + hh) * C * C + t * C + j0, 0.f, 0.f, 0.f, 0.f);
+            }
+        });
+        __syncthreads();   // the q, k rows are dead from here: their space holds T
+
+    // Diagonal blocks D_b: one wave per head, lane = (block b, column j).
         if (wave < nh) {
             const int bb = lane >> 4, j = lane & 15;
             if (bb < RT) {
@@ -409,27 +477,6 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
 // ---------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// Byte layout of a staged tile with rows of RB bytes: row r holds its 16-byte
-// chunk j at position j ^ perm(r).  perm is injective over 16 consecutive rows
-// of one 256-byte bank line and moves 4 consecutive rows by even amounts, so
-// both read patterns above are conflict-free.
-template <int RB>
-struct Swz {
-    static_assert(RB % 16 == 0 && RB <= 256, "rows of 16..256 bytes");
-    static constexpr int NCH = RB / 16;
-    static constexpr int RPL = 256 / RB;   // rows per 256-byte bank line
-    __device__ static inline int perm(int r)
-    {
-        if constexpr (NCH < 4) {
-            return 0;
-        } else {
-            const int u = r / RPL;
-            return ((u & (NCH / 2 - 1)) << 1) | ((u / (NCH / 2)) & 1);
-        }
-    }
-    __device__ static inline int off(int r, int b) { return r * RB + ((((b >> 4) ^ perm(r)) << 4) | (b & 15)); }
-};
-
 // Tiles read in the row order of the 32-wide chain below: a 16-lane operand
 // read takes rows r0 + 8 a + b (a, b < 4, r0 a multiple of 4), and the
 // transpose read of K takes rows 8 g + e (e < 4) in 16-byte chunks 4 a + q
@@ -500,13 +547,6 @@ struct Chain<Mma<float>> {
     __device__ static inline int a_col(int s, int lane) { return 16 * (s >> 2) + 4 * (lane >> 4) + (s & 3); }
     __device__ static inline float b_frag(const f32x4 *t, int s) { return t[s >> 2][s & 3]; }
 };
-
-// A operand fragment (kPerLane consecutive elements of one row) of a staged tile.
-template <typename M, typename S, typename E>
-__device__ inline typename M::frag staged_frag(const unsigned char *base, int row, int col)
-{
-    return M::load(reinterpret_cast<const E *>(base + S::off(row, col * (int)sizeof(E))));
-}
 
 // A operand of the S update: K^T, output rows = key indices in the order
 // Chain<MK>::row(sr, .), contraction over chunk rows in the order of
