@@ -207,7 +207,6 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem_qk[U1];
     __shared__ __attribute__((aligned(16))) float Nm[HB * C * LDF];
-    __shared__ __attribute__((aligned(16))) float Yw[kWaves][16][17];
     const unsigned char *Ks = smem_qk;                  // staged k rows
     const unsigned char *Qs = smem_qk + TILE;           // staged q rows
     float *Tf = reinterpret_cast<float *>(smem_qk);     // [HB][C][LDF], after the Gram products
@@ -357,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
         });
         __syncthreads();   // the q, k rows are dead from here: their space holds T
 
-    // Diagonal blocks D_b: one wave per head, lane = (block b, column j).
+        // Diagonal blocks D_b: one wave per head, lane = (block b, column j).
         if (wave < nh) {
             const int bb = lane >> 4, j = lane & 15;
             if (bb < RT) {
@@ -379,46 +378,56 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
         }
         __syncthreads();
 
-        // Blocks below the diagonal, one block-diagonal (distance d) at a time.
-        for (int d = 1; d < RT; ++d) {
-            const int nblk = nh * (RT - d);
-            // Y = sum_m N_{b,m} T_{m,b'}   (b = b' + d), one wave per block
-            for (int base = 0; base < nblk; base += kWaves) {
-                const int blk = base + wave;
-                if (blk < nblk) {
-                    const int hh = blk / (RT - d), bp = blk % (RT - d), bq = bp + d;
-                    const float *Nh = Nm + hh * C * LDF;
-                    const float *Th = Tf + hh * C * LDF;
-                    f32x4 acc = zero4();
-                    for (int m = bp; m < bq; ++m) {
+        // Blocks below the diagonal.  Block column b' of T depends on nothing but itself,
+        // D and N:  T_{b',b'} = D_{b'},  T_{b,b'} = -D_b sum_{b' <= m < b} N_{b,m} T_{m,b'},
+        // so each (head, block column) is one chain of products, run by one wave with the
+        // column's blocks held in registers.  A block enters the next product as its B
+        // operand as it stands in the accumulators: in step s, lane group g contributes the
+        // contraction indices 4 g + s, whose B rows are its own accumulator slot s (and the
+        // A operand takes the same columns).  The chains are dealt to the waves in snake
+        // order, longest first.
+        if constexpr (RT > 1) {
+            const int nchains = nh * (RT - 1);
+            const int r16 = lane & 15, g4 = 4 * (lane >> 4);
+            for (int round = 0; round * kWaves < nchains; ++round) {
+                const int ch = round * kWaves + ((round & 1) ? kWaves - 1 - wv : wv);
+                if (ch >= nchains)
+                    continue;
+                const int bp = ch / nh, hh = ch % nh;
+                const float *Nh = Nm + hh * C * LDF;
+                float *Th = Tf + hh * C * LDF;
+                static_for<RT - 1>([&](auto bpc) {
+                    constexpr int BP = decltype(bpc)::value;
+                    if (BP != bp)
+                        return;
+                    f32x4 tb[RT];
 #pragma unroll
-                        for (int k4 = 0; k4 < 16; k4 += 4) {
-                            const float av = Nh[(bq * 16 + (lane & 15)) * LDF + m * 16 + k4 + (lane >> 4)];
-                            const float bv = Th[(m * 16 + k4 + (lane >> 4)) * LDF + bp * 16 + (lane & 15)];
-                            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
+                    for (int i = 0; i < 4; ++i)
+                        tb[BP][i] = Th[(BP * 16 + g4 + i) * LDF + BP * 16 + r16];
+                    static_for<RT - 1 - BP>([&](auto dc) {
+                        constexpr int B = BP + 1 + decltype(dc)::value;
+                        f32x4 y = zero4();
+                        static_for<B - BP>([&](auto mc) {
+                            constexpr int M = BP + decltype(mc)::value;
+                            const f32x4 av = *reinterpret_cast<const f32x4 *>(Nh + (B * 16 + r16) * LDF + M * 16 + g4);
+#pragma unroll
+                            for (int st = 0; st < 4; ++st)
+                                y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], tb[M][st], y, 0, 0, 0);
+                        });
+                        const f32x4 dv = *reinterpret_cast<const f32x4 *>(Th + (B * 16 + r16) * LDF + B * 16 + g4);
+                        f32x4 t = zero4();
+#pragma unroll
+                        for (int st = 0; st < 4; ++st)
+                            t = __builtin_amdgcn_mfma_f32_16x16x4f32(dv[st], y[st], t, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            tb[B][i] = -t[i];
+                            Th[(B * 16 + g4 + i) * LDF + BP * 16 + r16] = -t[i];
                         }
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        Yw[wave][tile_row(lane, i)][tile_col(lane)] = acc[i];
-                }
-                __syncthreads();
-                if (blk < nblk) {
-                    const int hh = blk / (RT - d), bp = blk % (RT - d), bq = bp + d;
-                    float *Th = Tf + hh * C * LDF;
-                    f32x4 acc = zero4();
-#pragma unroll
-                    for (int k4 = 0; k4 < 16; k4 += 4) {
-                        const float av = Th[(bq * 16 + (lane & 15)) * LDF + bq * 16 + k4 + (lane >> 4)];
-                        const float bv = Yw[wave][k4 + (lane >> 4)][lane & 15];
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc, 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        Th[(bq * 16 + tile_row(lane, i)) * LDF + bp * 16 + tile_col(lane)] = -acc[i];
-                }
-                __syncthreads();
+                    });
+                });
             }
+            __syncthreads();
         }
 
         // T to global, zero above the diagonal blocks.
