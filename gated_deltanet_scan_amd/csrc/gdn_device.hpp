@@ -132,15 +132,20 @@ struct LdsPad {
     static constexpr int value = 16 / sizeof(E);
 };
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ inline float wave_inclusive_sum(float x, int lane)
+// Inclusive prefix sum over the 64 lanes of a wave, on the DPP lane network (no
+// LDS traffic): a Hillis-Steele scan inside each row of 16 lanes (shifts 1, 2, 4,
+// 8; lanes shifted in from outside the row add 0), then the row totals carried
+// forward by the row broadcasts of lanes 15 (into rows 1 and 3) and 31 (into rows
+// 2 and 3).
+__device__ inline float wave_inclusive_sum(float x)
 {
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        float y = __shfl_up(x, d, kWave);
-        if (lane >= d)
-            x += y;
-    }
+    constexpr int kRowShr = 0x110, kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+    x += __builtin_amdgcn_update_dpp(0.f, x, kRowShr + 1, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, kRowShr + 2, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, kRowShr + 4, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, kRowShr + 8, 0xf, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, kRowBcast15, 0xa, 0xf, false);
+    x += __builtin_amdgcn_update_dpp(0.f, x, kRowBcast31, 0xc, 0xf, false);
     return x;
 }
 

@@ -166,9 +166,10 @@ __device__ inline typename M::frag staged_frag(const unsigned char *base, int ro
 // All global reads are issued first: the chunk's q and k rows go straight
 // into LDS (direct-to-LDS loads, rows in the Swz chunk order; rows past the
 // end of the sequence repeat its last row, their products are masked), and
-// g, beta are read while they are in flight, so the in-chunk cumulative sum
-// G and the decay record are done under the latency of the big loads.  The
-// Gram products K K^T and Q K^T are formed tile by tile on the matrix cores
+// g, beta of every value head of the pass into registers of every wave.
+// Each wave forms the in-chunk cumulative sum G with a DPP lane scan and
+// keeps its own LDS copy of G and beta (read back by itself, so no barrier).
+// The Gram products K K^T and Q K^T are formed tile by tile on the matrix cores
 // in transposed orientation (a lane holds one row t and four consecutive
 // columns j), and the log-space mask and decay are applied to the tile in
 // registers: N goes to LDS for the solve, A straight to global memory.
@@ -207,6 +208,8 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem_qk[U1];
     __shared__ __attribute__((aligned(16))) float Nm[HB * C * LDF];
+    __shared__ __attribute__((aligned(16))) float Gw[kWaves][HB][C];   // each wave's copy of G
+    __shared__ __attribute__((aligned(16))) float Bw[kWaves][HB][C];   // and of beta
     const unsigned char *Ks = smem_qk;                  // staged k rows
     const unsigned char *Qs = smem_qk + TILE;           // staged q rows
     float *Tf = reinterpret_cast<float *>(smem_qk);     // [HB][C][LDF], after the Gram products
@@ -283,8 +286,13 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
         // C - 1 holds G at the last real token), and the decay record of the chunk
         float Gr[HB];
 #pragma unroll
-        for (int hh = 0; hh < HB; ++hh)
-            Gr[hh] = wave_inclusive_sum(gv[hh], lane);
+        for (int hh = 0; hh < HB; ++hh) {
+            Gr[hh] = wave_inclusive_sum(gv[hh]);
+            if (lane < C) {   // this wave's own copy: read back below by the same wave only
+                Gw[wv][hh][lane] = Gr[hh];
+                Bw[wv][hh][lane] = bv[hh];
+            }
+        }
         if (wv < nh && lane < C) {
             const int h = hq * group + hb + wv;
             const float G = wv == 0 ? Gr[0] : Gr[HB - 1];
@@ -297,6 +305,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
             rec[3 * C + lane] = (wv == 0 ? bv[0] : bv[HB - 1]) * eg;
         }
 
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         // Gram tiles, transposed: the tiles of block row tr (rows t) and block column tc
         // (columns j) are computed as K_j . K_t and K_j . Q_t, so lane l holds row
         // t = 16 tr + l % 16 and columns j = 16 tc + 4 (l / 16) + {0..3}.  The lower-triangle
@@ -333,14 +342,14 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
                     if (hh >= nh)
                         break;
                     const int h = hq * group + hb + hh;
-                    const float gt = __shfl(Gr[hh], t, kWave), bt = __shfl(bv[hh], t, kWave);
+                    const float gt = Gw[wv][hh][t], bt = Bw[wv][hh][t];
+                    const f32x4 gj = *reinterpret_cast<const f32x4 *>(&Gw[wv][hh][j0]);
                     f32x4 nv, av;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         // exp(G_t - G_j) only for j <= t, where the exponent is <= 0 (log-space mask)
                         const int j = j0 + e;
-                        const float gj = __shfl(Gr[hh], j, kWave);
-                        const float ed = (j <= t) ? __expf(gt - gj) : 0.f;
+                        const float ed = (j <= t) ? __expf(gt - gj[e]) : 0.f;
                         nv[e] = (j < t) ? bt * ed * kk[e] : 0.f;
                         av[e] = (t < len) ? scale * ed * qk[e] : 0.f;
                     }
