@@ -311,14 +311,17 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
         // t = 16 tr + l % 16 and columns j = 16 tc + 4 (l / 16) + {0..3}.  The lower-triangle
         // tiles (tc <= tr) give N (to LDS; the solve reads nothing above the diagonal) and A
         // (to global memory); A tiles above the diagonal are stored as zeros.  The tiles are
-        // dealt to the waves round-robin at compile time.
+        // dealt to the waves round-robin at compile time, so each wave runs its own items as
+        // straight-line code (the reads of one item overlap the products of the previous).
         const int r16 = lane & 15, kq = (lane >> 4) * MK::kPerLane;
-        static_for<RT * RT>([&](auto pc) {
+        auto gram_items = [&](auto wc) __attribute__((always_inline)) {
+          constexpr int W = decltype(wc)::value;
+          static_for<RT * RT>([&](auto pc) {
             constexpr int P = decltype(pc)::value;
             constexpr int tr = P / RT, tc = P % RT;
             constexpr bool lower = tc <= tr;
             constexpr int idx = lower ? tr * (tr + 1) / 2 + tc : (tr * RT + tc) + 2;   // deal index
-            if (idx % kWaves != wv)
+            if constexpr (idx % kWaves != W)
                 return;
             const int t = tr * 16 + r16;
             const int j0 = tc * 16 + 4 * (lane >> 4);
@@ -362,7 +365,14 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
                     if (hh < nh)
                         store4(amat + (slot * hv + hq * group + hb + hh) * C * C + t * C + j0, 0.f, 0.f, 0.f, 0.f);
             }
-        });
+          });
+        };
+        switch (wv) {
+        case 0: gram_items(std::integral_constant<int, 0>{}); break;
+        case 1: gram_items(std::integral_constant<int, 1>{}); break;
+        case 2: gram_items(std::integral_constant<int, 2>{}); break;
+        default: gram_items(std::integral_constant<int, 3>{}); break;
+        }
         __syncthreads();   // the q, k rows are dead from here: their space holds T
 
         // Diagonal blocks D_b: one wave per head, lane = (block b, column j).
