@@ -1041,9 +1041,9 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_kernel(
 // ---------------------------------------------------------------------------
 // Scan kernel for few (sequence, head) pairs (bf16 io, chunk 64): one chunk
 // step is spread over 4 compute waves by chunk rows (and key rows for the S
-// update), exchanging X, D and the transposed bf16 copy of S through LDS; 4
-// loader waves stage the next chunk and write out the previous chunk's
-// outputs.  With few pairs the chip has more CUs than workgroups and the
+// update), exchanging X, D and the transposed bf16 copy of S through LDS, and
+// storing the chunk's outputs straight from registers; 4 loader waves stage
+// the next chunk.  With few pairs the chip has more CUs than workgroups and the
 // chain of chunk steps is latency-bound, which this split shortens.  (Wide
 // batches use gdn_chunk_scan_bf16_kernel.)
 // ---------------------------------------------------------------------------
@@ -1072,7 +1072,6 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     constexpr int PAD = LdsPad<E>::value;
     constexpr int LDK = key_row_stride<E>(DK);
     constexpr int LDC = C + PAD;
-    constexpr int LDV = DVS + PAD;
     constexpr int RT = C / 16, CT = DVS / 16, SR = DK / 16;
     constexpr int SR_PER = (SR + kWaves - 1) / kWaves;
     constexpr int RT_PER = (RT + kWaves - 1) / kWaves;
@@ -1112,7 +1111,6 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     __shared__ __attribute__((aligned(16))) E Dt[DVS * LDC];
     __shared__ __attribute__((aligned(16))) E LDt[DVS * LDC];
     __shared__ __attribute__((aligned(16))) E St[DVS * LDK];
-    __shared__ __attribute__((aligned(16))) E Os[C * LDV];
 
     // the stage buffers as LDS addresses (the direct loads write LDS by address)
     __attribute__((address_space(3))) unsigned char *const lds_stage =
@@ -1257,28 +1255,16 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         default: fn(std::integral_constant<int, 3>{}); break;
         }
     };
-    // Outputs of a finished chunk (staged in Os by the compute waves): coalesced
-    // 16-byte rows to global, written by the loaders.
-    auto flush = [&](int64_t t0, int len) __attribute__((always_inline)) {
-        constexpr int O_VECS = C * DVS / VN;
-        for (int i = tid - kThreads; i < O_VECS; i += kThreads) {
-            const int r = i / (DVS / VN), c0 = (i % (DVS / VN)) * VN;
-            if (r < len)
-                *reinterpret_cast<V16 *>(o + ((size_t)(t0 + r) * hv + h) * dv + (size_t)s * DVS + c0) =
-                    *reinterpret_cast<const V16 *>(Os + r * LDV + c0);
-        }
-    };
-
     // ---- compute waves: one chunk step on stage buffer `cur` (barriers B1 and B2 inside) ----
-    auto step = [&](int cur) __attribute__((always_inline)) {
+    auto step = [&](int cur, int64_t t0, int len) __attribute__((always_inline)) {
         const unsigned char *stg = stage_mem + cur * STAGE;
         const float *Gs = reinterpret_cast<const float *>(stg + OFF_D);   // scale exp(G)
         const float *Lam = Gs + C;                                         // exp(G_last - G)
         const float *Bet = Gs + 2 * C;                                     // beta
         const float *BGam = Gs + 3 * C;                                    // beta exp(G)
 
-        // P1: Q S and K S for row tile rt (all column tiles); X = diag(beta)(V - diag(exp G) K S)
-        //     goes to Xt (transposed); diag(exp G) Q S stays in oacc for P3.
+        // P1: (Q S)^T and K S for row tile rt (all column tiles); X = diag(beta)(V - diag(exp G)
+        //     K S) goes to Xt (transposed); (diag(exp G) Q S)^T stays in oacc for P3.
         f32x4 oacc[RT_PER][CT];
         f32x4 kacc[RT_PER][CT];
 #pragma unroll
@@ -1298,7 +1284,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) {
                         const typename MK::frag bs = MK::load(St + (ct * 16 + r) * LDK + k0 + kk);
-                        oacc[u][ct] = MK::mma(aq, bs, oacc[u][ct]);
+                        oacc[u][ct] = MK::mma(bs, aq, oacc[u][ct]);   // (Q S)^T: lane = token
                         kacc[u][ct] = MK::mma(ak, bs, kacc[u][ct]);
                     }
                 }
@@ -1311,7 +1297,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
                         const int rr = rt * 16 + tile_row(lane, i);
                         const E vv = *reinterpret_cast<const E *>(stg + OFF_V + SV::off(rr, col * ES));
                         x[i] = Bet[rr] * to_f32(vv) - BGam[rr] * kacc[u][ct][i];
-                        oacc[u][ct][i] *= Gs[rr];
+                        oacc[u][ct][i] *= Gs[rt * 16 + (lane & 15)];
                     }
                     store4(Xt + col * LDC + rt * 16 + tile_row(lane, 0), x[0], x[1], x[2], x[3]);
                 }
@@ -1348,7 +1334,9 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         }
         __syncthreads();   // B2
 
-        // P3: O = scale diag(exp G) Q S + (scale A) D, staged in Os
+        // P3: O = scale diag(exp G) Q S + (scale A) D, computed transposed (O^T = (Q S)^T
+        //     + D^T A^T, the same fragments with the operand roles swapped) so that each lane
+        //     holds four consecutive output columns of one token and stores them at once
 #pragma unroll
         for (int u = 0; u < RT_PER; ++u) {
             const int rt = wave + u * kWaves;
@@ -1359,14 +1347,16 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
                     const auto aa = staged_frag<MC, SC, E>(stg + OFF_A, rt * 16 + r, k0 + kk);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
-                        oacc[u][ct] = MC::mma(aa, MC::load(Dt + (ct * 16 + r) * LDC + k0 + kk), oacc[u][ct]);
+                        oacc[u][ct] = MC::mma(MC::load(Dt + (ct * 16 + r) * LDC + k0 + kk), aa, oacc[u][ct]);
                 }
+                // O^T tile: lane = token rt * 16 + l % 16, four consecutive output columns
+                const int tok = rt * 16 + (lane & 15);
+                if (tok < len) {
 #pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        Os[(rt * 16 + tile_row(lane, i)) * LDV + ct * 16 + tile_col(lane)] =
-                            (E)oacc[u][ct][i];
+                    for (int ct = 0; ct < CT; ++ct)
+                        store4(o + ((size_t)(t0 + tok) * hv + h) * dv + (size_t)s * DVS + ct * 16 + 4 * (lane >> 4),
+                               oacc[u][ct][0], oacc[u][ct][1], oacc[u][ct][2], oacc[u][ct][3]);
+                }
             }
         }
         // P4: S <- exp(G_last) S + K^T diag(lambda) D; refresh the transposed copy
@@ -1395,7 +1385,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     };
 
     // ---- pipeline: while the compute waves work on chunk c (stage c & 1), the loaders
-    //      flush the outputs of chunk c - 1 and stage chunk c + 1 into the other buffer.
+    //      stage chunk c + 1 into the other buffer.
     //      The direct loads are not tracked by the compiler's LDS dependences: each loader
     //      waits for its own loads before the barrier that publishes the stage. ----
     if (loader) {
@@ -1405,10 +1395,6 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     __syncthreads();
     for (int c = c_begin; c < c_end; ++c) {
         if (loader) {
-            if (c > c_begin) {
-                const int64_t pt0 = a + (int64_t)(c - 1) * C;
-                flush(pt0, (int)min<int64_t>(C, b - pt0));
-            }
             if (c + 1 < c_end)
                 by_loader([&](auto wc) { issue_jobs(wc, c + 1); });
             // B1 and B2 of the compute waves: the loaders publish nothing there, so they
@@ -1417,14 +1403,12 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
             __builtin_amdgcn_s_barrier();
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         } else {
-            step(c & 1);
+            const int64_t ct0 = a + (int64_t)c * C;
+            step(c & 1, ct0, (int)min<int64_t>(C, b - ct0));
         }
-        __syncthreads();       // end of step: St, Os and the next stage are complete
+        __syncthreads();       // end of step: St and the next stage are complete
     }
-    if (loader) {
-        const int64_t pt0 = a + (int64_t)(c_end - 1) * C;
-        flush(pt0, (int)min<int64_t>(C, b - pt0));
-    } else {
+    if (!loader) {
         // ---- final state ----
 #pragma unroll
         for (int u = 0; u < SR_PER; ++u) {
