@@ -94,7 +94,8 @@ PrefillWorkspace prefill_workspace(int32_t hv, int32_t chunk, int32_t io_dtype, 
     if (max_chunks > INT32_MAX)
         return w;
     w.max_chunks = (int32_t)max_chunks;
-    w.table_bytes = (((size_t)num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
+    // chunk table (num_seqs + 1 entries), then the scan order of the sequences (num_seqs)
+    w.table_bytes = ((2 * (size_t)num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
     // per chunk slot and value head: T and A (C x C io elements each) and the decay
     // record scale exp(G), exp(G_last - G), beta, beta exp(G) (4 C floats)
     const size_t mats = 2 * (size_t)max_chunks * (size_t)hv * (size_t)chunk * (size_t)chunk * io_size(io_dtype);

@@ -21,7 +21,7 @@ struct PrefillArgs {
     void *o;
     void *workspace;
     int32_t max_chunks;    // chunk slots the workspace holds (upper bound on the chunks of the batch)
-    size_t table_bytes;    // bytes of the chunk table at the start of the workspace
+    size_t table_bytes;    // bytes of the chunk table and sequence order at the start of the workspace
     int32_t seg_len;       // > 0: segment mode, local chunks per sequence per segment (0: global mode)
     int32_t max_seq_chunks;  // segment mode: chunks of the longest sequence
     void *stream;
@@ -50,7 +50,8 @@ struct SnapshotArgs {
     void *stream;
 };
 
-// Workspace layout of the prefill: [chunk table | T matrices | A matrices].
+// Workspace layout of the prefill: [chunk table, sequence order | T matrices | A matrices |
+// decay records].
 struct PrefillWorkspace {
     int32_t max_chunks;
     size_t table_bytes;

@@ -83,6 +83,31 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_table_kernel(
         chunk_start[num_seqs] = (int32_t)min<int64_t>(carry, max_chunks);
 }
 
+// Order in which the scan kernels take the sequences: by decreasing length
+// (ties by index), so that the workgroups of the longest chains of chunk steps
+// are dispatched first and the short ones fill the compute units they free.
+// order[rank] = n; the ranks form a permutation, so every entry is written
+// once.  Quadratic in the number of sequences (used for small batches only).
+__global__ __launch_bounds__(kThreads) void gdn_seq_order_kernel(const int32_t *__restrict__ cu, int32_t num_seqs,
+                                                               int64_t total_tokens, int32_t *__restrict__ order)
+{
+    const int n = blockIdx.x * kThreads + threadIdx.x;
+    if (n >= num_seqs)
+        return;
+    auto length = [&](int m) {
+        const int64_t a = min<int64_t>(max<int64_t>(cu[m], 0), total_tokens);
+        const int64_t b = min<int64_t>(max<int64_t>(cu[m + 1], a), total_tokens);
+        return b - a;
+    };
+    const int64_t len = length(n);
+    int rank = 0;
+    for (int m = 0; m < num_seqs; ++m) {
+        const int64_t lm = length(m);
+        rank += (lm > len || (lm == len && m < n)) ? 1 : 0;
+    }
+    order[rank] = n;
+}
+
 // Sequence that owns chunk entry e: chunk_start[n] <= e < chunk_start[n+1].
 __device__ inline int find_sequence(const int32_t *chunk_start, int32_t num_seqs, int32_t e)
 {
@@ -108,7 +133,11 @@ struct SlotMap {
     const int32_t *chunk_start;  // global mode: per-sequence first slot; NULL in segment mode
     int32_t seg_first;           // first local chunk index of this launch
     int32_t seg_len;             // local chunks per sequence in this launch
+    const int32_t *seq_order;    // scan kernels: the sequence of rank r is seq_order[r]; NULL: r
 };
+
+// Sequence of the scan work item with sequence rank r.
+__device__ inline int ranked_sequence(const SlotMap &m, int r) { return m.seq_order ? m.seq_order[r] : r; }
 
 // Number of chunks of sequence n (consistent with the clamping of the chunk table).
 __device__ inline int seq_chunks(const SlotMap &m, const int32_t *cu, int n, int64_t total_tokens, int chunk)
@@ -690,7 +719,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_kernel(
     const int s = j8 % nv;
     if (pair >= pairs)
         return;
-    const int n = pair / hv, h = pair - (pair / hv) * hv;
+    const int n = ranked_sequence(map, pair / hv), h = pair - (pair / hv) * hv;
     const int hq = h / (hv / hqk);
     int64_t a, b;
     seq_range(cu, n, total_tokens, a, b);
@@ -1126,7 +1155,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     const int s = j8 % nv;
     if (pair >= pairs)
         return;
-    const int n = pair / hv, h = pair - (pair / hv) * hv;
+    const int n = ranked_sequence(map, pair / hv), h = pair - (pair / hv) * hv;
     const int hq = h / (hv / hqk);
     int64_t a, b;
     seq_range(cu, n, total_tokens, a, b);
@@ -1505,7 +1534,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
     const int s = j8 % nv;
     if (pair >= pairs)
         return;
-    const int n = pair / hv, h = pair - (pair / hv) * hv;
+    const int n = ranked_sequence(map, pair / hv), h = pair - (pair / hv) * hv;
     const int hq = h / (hv / hqk);
     int64_t a, b;
     seq_range(cu, n, total_tokens, a, b);
@@ -1931,6 +1960,9 @@ static void launch_scan_bf16(const PrefillArgs &p, const SlotMap &map, const bf1
                           p.dv, tmat, amat, dec, sin, sout, static_cast<bf16 *>(p.o), p.scale);
 }
 
+// Batches of at most this many sequences are scanned longest first.
+constexpr int32_t kMaxOrderedSeqs = 4096;
+
 template <typename E, int C, int DK>
 static hipError_t launch_prefill_t(const PrefillArgs &p)
 {
@@ -1969,10 +2001,21 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
                               p.scale);
     };
 
+    // Longest sequences first in the scans (their chains of chunk steps bound the time).
+    const int32_t *order = nullptr;
+    if (p.num_seqs > 1 && p.num_seqs <= kMaxOrderedSeqs) {
+        int32_t *ord = chunk_start + p.num_seqs + 1;   // after the chunk table
+        const ProfEvents ev = prof_events(PROF_CHUNK_TABLE);
+        hipExtLaunchKernelGGL(gdn_seq_order_kernel, dim3((unsigned)((p.num_seqs + kThreads - 1) / kThreads)),
+                              dim3(kThreads), 0, st, ev.start, ev.stop, 0, p.cu_seqlens, p.num_seqs, p.total_tokens,
+                              ord);
+        order = ord;
+    }
+
     if (p.seg_len > 0) {
         // Segment mode: local chunks [s0, s0 + seg_len) of every sequence per step.
         for (int32_t s0 = 0; s0 < p.max_seq_chunks; s0 += p.seg_len) {
-            const SlotMap map{nullptr, s0, p.seg_len};
+            const SlotMap map{nullptr, s0, p.seg_len, order};
             prep(map, (int64_t)p.num_seqs * p.seg_len);
             scan(map, s0 == 0 ? p.initial_state : p.final_state, p.final_state);
         }
@@ -1984,7 +2027,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
         hipExtLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
                               p.cu_seqlens, p.num_seqs, p.total_tokens, (int32_t)C, p.max_chunks, chunk_start);
     }
-    const SlotMap map{chunk_start, 0, INT32_MAX};
+    const SlotMap map{chunk_start, 0, INT32_MAX, order};
     if (p.max_chunks > 0)
         prep(map, p.max_chunks);
     scan(map, p.initial_state, p.final_state);

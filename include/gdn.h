@@ -171,7 +171,7 @@ gdn_status gdn_state_snapshot(const gdn_shape *shape,
  * launches.
  * gdn_profile_collect() waits for the recorded events of one kernel and
  * returns how many launches were recorded and their summed duration in ms.
- * Kernel identifiers: 0 chunk table, 1 prep (Gram products and solve),
+ * Kernel identifiers: 0 chunk table and scan order, 1 prep (Gram products and solve),
  * 2 chunk scan (state pass and outputs), 3 decode, 4 snapshot.
  * The events are created on first use and kept until the process ends;
  * no device memory is allocated.
