@@ -1979,12 +1979,14 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
             // 32 columns per wave; a whole 128-column head per workgroup when the batch
             // has enough (sequence, head) pairs to fill the chip, else 64 columns
             // Few (sequence, head) pairs: the chain of chunk steps is latency-bound, so a
-            // step is spread over the rows of 4 waves (16-column slices).  Many pairs:
-            // whole 128-column heads with each wave owning 32 columns.
+            // step is spread over the rows of 4 waves (16-column slices, 8 workgroups per
+            // pair).  More pairs: whole 128-column heads per workgroup, 8 waves of 16
+            // columns each (two waves per SIMD hide each other's latencies).  Measured
+            // crossover: 64 pairs (1024-token sequences, 16 chunk steps).
             const int64_t pairs = (int64_t)p.num_seqs * p.hv;
             if constexpr (DK == 128) {
-                if (pairs >= 256) {
-                    launch_scan_bf16<DK, 4, 2>(p, map, tmat, amat, dec, sin, sout, st);
+                if (pairs > 64) {
+                    launch_scan_bf16<DK, 8, 1>(p, map, tmat, amat, dec, sin, sout, st);
                     return;
                 }
             }

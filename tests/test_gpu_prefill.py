@@ -74,7 +74,8 @@ def test_every_kernel_instance(io, d, chunk, host_offsets):
 
 @pytest.mark.parametrize("nseq", [40, 160])
 def test_wide_slices_many_sequences(nseq):
-    """Enough (sequence, head) pairs that the scan takes 32- and 64-column dv slices."""
+    """Enough (sequence, head) pairs that the scan takes whole 128-column heads per workgroup
+    (the wide-batch kernel) instead of the row-split one."""
     gen = torch.Generator().manual_seed(nseq)
     lengths = [int(x) for x in torch.randint(0, 200, (nseq,), generator=gen)]
     for host_offsets in (True, False):
