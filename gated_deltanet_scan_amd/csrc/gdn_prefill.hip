@@ -211,8 +211,10 @@ __device__ inline typename M::frag staged_frag(const unsigned char *base, int ro
 // of the NPU page applied to the block-triangular split, in fp32 on the
 // matrix cores.
 // ---------------------------------------------------------------------------
+constexpr int kPrepWaves = 4;   // waves of a prep workgroup (two workgroups fit a CU)
+
 template <typename E, int C, int DK>
-__global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
+__global__ __launch_bounds__(kPrepWaves * kWave) void gdn_prep_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, SlotMap map, int32_t num_seqs,
     int64_t total_tokens, int32_t hqk, int32_t hv, E *__restrict__ tmat, E *__restrict__ amat,
@@ -231,14 +233,15 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
     constexpr int U1 = 2 * TILE > F_BYTES ? 2 * TILE : F_BYTES;   // k, q rows, then T of HB heads
     constexpr int NCK = TILE / 16;                    // 16-byte chunks of a staged tile
     constexpr int NJ1 = (NCK + 63) / 64;              // 64-lane load jobs per tile
-    constexpr int NJ_PER = (2 * NJ1 + kWaves - 1) / kWaves;
+    constexpr int PW = kPrepWaves, NT = PW * kWave;
+    constexpr int NJ_PER = (2 * NJ1 + PW - 1) / PW;
     static_assert(DK * ES >= 16 && DK * ES <= 256, "staged rows of 16 .. 256 bytes");
     static_assert(C <= kWave, "one lane per token of a chunk");
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem_qk[U1];
     __shared__ __attribute__((aligned(16))) float Nm[HB * C * LDF];
-    __shared__ __attribute__((aligned(16))) float Gw[kWaves][HB][C];   // each wave's copy of G
-    __shared__ __attribute__((aligned(16))) float Bw[kWaves][HB][C];   // and of beta
+    __shared__ __attribute__((aligned(16))) float Gw[PW][HB][C];   // each wave's copy of G
+    __shared__ __attribute__((aligned(16))) float Bw[PW][HB][C];   // and of beta
     const unsigned char *Ks = smem_qk;                  // staged k rows
     const unsigned char *Qs = smem_qk + TILE;           // staged q rows
     float *Tf = reinterpret_cast<float *>(smem_qk);     // [HB][C][LDF], after the Gram products
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
         const E *qb = q + ((size_t)t0 * hqk + hq) * DK;
 #pragma unroll
         for (int u = 0; u < NJ_PER; ++u) {
-            const int J = wave + u * kWaves;
+            const int J = wave + u * PW;
             if (J < 2 * NJ1) {
                 const int idx = J % NJ1;
                 const int P = min(idx * 64 + lane, NCK - 1);
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
             constexpr int tr = P / RT, tc = P % RT;
             constexpr bool lower = tc <= tr;
             constexpr int idx = lower ? tr * (tr + 1) / 2 + tc : (tr * RT + tc) + 2;   // deal index
-            if constexpr (idx % kWaves != W)
+            if constexpr (idx % PW != W)
                 return;
             const int t = tr * 16 + r16;
             const int j0 = tc * 16 + 4 * (lane >> 4);
@@ -396,12 +399,10 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
             }
           });
         };
-        switch (wv) {
-        case 0: gram_items(std::integral_constant<int, 0>{}); break;
-        case 1: gram_items(std::integral_constant<int, 1>{}); break;
-        case 2: gram_items(std::integral_constant<int, 2>{}); break;
-        default: gram_items(std::integral_constant<int, 3>{}); break;
-        }
+        static_for<PW>([&](auto wc) {
+            if (decltype(wc)::value == wv)
+                gram_items(wc);
+        });
         __syncthreads();   // the q, k rows are dead from here: their space holds T
 
         // Diagonal blocks D_b: one wave per head, lane = (block b, column j).
@@ -437,8 +438,8 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
         if constexpr (RT > 1) {
             const int nchains = nh * (RT - 1);
             const int r16 = lane & 15, g4 = 4 * (lane >> 4);
-            for (int round = 0; round * kWaves < nchains; ++round) {
-                const int ch = round * kWaves + ((round & 1) ? kWaves - 1 - wv : wv);
+            for (int round = 0; round * PW < nchains; ++round) {
+                const int ch = round * PW + ((round & 1) ? PW - 1 - wv : wv);
                 if (ch >= nchains)
                     continue;
                 const int bp = ch / nh, hh = ch % nh;
@@ -479,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void gdn_prep_kernel(
         }
 
         // T to global, zero above the diagonal blocks.
-        for (int idx = tid; idx < nh * C * C / VN; idx += kThreads) {
+        for (int idx = tid; idx < nh * C * C / VN; idx += NT) {
             const int hh = idx / (C * C / VN);
             const int rem = (idx - hh * (C * C / VN)) * VN;
             const int t = rem / C, j0 = rem - (rem / C) * C;
@@ -1997,7 +1998,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
     };
     auto prep = [&](const SlotMap &map, int64_t slots) {
         const ProfEvents ev = prof_events(PROF_PREP);
-        hipExtLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), dim3((unsigned)slots, p.hqk), dim3(kThreads), 0, st,
+        hipExtLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), dim3((unsigned)slots, p.hqk), dim3(kPrepWaves * kWave), 0, st,
                               ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k), p.g,
                               p.beta, p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv, tmat, amat, dec,
                               p.scale);
