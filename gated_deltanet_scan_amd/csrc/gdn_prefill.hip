@@ -1644,7 +1644,9 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
         loff[decltype(rc)::value] = round_bytes(rc, row, ecol);
         lblk[decltype(rc)::value] = blk;
     });
-    auto issue_stage = [&](auto bufc, int c) __attribute__((always_inline)) {
+    // Rounds [LO, HI) of the staging of chunk c into buffer BUF.
+    auto issue_rounds = [&](auto bufc, int c, auto loc, auto hic) __attribute__((always_inline)) {
+        constexpr int LO = decltype(loc)::value, HI = decltype(hic)::value;
         __attribute__((address_space(3))) unsigned char *stg = stage_lds(bufc);
         const int64_t t0 = a + (int64_t)c * C;
         const int last = (int)min<int64_t>(C, b - t0) - 1;
@@ -1659,6 +1661,8 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
         const bool full = last == C - 1;
         static_for<NR>([&](auto rc) __attribute__((always_inline)) {
             constexpr int R = decltype(rc)::value;
+            if constexpr (R < LO || R >= HI)
+                return;
             uint32_t off = loff[R];
             if constexpr (R < RT0 || (R >= RV0 && R < RD0)) {
                 if (!full) {   // ragged last chunk: rows past its end repeat its last row
@@ -1673,6 +1677,18 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
                                                  (__attribute__((address_space(3))) void *)(stg + lblk[R]), 16, 0,
                                                  0);
         });
+    };
+    auto issue_stage = [&](auto bufc, int c) __attribute__((always_inline)) {
+        issue_rounds(bufc, c, std::integral_constant<int, 0>{}, std::integral_constant<int, NR>{});
+    };
+    // The next chunk's staging is issued in four parts spread over the step (q and k
+    // rounds first, the decay record last): issued at once, the last waves to issue would
+    // stall for the whole transfer before starting their products.
+    constexpr int kPartEnd[4] = {RT0, RV0, RD0, NR};
+    auto stage_part = [&](auto bufc, int c, auto pc) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value;
+        issue_rounds(bufc, c, std::integral_constant<int, P == 0 ? 0 : kPartEnd[P == 0 ? 0 : P - 1]>{},
+                     std::integral_constant<int, kPartEnd[P]>{});
     };
     auto stage_done = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1701,7 +1717,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
         vtro[ct] = vtr(ct);
 
     // ---- one chunk step of this wave's WC columns on stage buffer BUF ----
-    auto step = [&](auto bufc, int64_t t0, int len) __attribute__((always_inline)) {
+    auto step = [&](auto bufc, int64_t t0, int len, auto &&stage_hook) __attribute__((always_inline)) {
         const unsigned char *stg = stage_ptr(bufc);
         auto frag = [&](int off) __attribute__((always_inline)) {
             return *reinterpret_cast<const bf16x8 *>(stg + off);
@@ -1715,6 +1731,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
         };
 
         // [Q;K] S: (Q S)^T with S^T as the A operand; K S with K rows in the order of CH
+        stage_hook(std::integral_constant<int, 0>{});
         bf16x8 sb[NSK][CT];
         pack_s(sb);
         f32x4 qacc[RT][CT], xacc[RT][CT];
@@ -1742,6 +1759,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
                 }
         }
 
+        stage_hook(std::integral_constant<int, 1>{});
         // T fragments, then X = beta v - beta exp(G) (K S)
         bf16x8 ft[NSC][RT];
 #pragma unroll
@@ -1784,6 +1802,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
 
 
+        stage_hook(std::integral_constant<int, 2>{});
         bf16x8 db[NSC][CT], lb[NSC][CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
@@ -1833,6 +1852,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        stage_hook(std::integral_constant<int, 3>{});
         // A fragments (A carries the output scale)
         bf16x8 fa[NSC][RT];
 #pragma unroll
@@ -1877,17 +1897,21 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
     issue_stage(buf0, c_begin);
     stage_done();
     for (int c = c_begin;;) {
-        if (c + 1 < c_end)
-            issue_stage(buf1, c + 1);
+        bool more = c + 1 < c_end;
         int64_t t0 = a + (int64_t)c * C;
-        step(buf0, t0, (int)min<int64_t>(C, b - t0));
+        step(buf0, t0, (int)min<int64_t>(C, b - t0), [&](auto pc) __attribute__((always_inline)) {
+            if (more)
+                stage_part(buf1, c + 1, pc);
+        });
         stage_done();
         if (++c >= c_end)
             break;
-        if (c + 1 < c_end)
-            issue_stage(buf0, c + 1);
+        more = c + 1 < c_end;
         t0 = a + (int64_t)c * C;
-        step(buf1, t0, (int)min<int64_t>(C, b - t0));
+        step(buf1, t0, (int)min<int64_t>(C, b - t0), [&](auto pc) __attribute__((always_inline)) {
+            if (more)
+                stage_part(buf0, c + 1, pc);
+        });
         stage_done();
         if (++c >= c_end)
             break;
