@@ -11,8 +11,9 @@ Several copies of the batch are rotated so that repeated steps do not run
 out of the 256 MB last-level cache.  The same run also measures the decode
 step (64 sequences, state updated in place, state sets rotated), the long
 32k prefill and the 16-sequence varlen prefill, each with its per-kernel
-durations from HIP events recorded on the library's launch stream; and the
-fp64 CPU oracle on a bounded sample of the headline workload.
+durations from HIP events recorded on the library's launch stream; the gated
+RMSNorm that follows the scan, on the 1k and 32k output shapes; and the fp64
+CPU oracle on a bounded sample of the headline workload.
 
 Prints ONE JSON line.
 """
@@ -44,6 +45,7 @@ KERNEL_SOURCES = {
     "gdn_chunk_scan_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_prep_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_decode_kernel": ("gated_deltanet_scan_amd/csrc/gdn_decode.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
+    "gdn_gated_rmsnorm_kernel": ("gated_deltanet_scan_amd/csrc/gdn_norm.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
 }
 
 
@@ -272,6 +274,42 @@ def measure_decode(name, steps, warmup):
     }
 
 
+def measure_norm(tokens, steps, warmup, hv=32, dv=128):
+    """The gated RMSNorm after the scan (gdn_gated_rmsnorm) on a [tokens, HV, dv] bf16 output:
+    algorithmic bytes = o and z read once, y written once (3 * tokens * HV * dv * 2) plus the
+    weight.  Input sets are rotated so that the working set exceeds the last-level cache."""
+    import torch
+
+    import gated_deltanet_scan_amd as gdn
+    from gated_deltanet_scan_amd import synthetic
+    x = synthetic.make_norm_inputs(tokens, hv, dv, torch.bfloat16, seed=2000)
+    dev = torch.device("cuda:0")
+    base = {k: v.to(dev) for k, v in x.items()}
+    nbytes = 3 * tokens * hv * dv * 2 + dv * 4
+    n_sets = int(min(16, max(1, math.ceil(CACHE_DEFEAT_BYTES / nbytes))))
+    calls = []
+    for i in range(n_sets):
+        d = base if i == 0 else {k: v.clone() for k, v in base.items()}
+        calls.append(gdn.prepare_gated_rmsnorm(d["o"], d["z"], d["weight"], eps=1e-6))
+    for i in range(warmup):
+        calls[i % n_sets]()
+    _sync()
+    gdn.profile_enable(True)
+    for i in range(steps):
+        calls[i % n_sets]()
+    _sync()
+    n, tot = gdn.profile_collect(5)
+    gdn.profile_enable(False)
+    us = tot / n * 1e3
+    achieved = nbytes / (us * 1e-6) / 1e9
+    return {"shape": [tokens, hv, dv], "dtype": "bf16", "eps": 1e-6, "kernel_avg_us": us,
+            "tokens_per_s": tokens / (us * 1e-6), "rotated_sets": n_sets,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": achieved / PEAK_HBM_GBS, "kernel": "gdn_gated_rmsnorm_kernel",
+                         "traffic": measured_traffic("gdn_gated_rmsnorm_kernel", "norm_%d" % tokens),
+                         "avg_us": us, "algorithmic_bytes": nbytes}}
+
+
 def cpu_baseline(name, seconds):
     import oracle
     from gated_deltanet_scan_amd import synthetic
@@ -351,6 +389,9 @@ def main():
             print("[bench] prefill %s" % name, file=sys.stderr, flush=True)
             r = measure_prefill(name, max(5, min(args.steps, 20)), 2)
             extra[name] = {k: v for k, v in r.items() if not k.startswith("_")}
+        for tokens in (1024, 32768):
+            print("[bench] gated RMSNorm %d tokens" % tokens, file=sys.stderr, flush=True)
+            extra["gated_rmsnorm_%d" % tokens] = measure_norm(tokens, max(10, min(args.steps, 50)), 3)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -65,6 +65,8 @@ def load_library():
         lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_state_snapshot.argtypes = [SP, vp, vp, i32, vp, vp, i32, i32, vp]
         lib.gdn_state_snapshot.restype = ctypes.c_int
+        lib.gdn_gated_rmsnorm.argtypes = [SP, vp, vp, vp, vp, i64, ctypes.c_float, vp]
+        lib.gdn_gated_rmsnorm.restype = ctypes.c_int
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_last_error.argtypes = []
@@ -308,7 +310,50 @@ def state_snapshot(src, dst, src_rows=None, dst_rows=None, num_rows=None):
     return dst
 
 
-PROF_CHUNK_TABLE, PROF_PREP, PROF_SCAN, PROF_DECODE, PROF_SNAPSHOT = range(5)
+def _norm_call(o, z, weight, eps, out):
+    lib = load_library()
+    _need(o, "o", ndim=3)
+    dev = o.device
+    if dev.type != "cuda":
+        raise ValueError("o must be on a GPU")
+    io = o.dtype
+    if io not in _IO_DTYPES:
+        raise TypeError("io dtype must be float32 or bfloat16")
+    _need(z, "z", io, dev, 3)
+    if tuple(z.shape) != tuple(o.shape):
+        raise ValueError("z must be shaped like o")
+    t, hv, dv = o.shape
+    _need(weight, "weight", torch.float32, dev, 1)
+    if weight.shape[0] != dv:
+        raise ValueError("weight must be [dv]")
+    if out is None:
+        out = torch.empty_like(o)
+    _need(out, "out", io, dev, 3)
+    if tuple(out.shape) != tuple(o.shape):
+        raise ValueError("out must be shaped like o")
+    shape = make_shape(1, hv, dv, dv, 64, _IO_DTYPES[io], 1.0)
+    args = (ctypes.byref(shape), _ptr(o), _ptr(z), _ptr(weight), _ptr(out), t, float(eps))
+    keep = (shape, o, z, weight)
+    return lib, args, keep, dev, out
+
+
+def gated_rmsnorm(o, z, weight, *, eps=1e-6, out=None):
+    """y = o / sqrt(mean(o^2) + eps) * weight * silu(z) per (token, head) row (gdn_gated_rmsnorm).
+
+    o, z [T, HV, dv] (fp32 or bf16); weight [dv] fp32.  `out` may be o or z (in place).
+    Returns y [T, HV, dv].
+    """
+    lib, args, keep, dev, out = _norm_call(o, z, weight, eps, out)
+    _check(lib, lib.gdn_gated_rmsnorm(*args, _stream(dev)))
+    return out
+
+
+def prepare_gated_rmsnorm(o, z, weight, *, eps=1e-6, out=None) -> PreparedCall:
+    lib, args, keep, dev, out = _norm_call(o, z, weight, eps, out)
+    return PreparedCall(lib.gdn_gated_rmsnorm, lib, args, keep, dev, out)
+
+
+PROF_CHUNK_TABLE, PROF_PREP, PROF_SCAN, PROF_DECODE, PROF_SNAPSHOT, PROF_NORM = range(6)
 
 
 def profile_enable(on: bool = True):

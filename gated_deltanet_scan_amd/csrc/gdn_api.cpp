@@ -312,6 +312,51 @@ gdn_status gdn_decode_step(const gdn_shape *shape, const void *q, const void *k,
     return ok();
 }
 
+gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, const void *o, const void *z, const float *weight, void *y,
+                             int64_t tokens, float eps, void *stream)
+{
+    gdn_status st = check_shape(shape);
+    if (st != GDN_OK)
+        return st;
+    const gdn_shape &s = *shape;
+    if (s.dv != 32 && s.dv != 64 && s.dv != 128)
+        return fail(GDN_ERR_UNSUPPORTED, "no gated RMSNorm kernel for dv=%d (dv in {32,64,128})", s.dv);
+    if (tokens < 0)
+        return fail(GDN_ERR_INVALID_ARG, "negative token count");
+    if (!std::isfinite(eps) || eps < 0.f)
+        return fail(GDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    if (tokens == 0)
+        return ok();
+    if (tokens > (int64_t(1) << 32) / s.num_v_heads)
+        return fail(GDN_ERR_INVALID_ARG, "tokens * HV too large (at most 2^32 rows per call)");
+    if (!o || !z || !weight || !y)
+        return fail(GDN_ERR_INVALID_ARG, "o, z, weight and y are required");
+    if (!aligned(o, 16) || !aligned(z, 16) || !aligned(y, 16) || !aligned(weight, 16))
+        return fail(GDN_ERR_INVALID_ARG, "o, z, y and weight must be 16-byte aligned");
+    const size_t bytes = (size_t)tokens * s.num_v_heads * s.dv * io_size(s.io_dtype);
+    // y may be o or z exactly (in place), but no buffer may overlap another partially
+    if ((y != o && overlaps(y, bytes, o, bytes)) || (y != z && overlaps(y, bytes, z, bytes)))
+        return fail(GDN_ERR_INVALID_ARG, "y partially overlaps o or z");
+    if (overlaps(y, bytes, weight, (size_t)s.dv * sizeof(float)))
+        return fail(GDN_ERR_INVALID_ARG, "y overlaps the weight");
+
+    gdn::NormArgs p{};
+    p.hv = s.num_v_heads;
+    p.dv = s.dv;
+    p.io_dtype = s.io_dtype;
+    p.o = o;
+    p.z = z;
+    p.weight = weight;
+    p.y = y;
+    p.tokens = tokens;
+    p.eps = eps;
+    p.stream = stream;
+    const hipError_t err = gdn::launch_norm(p);
+    if (err != hipSuccess)
+        return fail(GDN_ERR_HIP, "gated RMSNorm launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
 gdn_status gdn_state_snapshot(const gdn_shape *shape, const float *src, const int32_t *src_rows,
                               int32_t src_capacity, float *dst, const int32_t *dst_rows, int32_t dst_capacity,
                               int32_t num_rows, void *stream)

@@ -38,6 +38,16 @@ struct DecodeArgs {
     void *stream;
 };
 
+struct NormArgs {
+    int32_t hv, dv, io_dtype;
+    const void *o, *z;
+    const float *weight;
+    void *y;
+    int64_t tokens;
+    float eps;
+    void *stream;
+};
+
 struct SnapshotArgs {
     const float *src;
     const int32_t *src_rows;
@@ -70,5 +80,6 @@ int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, 
 hipError_t launch_prefill(const PrefillArgs &p);
 hipError_t launch_decode(const DecodeArgs &p);
 hipError_t launch_snapshot(const SnapshotArgs &p);
+hipError_t launch_norm(const NormArgs &p);
 
 }  // namespace gdn

@@ -13,6 +13,7 @@ enum ProfKernel : int32_t {
     PROF_SCAN = 2,
     PROF_DECODE = 3,
     PROF_SNAPSHOT = 4,
+    PROF_NORM = 5,
 };
 
 // Start and stop events for one launch of `kernel`: both null while timing is

@@ -137,3 +137,20 @@ def accept_counts(seed: int, n: int, block: int = 16) -> List[int]:
     """Accepted prefix length per sequence after a verify block: U{1..block-1}."""
     gen = torch.Generator().manual_seed(int(seed))
     return [int(x) for x in torch.randint(1, block, (n,), generator=gen)]
+
+
+def make_norm_inputs(tokens, hv, dv, io_dtype=torch.bfloat16, seed=0):
+    """Inputs of the gated RMSNorm after the DeltaNet output, drawn on the CPU.
+
+    o [tokens, HV, dv] in io_dtype: N(0, 1) rows scaled per value head by an RMS drawn
+    log-uniformly in [1e-3, 2e-2] (the per-head output RMS range the NPU page reports,
+    section "How it works"); z [tokens, HV, dv] in io_dtype: N(0, 2^2); weight [dv] fp32:
+    U(0.5, 1.5).
+    """
+    gen = torch.Generator().manual_seed(int(seed))
+    rms = torch.exp(torch.empty(hv).uniform_(float(torch.log(torch.tensor(1e-3))),
+                                             float(torch.log(torch.tensor(2e-2))), generator=gen))
+    o = (torch.randn(tokens, hv, dv, generator=gen) * rms[None, :, None]).to(io_dtype)
+    z = (2.0 * torch.randn(tokens, hv, dv, generator=gen)).to(io_dtype)
+    w = torch.empty(dv).uniform_(0.5, 1.5, generator=gen).float()
+    return dict(o=o.contiguous(), z=z.contiguous(), weight=w.contiguous())

@@ -163,6 +163,27 @@ gdn_status gdn_state_snapshot(const gdn_shape *shape,
                               int32_t num_rows, void *stream);
 
 /*
+ * Gated RMSNorm of the DeltaNet output, the step right after the recurrence
+ * (NPU page "Qwen3.5-9B -- every component on the Intel NPU", section "How it
+ * works": the output feeds a gated RMSNorm that is scale-invariant in it; the
+ * SSM norm epsilon is 1e-6 for Qwen3.5, Candle pull-request page, section "Bug
+ * elimination log", bug 7).  For every token t and value head h, over the dv
+ * elements of the row:
+ *     y = o / sqrt(mean(o^2) + eps) * weight * silu(z),   silu(z) = z / (1 + exp(-z))
+ *
+ *   o, z    [tokens, HV, dv]  io dtype (z: the gate, shaped like o)
+ *   weight  [dv]              fp32, shared by the heads
+ *   y       [tokens, HV, dv]  io dtype out; may be o or z itself (in place),
+ *                             must not overlap either partially, nor weight
+ *   eps     finite, >= 0
+ * Uses HV, dv and io_dtype of `shape` (dk, HQK and scale are not read beyond
+ * the shape checks).  dv in {32, 64, 128}; o, z, y and weight 16-byte
+ * aligned.  tokens == 0 is a no-op.
+ */
+gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, const void *o, const void *z, const float *weight,
+                             void *y, int64_t tokens, float eps, void *stream);
+
+/*
  * Kernel timing for benchmarks (not needed for normal use).
  * gdn_profile_enable(1) clears the record and starts timing every kernel the
  * library launches, on any thread: each launch carries a start and a stop HIP
@@ -172,7 +193,7 @@ gdn_status gdn_state_snapshot(const gdn_shape *shape,
  * gdn_profile_collect() waits for the recorded events of one kernel and
  * returns how many launches were recorded and their summed duration in ms.
  * Kernel identifiers: 0 chunk table and scan order, 1 prep (Gram products and solve),
- * 2 chunk scan (state pass and outputs), 3 decode, 4 snapshot.
+ * 2 chunk scan (state pass and outputs), 3 decode, 4 snapshot, 5 gated RMSNorm.
  * The events are created on first use and kept until the process ends;
  * no device memory is allocated.
  */

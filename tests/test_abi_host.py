@@ -47,7 +47,7 @@ def prefill(lib, sh, T=128, N=1, cu_host=None, ws_bytes=None, ws=None, q=None, g
 
 def test_every_declared_function_is_exported(lib):
     names = gdn.header_functions()
-    assert set(names) >= {"gdn_prefill_chunked", "gdn_decode_step", "gdn_state_snapshot",
+    assert set(names) >= {"gdn_prefill_chunked", "gdn_decode_step", "gdn_state_snapshot", "gdn_gated_rmsnorm",
                           "gdn_prefill_workspace_bytes", "gdn_status_string", "gdn_last_error", "gdn_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -141,6 +141,23 @@ def test_snapshot_rejects_bad_arguments(lib):
     assert lib.gdn_state_snapshot(ctypes.byref(sh), None, None, 4, fake(2), None, 4, 2, None) == \
         binding.GDN_ERR_INVALID_ARG
     assert lib.gdn_state_snapshot(ctypes.byref(sh), fake(1), None, 4, fake(2), None, 4, 0, None) == binding.GDN_OK
+
+
+def test_gated_rmsnorm_rejects_bad_arguments(lib):
+    sh = shape()
+    o, z, w, y = fake(1), fake(2), fake(3), fake(4)
+    f = lib.gdn_gated_rmsnorm
+    assert f(ctypes.byref(shape(d=96)), o, z, w, y, 4, ctypes.c_float(1e-6), None) == binding.GDN_ERR_UNSUPPORTED
+    assert f(ctypes.byref(sh), o, z, w, y, -1, ctypes.c_float(1e-6), None) == binding.GDN_ERR_INVALID_ARG
+    assert f(ctypes.byref(sh), o, z, w, y, 4, ctypes.c_float(-1.0), None) == binding.GDN_ERR_INVALID_ARG
+    assert f(ctypes.byref(sh), o, z, w, y, 4, ctypes.c_float(float("inf")), None) == binding.GDN_ERR_INVALID_ARG
+    assert f(ctypes.byref(sh), o, None, w, y, 4, ctypes.c_float(1e-6), None) == binding.GDN_ERR_INVALID_ARG
+    assert f(ctypes.byref(sh), o, z, ctypes.c_void_p(fake(3).value + 4), y, 4, ctypes.c_float(1e-6), None) == \
+        binding.GDN_ERR_INVALID_ARG                                             # misaligned weight
+    assert f(ctypes.byref(sh), o, z, w, ctypes.c_void_p(fake(1).value + 256), 4, ctypes.c_float(1e-6), None) == \
+        binding.GDN_ERR_INVALID_ARG                                             # y partially over o
+    assert b"partially" in lib.gdn_last_error()
+    assert f(ctypes.byref(sh), o, z, w, y, 0, ctypes.c_float(1e-6), None) == binding.GDN_OK
 
 
 def test_binding_refuses_cpu_tensors():
