@@ -11,9 +11,9 @@ Several copies of the batch are rotated so that repeated steps do not run
 out of the 256 MB last-level cache.  The same run also measures the decode
 step (64 sequences, state updated in place, state sets rotated), the long
 32k prefill and the 16-sequence varlen prefill, each with its per-kernel
-durations from HIP events recorded on the library's launch stream; the gated
-RMSNorm that follows the scan, on the 1k and 32k output shapes; and the fp64
-CPU oracle on a bounded sample of the headline workload.
+durations from HIP events recorded on the library's launch stream; the conv1d
+ahead of the scan and the gated RMSNorm after it, on the 1k and 32k shapes; and
+the fp64 CPU oracle on a bounded sample of the headline workload.
 
 Prints ONE JSON line.
 """
@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     "gdn_prep_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_decode_kernel": ("gated_deltanet_scan_amd/csrc/gdn_decode.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_gated_rmsnorm_kernel": ("gated_deltanet_scan_amd/csrc/gdn_norm.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
+    "gdn_conv_kernel": ("gated_deltanet_scan_amd/csrc/gdn_conv.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
 }
 
 
@@ -310,6 +311,44 @@ def measure_norm(tokens, steps, warmup, hv=32, dv=128):
                          "avg_us": us, "algorithmic_bytes": nbytes}}
 
 
+def measure_conv(tokens, steps, warmup, hqk=16, hv=32, d=128, width=4):
+    """The conv1d ahead of the scan (gdn_conv1d_qkv, q/k head L2 norms, conv state read and
+    updated in place) on one sequence of `tokens` bf16 tokens with the Qwen3.5-9B heads:
+    algorithmic bytes = x read once and q, k, v written once (2 * T * C * 2) plus the weight
+    and the state read and written.  Input sets are rotated past the last-level cache."""
+    import torch
+
+    import gated_deltanet_scan_amd as gdn
+    from gated_deltanet_scan_amd import synthetic
+    x = synthetic.make_conv_inputs([tokens], hqk, hv, d, d, width, torch.bfloat16, seed=3000)
+    dev = torch.device("cuda:0")
+    C = 2 * hqk * d + hv * d
+    nbytes = 2 * tokens * C * 2 + C * width * 4 + 2 * C * (width - 1) * 4
+    n_sets = int(min(16, max(1, math.ceil(CACHE_DEFEAT_BYTES / nbytes))))
+    calls = []
+    for i in range(n_sets):
+        xx, w, cu, st = (x["x"].to(dev).clone(), x["weight"].to(dev), x["cu_seqlens"].to(dev),
+                         x["state"].to(dev).clone())
+        calls.append(gdn.prepare_conv1d_qkv(xx, w, hqk, hv, d, d, cu, st, st, l2norm=True, eps=1e-6))
+    for i in range(warmup):
+        calls[i % n_sets]()
+    _sync()
+    gdn.profile_enable(True)
+    for i in range(steps):
+        calls[i % n_sets]()
+    _sync()
+    n, tot = gdn.profile_collect(6)      # the conv and its state update
+    gdn.profile_enable(False)
+    us = tot / steps * 1e3
+    achieved = nbytes / (us * 1e-6) / 1e9
+    return {"shape": {"tokens": tokens, "channels": C, "width": width}, "dtype": "bf16", "kernel_avg_us": us,
+            "launches_per_step": n / steps, "tokens_per_s": tokens / (us * 1e-6), "rotated_sets": n_sets,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": achieved / PEAK_HBM_GBS, "kernel": "gdn_conv_kernel",
+                         "traffic": measured_traffic("gdn_conv_kernel", "conv_%d" % tokens),
+                         "avg_us": us, "algorithmic_bytes": nbytes}}
+
+
 def cpu_baseline(name, seconds):
     import oracle
     from gated_deltanet_scan_amd import synthetic
@@ -392,6 +431,9 @@ def main():
         for tokens in (1024, 32768):
             print("[bench] gated RMSNorm %d tokens" % tokens, file=sys.stderr, flush=True)
             extra["gated_rmsnorm_%d" % tokens] = measure_norm(tokens, max(10, min(args.steps, 50)), 3)
+        for tokens in (1024, 32768):
+            print("[bench] conv1d %d tokens" % tokens, file=sys.stderr, flush=True)
+            extra["conv1d_qkv_%d" % tokens] = measure_conv(tokens, max(10, min(args.steps, 50)), 3)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

@@ -67,6 +67,9 @@ def load_library():
         lib.gdn_state_snapshot.restype = ctypes.c_int
         lib.gdn_gated_rmsnorm.argtypes = [SP, vp, vp, vp, vp, i64, ctypes.c_float, vp]
         lib.gdn_gated_rmsnorm.restype = ctypes.c_int
+        lib.gdn_conv1d_qkv.argtypes = [SP, vp, vp, i32, vp, i32, i64, vp, vp, i32, i32, ctypes.c_float, vp, vp, vp,
+                                       vp]
+        lib.gdn_conv1d_qkv.restype = ctypes.c_int
         lib.gdn_status_string.argtypes = [ctypes.c_int]
         lib.gdn_status_string.restype = ctypes.c_char_p
         lib.gdn_last_error.argtypes = []
@@ -85,7 +88,7 @@ def header_functions():
     """Names of the functions include/gdn.h declares."""
     text = open(HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
 
 
 def _status_name(status: int) -> str:
@@ -353,7 +356,65 @@ def prepare_gated_rmsnorm(o, z, weight, *, eps=1e-6, out=None) -> PreparedCall:
     return PreparedCall(lib.gdn_gated_rmsnorm, lib, args, keep, dev, out)
 
 
-PROF_CHUNK_TABLE, PROF_PREP, PROF_SCAN, PROF_DECODE, PROF_SNAPSHOT, PROF_NORM = range(6)
+def _conv_call(x, weight, hqk, hv, dk, dv, cu_seqlens, state_in, state_out, silu, l2norm, eps, out):
+    lib = load_library()
+    _need(x, "x", ndim=2)
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be on a GPU")
+    io = x.dtype
+    if io not in _IO_DTYPES:
+        raise TypeError("io dtype must be float32 or bfloat16")
+    T, C = x.shape
+    if C != 2 * hqk * dk + hv * dv:
+        raise ValueError("x must have 2 * HQK * dk + HV * dv channels")
+    _need(weight, "weight", torch.float32, dev, 2)
+    if weight.shape[0] != C:
+        raise ValueError("weight must be [C, K]")
+    K = int(weight.shape[1])
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, dev, 1)
+    n = cu_seqlens.numel() - 1
+    for t, name in ((state_in, "state_in"), (state_out, "state_out")):
+        if t is not None:
+            _need(t, name, torch.float32, dev, 3)
+            if tuple(t.shape) != (n, C, K - 1):
+                raise ValueError("%s must be [N, C, K-1]" % name)
+    if out is None:
+        out = (torch.empty(T, hqk, dk, dtype=io, device=dev), torch.empty(T, hqk, dk, dtype=io, device=dev),
+               torch.empty(T, hv, dv, dtype=io, device=dev))
+    q, k, v = out
+    shape = make_shape(hqk, hv, dk, dv, 64, _IO_DTYPES[io], 1.0)
+    args = (ctypes.byref(shape), _ptr(x), _ptr(weight), K, _ptr(cu_seqlens), n, T, _ptr(state_in), _ptr(state_out),
+            1 if silu else 0, 1 if l2norm else 0, float(eps), _ptr(q), _ptr(k), _ptr(v))
+    keep = (shape, x, weight, cu_seqlens, state_in, state_out)
+    return lib, args, keep, dev, out
+
+
+def conv1d_qkv(x, weight, hqk, hv, dk, dv, cu_seqlens=None, state_in=None, state_out=None, *, silu=False,
+               l2norm=True, eps=1e-6, out=None):
+    """Depthwise causal conv1d over the packed projections [q heads | k heads | v heads], with
+    the conv state, then q and k L2-normalised per head (gdn_conv1d_qkv).
+
+    x [T, 2*HQK*dk + HV*dv] (fp32 or bf16); weight [C, K] fp32; cu_seqlens int32 [N+1] on the GPU
+    (None = one sequence); state_in / state_out [N, C, K-1] fp32 or None (state_out may be
+    state_in).  Returns (q [T, HQK, dk], k [T, HQK, dk], v [T, HV, dv]).
+    """
+    lib, args, keep, dev, out = _conv_call(x, weight, hqk, hv, dk, dv, cu_seqlens, state_in, state_out, silu,
+                                           l2norm, eps, out)
+    _check(lib, lib.gdn_conv1d_qkv(*args, _stream(dev)))
+    return out
+
+
+def prepare_conv1d_qkv(x, weight, hqk, hv, dk, dv, cu_seqlens=None, state_in=None, state_out=None, *, silu=False,
+                       l2norm=True, eps=1e-6, out=None) -> PreparedCall:
+    lib, args, keep, dev, out = _conv_call(x, weight, hqk, hv, dk, dv, cu_seqlens, state_in, state_out, silu,
+                                           l2norm, eps, out)
+    return PreparedCall(lib.gdn_conv1d_qkv, lib, args, keep, dev, out)
+
+
+PROF_CHUNK_TABLE, PROF_PREP, PROF_SCAN, PROF_DECODE, PROF_SNAPSHOT, PROF_NORM, PROF_CONV = range(7)
 
 
 def profile_enable(on: bool = True):

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libgdn.so")
-SOURCES = ["gdn_api.cpp", "gdn_profile.cpp", "gdn_prefill.hip", "gdn_decode.hip", "gdn_norm.hip"]
+SOURCES = ["gdn_api.cpp", "gdn_profile.cpp", "gdn_prefill.hip", "gdn_decode.hip", "gdn_norm.hip", "gdn_conv.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

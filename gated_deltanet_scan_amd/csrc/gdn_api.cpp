@@ -312,6 +312,87 @@ gdn_status gdn_decode_step(const gdn_shape *shape, const void *q, const void *k,
     return ok();
 }
 
+gdn_status gdn_conv1d_qkv(const gdn_shape *shape, const void *x, const float *weight, int32_t width,
+                          const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens, const float *state_in,
+                          float *state_out, int32_t silu, int32_t l2norm, float eps, void *q, void *k, void *v,
+                          void *stream)
+{
+    gdn_status st = check_shape(shape);
+    if (st != GDN_OK)
+        return st;
+    const gdn_shape &s = *shape;
+    if ((s.dk != 32 && s.dk != 64 && s.dk != 128) || (s.dv != 32 && s.dv != 64 && s.dv != 128))
+        return fail(GDN_ERR_UNSUPPORTED, "no conv kernel for dk=%d dv=%d (each in {32,64,128})", s.dk, s.dv);
+    if (width < 1 || width > 8)
+        return fail(GDN_ERR_UNSUPPORTED, "conv width %d not in 1..8", width);
+    if (num_seqs < 0 || total_tokens < 0)
+        return fail(GDN_ERR_INVALID_ARG, "negative num_seqs or total_tokens");
+    if (num_seqs == 0) {
+        if (total_tokens != 0)
+            return fail(GDN_ERR_INVALID_ARG, "tokens without sequences");
+        return ok();
+    }
+    if (!std::isfinite(eps) || eps < 0.f)
+        return fail(GDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    const int64_t channels = 2 * (int64_t)s.num_qk_heads * s.dk + (int64_t)s.num_v_heads * s.dv;
+    if (channels > (int64_t(1) << 24) || total_tokens > (int64_t(1) << 31))
+        return fail(GDN_ERR_INVALID_ARG, "too many channels or tokens");
+    const int64_t waves_per_token = (channels + 64 * (16 / (int64_t)io_size(s.io_dtype)) - 1) /
+                                    (64 * (16 / (int64_t)io_size(s.io_dtype)));
+    if (total_tokens * waves_per_token > (int64_t(1) << 33))
+        return fail(GDN_ERR_INVALID_ARG, "total_tokens * C too large for one launch");
+    if (!cu_seqlens || !weight || (total_tokens > 0 && (!x || !q || !k || !v)))
+        return fail(GDN_ERR_INVALID_ARG, "x, weight, cu_seqlens, q, k and v are required");
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(weight, 16))
+        return fail(GDN_ERR_INVALID_ARG, "x, weight, q, k and v must be 16-byte aligned");
+    if (!aligned(cu_seqlens, 4) || !aligned(state_in, 4) || !aligned(state_out, 4))
+        return fail(GDN_ERR_INVALID_ARG, "cu_seqlens and the states must be 4-byte aligned");
+    const size_t es = io_size(s.io_dtype);
+    const size_t x_bytes = (size_t)total_tokens * channels * es;
+    const size_t qk_bytes = (size_t)total_tokens * s.num_qk_heads * s.dk * es;
+    const size_t v_bytes = (size_t)total_tokens * s.num_v_heads * s.dv * es;
+    const size_t st_bytes = (size_t)num_seqs * channels * (width - 1) * sizeof(float);
+    const void *outs[] = {q, k, v};
+    const size_t ob[] = {qk_bytes, qk_bytes, v_bytes};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(outs[i], ob[i], x, x_bytes) || overlaps(outs[i], ob[i], weight, (size_t)channels * width * 4) ||
+            overlaps(outs[i], ob[i], state_in, st_bytes) || overlaps(outs[i], ob[i], state_out, st_bytes))
+            return fail(GDN_ERR_INVALID_ARG, "q, k or v overlaps an input or a state");
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], ob[i], outs[j], ob[j]))
+                return fail(GDN_ERR_INVALID_ARG, "q, k and v overlap each other");
+    }
+    if (state_out && state_out != state_in && overlaps(state_out, st_bytes, state_in, st_bytes))
+        return fail(GDN_ERR_INVALID_ARG, "state_out partially overlaps state_in");
+    if (overlaps(state_out, st_bytes, x, x_bytes) || overlaps(state_out, st_bytes, weight, (size_t)channels * width * 4))
+        return fail(GDN_ERR_INVALID_ARG, "state_out overlaps x or the weight");
+
+    gdn::ConvArgs p{};
+    p.dk = s.dk;
+    p.io_dtype = s.io_dtype;
+    p.width = width;
+    p.channels = (int32_t)channels;
+    p.nq = s.num_qk_heads * s.dk;
+    p.x = x;
+    p.weight = weight;
+    p.cu_seqlens = cu_seqlens;
+    p.num_seqs = num_seqs;
+    p.tokens = total_tokens;
+    p.state_in = state_in;
+    p.state_out = width > 1 ? state_out : nullptr;
+    p.silu = silu ? 1 : 0;
+    p.l2norm = l2norm ? 1 : 0;
+    p.eps = eps;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.stream = stream;
+    const hipError_t err = gdn::launch_conv(p);
+    if (err != hipSuccess)
+        return fail(GDN_ERR_HIP, "conv launch failed: %s", hipGetErrorString(err));
+    return ok();
+}
+
 gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, const void *o, const void *z, const float *weight, void *y,
                              int64_t tokens, float eps, void *stream)
 {

@@ -38,6 +38,22 @@ struct DecodeArgs {
     void *stream;
 };
 
+struct ConvArgs {
+    int32_t dk, io_dtype, width;
+    int32_t channels, nq;          // channels = 2 nq + HV dv, nq = HQK dk
+    const void *x;
+    const float *weight;
+    const int32_t *cu_seqlens;
+    int32_t num_seqs;
+    int64_t tokens;
+    const float *state_in;
+    float *state_out;
+    int32_t silu, l2norm;
+    float eps;
+    void *q, *k, *v;
+    void *stream;
+};
+
 struct NormArgs {
     int32_t hv, dv, io_dtype;
     const void *o, *z;
@@ -81,5 +97,6 @@ hipError_t launch_prefill(const PrefillArgs &p);
 hipError_t launch_decode(const DecodeArgs &p);
 hipError_t launch_snapshot(const SnapshotArgs &p);
 hipError_t launch_norm(const NormArgs &p);
+hipError_t launch_conv(const ConvArgs &p);
 
 }  // namespace gdn

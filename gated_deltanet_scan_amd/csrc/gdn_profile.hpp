@@ -14,6 +14,7 @@ enum ProfKernel : int32_t {
     PROF_DECODE = 3,
     PROF_SNAPSHOT = 4,
     PROF_NORM = 5,
+    PROF_CONV = 6,
 };
 
 // Start and stop events for one launch of `kernel`: both null while timing is

@@ -154,3 +154,26 @@ def make_norm_inputs(tokens, hv, dv, io_dtype=torch.bfloat16, seed=0):
     z = (2.0 * torch.randn(tokens, hv, dv, generator=gen)).to(io_dtype)
     w = torch.empty(dv).uniform_(0.5, 1.5, generator=gen).float()
     return dict(o=o.contiguous(), z=z.contiguous(), weight=w.contiguous())
+
+
+def make_conv_inputs(lengths, hqk, hv, dk, dv, width=4, io_dtype=torch.bfloat16, seed=0, with_state=True):
+    """Inputs of the depthwise causal conv ahead of the recurrence, drawn on the CPU.
+
+    x [T, 2 HQK dk + HV dv] in io_dtype: N(0, 1) (the packed q, k, v projections);
+    weight [C, width] fp32: N(0, 1 / width); cu_seqlens [N+1] int32; state [N, C, width-1]
+    fp32 holding earlier inputs (N(0, 1) rounded to io_dtype, as a conv state holds past x),
+    or None.
+    """
+    gen = torch.Generator().manual_seed(int(seed))
+    lengths = [int(x) for x in lengths]
+    T = sum(lengths)
+    C = 2 * hqk * dk + hv * dv
+    x = torch.randn(T, C, generator=gen).to(io_dtype)
+    w = (torch.randn(C, width, generator=gen) / float(width) ** 0.5).float()
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    if lengths:
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    state = None
+    if with_state:
+        state = torch.randn(len(lengths), C, width - 1, generator=gen).to(io_dtype).float()
+    return dict(x=x.contiguous(), weight=w.contiguous(), cu_seqlens=cu, state=state)

@@ -163,6 +163,39 @@ gdn_status gdn_state_snapshot(const gdn_shape *shape,
                               int32_t num_rows, void *stream);
 
 /*
+ * The depthwise causal conv1d ahead of the recurrence, with its conv state,
+ * fused with the L2 normalisation of the q and k heads.  The pages put the
+ * conv in the layer ahead of the recurrence and keep one conv state per layer
+ * between calls (NPU page "Qwen3.5-9B -- every component on the Intel NPU",
+ * section "How it works": 24 conv states and 24 recurrent states; section
+ * "New in v2": prefix reuse keeps the recurrent/conv/KV state); it is a
+ * cross-correlation over the window ending at the current token, as PyTorch's
+ * left-padded Conv1d (Candle pull-request page, section "Bug elimination
+ * log", bug 2).  For channel c of token t of a sequence starting at token a:
+ *     y[t, c] = sum_{i<K} weight[c, i] * x[t - K + 1 + i, c]
+ * where x[a - m] (m = 1 .. K-1) is state_in[n, c, K-1-m] (zero with no state).
+ * Then y = silu(y) = y / (1 + exp(-y)) if `silu`; the channels are
+ * [q heads | k heads | v heads], and if `l2norm` each q and k head is divided
+ * by sqrt(sum of its squares + eps).
+ *
+ *   x          [total_tokens, C] io dtype, C = 2 HQK dk + HV dv
+ *   weight     [C, K] fp32, K = width in 1..8
+ *   cu_seqlens DEVICE int32 [num_seqs + 1] token offsets (as for the prefill)
+ *   state_in   [num_seqs, C, K-1] fp32 (oldest input first) or NULL (zeros)
+ *   state_out  [num_seqs, C, K-1] fp32 or NULL (not written); receives the last
+ *              K-1 inputs of each sequence (older state entries for a sequence
+ *              shorter than K-1).  May be state_in itself (updated in place).
+ *   q, k       [total_tokens, HQK, dk] io dtype out; v [total_tokens, HV, dv]
+ * dk and dv in {32, 64, 128}.  x, weight, q, k and v 16-byte aligned.
+ * Outputs must not overlap any input or each other; state_out must not
+ * overlap x or weight (nor state_in partially).
+ */
+gdn_status gdn_conv1d_qkv(const gdn_shape *shape, const void *x, const float *weight, int32_t width,
+                          const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                          const float *state_in, float *state_out, int32_t silu, int32_t l2norm, float eps,
+                          void *q, void *k, void *v, void *stream);
+
+/*
  * Gated RMSNorm of the DeltaNet output, the step right after the recurrence
  * (NPU page "Qwen3.5-9B -- every component on the Intel NPU", section "How it
  * works": the output feeds a gated RMSNorm that is scale-invariant in it; the
@@ -193,7 +226,8 @@ gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, const void *o, const void *
  * gdn_profile_collect() waits for the recorded events of one kernel and
  * returns how many launches were recorded and their summed duration in ms.
  * Kernel identifiers: 0 chunk table and scan order, 1 prep (Gram products and solve),
- * 2 chunk scan (state pass and outputs), 3 decode, 4 snapshot, 5 gated RMSNorm.
+ * 2 chunk scan (state pass and outputs), 3 decode, 4 snapshot, 5 gated RMSNorm,
+ * 6 conv1d (and its state update).
  * The events are created on first use and kept until the process ends;
  * no device memory is allocated.
  */

@@ -48,6 +48,7 @@ def prefill(lib, sh, T=128, N=1, cu_host=None, ws_bytes=None, ws=None, q=None, g
 def test_every_declared_function_is_exported(lib):
     names = gdn.header_functions()
     assert set(names) >= {"gdn_prefill_chunked", "gdn_decode_step", "gdn_state_snapshot", "gdn_gated_rmsnorm",
+                          "gdn_conv1d_qkv",
                           "gdn_prefill_workspace_bytes", "gdn_status_string", "gdn_last_error", "gdn_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -158,6 +159,29 @@ def test_gated_rmsnorm_rejects_bad_arguments(lib):
         binding.GDN_ERR_INVALID_ARG                                             # y partially over o
     assert b"partially" in lib.gdn_last_error()
     assert f(ctypes.byref(sh), o, z, w, y, 0, ctypes.c_float(1e-6), None) == binding.GDN_OK
+
+
+def test_conv1d_rejects_bad_arguments(lib):
+    sh = shape(hqk=2, hv=4, d=64)
+    f = lib.gdn_conv1d_qkv
+    x, w, cu, si, so, q, k, v = (fake(i) for i in range(1, 9))
+    eps = ctypes.c_float(1e-6)
+    assert f(ctypes.byref(shape(d=96)), x, w, 4, cu, 1, 10, si, so, 0, 1, eps, q, k, v, None) == \
+        binding.GDN_ERR_UNSUPPORTED
+    assert f(ctypes.byref(sh), x, w, 9, cu, 1, 10, si, so, 0, 1, eps, q, k, v, None) == binding.GDN_ERR_UNSUPPORTED
+    assert f(ctypes.byref(sh), x, w, 0, cu, 1, 10, si, so, 0, 1, eps, q, k, v, None) == binding.GDN_ERR_UNSUPPORTED
+    assert f(ctypes.byref(sh), x, w, 4, cu, -1, 10, si, so, 0, 1, eps, q, k, v, None) == binding.GDN_ERR_INVALID_ARG
+    assert f(ctypes.byref(sh), x, w, 4, cu, 0, 10, si, so, 0, 1, eps, q, k, v, None) == binding.GDN_ERR_INVALID_ARG
+    assert f(ctypes.byref(sh), x, w, 4, None, 1, 10, si, so, 0, 1, eps, q, k, v, None) == binding.GDN_ERR_INVALID_ARG
+    assert f(ctypes.byref(sh), x, w, 4, cu, 1, 10, si, so, 0, 1, ctypes.c_float(-1.0), q, k, v, None) == \
+        binding.GDN_ERR_INVALID_ARG
+    assert f(ctypes.byref(sh), ctypes.c_void_p(fake(1).value + 8), w, 4, cu, 1, 10, si, so, 0, 1, eps, q, k, v,
+             None) == binding.GDN_ERR_INVALID_ARG                                 # misaligned x
+    assert f(ctypes.byref(sh), x, w, 4, cu, 1, 10, si, so, 0, 1, eps, q, q, v, None) == \
+        binding.GDN_ERR_INVALID_ARG                                               # q and k overlap
+    assert f(ctypes.byref(sh), x, w, 4, cu, 1, 10, si, ctypes.c_void_p(fake(4).value + 64), 0, 1, eps, q, k, v,
+             None) == binding.GDN_ERR_INVALID_ARG                                 # state_out partially over state_in
+    assert f(ctypes.byref(sh), x, w, 4, cu, 0, 0, si, so, 0, 1, eps, q, k, v, None) == binding.GDN_OK
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,118 @@
+"""GPU parity of the depthwise causal conv1d with q/k head L2 norms (gdn_conv1d_qkv)
+against the fp64 oracle (oracle/conv1d.py).
+
+Cases: both io dtypes, dk = dv in {32, 64, 128}, conv widths 1, 2, 4 and 8, packed
+batches with empty sequences and sequences shorter than the window, with and without
+a conv state, silu on and off, the L2 norm on and off, the state updated in place, a
+sequence split in two calls with the state carried (bitwise equal to one call), the
+Qwen3.5-9B 1k prefill shape, and the conv feeding the chunked prefill end to end.
+Bars: 1e-4 (fp32 io) and 2e-2 (bf16 io) on q, k and v (max-norm relative per tensor);
+the new conv state is a copy of inputs and must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_scan_amd as gdn
+import oracle
+from gated_deltanet_scan_amd import synthetic as S
+from gpu_helpers import rel_err, say
+from oracle.conv1d import conv_qkv
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+
+
+def _gpu(inp, hqk, hv, dk, dv, silu, l2norm, inplace=False):
+    x, w, cu = inp["x"].cuda(), inp["weight"].cuda(), inp["cu_seqlens"].cuda()
+    s_in = inp["state"].cuda() if inp["state"] is not None else None
+    K = w.shape[1]
+    n = cu.numel() - 1
+    if inplace and s_in is not None:
+        s_out = s_in
+    else:
+        s_out = torch.full((n, x.shape[1], K - 1), float("nan"), device="cuda") if K > 1 else None
+    q, k, v = gdn.conv1d_qkv(x, w, hqk, hv, dk, dv, cu, s_in, s_out, silu=silu, l2norm=l2norm, eps=1e-6)
+    torch.cuda.synchronize()
+    return q, k, v, s_out
+
+
+def _check(inp, hqk, hv, dk, dv, io, silu, l2norm, label, inplace=False):
+    K = inp["weight"].shape[1]
+    say(label, "T=%d" % inp["x"].shape[0], "N=%d" % (inp["cu_seqlens"].numel() - 1), "heads", hqk, hv, "d", dk, dv,
+        "K", K, io, "silu" if silu else "", "l2norm" if l2norm else "", "in place" if inplace else "")
+    q_ref, k_ref, v_ref, s_ref = conv_qkv(inp["x"], inp["weight"], hqk, hv, dk, dv, inp["cu_seqlens"],
+                                          inp["state"], silu=silu, l2norm=l2norm, eps=1e-6)
+    q, k, v, s_out = _gpu(inp, hqk, hv, dk, dv, silu, l2norm, inplace)
+    errs = [rel_err(t.double().cpu().numpy(), r) for t, r in ((q, q_ref), (k, k_ref), (v, v_ref))]
+    say(label, "max rel err q %.3e k %.3e v %.3e" % tuple(errs))
+    assert max(errs) <= TOL[io], (label, errs)
+    if s_out is not None:
+        np.testing.assert_array_equal(s_out.cpu().numpy(), s_ref.astype(np.float32))
+    return q, k, v, s_out
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("K", [1, 2, 4, 8])
+def test_shapes_and_widths(io, d, K):
+    lengths = [5, 1, 0, 37, 3]
+    inp = S.make_conv_inputs(lengths, 2, 4, d, d, K, io, seed=100 * d + K)
+    _check(inp, 2, 4, d, d, io, silu=False, l2norm=True, label="shape_d%d_K%d" % (d, K))
+
+
+@pytest.mark.parametrize("silu", [False, True])
+@pytest.mark.parametrize("l2norm", [False, True])
+@pytest.mark.parametrize("with_state", [False, True])
+def test_options(silu, l2norm, with_state):
+    inp = S.make_conv_inputs([9, 2, 20], 2, 4, 64, 64, 4, torch.float32, seed=7, with_state=with_state)
+    _check(inp, 2, 4, 64, 64, torch.float32, silu, l2norm, "options")
+
+
+def test_state_in_place():
+    inp = S.make_conv_inputs([6, 1, 0, 2, 40], 2, 4, 128, 128, 4, torch.bfloat16, seed=9)
+    _check(inp, 2, 4, 128, 128, torch.bfloat16, False, True, "in_place", inplace=True)
+
+
+def test_split_with_carried_state_is_bitwise_one_call():
+    inp = S.make_conv_inputs([50], 2, 4, 128, 128, 4, torch.bfloat16, seed=11)
+    x, w = inp["x"].cuda(), inp["weight"].cuda()
+    s0 = inp["state"].cuda()
+    whole = gdn.conv1d_qkv(x, w, 2, 4, 128, 128, None, s0, None)
+    s1 = torch.empty_like(s0)
+    a = gdn.conv1d_qkv(x[:17].contiguous(), w, 2, 4, 128, 128, None, s0, s1)
+    b = gdn.conv1d_qkv(x[17:].contiguous(), w, 2, 4, 128, 128, None, s1, None)
+    torch.cuda.synchronize()
+    for part in range(3):
+        assert torch.equal(torch.cat([a[part], b[part]]), whole[part])
+
+
+def test_prefill_1k_shape():
+    inp = S.make_conv_inputs([1024], 16, 32, 128, 128, 4, torch.bfloat16, seed=1001)
+    _check(inp, 16, 32, 128, 128, torch.bfloat16, False, True, "prefill_1k_shape")
+
+
+def test_conv_feeds_the_chunked_prefill():
+    """Upstream step end to end: conv (with state) -> chunked prefill, against the oracle's
+    conv followed by the oracle's recurrence."""
+    hqk, hv, d = 2, 4, 128
+    lengths = [70, 5, 130]
+    inp = S.make_conv_inputs(lengths, hqk, hv, d, d, 4, torch.bfloat16, seed=13)
+    gen = torch.Generator().manual_seed(14)
+    T = sum(lengths)
+    g = -(0.5 + 6.5 * torch.rand(T, hv, generator=gen))
+    beta = torch.sigmoid(torch.randn(T, hv, generator=gen))
+    say("conv_then_prefill", "lengths", lengths)
+    q, k, v, _ = _gpu(inp, hqk, hv, d, d, silu=False, l2norm=True)
+    cu = inp["cu_seqlens"]
+    o, _ = gdn.prefill_chunked(q, k, v, g.cuda(), beta.cuda(), cu, None, chunk=64)
+    torch.cuda.synchronize()
+    q_ref, k_ref, v_ref, _ = conv_qkv(inp["x"], inp["weight"], hqk, hv, d, d, cu, inp["state"], l2norm=True)
+    # the recurrence of the oracle on the GPU's rounded conv outputs (the scan's own inputs)
+    o_ref, _ = oracle.gdn_forward(q.cpu(), k.cpu(), v.cpu(), g, beta, cu)
+    err = rel_err(o.double().cpu().numpy(), o_ref)
+    say("conv_then_prefill", "max rel err o %.3e" % err)
+    assert err <= 2e-2
+    # and the conv outputs themselves against the oracle's
+    assert rel_err(q.double().cpu().numpy(), q_ref) <= 2e-2
