@@ -149,6 +149,29 @@ __device__ inline float wave_inclusive_sum(float x)
     return x;
 }
 
+// Sum over each aligned group of L lanes (L a power of two up to 64), returned to every lane
+// of the group.  Within a 16-lane row the exchanges are DPP moves: swap neighbours, swap
+// pairs, mirror each half-row, mirror the row; beyond a row they are cross-lane reads.
+template <int L>
+__device__ inline float group_sum(float x)
+{
+    static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "a power of two up to the wave");
+    constexpr int kSwap1 = 0xb1, kSwap2 = 0x4e, kHalfMirror = 0x141, kMirror = 0x140;
+    if constexpr (L >= 2)
+        x += __builtin_amdgcn_update_dpp(0.f, x, kSwap1, 0xf, 0xf, false);
+    if constexpr (L >= 4)
+        x += __builtin_amdgcn_update_dpp(0.f, x, kSwap2, 0xf, 0xf, false);
+    if constexpr (L >= 8)
+        x += __builtin_amdgcn_update_dpp(0.f, x, kHalfMirror, 0xf, 0xf, false);
+    if constexpr (L >= 16)
+        x += __builtin_amdgcn_update_dpp(0.f, x, kMirror, 0xf, 0xf, false);
+    if constexpr (L >= 32)
+        x += __shfl_xor(x, 16, kWave);
+    if constexpr (L >= 64)
+        x += __shfl_xor(x, 32, kWave);
+    return x;
+}
+
 // Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 (compile-time loop).
 template <typename F, int... Is>
 __device__ inline void static_for_impl(F &&f, std::integer_sequence<int, Is...>)

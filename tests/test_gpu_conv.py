@@ -93,6 +93,48 @@ def test_prefill_1k_shape():
     _check(inp, 16, 32, 128, 128, torch.bfloat16, False, True, "prefill_1k_shape")
 
 
+# Large enough that each wave walks several 16-token blocks (the launcher spreads the token
+# blocks over about one round of resident waves): sequence starts then fall inside later
+# blocks of a wave and at wave boundaries, and the window is carried from block to block.
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16], ids=["fp32", "bf16"])
+@pytest.mark.parametrize("inplace", [False, True], ids=["state_out", "in_place"])
+def test_waves_over_several_blocks(io, inplace):
+    lengths = [6000, 3, 700, 1, 1, 0, 9500, 40, 17, 2, 255, 257, 3000]   # 3 (bf16) or 5 (fp32) blocks a wave
+    inp = S.make_conv_inputs(lengths, 16, 32, 128, 128, 4, io, seed=21 + int(inplace))
+    _check(inp, 16, 32, 128, 128, io, False, True, "multi_block_waves", inplace=inplace)
+
+
+def test_runs_of_empty_sequences():
+    """More sequence ends at one token than a wave fetches offsets for (63): the sequence of
+    a token is then searched for again."""
+    lengths = [1000] + [0] * 70 + [17] + [0] * 5 + [1] * 30 + [12000]   # 2 blocks a wave
+    inp = S.make_conv_inputs(lengths, 16, 32, 128, 128, 4, torch.bfloat16, seed=23)
+    _check(inp, 16, 32, 128, 128, torch.bfloat16, True, True, "empty_runs")
+
+
+def test_full_32k_shape_sampled():
+    """The conv at the size the benchmark times (32768 tokens of the Qwen3.5-9B heads, 4
+    blocks per wave), checked on sampled slices: each slice's outputs come from the oracle run
+    on the slice with the K-1 inputs before it as its state (a sequence split with the state
+    carried equals the whole), the first slice with the real state."""
+    hqk, hv, d, K, T = 16, 32, 128, 4, 32768
+    inp = S.make_conv_inputs([T], hqk, hv, d, d, K, torch.bfloat16, seed=25)
+    say("full_32k", "T=%d" % T)
+    q, k, v, s_out = _gpu(inp, hqk, hv, d, d, silu=False, l2norm=True)
+    x = inp["x"]
+    slices = [(0, 40), (250, 262), (4090, 4100), (16370, 16400), (20000, 20017), (32700, 32768)]
+    for a, b in slices:
+        if a == 0:
+            st = inp["state"]
+        else:
+            st = x[a - (K - 1):a].float().t().unsqueeze(0).contiguous()
+        q_ref, k_ref, v_ref, _ = conv_qkv(x[a:b], inp["weight"], hqk, hv, d, d, None, st, l2norm=True, eps=1e-6)
+        errs = [rel_err(t[a:b].double().cpu().numpy(), r) for t, r in ((q, q_ref), (k, k_ref), (v, v_ref))]
+        say("full_32k", "tokens %d..%d max rel err q %.3e k %.3e v %.3e" % ((a, b) + tuple(errs)))
+        assert max(errs) <= TOL[torch.bfloat16], (a, b, errs)
+    np.testing.assert_array_equal(s_out[0].cpu().numpy(), x[T - (K - 1):].float().t().numpy())
+
+
 def test_conv_feeds_the_chunked_prefill():
     """Upstream step end to end: conv (with state) -> chunked prefill, against the oracle's
     conv followed by the oracle's recurrence."""
