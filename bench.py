@@ -313,9 +313,11 @@ def measure_norm(tokens, steps, warmup, hv=32, dv=128):
 
 def measure_conv(tokens, steps, warmup, hqk=16, hv=32, d=128, width=4):
     """The conv1d ahead of the scan (gdn_conv1d_qkv, q/k head L2 norms, conv state read and
-    updated in place) on one sequence of `tokens` bf16 tokens with the Qwen3.5-9B heads:
-    algorithmic bytes = x read once and q, k, v written once (2 * T * C * 2) plus the weight
-    and the state read and written.  Input sets are rotated past the last-level cache."""
+    updated in place) on one sequence of `tokens` bf16 tokens with the Qwen3.5-9B heads.
+    Algorithmic bytes of the conv kernel: x read once and q, k, v written once (2 * T * C * 2),
+    the taps (C * K * 4) and the state entries it reads (C * (K-1) * 4).  The state update is
+    its own small kernel (timed apart; the step is both).  Input sets are rotated past the
+    last-level cache."""
     import torch
 
     import gated_deltanet_scan_amd as gdn
@@ -323,7 +325,7 @@ def measure_conv(tokens, steps, warmup, hqk=16, hv=32, d=128, width=4):
     x = synthetic.make_conv_inputs([tokens], hqk, hv, d, d, width, torch.bfloat16, seed=3000)
     dev = torch.device("cuda:0")
     C = 2 * hqk * d + hv * d
-    nbytes = 2 * tokens * C * 2 + C * width * 4 + 2 * C * (width - 1) * 4
+    nbytes = 2 * tokens * C * 2 + C * width * 4 + C * (width - 1) * 4
     n_sets = int(min(16, max(1, math.ceil(CACHE_DEFEAT_BYTES / nbytes))))
     calls = []
     for i in range(n_sets):
@@ -337,12 +339,16 @@ def measure_conv(tokens, steps, warmup, hqk=16, hv=32, d=128, width=4):
     for i in range(steps):
         calls[i % n_sets]()
     _sync()
-    n, tot = gdn.profile_collect(6)      # the conv and its state update
+    n, tot = gdn.profile_collect(6)      # the conv
+    n_st, tot_st = gdn.profile_collect(7)   # its state update
     gdn.profile_enable(False)
     us = tot / steps * 1e3
+    us_state = tot_st / steps * 1e3
     achieved = nbytes / (us * 1e-6) / 1e9
     return {"shape": {"tokens": tokens, "channels": C, "width": width}, "dtype": "bf16", "kernel_avg_us": us,
-            "launches_per_step": n / steps, "tokens_per_s": tokens / (us * 1e-6), "rotated_sets": n_sets,
+            "state_update_avg_us": us_state, "step_us": us + us_state,
+            "launches_per_step": (n + n_st) / steps, "tokens_per_s": tokens / ((us + us_state) * 1e-6),
+            "rotated_sets": n_sets,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": achieved / PEAK_HBM_GBS, "kernel": "gdn_conv_kernel",
                          "traffic": measured_traffic("gdn_conv_kernel", "conv_%d" % tokens),
@@ -384,6 +390,10 @@ def main():
                     help="run only the headline prefill loop (for rocprofv3 kernel traces and counters)")
     ap.add_argument("--profile-decode", action="store_true",
                     help="run only the decode loop (for rocprofv3 kernel traces and counters)")
+    ap.add_argument("--profile-norm", action="store_true",
+                    help="run only the gated RMSNorm loop at 32768 tokens (for rocprofv3)")
+    ap.add_argument("--profile-conv", action="store_true",
+                    help="run only the conv1d loop at 32768 tokens (for rocprofv3)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run only a plain device copy of MIB MiB, 10 times (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -412,6 +422,10 @@ def main():
     if args.profile_decode:
         dec = measure_decode("decode_64", args.steps, args.warmup)
         print(json.dumps(dec))
+        return
+    if args.profile_norm or args.profile_conv:
+        fn = measure_norm if args.profile_norm else measure_conv
+        print(json.dumps(fn(32768, args.steps, args.warmup)))
         return
     print("[bench] prefill %s" % args.workload, file=sys.stderr, flush=True)
     pre = measure_prefill(args.workload, args.steps, args.warmup)

@@ -414,7 +414,7 @@ def prepare_conv1d_qkv(x, weight, hqk, hv, dk, dv, cu_seqlens=None, state_in=Non
     return PreparedCall(lib.gdn_conv1d_qkv, lib, args, keep, dev, out)
 
 
-PROF_CHUNK_TABLE, PROF_PREP, PROF_SCAN, PROF_DECODE, PROF_SNAPSHOT, PROF_NORM, PROF_CONV = range(7)
+PROF_CHUNK_TABLE, PROF_PREP, PROF_SCAN, PROF_DECODE, PROF_SNAPSHOT, PROF_NORM, PROF_CONV, PROF_CONV_STATE = range(8)
 
 
 def profile_enable(on: bool = True):

@@ -290,7 +290,7 @@ static hipError_t launch_conv_t(const ConvArgs &p)
     if constexpr (KW > 1) {
         if (p.state_out) {
             const int64_t items = (int64_t)p.num_seqs * p.channels;
-            const ProfEvents ev = prof_events(PROF_CONV);
+            const ProfEvents ev = prof_events(PROF_CONV_STATE);
             hipExtLaunchKernelGGL((gdn_conv_state_kernel<E, KW>), dim3((unsigned)((items + kThreads - 1) / kThreads)),
                                   dim3(kThreads), 0, st, ev.start, ev.stop, 0, static_cast<const E *>(p.x),
                                   p.cu_seqlens, p.num_seqs, p.tokens, p.channels, p.state_in, p.state_out);

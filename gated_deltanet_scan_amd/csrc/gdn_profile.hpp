@@ -15,6 +15,7 @@ enum ProfKernel : int32_t {
     PROF_SNAPSHOT = 4,
     PROF_NORM = 5,
     PROF_CONV = 6,
+    PROF_CONV_STATE = 7,
 };
 
 // Start and stop events for one launch of `kernel`: both null while timing is

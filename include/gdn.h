@@ -227,7 +227,7 @@ gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, const void *o, const void *
  * returns how many launches were recorded and their summed duration in ms.
  * Kernel identifiers: 0 chunk table and scan order, 1 prep (Gram products and solve),
  * 2 chunk scan (state pass and outputs), 3 decode, 4 snapshot, 5 gated RMSNorm,
- * 6 conv1d (and its state update).
+ * 6 conv1d, 7 conv state update.
  * The events are created on first use and kept until the process ends;
  * no device memory is allocated.
  */
