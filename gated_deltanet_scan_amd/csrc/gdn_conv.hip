@@ -14,13 +14,17 @@
 // heads are then divided by sqrt(sum of squares + eps), and the three parts
 // are written as the q, k and v operands of the recurrence.
 //
-// gdn_conv_kernel: each lane owns 16 bytes of channels (8 bf16 or 4 fp32), a
-// wave 64 such slots over 16 consecutive tokens: the lane loads its taps and
-// the block's rows with the K-1 rows before it at once, then forms the 16
-// outputs from registers.  A block whose windows reach before the start of
-// its sequence (or across two sequences) takes the taps before each
-// sequence's first token from that sequence's state instead.  The head norms
-// reduce over the dk / 8 (or dk / 4) lanes of a head with xor shuffles.
+// gdn_conv_kernel: each lane owns 16 bytes of channels (8 bf16 or 4 fp32) and
+// a wave 64 such slots; a wave walks a range of tokens in blocks of 16.  The
+// lane loads its taps once, keeps the current token's window in fp32
+// registers (each row converted once, moving down one tap per token) and
+// refills a block's row registers with the next block's rows as they are
+// consumed, so a block of loads is in flight during compute.  The sequence of
+// a token comes from one wide search for the range's first token plus one
+// load of the next 63 sequence offsets (a ballot count per token).  Where a
+// sequence starts within reach, the window's taps before its first token are
+// that sequence's state entries.  The head norms sum over the dk / 8 (or
+// dk / 4) lanes of a head with DPP row moves.
 // gdn_conv_state_kernel: one thread per (sequence, channel) gathers the last
 // K-1 inputs (from the old state when the sequence is shorter) into registers
 // and then writes them, so the state can be updated in place; it runs after
@@ -50,7 +54,8 @@ __device__ inline int conv_sequence(const int32_t *cu, int32_t num_seqs, int64_t
 }
 
 // Workgroups go to the 8 XCDs in turn; renumbered, each XCD takes a contiguous range of the
-// work, so the K-1 rows a wave re-reads from the token block before its own sit in its L2.
+// work, so the K-1 rows a wave reads before its range (the previous range's last rows) were
+// fetched by a wave of the same XCD and sit in its L2.
 __device__ inline int64_t xcd_contiguous(int64_t b, int64_t nb)
 {
     const int64_t q = nb / 8, r = nb % 8, x = b % 8, s = b / 8;

@@ -188,7 +188,17 @@ gdn_status gdn_state_snapshot(const gdn_shape *shape,
  *   q, k       [total_tokens, HQK, dk] io dtype out; v [total_tokens, HV, dv]
  * dk and dv in {32, 64, 128}.  x, weight, q, k and v 16-byte aligned.
  * Outputs must not overlap any input or each other; state_out must not
- * overlap x or weight (nor state_in partially).
+ * overlap x or weight (nor state_in partially).  With width 1 there is no
+ * state: state_in and state_out are neither read nor written.
+ * cu_seqlens must start at 0, be non-decreasing and end at total_tokens; this
+ * is not checked on the device (other offsets give unspecified values, never
+ * an access outside the buffers).
+ * All buffers are caller-owned device memory; the call only enqueues work on
+ * `stream` (a hipStream_t).  Argument errors are returned before any launch:
+ * GDN_ERR_UNSUPPORTED for dk, dv or width outside the lists above,
+ * GDN_ERR_INVALID_ARG for null, misaligned or overlapping buffers, negative
+ * counts, tokens without sequences or a bad eps.  num_seqs == 0 (with
+ * total_tokens == 0) is a no-op; an empty sequence keeps its state.
  */
 gdn_status gdn_conv1d_qkv(const gdn_shape *shape, const void *x, const float *weight, int32_t width,
                           const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
@@ -212,6 +222,10 @@ gdn_status gdn_conv1d_qkv(const gdn_shape *shape, const void *x, const float *we
  * Uses HV, dv and io_dtype of `shape` (dk, HQK and scale are not read beyond
  * the shape checks).  dv in {32, 64, 128}; o, z, y and weight 16-byte
  * aligned.  tokens == 0 is a no-op.
+ * All buffers are caller-owned device memory; the call only enqueues work on
+ * `stream` (a hipStream_t).  Argument errors are returned before any launch:
+ * GDN_ERR_UNSUPPORTED for dv outside the list, GDN_ERR_INVALID_ARG for null,
+ * misaligned or partially overlapping buffers, negative tokens or a bad eps.
  */
 gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, const void *o, const void *z, const float *weight,
                              void *y, int64_t tokens, float eps, void *stream);
