@@ -4,9 +4,10 @@
 Cases: both io dtypes, every supported dv, token counts that leave a ragged last
 wave, the 1k prefill output shape (1024 tokens x 32 value heads x 128), per-head
 output RMS across the pages' 1e-3..2e-2 range with eps = 1e-6 (eps matters there)
-and eps = 1, in place on o and on z, all-zero rows, a large dynamic range, zero
-tokens, and run-to-run determinism.  Bars as for the prefill outputs: 1e-4 for
-fp32 io, 2e-2 for bf16 io (max-norm relative error per tensor).
+and eps = 1, the 32768-token shape the benchmark times (sampled rows), in place on
+o and on z, all-zero rows, a large dynamic range, zero tokens, and run-to-run
+determinism.  Bars as for the prefill outputs: 1e-4 for fp32 io, 2e-2 for bf16 io
+(max-norm relative error per tensor).
 """
 import numpy as np
 import pytest
@@ -48,6 +49,20 @@ def test_shapes(io, dv, tokens, hv):
 def test_prefill_1k_output_shape(io, eps):
     inp = S.make_norm_inputs(1024, 32, 128, io, seed=1001)
     _run(inp, io, eps, "prefill_1k_out")
+
+
+def test_full_32k_shape_sampled():
+    """The size the benchmark times (32768 tokens x 32 value heads x 128, bf16), checked on
+    every 61st token row (rows are independent) and the last one."""
+    inp = S.make_norm_inputs(32768, 32, 128, torch.bfloat16, seed=3001)
+    say("norm_32k", "o", tuple(inp["o"].shape), "bf16, eps 1e-6")
+    y = gdn.gated_rmsnorm(inp["o"].cuda(), inp["z"].cuda(), inp["weight"].cuda(), eps=1e-6)
+    torch.cuda.synchronize()
+    rows = torch.cat([torch.arange(0, 32768, 61), torch.tensor([32767])])
+    want = ref_norm(inp["o"][rows], inp["z"][rows], inp["weight"], 1e-6)
+    err = rel_err(y[rows.cuda()].double().cpu().numpy(), want)
+    say("norm_32k", "%d sampled tokens, max rel err %.3e" % (len(rows), err))
+    assert err <= TOL[torch.bfloat16], err
 
 
 @pytest.mark.parametrize("where", ["o", "z"])
