@@ -65,6 +65,8 @@ def load_library():
         lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_state_snapshot.argtypes = [SP, vp, vp, i32, vp, vp, i32, i32, vp]
         lib.gdn_state_snapshot.restype = ctypes.c_int
+        lib.gdn_conv_state_snapshot.argtypes = [i64, i32, vp, vp, i32, vp, vp, i32, i32, vp]
+        lib.gdn_conv_state_snapshot.restype = ctypes.c_int
         lib.gdn_gated_rmsnorm.argtypes = [SP, vp, vp, vp, vp, i64, ctypes.c_float, vp]
         lib.gdn_gated_rmsnorm.restype = ctypes.c_int
         lib.gdn_conv1d_qkv.argtypes = [SP, vp, vp, i32, vp, i32, i64, vp, vp, i32, i32, ctypes.c_float, vp, vp, vp,
@@ -280,16 +282,10 @@ def prepare_decode(q, k, v, g, beta, state, *, scale=None, out=None) -> Prepared
     return PreparedCall(lib.gdn_decode_step, lib, args, keep, dev, out)
 
 
-def state_snapshot(src, dst, src_rows=None, dst_rows=None, num_rows=None):
-    """dst[dst_rows[i]] = src[src_rows[i]] over whole per-sequence states (gdn_state_snapshot).
-
-    src, dst [capacity, HV, dk, dv] fp32; the index tensors are int32 on the same GPU (None =
-    identity).  Restore is the same call with src and dst swapped.
-    """
-    lib = load_library()
-    _need(src, "src", torch.float32, None, 4)
+def _snapshot_rows(src, dst, src_rows, dst_rows, num_rows):
+    _need(src, "src", torch.float32, None, None)
     dev = src.device
-    _need(dst, "dst", torch.float32, dev, 4)
+    _need(dst, "dst", torch.float32, dev, None)
     if tuple(src.shape[1:]) != tuple(dst.shape[1:]):
         raise ValueError("src and dst must have the same per-sequence shape")
     for t, name in ((src_rows, "src_rows"), (dst_rows, "dst_rows")):
@@ -305,6 +301,37 @@ def state_snapshot(src, dst, src_rows=None, dst_rows=None, num_rows=None):
     for t, name in ((src_rows, "src_rows"), (dst_rows, "dst_rows")):
         if t is not None and t.numel() < num_rows:
             raise ValueError("%s has fewer than num_rows entries" % name)
+    return dev, int(num_rows)
+
+
+def conv_state_snapshot(src, dst, src_rows=None, dst_rows=None, num_rows=None):
+    """dst[dst_rows[i]] = src[src_rows[i]] over whole per-sequence conv states
+    (gdn_conv_state_snapshot).
+
+    src, dst [capacity, C, width - 1] fp32; the index tensors are int32 on the same GPU
+    (None = identity).  Restore is the same call with src and dst swapped.
+    """
+    lib = load_library()
+    if src.dim() != 3:
+        raise ValueError("conv states are [capacity, C, width - 1]")
+    dev, num_rows = _snapshot_rows(src, dst, src_rows, dst_rows, num_rows)
+    channels, taps = src.shape[1], src.shape[2]
+    status = lib.gdn_conv_state_snapshot(int(channels), int(taps) + 1, _ptr(src), _ptr(src_rows), src.shape[0],
+                                         _ptr(dst), _ptr(dst_rows), dst.shape[0], num_rows, _stream(dev))
+    _check(lib, status)
+    return dst
+
+
+def state_snapshot(src, dst, src_rows=None, dst_rows=None, num_rows=None):
+    """dst[dst_rows[i]] = src[src_rows[i]] over whole per-sequence states (gdn_state_snapshot).
+
+    src, dst [capacity, HV, dk, dv] fp32; the index tensors are int32 on the same GPU (None =
+    identity).  Restore is the same call with src and dst swapped.
+    """
+    lib = load_library()
+    if src.dim() != 4:
+        raise ValueError("states are [capacity, HV, dk, dv]")
+    dev, num_rows = _snapshot_rows(src, dst, src_rows, dst_rows, num_rows)
     hv, dk, dv = src.shape[1:]
     shape = make_shape(1, hv, dk, dv, 64, GDN_DTYPE_F32, 1.0)
     status = lib.gdn_state_snapshot(ctypes.byref(shape), _ptr(src), _ptr(src_rows), src.shape[0], _ptr(dst),

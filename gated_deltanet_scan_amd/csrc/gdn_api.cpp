@@ -438,24 +438,23 @@ gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, const void *o, const void *
     return ok();
 }
 
-gdn_status gdn_state_snapshot(const gdn_shape *shape, const float *src, const int32_t *src_rows,
-                              int32_t src_capacity, float *dst, const int32_t *dst_rows, int32_t dst_capacity,
-                              int32_t num_rows, void *stream)
+// Gather/scatter of whole rows of row_floats fp32 values (the checks and the launch shared by
+// the recurrent-state and the conv-state snapshots).
+static gdn_status snapshot_rows(int64_t row_floats, const float *src, const int32_t *src_rows, int32_t src_capacity,
+                                float *dst, const int32_t *dst_rows, int32_t dst_capacity, int32_t num_rows,
+                                void *stream)
 {
-    gdn_status st = check_shape(shape);
-    if (st != GDN_OK)
-        return st;
     if (num_rows < 0 || src_capacity < 0 || dst_capacity < 0)
         return fail(GDN_ERR_INVALID_ARG, "negative row count or capacity");
-    if (num_rows == 0)
+    if (num_rows == 0 || row_floats == 0)
         return ok();
     if (!src || !dst)
         return fail(GDN_ERR_INVALID_ARG, "src and dst are required");
     if (!aligned(src, 16) || !aligned(dst, 16) || !aligned(src_rows, 4) || !aligned(dst_rows, 4))
         return fail(GDN_ERR_INVALID_ARG, "src/dst must be 16-byte aligned, row indices 4-byte aligned");
-    const int64_t row_floats = (int64_t)shape->num_v_heads * shape->dk * shape->dv;
     if (row_floats % 4 != 0)
-        return fail(GDN_ERR_UNSUPPORTED, "HV * dk * dv must be a multiple of 4");
+        return fail(GDN_ERR_UNSUPPORTED, "a row of %lld floats is not a whole number of 16-byte vectors",
+                    (long long)row_floats);
     if (!src_rows && num_rows > src_capacity)
         return fail(GDN_ERR_INVALID_ARG, "num_rows=%d exceeds src_capacity=%d", num_rows, src_capacity);
     if (!dst_rows && num_rows > dst_capacity)
@@ -477,6 +476,29 @@ gdn_status gdn_state_snapshot(const gdn_shape *shape, const float *src, const in
     if (err != hipSuccess)
         return fail(GDN_ERR_HIP, "snapshot launch failed: %s", hipGetErrorString(err));
     return ok();
+}
+
+gdn_status gdn_state_snapshot(const gdn_shape *shape, const float *src, const int32_t *src_rows,
+                              int32_t src_capacity, float *dst, const int32_t *dst_rows, int32_t dst_capacity,
+                              int32_t num_rows, void *stream)
+{
+    gdn_status st = check_shape(shape);
+    if (st != GDN_OK)
+        return st;
+    const int64_t row_floats = (int64_t)shape->num_v_heads * shape->dk * shape->dv;
+    return snapshot_rows(row_floats, src, src_rows, src_capacity, dst, dst_rows, dst_capacity, num_rows, stream);
+}
+
+gdn_status gdn_conv_state_snapshot(int64_t channels, int32_t width, const float *src, const int32_t *src_rows,
+                                   int32_t src_capacity, float *dst, const int32_t *dst_rows, int32_t dst_capacity,
+                                   int32_t num_rows, void *stream)
+{
+    if (channels <= 0 || channels > (int64_t)1 << 24)
+        return fail(GDN_ERR_INVALID_ARG, "channels=%lld not in 1..2^24", (long long)channels);
+    if (width < 1 || width > 8)
+        return fail(GDN_ERR_UNSUPPORTED, "conv width %d not in 1..8", width);
+    return snapshot_rows(channels * (width - 1), src, src_rows, src_capacity, dst, dst_rows, dst_capacity, num_rows,
+                         stream);
 }
 
 const char *gdn_status_string(gdn_status status)

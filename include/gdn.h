@@ -206,6 +206,33 @@ gdn_status gdn_conv1d_qkv(const gdn_shape *shape, const void *x, const float *we
                           void *q, void *k, void *v, void *stream);
 
 /*
+ * Conv state snapshot / restore: copies whole per-sequence conv states
+ * (C x (width - 1) fp32 each, C = 2 HQK dk + HV dv channels) between two
+ * buffers, so that a verify pass through the conv can be rolled back with
+ * the recurrent state (NPU page "Qwen3.5-9B -- every component on the Intel
+ * NPU", section "New in v2": the draft is verified after a snapshot, and prefix
+ * reuse keeps the recurrent/conv/KV state).
+ *
+ * For i in [0, num_rows): dst[dst_rows ? dst_rows[i] : i] =
+ *                         src[src_rows ? src_rows[i] : i].
+ *   src, dst          [capacity, C, width - 1] fp32 device buffers, 16-byte
+ *                     aligned; they must not overlap.
+ *   src_rows, dst_rows  optional device int32 index arrays of num_rows
+ *                     entries (gather / scatter); entries outside
+ *                     [0, src_capacity) resp. [0, dst_capacity) are skipped.
+ *                     Restore is the same call with the buffers swapped.
+ *   With both index arrays NULL, num_rows must not exceed either capacity.
+ * channels in 1..2^24, width in 1..8 (width 1: no state, a no-op);
+ * C * (width - 1) must be a multiple of 4.  Caller-owned device memory; the
+ * call only enqueues work on `stream`; argument errors are returned before any
+ * launch.
+ */
+gdn_status gdn_conv_state_snapshot(int64_t channels, int32_t width,
+                                   const float *src, const int32_t *src_rows, int32_t src_capacity,
+                                   float *dst, const int32_t *dst_rows, int32_t dst_capacity,
+                                   int32_t num_rows, void *stream);
+
+/*
  * Gated RMSNorm of the DeltaNet output, the step right after the recurrence
  * (NPU page "Qwen3.5-9B -- every component on the Intel NPU", section "How it
  * works": the output feeds a gated RMSNorm that is scale-invariant in it; the

@@ -48,7 +48,7 @@ def prefill(lib, sh, T=128, N=1, cu_host=None, ws_bytes=None, ws=None, q=None, g
 def test_every_declared_function_is_exported(lib):
     names = gdn.header_functions()
     assert set(names) >= {"gdn_prefill_chunked", "gdn_decode_step", "gdn_state_snapshot", "gdn_gated_rmsnorm",
-                          "gdn_conv1d_qkv",
+                          "gdn_conv1d_qkv", "gdn_conv_state_snapshot",
                           "gdn_prefill_workspace_bytes", "gdn_status_string", "gdn_last_error", "gdn_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -142,6 +142,22 @@ def test_snapshot_rejects_bad_arguments(lib):
     assert lib.gdn_state_snapshot(ctypes.byref(sh), None, None, 4, fake(2), None, 4, 2, None) == \
         binding.GDN_ERR_INVALID_ARG
     assert lib.gdn_state_snapshot(ctypes.byref(sh), fake(1), None, 4, fake(2), None, 4, 0, None) == binding.GDN_OK
+
+
+def test_conv_state_snapshot_rejects_bad_arguments(lib):
+    f = lib.gdn_conv_state_snapshot
+    C, W = 768, 4
+    assert f(C, W, fake(1), None, 4, fake(2), None, 4, 5, None) == binding.GDN_ERR_INVALID_ARG   # rows > capacity
+    assert f(C, W, fake(1), None, 4, ctypes.c_void_p(fake(1).value + 16), None, 4, 2, None) == \
+        binding.GDN_ERR_INVALID_ARG   # overlap
+    assert f(C, W, ctypes.c_void_p(fake(1).value + 4), None, 4, fake(2), None, 4, 2, None) == \
+        binding.GDN_ERR_INVALID_ARG   # misaligned
+    assert f(C, W, None, None, 4, fake(2), None, 4, 2, None) == binding.GDN_ERR_INVALID_ARG
+    assert f(0, W, fake(1), None, 4, fake(2), None, 4, 2, None) == binding.GDN_ERR_INVALID_ARG
+    assert f(C, 9, fake(1), None, 4, fake(2), None, 4, 2, None) == binding.GDN_ERR_UNSUPPORTED
+    assert f(6, 2, fake(1), None, 4, fake(2), None, 4, 2, None) == binding.GDN_ERR_UNSUPPORTED   # 6 floats a row
+    assert f(C, 1, None, None, 4, None, None, 4, 2, None) == binding.GDN_OK   # width 1: no state
+    assert f(C, W, fake(1), None, 4, fake(2), None, 4, 0, None) == binding.GDN_OK
 
 
 def test_gated_rmsnorm_rejects_bad_arguments(lib):

@@ -5,7 +5,11 @@ Cases: both io dtypes, dk = dv in {32, 64, 128}, conv widths 1, 2, 4 and 8, pack
 batches with empty sequences and sequences shorter than the window, with and without
 a conv state, silu on and off, the L2 norm on and off, the state updated in place, a
 sequence split in two calls with the state carried (bitwise equal to one call), the
-Qwen3.5-9B 1k prefill shape, and the conv feeding the chunked prefill end to end.
+Qwen3.5-9B 1k prefill shape, packed batches large enough that each wave walks several
+token blocks, runs of empty sequences longer than a wave's offset window, the
+32768-token shape the benchmark times (sampled slices), a verify-and-rollback of the
+conv states through gdn_conv_state_snapshot, and the conv feeding the chunked
+prefill end to end.
 Bars: 1e-4 (fp32 io) and 2e-2 (bf16 io) on q, k and v (max-norm relative per tensor);
 the new conv state is a copy of inputs and must match bit for bit.
 """
@@ -133,6 +137,47 @@ def test_full_32k_shape_sampled():
         say("full_32k", "tokens %d..%d max rel err q %.3e k %.3e v %.3e" % ((a, b) + tuple(errs)))
         assert max(errs) <= TOL[torch.bfloat16], (a, b, errs)
     np.testing.assert_array_equal(s_out[0].cpu().numpy(), x[T - (K - 1):].float().t().numpy())
+
+
+def test_conv_state_snapshot_verify_and_rollback():
+    """Verify and roll back through the conv (NPU page, "New in v2"): after a prefix, the conv
+    states are saved (scattered into a pool), a 16-token draft per sequence moves them on,
+    they are restored, and the m_n accepted draft tokens are fed again.  The states then equal
+    the oracle's over the prefix plus the accepted tokens (bit for bit), and so do the outputs
+    of the accepted tokens."""
+    hqk, hv, d, K = 2, 4, 128, 4
+    prefix = [40, 3, 0, 70, 17]
+    m = [0, 1, 7, 15, 16]
+    N = len(prefix)
+    inp = S.make_conv_inputs(prefix, hqk, hv, d, d, K, torch.bfloat16, seed=61)
+    x, w = inp["x"].cuda(), inp["weight"].cuda()
+    C = x.shape[1]
+    state = inp["state"].cuda().clone()
+    say("conv_rollback", "prefix", prefix, "accepted", m)
+    gdn.conv1d_qkv(x, w, hqk, hv, d, d, inp["cu_seqlens"].cuda(), state, state)
+    pool = torch.full((8, C, K - 1), float("nan"), device="cuda")
+    rows = torch.tensor([6, 0, 3, 1, 5], dtype=torch.int32, device="cuda")
+    gdn.conv_state_snapshot(state, pool, dst_rows=rows)
+    draft = S.make_conv_inputs([16] * N, hqk, hv, d, d, K, torch.bfloat16, seed=62)["x"]
+    cu16 = torch.arange(0, 16 * N + 1, 16, dtype=torch.int32)
+    gdn.conv1d_qkv(draft.cuda(), w, hqk, hv, d, d, cu16.cuda(), state, state)
+    gdn.conv_state_snapshot(pool, state, src_rows=rows)
+    acc = torch.cat([draft[16 * n:16 * n + m[n]] for n in range(N)])
+    cu_m = torch.tensor([0] + list(np.cumsum(m)), dtype=torch.int32)
+    q, k, v = gdn.conv1d_qkv(acc.cuda(), w, hqk, hv, d, d, cu_m.cuda(), state, state)
+    torch.cuda.synchronize()
+
+    cu = [int(t) for t in inp["cu_seqlens"]]
+    full = torch.cat([torch.cat([inp["x"][cu[n]:cu[n + 1]], draft[16 * n:16 * n + m[n]]]) for n in range(N)])
+    cu_full = torch.tensor([0] + list(np.cumsum([prefix[n] + m[n] for n in range(N)])), dtype=torch.int32)
+    q_ref, k_ref, v_ref, s_ref = conv_qkv(full, inp["weight"], hqk, hv, d, d, cu_full, inp["state"], l2norm=True,
+                                          eps=1e-6)
+    np.testing.assert_array_equal(state.cpu().numpy(), s_ref.astype(np.float32))
+    tail = torch.cat([torch.arange(int(cu_full[n]) + prefix[n], int(cu_full[n + 1])) for n in range(N)])
+    for got, ref, name in ((q, q_ref, "q"), (k, k_ref, "k"), (v, v_ref, "v")):
+        err = rel_err(got.double().cpu().numpy(), ref[tail.numpy()])
+        say("conv_rollback", "%s max rel err %.3e" % (name, err))
+        assert err <= TOL[torch.bfloat16], (name, err)
 
 
 def test_conv_feeds_the_chunked_prefill():
