@@ -61,6 +61,9 @@ def load_library():
         lib.gdn_prefill_workspace_bytes.restype = sz
         lib.gdn_prefill_chunked.argtypes = [SP, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, sz, vp]
         lib.gdn_prefill_chunked.restype = ctypes.c_int
+        lib.gdn_prefill_chunked_gated_rmsnorm.argtypes = [SP, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, vp,
+                                                          ctypes.c_float, vp, vp, sz, vp]
+        lib.gdn_prefill_chunked_gated_rmsnorm.restype = ctypes.c_int
         lib.gdn_decode_step.argtypes = [SP, vp, vp, vp, vp, vp, vp, vp, i32, vp]
         lib.gdn_decode_step.restype = ctypes.c_int
         lib.gdn_state_snapshot.argtypes = [SP, vp, vp, i32, vp, vp, i32, i32, vp]
@@ -209,6 +212,36 @@ def prefill_chunked(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, sc
     return out, final_state
 
 
+def _prefill_norm_call(q, k, v, g, beta, z, norm_weight, cu_seqlens, initial_state, eps, scale, chunk, final_state,
+                       out, workspace):
+    """gdn_prefill_chunked's arguments with the gate, the norm weight and eps added."""
+    lib, args, keep, dev, out, final_state = _prefill_call(q, k, v, g, beta, cu_seqlens, initial_state, scale,
+                                                           chunk, final_state, out, workspace)
+    _need(z, "z", q.dtype, dev, 3)
+    if tuple(z.shape) != tuple(out.shape):
+        raise ValueError("z must be shaped like the output, %s" % (tuple(out.shape),))
+    _need(norm_weight, "norm_weight", torch.float32, dev, 1)
+    if norm_weight.shape[0] != out.shape[2]:
+        raise ValueError("norm_weight must be [dv]")
+    # (shape, q, k, v, g, beta, cu, N, T, cu_host, s0, final) + (z, weight, eps) + (y, workspace, bytes)
+    args = args[:12] + (_ptr(z), _ptr(norm_weight), ctypes.c_float(float(eps))) + args[12:]
+    return lib, args, keep + (z, norm_weight), dev, out, final_state
+
+
+def prefill_chunked_gated_rmsnorm(q, k, v, g, beta, z, norm_weight, cu_seqlens=None, initial_state=None, *,
+                                  eps=1e-6, scale=None, chunk=64, final_state=None, out=None, workspace=None):
+    """Chunked prefill followed by the gated RMSNorm of its output rows
+    (gdn_prefill_chunked_gated_rmsnorm): y = o / sqrt(mean(o^2) + eps) * norm_weight * silu(z)
+    per (token, value head) row, in place on y right after the scans.  z [T, HV, dv] in the
+    io dtype, norm_weight [dv] fp32; the other arguments as for prefill_chunked.  Returns
+    (y, final_state)."""
+    lib, args, keep, dev, out, final_state = _prefill_norm_call(q, k, v, g, beta, z, norm_weight, cu_seqlens,
+                                                                initial_state, eps, scale, chunk, final_state,
+                                                                out, workspace)
+    _check(lib, lib.gdn_prefill_chunked_gated_rmsnorm(*args, _stream(dev)))
+    return out, final_state
+
+
 class PreparedCall:
     """A library call whose arguments were validated and marshalled once; calling it enqueues
     the kernels again on the current stream with the same buffers (for timing loops)."""
@@ -231,6 +264,15 @@ def prepare_prefill(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, sc
     lib, args, keep, dev, out, final_state = _prefill_call(q, k, v, g, beta, cu_seqlens, initial_state, scale,
                                                            chunk, final_state, out, workspace)
     return PreparedCall(lib.gdn_prefill_chunked, lib, args, keep, dev, (out, final_state))
+
+
+def prepare_prefill_gated_rmsnorm(q, k, v, g, beta, z, norm_weight, cu_seqlens=None, initial_state=None, *,
+                                  eps=1e-6, scale=None, chunk=64, final_state=None, out=None,
+                                  workspace=None) -> PreparedCall:
+    lib, args, keep, dev, out, final_state = _prefill_norm_call(q, k, v, g, beta, z, norm_weight, cu_seqlens,
+                                                                initial_state, eps, scale, chunk, final_state,
+                                                                out, workspace)
+    return PreparedCall(lib.gdn_prefill_chunked_gated_rmsnorm, lib, args, keep, dev, (out, final_state))
 
 
 def _decode_call(q, k, v, g, beta, state, scale, out):

@@ -142,10 +142,17 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape, int64_t total_tokens,
         .total_bytes;
 }
 
-gdn_status gdn_prefill_chunked(const gdn_shape *shape, const void *q, const void *k, const void *v,
-                               const float *g, const float *beta, const int32_t *cu_seqlens, int32_t num_seqs,
-                               int64_t total_tokens, const int32_t *cu_seqlens_host, const float *initial_state,
-                               float *final_state, void *o, void *workspace, size_t workspace_bytes, void *stream)
+// The gated RMSNorm applied to the prefill's output rows (gdn_prefill_chunked_gated_rmsnorm).
+struct NormIn {
+    const void *z;
+    const float *weight;
+    float eps;
+};
+
+static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                               const int32_t *cu_seqlens_host, const float *initial_state, float *final_state, void *o,
+                               void *workspace, size_t workspace_bytes, void *stream, const NormIn *norm)
 {
     gdn_status st = check_shape(shape);
     if (st != GDN_OK)
@@ -170,6 +177,14 @@ gdn_status gdn_prefill_chunked(const gdn_shape *shape, const void *q, const void
         return fail(GDN_ERR_INVALID_ARG, "cu_seqlens and final_state are required");
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o))
         return fail(GDN_ERR_INVALID_ARG, "q, k, v, g, beta and o are required when total_tokens > 0");
+    if (norm) {
+        if (total_tokens > 0 && (!norm->z || !norm->weight))
+            return fail(GDN_ERR_INVALID_ARG, "z and the norm weight are required when total_tokens > 0");
+        if (!aligned(norm->z, 16) || !aligned(norm->weight, 16))
+            return fail(GDN_ERR_INVALID_ARG, "z and the norm weight must be 16-byte aligned");
+        if (!std::isfinite(norm->eps) || norm->eps < 0.f)
+            return fail(GDN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+    }
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(final_state, 16) ||
         !aligned(initial_state, 16))
         return fail(GDN_ERR_INVALID_ARG, "q, k, v, o and state pointers must be 16-byte aligned");
@@ -200,9 +215,11 @@ gdn_status gdn_prefill_chunked(const gdn_shape *shape, const void *q, const void
     const size_t v_bytes = (size_t)total_tokens * s.num_v_heads * s.dv * es;
     const size_t gb_bytes = (size_t)total_tokens * s.num_v_heads * sizeof(float);
     const size_t state_bytes = (size_t)num_seqs * s.num_v_heads * s.dk * s.dv * sizeof(float);
-    const void *inputs[] = {q, k, v, g, beta, initial_state, workspace};
-    const size_t in_bytes[] = {qk_bytes, qk_bytes, v_bytes, gb_bytes, gb_bytes, state_bytes, ws.total_bytes};
-    for (int i = 0; i < 7; ++i) {
+    const void *inputs[] = {q, k, v, g, beta, initial_state, workspace, norm ? norm->z : nullptr,
+                            norm ? norm->weight : nullptr};
+    const size_t in_bytes[] = {qk_bytes, qk_bytes, v_bytes, gb_bytes, gb_bytes, state_bytes, ws.total_bytes,
+                               v_bytes, (size_t)s.dv * sizeof(float)};
+    for (int i = 0; i < 9; ++i) {
         if (overlaps(o, v_bytes, inputs[i], in_bytes[i]))
             return fail(GDN_ERR_INVALID_ARG, "o overlaps an input or the workspace");
         if (i != 5 && overlaps(final_state, state_bytes, inputs[i], in_bytes[i]))
@@ -249,11 +266,37 @@ gdn_status gdn_prefill_chunked(const gdn_shape *shape, const void *q, const void
             p.max_seq_chunks = 1;
         }
     }
+    if (norm) {
+        p.norm_z = norm->z;
+        p.norm_weight = norm->weight;
+        p.norm_eps = norm->eps;
+    }
     p.stream = stream;
     const hipError_t err = gdn::launch_prefill(p);
     if (err != hipSuccess)
         return fail(GDN_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(err));
     return ok();
+}
+
+gdn_status gdn_prefill_chunked(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                               const float *g, const float *beta, const int32_t *cu_seqlens, int32_t num_seqs,
+                               int64_t total_tokens, const int32_t *cu_seqlens_host, const float *initial_state,
+                               float *final_state, void *o, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return prefill_impl(shape, q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, cu_seqlens_host, initial_state,
+                        final_state, o, workspace, workspace_bytes, stream, nullptr);
+}
+
+gdn_status gdn_prefill_chunked_gated_rmsnorm(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                                             const float *g, const float *beta, const int32_t *cu_seqlens,
+                                             int32_t num_seqs, int64_t total_tokens, const int32_t *cu_seqlens_host,
+                                             const float *initial_state, float *final_state, const void *z,
+                                             const float *norm_weight, float eps, void *y, void *workspace,
+                                             size_t workspace_bytes, void *stream)
+{
+    const NormIn norm{z, norm_weight, eps};
+    return prefill_impl(shape, q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, cu_seqlens_host, initial_state,
+                        final_state, y, workspace, workspace_bytes, stream, &norm);
 }
 
 gdn_status gdn_decode_step(const gdn_shape *shape, const void *q, const void *k, const void *v, const float *g,

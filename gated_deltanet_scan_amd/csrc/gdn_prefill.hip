@@ -1998,6 +1998,26 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
     E *amat = tmat + (size_t)p.max_chunks * p.hv * C * C;
     float *dec = reinterpret_cast<float *>(amat + (size_t)p.max_chunks * p.hv * C * C);
     const int nw = pick_waves<E>(p.dv);
+    // The gated RMSNorm of the output rows, if asked for: in place, after the scans.
+    auto finish = [&]() -> hipError_t {
+        if (p.norm_z && p.total_tokens > 0) {
+            NormArgs n{};
+            n.hv = p.hv;
+            n.dv = p.dv;
+            n.io_dtype = p.io_dtype;
+            n.o = p.o;
+            n.z = p.norm_z;
+            n.weight = p.norm_weight;
+            n.y = p.o;
+            n.tokens = p.total_tokens;
+            n.eps = p.norm_eps;
+            n.stream = p.stream;
+            const hipError_t e = launch_norm(n);
+            if (e != hipSuccess)
+                return e;
+        }
+        return hipGetLastError();
+    };
 
     auto scan = [&](const SlotMap &map, const float *sin, float *sout) {
         if constexpr (std::is_same<E, bf16>::value && C == 64) {
@@ -2046,7 +2066,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
             prep(map, (int64_t)p.num_seqs * p.seg_len);
             scan(map, s0 == 0 ? p.initial_state : p.final_state, p.final_state);
         }
-        return hipGetLastError();
+        return finish();
     }
 
     {
@@ -2058,7 +2078,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
     if (p.max_chunks > 0)
         prep(map, p.max_chunks);
     scan(map, p.initial_state, p.final_state);
-    return hipGetLastError();
+    return finish();
 }
 
 hipError_t launch_prefill(const PrefillArgs &p)

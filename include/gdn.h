@@ -206,6 +206,32 @@ gdn_status gdn_conv1d_qkv(const gdn_shape *shape, const void *x, const float *we
                           void *q, void *k, void *v, void *stream);
 
 /*
+ * Chunked prefill whose output rows go through the gated RMSNorm of the
+ * layer before they are stored (NPU page "Qwen3.5-9B -- every component on
+ * the Intel NPU", section "How it works": the DeltaNet output feeds a gated
+ * RMSNorm; eps 1e-6 for Qwen3.5, Candle pull-request page, section "Bug
+ * elimination log", bug 7).  Every argument as for gdn_prefill_chunked, with
+ * o replaced by
+ *   y            [total_tokens, HV, dv] io dtype out:
+ *                y = o / sqrt(mean(o^2) + eps) * norm_weight * silu(z) per
+ *                (token, value head) row, silu(z) = z / (1 + exp(-z))
+ * and
+ *   z            [total_tokens, HV, dv] io dtype (the gate), 16-byte aligned
+ *   norm_weight  [dv] fp32, shared by the heads, 16-byte aligned
+ *   eps          finite, >= 0
+ * y must not overlap z, norm_weight or any other input.  The norm runs on the
+ * same stream right after the scans, in place on y (one pass over y and z).
+ */
+gdn_status gdn_prefill_chunked_gated_rmsnorm(const gdn_shape *shape,
+                                             const void *q, const void *k, const void *v,
+                                             const float *g, const float *beta,
+                                             const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                             const int32_t *cu_seqlens_host,
+                                             const float *initial_state, float *final_state,
+                                             const void *z, const float *norm_weight, float eps, void *y,
+                                             void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Conv state snapshot / restore: copies whole per-sequence conv states
  * (C x (width - 1) fp32 each, C = 2 HQK dk + HV dv channels) between two
  * buffers, so that a verify pass through the conv can be rolled back with
