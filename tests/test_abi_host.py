@@ -48,7 +48,7 @@ def prefill(lib, sh, T=128, N=1, cu_host=None, ws_bytes=None, ws=None, q=None, g
 def test_every_declared_function_is_exported(lib):
     names = gdn.header_functions()
     assert set(names) >= {"gdn_prefill_chunked", "gdn_decode_step", "gdn_state_snapshot", "gdn_gated_rmsnorm",
-                          "gdn_conv1d_qkv", "gdn_conv_state_snapshot",
+                          "gdn_conv1d_qkv", "gdn_conv_state_snapshot", "gdn_prefill_chunked_gated_rmsnorm",
                           "gdn_prefill_workspace_bytes", "gdn_status_string", "gdn_last_error", "gdn_version"}
     for name in names:
         assert hasattr(lib, name), name
@@ -89,6 +89,27 @@ def test_prefill_rejects_bad_cu_seqlens(lib):
     assert prefill(lib, sh, T=100, N=2, cu_host=[0, 60, 50]) == binding.GDN_ERR_INVALID_ARG
     assert b"decreases" in lib.gdn_last_error()
     assert prefill(lib, sh, T=100, N=2, cu_host=[0, 50, 99]) == binding.GDN_ERR_INVALID_ARG
+
+
+def prefill_norm(lib, sh, T=128, z=None, w=None, eps=1e-6, y=None):
+    cu = np.array([0, T], dtype=np.int32)
+    need = lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), T, 1)
+    return lib.gdn_prefill_chunked_gated_rmsnorm(
+        ctypes.byref(sh), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), 1, T,
+        cu.ctypes.data_as(ctypes.c_void_p), fake(7), fake(8), z if z is not None else fake(11),
+        w if w is not None else fake(12), ctypes.c_float(eps), y if y is not None else fake(9), fake(10), need, None)
+
+
+def test_prefill_norm_rejects_bad_arguments(lib):
+    sh = shape()
+    assert prefill_norm(lib, sh, z=ctypes.c_void_p(fake(11).value + 8)) == binding.GDN_ERR_INVALID_ARG   # alignment
+    assert prefill_norm(lib, sh, eps=-1.0) == binding.GDN_ERR_INVALID_ARG
+    assert prefill_norm(lib, sh, eps=float("inf")) == binding.GDN_ERR_INVALID_ARG
+    assert prefill_norm(lib, sh, y=ctypes.c_void_p(fake(11).value + 256)) == binding.GDN_ERR_INVALID_ARG  # y over z
+    assert prefill_norm(lib, sh, w=ctypes.c_void_p(fake(9).value + 16)) == binding.GDN_ERR_INVALID_ARG   # y over w
+    assert lib.gdn_prefill_chunked_gated_rmsnorm(
+        ctypes.byref(sh), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), 1, 128, None, fake(7), fake(8),
+        None, fake(12), ctypes.c_float(1e-6), fake(9), fake(10), 1 << 30, None) == binding.GDN_ERR_INVALID_ARG
 
 
 def test_prefill_rejects_workspace_and_alignment(lib):
