@@ -2,8 +2,9 @@
 
 Cases: the five workloads at their full sizes (the tiny fp32 one, 1k prefill,
 32k prefill, the 16-sequence varlen batch), lengths below, at and above the
-chunk, multi-chunk ragged tails, zero-length sequences, every supported head
-size and chunk length in both io dtypes, the strong-decay (-6.72) segment,
+chunk, multi-chunk ragged tails, zero-length sequences, batches at and past
+the 4096-sequence ordering limit, every supported head size and chunk length
+in both io dtypes, the strong-decay (-6.72) segment,
 a weak-decay long-memory stress, in-place prefix reuse and run-to-run
 determinism.
 """
@@ -81,6 +82,22 @@ def test_wide_slices_many_sequences(nseq):
     for host_offsets in (True, False):
         _run(_case(lengths, 2, 4, 128, torch.bfloat16, seed=500 + nseq), 64, torch.bfloat16,
              "wide_n%d" % nseq, host_offsets=host_offsets)
+
+
+@pytest.mark.parametrize("nseq", [4096, 4100])
+def test_batches_at_and_past_the_ordering_limit(nseq):
+    """Up to 4096 sequences a ranking kernel orders the batch so that the scans start the
+    longest sequences first; past that the scans take the sequences in batch order.  Both
+    sides of the limit, with host and device offsets: mostly sequences of 0..4 tokens, with a
+    130-token one every 997, one value head per query/key head (4096+ pairs: the whole-head
+    scan)."""
+    gen = torch.Generator().manual_seed(nseq)
+    lengths = [int(x) for x in torch.randint(0, 5, (nseq,), generator=gen)]
+    for i in range(0, nseq, 997):
+        lengths[i] = 130
+    inp = _case(lengths, 1, 1, 128, torch.bfloat16, seed=700 + nseq)
+    for host_offsets in (True, False):
+        _run(inp, 64, torch.bfloat16, "ordering_n%d" % nseq, host_offsets=host_offsets)
 
 
 def test_long_sequence_spans_several_segments():
