@@ -2,7 +2,8 @@
 
 Cases: the five workloads at their full sizes (the tiny fp32 one, 1k prefill,
 32k prefill, the 16-sequence varlen batch), lengths below, at and above the
-chunk, multi-chunk ragged tails, zero-length sequences, batches at and past
+chunk, multi-chunk ragged tails, zero-length sequences, batches without tokens
+(and without sequences), batches at and past
 the 4096-sequence ordering limit, every supported head size and chunk length
 in both io dtypes, the strong-decay (-6.72) segment,
 a weak-decay long-memory stress, in-place prefix reuse and run-to-run
@@ -114,6 +115,36 @@ def test_zero_length_sequences_pass_state_through():
     s0 = inp["initial_state"]
     for n in (0, 2, 3, 5):
         assert torch.equal(St[n].cpu(), s0[n]), "empty sequence %d changed its state" % n
+
+
+@pytest.mark.parametrize("host_offsets", [True, False])
+def test_batches_without_tokens(host_offsets):
+    """No tokens at all: every final state is its initial state bit for bit (also in place),
+    or zeros without initial states (written over a NaN-filled buffer); a batch of no
+    sequences is a no-op."""
+    import gated_deltanet_scan_amd as gdn
+    inp = _case([0, 0, 0], 1, 2, 128, torch.bfloat16, seed=31)
+    say("no_tokens", "host offsets" if host_offsets else "device offsets")
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    cu = inp["cu_seqlens"] if host_offsets else d["cu_seqlens"]
+    o, St = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["initial_state"])
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0
+    assert torch.equal(St.cpu(), inp["initial_state"])
+    state = d["initial_state"].clone()
+    gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, state, final_state=state)
+    torch.cuda.synchronize()
+    assert torch.equal(state.cpu(), inp["initial_state"])
+    fs = torch.full_like(d["initial_state"], float("nan"))
+    o, St = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, None, final_state=fs)
+    torch.cuda.synchronize()
+    assert St.data_ptr() == fs.data_ptr()
+    assert not bool(torch.isnan(St).any()) and int(torch.count_nonzero(St)) == 0
+    cu0 = torch.zeros(1, dtype=torch.int32)
+    e = {k: d[k][:0] for k in ("q", "k", "v", "g", "beta")}
+    o, St = gdn.prefill_chunked(e["q"], e["k"], e["v"], e["g"], e["beta"], cu0 if host_offsets else cu0.cuda(), None)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0 and St.shape[0] == 0
 
 
 def test_zero_initial_state_and_gqa_groups_of_four():
