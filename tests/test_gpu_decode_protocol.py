@@ -55,6 +55,18 @@ def test_decode_every_head_size(io, d):
     _check_decode(_decode_inputs(5, 2, 4, d, io, seed=300 + d), io, "decode_d%d" % d)
 
 
+def test_decode_large_batch_and_empty_batch():
+    """A batch of 3000 sequences (one query/key head, one value head each: 12000 waves) at
+    parity, then a batch of no sequences, which must leave the state untouched."""
+    _check_decode(_decode_inputs(3000, 1, 1, 128, torch.bfloat16, seed=305), torch.bfloat16, "decode_n3000")
+    inp = _decode_inputs(2, 1, 2, 128, torch.bfloat16, seed=306)
+    d = to_dev(inp)
+    state = d["initial_state"].clone()
+    o = gdn.decode_step(d["q"][:0], d["k"][:0], d["v"][:0], d["g"][:0], d["beta"][:0], state[:0])
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0 and torch.equal(state.cpu(), inp["initial_state"])
+
+
 def test_decode_strong_decay_and_scale():
     inp = _decode_inputs(3, 1, 2, 128, torch.bfloat16, seed=310)
     inp["g"][:] = S.STRONG_DECAY
