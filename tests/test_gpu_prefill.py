@@ -196,11 +196,21 @@ def test_in_place_prefix_reuse_matches_two_calls():
     check_prefill(torch.cat(outs), state, o_ref, S_ref, inp["cu_seqlens"], torch.bfloat16, "prefix_reuse")
 
 
-def test_run_to_run_bitwise_determinism():
-    inp = _case([700, 33], 2, 4, 128, torch.bfloat16, seed=27)
-    o1, s1 = gpu_prefill(inp, 64)
-    o2, s2 = gpu_prefill(inp, 64)
-    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+@pytest.mark.parametrize("lengths,hqk,hv", [([700, 33], 2, 4), ([300, 5, 0, 129] * 5, 2, 4)])
+def test_run_to_run_bitwise_determinism(lengths, hqk, hv):
+    """Two runs give the same bits, for the row-split scan (8 pairs) and the whole-head scan
+    (80 pairs), with host offsets (segmented launches) and device offsets (one launch over the
+    chunk table); the two launch modes also agree bit for bit (same per-chunk arithmetic, the
+    state carried in fp32 between segments)."""
+    inp = _case(lengths, hqk, hv, 128, torch.bfloat16, seed=27)
+    say("determinism", "N=%d" % len(lengths), "pairs=%d" % (len(lengths) * hv))
+    runs = {}
+    for host_offsets in (True, False):
+        o1, s1 = gpu_prefill(inp, 64, host_offsets=host_offsets)
+        o2, s2 = gpu_prefill(inp, 64, host_offsets=host_offsets)
+        assert torch.equal(o1, o2) and torch.equal(s1, s2)
+        runs[host_offsets] = (o1, s1)
+    assert torch.equal(runs[True][0], runs[False][0]) and torch.equal(runs[True][1], runs[False][1])
 
 
 def test_chunk_length_does_not_change_the_answer():
