@@ -1085,9 +1085,11 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_kernel(
 // step is spread over 4 compute waves by chunk rows (and key rows for the S
 // update), exchanging X, D and the transposed bf16 copy of S through LDS, and
 // storing the chunk's outputs straight from registers; 4 loader waves stage
-// the next chunk.  With few pairs the chip has more CUs than workgroups and the
-// chain of chunk steps is latency-bound, which this split shortens.  (Wide
-// batches use gdn_chunk_scan_bf16_kernel.)
+// the chunks ahead of the compute waves: two steps ahead with three stage
+// buffers for dk = 128, one step ahead with two for smaller dk (whose two
+// buffers leave room for two workgroups per CU).  With few pairs the chip has
+// more CUs than workgroups and the chain of chunk steps is latency-bound, which
+// this split shortens.  (Wide batches use gdn_chunk_scan_bf16_kernel.)
 // ---------------------------------------------------------------------------
 // LDS row stride (elements) of the padded key-dimension tile St.  In dwords it
 // is a multiple of 4 with an odd quotient, so 16 rows read with 16-byte
@@ -1104,7 +1106,7 @@ constexpr int key_row_stride(int dk)
 
 constexpr int kScanThreads = 2 * kThreads;   // 4 compute waves + 4 loader waves
 
-template <typename E, int C, int DK, int DVS>
+template <typename E, int C, int DK, int DVS, int NSTAGE>
 __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v, const int32_t *__restrict__ cu,
     SlotMap map, int32_t num_seqs, int64_t total_tokens, int32_t hqk, int32_t hv, int32_t dv,
@@ -1149,10 +1151,18 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     constexpr int NJ = J_D + NJ_D;
     static_assert(STAGE % 16 == 0 && OFF_D % 16 == 0, "16-byte aligned stage blocks");
 
-    __shared__ __attribute__((aligned(1024))) unsigned char stage_mem[2 * STAGE];
+    // NSTAGE stage buffers: the loaders fill chunk c + NSTAGE - 1 while the compute waves
+    // work on chunk c.  With three, D and diag(lambda) D of a step live in the step's own
+    // Q region: they are written after B1, when that tile is dead (only P1 reads it), and
+    // the three buffers would not fit beside arrays of their own.
+    static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three stage buffers");
+    constexpr bool kDInQ = NSTAGE == 3;
+    static_assert(!kDInQ || 2 * DVS * LDC * ES <= C * DK * ES, "D and lambda D must fit the Q region");
+    static_assert(NSTAGE * STAGE + DVS * LDC * ES + (kDInQ ? 16 : 2 * DVS * LDC * ES) + DVS * LDK * ES <= 163840,
+                  "stage buffers and exchange tiles must fit the 160 KB of LDS");
+    __shared__ __attribute__((aligned(1024))) unsigned char stage_mem[NSTAGE * STAGE];
     __shared__ __attribute__((aligned(16))) E Xt[DVS * LDC];
-    __shared__ __attribute__((aligned(16))) E Dt[DVS * LDC];
-    __shared__ __attribute__((aligned(16))) E LDt[DVS * LDC];
+    __shared__ __attribute__((aligned(16))) E DLt_own[kDInQ ? 16 / ES : 2 * DVS * LDC];
     __shared__ __attribute__((aligned(16))) E St[DVS * LDK];
 
     // the stage buffers as LDS addresses (the direct loads write LDS by address)
@@ -1212,7 +1222,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         }
     }
 
-    // ---- loaders: chunk c straight into stage buffer c & 1 (direct-to-LDS loads) ----
+    // ---- loaders: chunk c straight into stage buffer c % NSTAGE (direct-to-LDS loads) ----
     // Job J (of NJ) moves 1 KB of the stage with one load: lane i writes the 16 bytes at
     // 16 i of the job's block.  Loader lw runs jobs lw, lw + 4, ...; which tile and rows a
     // job covers is fixed at compile time (one code path per loader), and all loads of a
@@ -1251,7 +1261,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     // Stage chunk c.  Rows past the chunk's last real row are loaded from it.
     auto issue_jobs = [&](auto wc, int c) __attribute__((always_inline)) {
         constexpr int W = decltype(wc)::value;
-        __attribute__((address_space(3))) unsigned char *stg = lds_stage + (c & 1) * STAGE;
+        __attribute__((address_space(3))) unsigned char *stg = lds_stage + (c % NSTAGE) * STAGE;
         const int64_t t0 = a + (int64_t)c * C;
         const int last = (int)min<int64_t>(C, b - t0) - 1;   // >= 0 for every chunk of the sequence
         const size_t slot = slot_begin + (size_t)(c - c_begin);
@@ -1301,6 +1311,8 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     // ---- compute waves: one chunk step on stage buffer `cur` (barriers B1 and B2 inside) ----
     auto step = [&](int cur, int64_t t0, int len) __attribute__((always_inline)) {
         const unsigned char *stg = stage_mem + cur * STAGE;
+        E *const Dt = kDInQ ? reinterpret_cast<E *>(stage_mem + cur * STAGE + OFF_Q) : DLt_own;
+        E *const LDt = Dt + DVS * LDC;
         const float *Gs = reinterpret_cast<const float *>(stg + OFF_D);   // scale exp(G)
         const float *Lam = Gs + C;                                         // exp(G_last - G)
         const float *Bet = Gs + 2 * C;                                     // beta
@@ -1427,29 +1439,52 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         }
     };
 
-    // ---- pipeline: while the compute waves work on chunk c (stage c & 1), the loaders
-    //      stage chunk c + 1 into the other buffer.
-    //      The direct loads are not tracked by the compiler's LDS dependences: each loader
-    //      waits for its own loads before the barrier that publishes the stage. ----
+    // ---- pipeline: while the compute waves work on chunk c (stage c % NSTAGE), the
+    //      loaders stage chunk c + NSTAGE - 1.  The direct loads are not tracked by the
+    //      compiler's LDS dependences: before the barrier that ends a step, each loader
+    //      waits until its loads of chunk c + 1 have landed, leaving those of a later chunk
+    //      in flight (the counter retires loads in issue order).  The loaders take bare
+    //      barriers: a fenced one would first wait for all their loads. ----
+    // wait for all of this loader's loads but those of one chunk (jobs W, W + 4, ... < NJ)
+    auto wait_all_but_one_chunk = [&](auto wc) __attribute__((always_inline)) {
+        constexpr int W = decltype(wc)::value;
+        constexpr int cnt = W < NJ ? (NJ - W + kWaves - 1) / kWaves : 0;
+        static_assert(cnt < 64, "vmcnt holds at most 63");
+        __builtin_amdgcn_s_waitcnt((cnt & 15) | ((cnt >> 4) << 14) | 0x0f70);   // vmcnt(cnt) only
+        asm volatile("" ::: "memory");
+    };
+    constexpr int AHEAD = NSTAGE - 1;
     if (loader) {
         by_loader([&](auto wc) { issue_jobs(wc, c_begin); });
+        if (AHEAD == 2 && c_begin + 1 < c_end)
+            by_loader([&](auto wc) {
+                issue_jobs(wc, c_begin + 1);
+                wait_all_but_one_chunk(wc);
+            });
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
     for (int c = c_begin; c < c_end; ++c) {
         if (loader) {
-            if (c + 1 < c_end)
-                by_loader([&](auto wc) { issue_jobs(wc, c + 1); });
-            // B1 and B2 of the compute waves: the loaders publish nothing there, so they
-            // take the bare barrier (a fenced one would first wait for all their loads)
+            if (c + AHEAD < c_end)
+                by_loader([&](auto wc) { issue_jobs(wc, c + AHEAD); });
+            // B1 and B2 of the compute waves: the loaders publish nothing there
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_s_barrier();
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            if (AHEAD == 2 && c + 2 < c_end)
+                by_loader([&](auto wc) { wait_all_but_one_chunk(wc); });
+            else
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();   // end of step: chunk c + 1 is staged
         } else {
             const int64_t ct0 = a + (int64_t)c * C;
-            step(c & 1, ct0, (int)min<int64_t>(C, b - ct0));
+            step(c % NSTAGE, ct0, (int)min<int64_t>(C, b - ct0));
+            __syncthreads();   // end of step: St is complete
         }
-        __syncthreads();       // end of step: St and the next stage are complete
     }
     if (!loader) {
         // ---- final state ----
@@ -1981,7 +2016,9 @@ static void launch_scan_rows(const PrefillArgs &p, const SlotMap &map, const bf1
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
     const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
     const ProfEvents ev = prof_events(PROF_SCAN);
-    hipExtLaunchKernelGGL((gdn_chunk_scan_rows_kernel<bf16, 64, DK, DVS>), dim3((unsigned)blocks),
+    // three stage buffers where one workgroup per CU is the occupancy anyway (dk = 128)
+    constexpr int NSTAGE = DK >= 128 ? 3 : 2;
+    hipExtLaunchKernelGGL((gdn_chunk_scan_rows_kernel<bf16, 64, DK, DVS, NSTAGE>), dim3((unsigned)blocks),
                           dim3(kScanThreads), 0, st, ev.start, ev.stop, 0, static_cast<const bf16 *>(p.q),
                           static_cast<const bf16 *>(p.k), static_cast<const bf16 *>(p.v), p.cu_seqlens, map,
                           p.num_seqs, p.total_tokens, p.hqk, p.hv, p.dv, tmat, amat, dec, sin, sout,
