@@ -5,12 +5,12 @@ import this package.  The product path (the HIP library and its Python
 binding) never imports, loads or calls anything here, and this package
 imports nothing from the product.
 
-`gdn_forward` runs the per-token recurrence of the Loop body on page
-"Qwen3.5-9B -- every component on the Intel NPU", section "How it works"
-(decay the state by exp(g_t), read S^T k_t, write back beta_t times the
-error, read the output with q_t), for every (sequence, value head) pair of a
-packed batch, in fp64, in plain C (gdn_oracle.c).  Decode is the same call
-with one token per sequence.
+`gdn_forward` runs the gated delta rule token by token in the closed form of
+the Qwen3.5-9B architecture page (section Gated DeltaNet), expanded as one read
+of the old state along the key, the decayed error written back as a rank-one
+update, and the output read along the query; for every (sequence, value head)
+pair of a packed batch, in fp64, in plain C (gdn_oracle.c).  Decode is the
+same call with one token per sequence.
 
 Parity pins for this oracle live in tests/test_oracle_pins.py.
 """

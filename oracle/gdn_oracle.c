@@ -6,18 +6,19 @@
  * CPU-baseline leg do.  It shares no code, header or table with the HIP
  * library under gated_deltanet_scan_amd/.
  *
- * What it computes (no chunks, no blocking, no fusion):
- *   "Qwen3.5-9B -- every component on the Intel NPU", section "How it works",
- *   Gated DeltaNet on the NPU: the per-token Loop body, applied to every
- *   token of a sequence in order, for every value head independently:
- *       S   <- S * exp(g_t)                      (decay the old state)
- *       kv  <- S^T k_t                           (what S stores for k_t)
- *       S   <- S + k_t (x) ((v_t - kv) * beta_t) (write back only the error)
- *       o_t <- S^T q_t                           (read with the query)
- *   The same update in closed form is given on the Qwen3.5-9B architecture
- *   page (section Gated DeltaNet): S_t = a_t (I - b_t k_t k_t^T) S_{t-1}
- *   + b_t k_t v_t^T, with a_t = exp(g_t) the forget gate and b_t the
- *   correction rate.
+ * What it computes (no chunks, no blocking, no fusion): the gated delta rule
+ * in the closed form of the Qwen3.5-9B architecture page (section Gated
+ * DeltaNet), one token at a time, for every value head independently.  With
+ * the forget gate a_t = exp(g_t) and the correction rate b_t, the state
+ * S (dk x dv) moves from S_{t-1} to
+ *     S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T.
+ * Expanded, this is one read of the old state along k_t and one rank-one
+ * write: with r = S_{t-1}^T k_t (the value the state returns for k_t),
+ *     e   = b_t (v_t - a_t r)          (the part of v_t the decayed state misses)
+ *     S_t = a_t S_{t-1} + k_t e^T
+ * and the token's output is the new state read along q_t, o_t = scale S_t^T q_t.
+ * The NPU page ("Qwen3.5-9B -- every component on the Intel NPU", section
+ * "How it works") runs the same rule as a per-token loop on the NPU.
  *
  * Readings where the pages are silent (each is listed with its reason in the
  * design notes of this repository):
@@ -32,7 +33,7 @@
  *     cu_seqlens[n] .. cu_seqlens[n+1]-1 and starts from its own state.
  *
  * Precision: every operand is taken as fp64 and every operation is done in
- * fp64, in the order written above.  Inputs are expected to be the exact
+ * fp64, in the order of the expanded form above.  Inputs are expected to be the exact
  * values the device receives (bf16 or fp32 widened without rounding).
  *
  * Parity pins: see the CPU tests (brute-force product of the closed-form
@@ -59,7 +60,7 @@ typedef struct {
 } job_t;
 
 /* One (sequence, value head) recurrence, token by token. */
-static void run_item(const job_t *J, int64_t item, double *S, double *kv)
+static void run_item(const job_t *J, int64_t item, double *S, double *r)
 {
     const int32_t hv = J->hv, dk = J->dk, dv = J->dv, hqk = J->hqk;
     const int32_t n = (int32_t)(item / hv);
@@ -81,22 +82,20 @@ static void run_item(const job_t *J, int64_t item, double *S, double *kv)
         const double b = J->beta[(size_t)t * hv + h];
         double *ot = J->o + ((size_t)t * hv + h) * dv;
 
-        /* S <- S * exp(g_t) */
-        for (size_t e = 0; e < state_elems; ++e)
-            S[e] *= alpha;
-        /* kv <- S^T k_t */
+        /* r = S_{t-1}^T k_t */
         for (int32_t j = 0; j < dv; ++j)
-            kv[j] = 0.0;
+            r[j] = 0.0;
         for (int32_t i = 0; i < dk; ++i)
             for (int32_t j = 0; j < dv; ++j)
-                kv[j] += kt[i] * S[(size_t)i * dv + j];
-        /* S <- S + k_t (x) ((v_t - kv) * beta_t) */
+                r[j] += kt[i] * S[(size_t)i * dv + j];
+        /* e = b_t (v_t - a_t r), kept in r */
         for (int32_t j = 0; j < dv; ++j)
-            kv[j] = (vt[j] - kv[j]) * b; /* kv now holds the error term */
+            r[j] = b * (vt[j] - alpha * r[j]);
+        /* S_t = a_t S_{t-1} + k_t e^T */
         for (int32_t i = 0; i < dk; ++i)
             for (int32_t j = 0; j < dv; ++j)
-                S[(size_t)i * dv + j] += kt[i] * kv[j];
-        /* o_t <- scale * S^T q_t */
+                S[(size_t)i * dv + j] = alpha * S[(size_t)i * dv + j] + kt[i] * r[j];
+        /* o_t = scale S_t^T q_t */
         for (int32_t j = 0; j < dv; ++j)
             ot[j] = 0.0;
         for (int32_t i = 0; i < dk; ++i)
@@ -112,10 +111,10 @@ static void *worker(void *arg)
 {
     job_t *J = (job_t *)arg;
     double *S = (double *)malloc((size_t)J->dk * J->dv * sizeof(double));
-    double *kv = (double *)malloc((size_t)J->dv * sizeof(double));
-    if (!S || !kv) {
+    double *r = (double *)malloc((size_t)J->dv * sizeof(double));
+    if (!S || !r) {
         free(S);
-        free(kv);
+        free(r);
         return (void *)1;
     }
     for (;;) {
@@ -124,10 +123,10 @@ static void *worker(void *arg)
         pthread_mutex_unlock(&J->lock);
         if (item >= J->num_items)
             break;
-        run_item(J, item, S, kv);
+        run_item(J, item, S, r);
     }
     free(S);
-    free(kv);
+    free(r);
     return NULL;
 }
 

@@ -15,15 +15,17 @@ import oracle
 import test_oracle_pins as pins
 
 MUTATIONS = {
-    "error_sign": ("kv[j] = (vt[j] - kv[j]) * b;", "kv[j] = (vt[j] + kv[j]) * b;"),
-    "drop_beta": ("kv[j] = (vt[j] - kv[j]) * b;", "kv[j] = (vt[j] - kv[j]);"),
+    "error_sign": ("r[j] = b * (vt[j] - alpha * r[j]);", "r[j] = b * (vt[j] + alpha * r[j]);"),
+    "drop_beta": ("r[j] = b * (vt[j] - alpha * r[j]);", "r[j] = (vt[j] - alpha * r[j]);"),
+    "error_undecayed": ("r[j] = b * (vt[j] - alpha * r[j]);", "r[j] = b * (vt[j] - r[j]);"),
     "decay_sign": ("const double alpha = exp(J->g[(size_t)t * hv + h]);",
                    "const double alpha = exp(-J->g[(size_t)t * hv + h]);"),
-    "drop_decay": ("S[e] *= alpha;", "S[e] *= 1.0;"),
+    "drop_decay": ("S[(size_t)i * dv + j] = alpha * S[(size_t)i * dv + j] + kt[i] * r[j];",
+                   "S[(size_t)i * dv + j] = S[(size_t)i * dv + j] + kt[i] * r[j];"),
     "gqa_modulo": ("const int32_t hq = (int32_t)(((int64_t)h * hqk) / hv);",
                    "const int32_t hq = (int32_t)(h % hqk);"),
-    "read_with_q": ("kv[j] += kt[i] * S[(size_t)i * dv + j];", "kv[j] += qt[i] * S[(size_t)i * dv + j];"),
-    "write_with_q": ("S[(size_t)i * dv + j] += kt[i] * kv[j];", "S[(size_t)i * dv + j] += qt[i] * kv[j];"),
+    "read_with_q": ("r[j] += kt[i] * S[(size_t)i * dv + j];", "r[j] += qt[i] * S[(size_t)i * dv + j];"),
+    "write_with_q": ("alpha * S[(size_t)i * dv + j] + kt[i] * r[j];", "alpha * S[(size_t)i * dv + j] + qt[i] * r[j];"),
     "output_with_k": ("ot[j] += qt[i] * S[(size_t)i * dv + j];", "ot[j] += kt[i] * S[(size_t)i * dv + j];"),
     "drop_scale": ("ot[j] *= J->scale;", "ot[j] *= 1.0;"),
     "g_head_index": ("exp(J->g[(size_t)t * hv + h])", "exp(J->g[(size_t)t * hv])"),
