@@ -157,6 +157,36 @@ def test_qkv_split_and_head_norms():
     assert not np.allclose(np.linalg.norm(wrong, axis=-1), 1.0)
 
 
+def _norm_variants(y, head_dim, eps, variant):
+    """l2_normalise_heads with a planted mistake in where eps enters (for the pin below)."""
+    h = np.asarray(y, dtype=np.float64).reshape(y.shape[0], -1, head_dim)
+    ss = np.sum(h * h, axis=-1, keepdims=True)
+    den = {"outside_root": np.sqrt(ss) + eps, "squared": np.sqrt(ss + eps * eps),
+           "dropped": np.sqrt(ss)}[variant]
+    return (h / den).reshape(y.shape)
+
+
+def check_head_norm_eps_closed_form(fn):
+    """A constant head of value c over d components with eps inside the root: every component
+    becomes c / sqrt(d c^2 + eps) (c = 0.5, d = 4, eps = 0.25: 0.5 / sqrt(1.25))."""
+    d, c, eps = 4, 0.5, 0.25
+    y = np.full((3, 2 * d), c)
+    out = fn(y, d, eps)
+    np.testing.assert_allclose(out, np.full_like(y, c / np.sqrt(d * c * c + eps)), rtol=1e-15)
+    # zero heads stay zero (eps keeps the division finite)
+    np.testing.assert_array_equal(fn(np.zeros((2, d)), d, eps), np.zeros((2, d)))
+
+
+def test_head_norm_eps_closed_form():
+    check_head_norm_eps_closed_form(l2_normalise_heads)
+
+
+@pytest.mark.parametrize("variant", ["outside_root", "squared", "dropped"])
+def test_head_norm_eps_pin_catches_planted_mistakes(variant):
+    with pytest.raises(AssertionError):
+        check_head_norm_eps_closed_form(lambda y, d, eps: _norm_variants(y, d, eps, variant))
+
+
 def test_rejects_bad_shapes():
     with pytest.raises(ValueError):
         causal_conv1d(np.ones((3, 4)), np.ones((5, 2)))
