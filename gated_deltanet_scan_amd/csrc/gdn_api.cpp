@@ -84,7 +84,7 @@ bool decode_supported(int32_t dk, int32_t dv, int32_t io_dtype)
     return dk == dv && (dk == 32 || dk == 64 || dk == 128);
 }
 
-PrefillWorkspace prefill_workspace(int32_t hv, int32_t chunk, int32_t io_dtype, int64_t total_tokens,
+PrefillWorkspace prefill_workspace(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype, int64_t total_tokens,
                                    int32_t num_seqs)
 {
     PrefillWorkspace w{0, 0, 0};
@@ -96,9 +96,11 @@ PrefillWorkspace prefill_workspace(int32_t hv, int32_t chunk, int32_t io_dtype, 
     w.max_chunks = (int32_t)max_chunks;
     // chunk table (num_seqs + 1 entries), then the scan order of the sequences (num_seqs)
     w.table_bytes = ((2 * (size_t)num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
-    // per chunk slot and value head: T and A (C x C io elements each) and the decay
-    // record scale exp(G), exp(G_last - G), beta, beta exp(G) (4 C floats)
-    const size_t mats = 2 * (size_t)max_chunks * (size_t)hv * (size_t)chunk * (size_t)chunk * io_size(io_dtype);
+    // per chunk slot and value head: T and A (C x C io elements each), or W (dk x C) and M
+    // (C x C) in the absorbed form, and the decay record exp(G), exp(G_last - G), beta,
+    // beta exp(G) (4 C floats)
+    const size_t first = prefill_absorbed(io_dtype, chunk) ? (size_t)dk : (size_t)chunk;
+    const size_t mats = (size_t)max_chunks * (size_t)hv * (first + (size_t)chunk) * (size_t)chunk * io_size(io_dtype);
     const size_t recs = (size_t)max_chunks * (size_t)hv * 4 * (size_t)chunk * sizeof(float);
     w.total_bytes = w.table_bytes + mats + recs;
     return w;
@@ -118,14 +120,20 @@ int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, 
     if (num_seqs <= 0 || max_seq_chunks <= 0)
         return 0;
     const size_t es = io_size(io_dtype);
-    const size_t per_slot = (size_t)hv * 2 * chunk * chunk * es + (size_t)chunk * 2 * hqk * dk * es;
+    const size_t first = prefill_absorbed(io_dtype, chunk) ? (size_t)dk : (size_t)chunk;
+    const size_t per_slot = (size_t)hv * (first + chunk) * chunk * es + (size_t)chunk * 2 * hqk * dk * es;
     const size_t state_bytes = (size_t)num_seqs * hv * dk * dk * sizeof(float);   // dk == dv
     const size_t seg_bytes = std::max(kSegmentBytes, kStateReuse * state_bytes);
     int64_t m = (int64_t)(seg_bytes / per_slot) / num_seqs;
     m = std::max<int64_t>(m, 1);
     m = std::min<int64_t>(m, max_seq_chunks);
-    m = std::min<int64_t>(m, slot_capacity / num_seqs);
-    return (int32_t)std::max<int64_t>(m, 0);
+    // The workspace is sized for the batch's chunks, not for num_seqs full segments: when it
+    // holds fewer local chunks per sequence than a segment wants (a skewed batch, e.g. one long
+    // sequence among many short ones), segments would be cut short and multiply the launches,
+    // each mostly empty.  Take the single launch over the chunk table instead.
+    if (m > slot_capacity / num_seqs)
+        return 0;
+    return (int32_t)m;
 }
 
 }  // namespace gdn
@@ -138,7 +146,8 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape, int64_t total_tokens,
         return 0;
     if (!gdn::prefill_supported(shape->dk, shape->dv, shape->chunk, shape->io_dtype))
         return 0;
-    return gdn::prefill_workspace(shape->num_v_heads, shape->chunk, shape->io_dtype, total_tokens, num_seqs)
+    return gdn::prefill_workspace(shape->num_v_heads, shape->dk, shape->chunk, shape->io_dtype, total_tokens,
+                                  num_seqs)
         .total_bytes;
 }
 
@@ -201,7 +210,7 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
                         cu_seqlens_host[num_seqs], (long long)total_tokens);
     }
     const gdn::PrefillWorkspace ws =
-        gdn::prefill_workspace(s.num_v_heads, s.chunk, s.io_dtype, total_tokens, num_seqs);
+        gdn::prefill_workspace(s.num_v_heads, s.dk, s.chunk, s.io_dtype, total_tokens, num_seqs);
     if (ws.total_bytes == 0)
         return fail(GDN_ERR_INVALID_ARG, "batch too large for the chunk table");
     if (!workspace || workspace_bytes < ws.total_bytes)

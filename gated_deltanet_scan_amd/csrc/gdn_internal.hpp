@@ -80,8 +80,12 @@ struct SnapshotArgs {
     void *stream;
 };
 
-// Workspace layout of the prefill: [chunk table, sequence order | T matrices | A matrices |
-// decay records].
+// Whether the prefill's chunk matrices take the absorbed form (W = K^T diag(lambda) T and
+// M = A T in place of T and A): bf16 io at chunk 64.  The kernels' AbsorbedForm agrees.
+inline bool prefill_absorbed(int32_t io_dtype, int32_t chunk) { return io_dtype == 1 && chunk == 64; }
+
+// Workspace layout of the prefill: [chunk table, sequence order | T (or W) matrices |
+// A (or M) matrices | decay records].
 struct PrefillWorkspace {
     int32_t max_chunks;
     size_t table_bytes;
@@ -90,7 +94,7 @@ struct PrefillWorkspace {
 
 bool prefill_supported(int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype);
 bool decode_supported(int32_t dk, int32_t dv, int32_t io_dtype);
-PrefillWorkspace prefill_workspace(int32_t hv, int32_t chunk, int32_t io_dtype, int64_t total_tokens,
+PrefillWorkspace prefill_workspace(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype, int64_t total_tokens,
                                    int32_t num_seqs);
 // Segment length (local chunks per sequence) for a batch whose longest sequence has
 // max_seq_chunks chunks; 0 selects the single-launch global mode.

@@ -1,12 +1,16 @@
 // gdn_prefill.hip -- chunked prefill of the gated delta rule on gfx950.
 //
-// The chunkwise-parallel form (NPU page "Qwen3.5-9B -- every component on
-// the Intel NPU", section "How it works"): for one chunk of C tokens of one
-// value head, with G the cumulative sum of g inside the chunk,
-//   N   = diag(beta) [exp(G_t - G_j) k_t.k_j]_{j<t}
-//   D   = (I + N)^-1 diag(beta) (V - diag(exp G) K S0)
-//   O   = diag(exp G) Q S0 + [exp(G_t - G_j) q_t.k_j]_{j<=t} D
-//   S_T = exp(G_T) S0 + K^T diag(exp(G_T - G)) D
+// The chunkwise-parallel form of the rule (NPU page "Qwen3.5-9B -- every
+// component on the Intel NPU", section "How it works").  In this file's
+// notation, for one chunk of C tokens of one value head entering with state
+// S: G is the running sum of g inside the chunk, gamma_t = exp(G_t),
+// lambda_t = exp(G_last - G_t), Gamma = exp(G_last); T is the inverse of the
+// unit lower-triangular matrix with beta_t exp(G_t - G_j) k_t.k_j below the
+// diagonal, and A holds exp(G_t - G_j) q_t.k_j on and below it.  Then
+//   X = diag(beta) (V - diag(gamma) K S)     (what the decayed state misses)
+//   D = T X                                  (the chunk's corrected writes)
+//   O = scale (diag(gamma) Q S + A D)        (the chunk's outputs)
+//   S <- Gamma S + K^T diag(lambda) D        (the state after the chunk)
 // Everything that does not depend on the state (the Gram products, the
 // decay matrix, the inverse of I + N, the decayed query-key matrix) is done
 // for many chunks at once by the prep kernel; the scan kernel then walks the
@@ -196,12 +200,34 @@ __device__ inline typename M::frag staged_frag(const unsigned char *base, int ro
     return M::load(reinterpret_cast<const E *>(base + S::off(row, col * (int)sizeof(E))));
 }
 
+// Which form the chunk matrices take for io type E and chunk C.  Direct form
+// (fp32 io, chunk 16): T = (I + N)^-1 and A, and the scan forms D = T X.
+// Absorbed form (bf16 io, chunk 64): the products with T are taken in the
+// prep, in fp32-accurate arithmetic, as
+//   W = K^T diag(lambda) T   (dk x C)  and   M = A T   (C x C),
+// so that the scan's step is X = diag(beta)(V - diag(gamma) K S),
+// O = scale diag(gamma) Q S + M X, S <- Gamma S + W X (the same products,
+// associated differently).  With bf16 matrix-core operands this matters: the
+// columns of T alternate in sign when keys are correlated, and D = T X would
+// be rounded to bf16 as an operand before its large entries cancel in K^T D
+// and A D; W and M are those cancelled sums, formed before any rounding.
+template <typename E, int C>
+struct AbsorbedForm {
+    static constexpr bool value = sizeof(E) == 2 && C == 64;
+};
+
+template <int C, int DK, int PW, int HB, int NKEEP>
+__device__ void absorb_products(const unsigned char *Ks, const float *Tf, float *Am, const float (*Gv)[C],
+                                f32x4 (&akeep)[NKEEP][HB], int nh, int wv, int lane, bf16 *wout, bf16 *mout);
+
 // ---------------------------------------------------------------------------
 // Prep kernel.  One workgroup per (chunk slot, query/key head); writes, for
 // every value head h of the group,
 //   tmat[slot][h] = (I + N)^-1   (C x C, row-major, unit lower triangular)
 //   amat[slot][h] = scale [exp(G_t - G_j) q_t.k_j]_{j<=t}  (C x C, zero above)
-//   dec[slot][h]  = [scale exp(G) | exp(G_last - G) | beta | beta exp(G)]
+//   dec[slot][h]  = [exp(G) | exp(G_last - G) | beta | beta exp(G)]
+// or, in the absorbed form (AbsorbedForm), W = K^T diag(lambda) T (dk x C,
+// row-major) in place of T and M = A T (C x C, row-major) in place of A.
 //
 // All global reads are issued first: the chunk's q and k rows go straight
 // into LDS (direct-to-LDS loads, rows in the Swz chunk order; rows past the
@@ -239,23 +265,28 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void gdn_prep_kernel(
     typedef typename Vec16<E>::type V16;
     typedef typename MmaFor<E, DK>::type MK;
     typedef Swz<DK * ES> SK;
+    // bf16 io at chunk 64: the products with T are taken here (absorbed form, see absorb_products)
+    constexpr bool ABSORB = AbsorbedForm<E, C>::value;
     constexpr int TILE = C * DK * ES;                 // bytes of the staged q (or k) rows
     constexpr int F_BYTES = HB * C * LDF * (int)sizeof(float);
-    constexpr int U1 = 2 * TILE > F_BYTES ? 2 * TILE : F_BYTES;   // k, q rows, then T of HB heads
+    // k, q rows, then T of HB heads: over both (direct form), or over q only (absorbed form,
+    // whose products with T still read k)
+    constexpr int U1 = ABSORB ? TILE + (TILE > F_BYTES ? TILE : F_BYTES) : (2 * TILE > F_BYTES ? 2 * TILE : F_BYTES);
     constexpr int NCK = TILE / 16;                    // 16-byte chunks of a staged tile
     constexpr int NJ1 = (NCK + 63) / 64;              // 64-lane load jobs per tile
     constexpr int PW = kPrepWaves, NT = PW * kWave;
     constexpr int NJ_PER = (2 * NJ1 + PW - 1) / PW;
     static_assert(DK * ES >= 16 && DK * ES <= 256, "staged rows of 16 .. 256 bytes");
     static_assert(C <= kWave, "one lane per token of a chunk");
+    static_assert(!ABSORB || PW == RT, "absorbed form: one block column of T per wave");
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem_qk[U1];
-    __shared__ __attribute__((aligned(16))) float Nm[HB * C * LDF];
+    __shared__ __attribute__((aligned(16))) float Nm[HB * C * LDF];   // N; then A (absorbed form)
     __shared__ __attribute__((aligned(16))) float Gw[PW][HB][C];   // each wave's copy of G
     __shared__ __attribute__((aligned(16))) float Bw[PW][HB][C];   // and of beta
     const unsigned char *Ks = smem_qk;                  // staged k rows
     const unsigned char *Qs = smem_qk + TILE;           // staged q rows
-    float *Tf = reinterpret_cast<float *>(smem_qk);     // [HB][C][LDF], after the Gram products
+    float *Tf = reinterpret_cast<float *>(smem_qk + (ABSORB ? TILE : 0));   // [HB][C][LDF], after the Gram products
     __attribute__((address_space(3))) unsigned char *const lds_qk =
         (__attribute__((address_space(3))) unsigned char *)smem_qk;
 
@@ -342,7 +373,7 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void gdn_prep_kernel(
             const float Glast = __shfl(G, C - 1, kWave);
             float *rec = dec + (slot * hv + h) * 4 * C;
             const float eg = expf(G);
-            rec[lane] = scale * eg;
+            rec[lane] = eg;
             rec[C + lane] = expf(Glast - G);
             rec[2 * C + lane] = wv == 0 ? bv[0] : bv[HB - 1];
             rec[3 * C + lane] = (wv == 0 ? bv[0] : bv[HB - 1]) * eg;
@@ -357,6 +388,9 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void gdn_prep_kernel(
         // dealt to the waves round-robin at compile time, so each wave runs its own items as
         // straight-line code (the reads of one item overlap the products of the previous).
         const int r16 = lane & 15, kq = (lane >> 4) * MK::kPerLane;
+        // absorbed form: the wave's A tiles (fp32) stay in registers until T is complete
+        constexpr int NKEEP = (RT * (RT + 1) / 2 + PW - 1) / PW;
+        f32x4 akeep[NKEEP][HB];
         auto gram_items = [&](auto wc) __attribute__((always_inline)) {
           constexpr int W = decltype(wc)::value;
           static_for<RT * RT>([&](auto pc) {
@@ -400,9 +434,12 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void gdn_prep_kernel(
                         av[e] = (t < len) ? scale * ed * qk[e] : 0.f;
                     }
                     *reinterpret_cast<f32x4 *>(Nm + (hh * C + t) * LDF + j0) = nv;
-                    store4(amat + (slot * hv + h) * C * C + t * C + j0, av[0], av[1], av[2], av[3]);
+                    if constexpr (ABSORB)
+                        akeep[idx / PW][hh] = av;
+                    else
+                        store4(amat + (slot * hv + h) * C * C + t * C + j0, av[0], av[1], av[2], av[3]);
                 }
-            } else {
+            } else if constexpr (!ABSORB) {
 #pragma unroll
                 for (int hh = 0; hh < HB; ++hh)
                     if (hh < nh)
@@ -490,6 +527,13 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void gdn_prep_kernel(
             __syncthreads();
         }
 
+        if constexpr (ABSORB) {
+            absorb_products<C, DK, PW, HB, NKEEP>(Ks, Tf, Nm, Gw[wv], akeep, nh, wv, lane,
+                                                  tmat + (slot * hv + hq * group + hb) * DK * C,
+                                                  amat + (slot * hv + hq * group + hb) * C * C);
+            __syncthreads();
+            continue;
+        }
         // T to global, zero above the diagonal blocks.
         for (int idx = tid; idx < nh * C * C / VN; idx += NT) {
             const int hh = idx / (C * C / VN);
@@ -657,6 +701,127 @@ struct KtOperand<float, MC, MK, S> {
         return *reinterpret_cast<const float *>(Kb + S::off(c, 4 * Chain<MK>::row(sr, lane & 15)));
     }
 };
+
+// Round x to bf16 (hi) and the remainder to bf16 (lo): hi + lo carries about 16
+// significant bits, and products of hi/lo pairs accumulated in fp32 give sums that
+// cancel accurately.
+__device__ inline void split_bf16(float x, bf16 &hi, bf16 &lo)
+{
+    hi = (bf16)x;
+    lo = (bf16)(x - (float)hi);
+}
+
+// Absorbed form of the chunk matrices (see AbsorbedForm), run by the prep after the
+// solve: T (fp32, [HB][C][LDF]) is complete in Tf, K is still staged in Ks (Swz rows),
+// and each wave holds its A tiles (fp32) in akeep, dealt as the Gram tiles were.
+// Wave wv owns block column jb = wv of T: its fp32 values, and those of diag(lambda) T,
+// become hi/lo bf16 operand pairs, and
+//   W^T (rows t of block jb, columns i) = (diag(lambda) T)^T K      (two products per step)
+//   M^T (rows j of block jb, columns t) = T^T A^T                   (three: hi hi, hi lo, lo hi)
+// are formed transposed so that each lane stores four consecutive elements of one row
+// of W or M.  M is zero above its diagonal blocks, written as such.
+template <int C, int DK, int PW, int HB, int NKEEP>
+__device__ void absorb_products(const unsigned char *Ks, const float *Tf, float *Am, const float (*Gv)[C],
+                                f32x4 (&akeep)[NKEEP][HB], int nh, int wv, int lane, bf16 *wout, bf16 *mout)
+{
+    constexpr int LDF = C + 4, RT = C / 16, NS = C / 32;
+    typedef Mma<bf16> M;
+    typedef KtOperand<bf16, M, MmaBf16K16, Swz<DK * 2>> KT;
+    static_assert(C % 32 == 0 && DK % 16 == 0, "32-wide chunk steps, 16-row key tiles");
+    const int r16 = lane & 15, G = lane >> 4;
+
+    // A (fp32) into the N region, which the solve no longer reads; tiles above the
+    // diagonal as zeros (the deal of the Gram tiles decides which wave writes what)
+    static_for<RT * RT>([&](auto pc) {
+        constexpr int P = decltype(pc)::value;
+        constexpr int tr = P / RT, tc = P % RT;
+        constexpr bool lower = tc <= tr;
+        constexpr int idx = lower ? tr * (tr + 1) / 2 + tc : (tr * RT + tc) + 2;
+        if (idx % PW != wv)
+            return;
+        const int t = tr * 16 + r16, j0 = tc * 16 + 4 * G;
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh) {
+            if (hh >= nh)
+                break;
+            f32x4 v = zero4();
+            if constexpr (lower)
+                v = akeep[idx / PW][hh];
+            *reinterpret_cast<f32x4 *>(Am + (hh * C + t) * LDF + j0) = v;
+        }
+    });
+    __syncthreads();
+
+    const int jb = wv, j = 16 * jb + r16;
+    for (int hh = 0; hh < nh; ++hh) {
+        const float *Th = Tf + hh * C * LDF;
+        const float *Ah = Am + hh * C * LDF;
+        const float gl = Gv[hh][C - 1];
+        // column j of T (zero above the diagonal blocks) and of diag(lambda) T, contraction
+        // rows 32 s + 8 G + {0..7}, as hi/lo pairs
+        bf16x8 thi[NS], tlo[NS], lhi[NS], llo[NS];
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int m = 32 * st + 8 * G + e;
+                const float tv = ((m >> 4) >= jb) ? Th[m * LDF + j] : 0.f;
+                const float lv = tv * expf(gl - Gv[hh][m]);
+                bf16 h0, l0, h1, l1;
+                split_bf16(tv, h0, l0);
+                split_bf16(lv, h1, l1);
+                thi[st][e] = h0;
+                tlo[st][e] = l0;
+                lhi[st][e] = h1;
+                llo[st][e] = l1;
+            }
+        }
+        // W^T tiles (rows t of block jb, columns i of key block it): lane stores
+        // W[16 it + l % 16][16 jb + 4 G .. + 3]
+        bf16 *wh = wout + (size_t)hh * DK * C;
+#pragma unroll
+        for (int it = 0; it < DK / 16; ++it) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int st = 0; st < NS; ++st) {
+                const bf16x8 kf = KT::load(Ks, it, st, lane);
+                acc = M::mma(lhi[st], kf, acc);
+                acc = M::mma(llo[st], kf, acc);
+            }
+            store4(wh + (16 * it + r16) * C + 16 * jb + 4 * G, acc[0], acc[1], acc[2], acc[3]);
+        }
+        // M^T tiles (rows j of block jb, columns t of block tt): lane stores
+        // M[16 tt + l % 16][16 jb + 4 G .. + 3]; zero for tt < jb
+        bf16 *mh = mout + (size_t)hh * C * C;
+#pragma unroll
+        for (int tt = 0; tt < RT; ++tt) {
+            f32x4 acc = zero4();
+            if (tt >= jb) {
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    const float *ar = Ah + (16 * tt + r16) * LDF + 32 * st + 8 * G;
+                    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(ar);
+                    const f32x4 a1 = *reinterpret_cast<const f32x4 *>(ar + 4);
+                    bf16x8 ahi, alo;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        bf16 h, l;
+                        split_bf16(a0[e], h, l);
+                        ahi[e] = h;
+                        alo[e] = l;
+                        split_bf16(a1[e], h, l);
+                        ahi[e + 4] = h;
+                        alo[e + 4] = l;
+                    }
+                    acc = M::mma(thi[st], ahi, acc);
+                    acc = M::mma(thi[st], alo, acc);
+                    acc = M::mma(tlo[st], ahi, acc);
+                }
+            }
+            store4(mh + (16 * tt + r16) * C + 16 * jb + 4 * G, acc[0], acc[1], acc[2], acc[3]);
+        }
+    }
+}
 
 __device__ inline void wave_lds_sync()
 {
@@ -889,7 +1054,6 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
-    const float inv_scale = 1.f / scale;
 
     // ---- one chunk step of this wave's 16 columns on stage buffer BUF ----
     // Operand fragments are read from LDS one group of products ahead of their
@@ -898,7 +1062,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_kernel(
     E *os = Os[w];
     auto step = [&](auto bufc, int64_t t0, int len) __attribute__((always_inline)) {
         const unsigned char *stg = stage_mem + decltype(bufc)::value * STAGE;
-        const float *Gs = reinterpret_cast<const float *>(stg + OFF_D);   // scale exp(G)
+        const float *Gs = reinterpret_cast<const float *>(stg + OFF_D);   // exp(G)
         const float *Lam = Gs + C;                                         // exp(G_last - G)
         const float *Bet = Gs + 2 * C;                                     // beta
         const float *BGam = Gs + 3 * C;                                    // beta exp(G)
@@ -1008,7 +1172,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_kernel(
             lb[st] = CC::b_frag(dacc, st);
 
         // S <- exp(G_last) S + K^T (diag(lambda) D)
-        const float gl = Gs[C - 1] * inv_scale;   // exp(G_last): G is flat past the last real token
+        const float gl = Gs[C - 1];   // exp(G_last): G is flat past the last real token
 #pragma unroll
         for (int sr = 0; sr < SR; ++sr) {
             sacc[sr] = sacc[sr] * gl;
@@ -1025,7 +1189,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_kernel(
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                qacc[rt][i] *= Gs[16 * rt + g4 + i];
+                qacc[rt][i] *= scale * Gs[16 * rt + g4 + i];
 #pragma unroll
         for (int st = 0; st < NSC; ++st)
 #pragma unroll
@@ -1110,7 +1274,7 @@ template <typename E, int C, int DK, int DVS, int NSTAGE>
 __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v, const int32_t *__restrict__ cu,
     SlotMap map, int32_t num_seqs, int64_t total_tokens, int32_t hqk, int32_t hv, int32_t dv,
-    const E *__restrict__ tmat, const E *__restrict__ amat, const float *__restrict__ dec, const float *state_in,
+    const E *__restrict__ wmat, const E *__restrict__ mmat, const float *__restrict__ dec, const float *state_in,
     float *state_out, E *__restrict__ o, float scale)
 {
     constexpr int ES = (int)sizeof(E);
@@ -1121,48 +1285,45 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     constexpr int SR_PER = (SR + kWaves - 1) / kWaves;
     constexpr int RT_PER = (RT + kWaves - 1) / kWaves;
     constexpr int VN = Vec16<E>::n;
-    typedef typename Vec16<E>::type V16;
     typedef typename MmaFor<E, C>::type MC;
     typedef typename MmaFor<E, DK>::type MK;
     typedef Swz<DK * ES> SK;
     typedef Swz<C * ES> SC;
     typedef Swz<DVS * ES> SV;
-    typedef KtOperand<E, MC, MmaBf16K16, SK> KT;   // natural row order of the key index
     static_assert(C <= kWave, "one lane per token of a chunk");
     static_assert(DVS % 16 == 0 && DK % 16 == 0 && C % 16 == 0, "16x16 tiles");
 
-    // stage buffer layout (bytes) and the 1 KB direct-to-LDS load jobs that fill it
+    // stage buffer layout (bytes) and the 1 KB direct-to-LDS load jobs that fill it:
+    // Q, K (C x DK), W (DK x C), M (C x C), the V slice (C x DVS) and the decay record
     constexpr int OFF_Q = 0;
     constexpr int OFF_K = OFF_Q + C * DK * ES;
-    constexpr int OFF_T = OFF_K + C * DK * ES;
-    constexpr int OFF_A = OFF_T + C * C * ES;
-    constexpr int OFF_V = OFF_A + C * C * ES;
+    constexpr int OFF_W = OFF_K + C * DK * ES;
+    constexpr int OFF_M = OFF_W + DK * C * ES;
+    constexpr int OFF_V = OFF_M + C * C * ES;
     constexpr int OFF_D = OFF_V + C * DVS * ES;
     constexpr int STAGE = OFF_D + 4 * C * 4;
     constexpr int NCK_QK = C * DK * ES / 16;   // 16-byte chunks per tile
-    constexpr int NCK_TA = C * C * ES / 16;
+    constexpr int NCK_W = DK * C * ES / 16;
+    constexpr int NCK_M = C * C * ES / 16;
     constexpr int NCK_V = C * DVS * ES / 16;
     constexpr int NCK_D = 4 * C * 4 / 16;
     constexpr int NJ_QK = (NCK_QK + 63) / 64;
-    constexpr int NJ_TA = (NCK_TA + 63) / 64;
+    constexpr int NJ_W = (NCK_W + 63) / 64;
+    constexpr int NJ_M = (NCK_M + 63) / 64;
     constexpr int NJ_V = (NCK_V + 63) / 64;
     constexpr int NJ_D = (NCK_D + 63) / 64;
-    constexpr int J_T = 2 * NJ_QK, J_V = J_T + 2 * NJ_TA, J_D = J_V + NJ_V;
+    constexpr int J_W = 2 * NJ_QK, J_M = J_W + NJ_W, J_V = J_M + NJ_M, J_D = J_V + NJ_V;
     constexpr int NJ = J_D + NJ_D;
     static_assert(STAGE % 16 == 0 && OFF_D % 16 == 0, "16-byte aligned stage blocks");
+    static_assert(AbsorbedForm<E, C>::value, "the row-split scan reads the absorbed form");
 
     // NSTAGE stage buffers: the loaders fill chunk c + NSTAGE - 1 while the compute waves
-    // work on chunk c.  With three, D and diag(lambda) D of a step live in the step's own
-    // Q region: they are written after B1, when that tile is dead (only P1 reads it), and
-    // the three buffers would not fit beside arrays of their own.
+    // work on chunk c
     static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three stage buffers");
-    constexpr bool kDInQ = NSTAGE == 3;
-    static_assert(!kDInQ || 2 * DVS * LDC * ES <= C * DK * ES, "D and lambda D must fit the Q region");
-    static_assert(NSTAGE * STAGE + DVS * LDC * ES + (kDInQ ? 16 : 2 * DVS * LDC * ES) + DVS * LDK * ES <= 163840,
+    static_assert(NSTAGE * STAGE + DVS * LDC * ES + DVS * LDK * ES <= 163840,
                   "stage buffers and exchange tiles must fit the 160 KB of LDS");
     __shared__ __attribute__((aligned(1024))) unsigned char stage_mem[NSTAGE * STAGE];
     __shared__ __attribute__((aligned(16))) E Xt[DVS * LDC];
-    __shared__ __attribute__((aligned(16))) E DLt_own[kDInQ ? 16 / ES : 2 * DVS * LDC];
     __shared__ __attribute__((aligned(16))) E St[DVS * LDK];
 
     // the stage buffers as LDS addresses (the direct loads write LDS by address)
@@ -1199,7 +1360,6 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         return;
     }
 
-    const float inv_scale = 1.f / scale;
 
     // ---- state slice into accumulators (compute wave w owns key-row tiles w, w+4, ...) ----
     f32x4 sacc[SR_PER][CT];
@@ -1232,7 +1392,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     const size_t slot_begin = slot_of(map, n, c_begin);   // chunk c sits in slot slot_begin + c - c_begin
     auto job_row = [&](auto jc) __attribute__((always_inline)) -> int {   // source row of this lane
         constexpr int J = decltype(jc)::value;
-        if constexpr (J < J_T)
+        if constexpr (J < J_W)
             return min((J % NJ_QK) * 64 + lane, NCK_QK - 1) / (DK * ES / 16);
         else if constexpr (J >= J_V && J < J_D)
             return min((J - J_V) * 64 + lane, NCK_V - 1) / (DVS * ES / 16);
@@ -1242,12 +1402,14 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     // element offset of this lane's 16 bytes from the tile's origin, given its source row
     auto job_off = [&](auto jc, int row) __attribute__((always_inline)) -> int {
         constexpr int J = decltype(jc)::value;
-        if constexpr (J < J_T) {
+        if constexpr (J < J_W) {
             const int P = min((J % NJ_QK) * 64 + lane, NCK_QK - 1);
             const int r = P / (DK * ES / 16), pos = P % (DK * ES / 16);
             return row * qk_row + (pos ^ SK::perm(r)) * VN;
-        } else if constexpr (J < J_V) {
-            const int P = min(((J - J_T) % NJ_TA) * 64 + lane, NCK_TA - 1);
+        } else if constexpr (J < J_V) {   // W or M: rows of C elements
+            constexpr int NCK_X = J < J_M ? NCK_W : NCK_M;
+            constexpr int IDX = J < J_M ? J - J_W : J - J_M;
+            const int P = min(IDX * 64 + lane, NCK_X - 1);
             const int r = P / (C * ES / 16), pos = P % (C * ES / 16);
             return r * C + (pos ^ SC::perm(r)) * VN;
         } else if constexpr (J < J_D) {
@@ -1268,8 +1430,8 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         const E *qb = q + ((size_t)t0 * hqk + hq) * DK;
         const E *kb = k + ((size_t)t0 * hqk + hq) * DK;
         const E *vb = v + ((size_t)t0 * hv + h) * dv + (size_t)s * DVS;
-        const E *tb = tmat + (slot * hv + h) * C * C;
-        const E *ab = amat + (slot * hv + h) * C * C;
+        const E *wb = wmat + (slot * hv + h) * DK * C;
+        const E *mb = mmat + (slot * hv + h) * C * C;
         const E *db = reinterpret_cast<const E *>(dec + (slot * hv + h) * 4 * C);
         static_for<NJ_PER>([&](auto uc) {
             constexpr int J = W + decltype(uc)::value * kWaves;
@@ -1277,10 +1439,10 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
                 constexpr std::integral_constant<int, J> jc{};
                 const E *base;
                 int off = job_off(jc, min(job_row(jc), last));
-                if constexpr (J < J_T)
+                if constexpr (J < J_W)
                     base = J >= NJ_QK ? kb : qb;
                 else if constexpr (J < J_V)
-                    base = (J - J_T) >= NJ_TA ? ab : tb;
+                    base = J >= J_M ? mb : wb;
                 else if constexpr (J < J_D)
                     base = vb;
                 else {
@@ -1288,12 +1450,12 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
                     off *= (int)(sizeof(float) / sizeof(E));
                 }
                 // lanes of the job that carry data, and the job's block in the stage
-                constexpr int NCK = J < J_T ? NCK_QK : J < J_V ? NCK_TA : J < J_D ? NCK_V : NCK_D;
-                constexpr int IDX = J < J_T ? J % NJ_QK : J < J_V ? (J - J_T) % NJ_TA : J < J_D ? J - J_V : J - J_D;
+                constexpr int NCK = J < J_W ? NCK_QK : J < J_M ? NCK_W : J < J_V ? NCK_M : J < J_D ? NCK_V : NCK_D;
+                constexpr int IDX = J < J_W ? J % NJ_QK : J < J_M ? J - J_W : J < J_V ? J - J_M
+                                  : J < J_D ? J - J_V : J - J_D;
                 constexpr int NL = NCK - IDX * 64 < 64 ? NCK - IDX * 64 : 64;
-                constexpr int BLK = (J < J_T ? (J >= NJ_QK ? OFF_K : OFF_Q)
-                                             : J < J_V ? ((J - J_T) >= NJ_TA ? OFF_A : OFF_T)
-                                                       : J < J_D ? OFF_V : OFF_D) + IDX * 1024;
+                constexpr int BLK = (J < J_W ? (J >= NJ_QK ? OFF_K : OFF_Q)
+                                             : J < J_M ? OFF_W : J < J_V ? OFF_M : J < J_D ? OFF_V : OFF_D) + IDX * 1024;
                 if (NL == 64 || lane < NL)
                     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
                                                      (__attribute__((address_space(3))) void *)(stg + BLK), 16, 0, 0);
@@ -1308,13 +1470,10 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         default: fn(std::integral_constant<int, 3>{}); break;
         }
     };
-    // ---- compute waves: one chunk step on stage buffer `cur` (barriers B1 and B2 inside) ----
+    // ---- compute waves: one chunk step on stage buffer `cur` (barrier B1 inside) ----
     auto step = [&](int cur, int64_t t0, int len) __attribute__((always_inline)) {
         const unsigned char *stg = stage_mem + cur * STAGE;
-        E *const Dt = kDInQ ? reinterpret_cast<E *>(stage_mem + cur * STAGE + OFF_Q) : DLt_own;
-        E *const LDt = Dt + DVS * LDC;
-        const float *Gs = reinterpret_cast<const float *>(stg + OFF_D);   // scale exp(G)
-        const float *Lam = Gs + C;                                         // exp(G_last - G)
+        const float *Gs = reinterpret_cast<const float *>(stg + OFF_D);   // exp(G)
         const float *Bet = Gs + 2 * C;                                     // beta
         const float *BGam = Gs + 3 * C;                                    // beta exp(G)
 
@@ -1352,7 +1511,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
                         const int rr = rt * 16 + tile_row(lane, i);
                         const E vv = *reinterpret_cast<const E *>(stg + OFF_V + SV::off(rr, col * ES));
                         x[i] = Bet[rr] * to_f32(vv) - BGam[rr] * kacc[u][ct][i];
-                        oacc[u][ct][i] *= Gs[rt * 16 + (lane & 15)];
+                        oacc[u][ct][i] *= scale * Gs[rt * 16 + (lane & 15)];
                     }
                     store4(Xt + col * LDC + rt * 16 + tile_row(lane, 0), x[0], x[1], x[2], x[3]);
                 }
@@ -1360,38 +1519,9 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         }
         __syncthreads();   // B1
 
-        // P2: D = T X -> Dt and (diag(lambda) D) -> LDt, both transposed
-#pragma unroll
-        for (int u = 0; u < RT_PER; ++u) {
-            const int rt = wave + u * kWaves;
-            if (rt < RT) {
-                f32x4 dacc[CT];
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-                    dacc[ct] = zero4();
-                const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
-#pragma unroll
-                for (int k0 = 0; k0 < C; k0 += MC::kStep) {
-                    const auto at = staged_frag<MC, SC, E>(stg + OFF_T, rt * 16 + r, k0 + kk);
-#pragma unroll
-                    for (int ct = 0; ct < CT; ++ct)
-                        dacc[ct] = MC::mma(at, MC::load(Xt + (ct * 16 + r) * LDC + k0 + kk), dacc[ct]);
-                }
-                const int r0 = rt * 16 + tile_row(lane, 0);
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct) {
-                    const int col = ct * 16 + tile_col(lane);
-                    store4(Dt + col * LDC + r0, dacc[ct][0], dacc[ct][1], dacc[ct][2], dacc[ct][3]);
-                    store4(LDt + col * LDC + r0, Lam[r0] * dacc[ct][0], Lam[r0 + 1] * dacc[ct][1],
-                           Lam[r0 + 2] * dacc[ct][2], Lam[r0 + 3] * dacc[ct][3]);
-                }
-            }
-        }
-        __syncthreads();   // B2
-
-        // P3: O = scale diag(exp G) Q S + (scale A) D, computed transposed (O^T = (Q S)^T
-        //     + D^T A^T, the same fragments with the operand roles swapped) so that each lane
-        //     holds four consecutive output columns of one token and stores them at once
+        // P3: O = scale diag(exp G) Q S + M X, computed transposed (O^T = (Q S)^T + X^T M^T,
+        //     the same fragments with the operand roles swapped) so that each lane holds four
+        //     consecutive output columns of one token and stores them at once
 #pragma unroll
         for (int u = 0; u < RT_PER; ++u) {
             const int rt = wave + u * kWaves;
@@ -1399,10 +1529,10 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
                 const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
 #pragma unroll
                 for (int k0 = 0; k0 < C; k0 += MC::kStep) {
-                    const auto aa = staged_frag<MC, SC, E>(stg + OFF_A, rt * 16 + r, k0 + kk);
+                    const auto am = staged_frag<MC, SC, E>(stg + OFF_M, rt * 16 + r, k0 + kk);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
-                        oacc[u][ct] = MC::mma(MC::load(Dt + (ct * 16 + r) * LDC + k0 + kk), aa, oacc[u][ct]);
+                        oacc[u][ct] = MC::mma(MC::load(Xt + (ct * 16 + r) * LDC + k0 + kk), am, oacc[u][ct]);
                 }
                 // O^T tile: lane = token rt * 16 + l % 16, four consecutive output columns
                 const int tok = rt * 16 + (lane & 15);
@@ -1414,8 +1544,8 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
                 }
             }
         }
-        // P4: S <- exp(G_last) S + K^T diag(lambda) D; refresh the transposed copy
-        const float gl = Gs[C - 1] * inv_scale;   // exp(G_last): G is flat past the last real token
+        // P4: S <- exp(G_last) S + W X; refresh the transposed copy
+        const float gl = Gs[C - 1];   // exp(G_last): G is flat past the last real token
 #pragma unroll
         for (int u = 0; u < SR_PER; ++u) {
             const int sr = wave + u * kWaves;
@@ -1426,10 +1556,10 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
                 const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
 #pragma unroll
                 for (int k0 = 0; k0 < C; k0 += MC::kStep) {
-                    const typename MC::frag akt = KT::load(stg + OFF_K, sr, k0 / MC::kStep, lane);
+                    const auto aw = staged_frag<MC, SC, E>(stg + OFF_W, sr * 16 + r, k0 + kk);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
-                        sacc[u][ct] = MC::mma(akt, MC::load(LDt + (ct * 16 + r) * LDC + k0 + kk), sacc[u][ct]);
+                        sacc[u][ct] = MC::mma(aw, MC::load(Xt + (ct * 16 + r) * LDC + k0 + kk), sacc[u][ct]);
                 }
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
@@ -1472,8 +1602,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         if (loader) {
             if (c + AHEAD < c_end)
                 by_loader([&](auto wc) { issue_jobs(wc, c + AHEAD); });
-            // B1 and B2 of the compute waves: the loaders publish nothing there
-            __builtin_amdgcn_s_barrier();
+            // B1 of the compute waves: the loaders publish nothing there
             __builtin_amdgcn_s_barrier();
             if (AHEAD == 2 && c + 2 < c_end)
                 by_loader([&](auto wc) { wait_all_but_one_chunk(wc); });
@@ -1504,9 +1633,9 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Scan kernel for bf16 io and chunk 64 (the Qwen3.5 shapes): the same chunk
-// step as gdn_chunk_scan_kernel above, with the chunk's matrix operands staged
-// in FRAGMENT ORDER.  Every operand tile is a sequence of 1 KB units of 16
+// Scan kernel for bf16 io and chunk 64 (the Qwen3.5 shapes): the chunk step
+// of the absorbed form (see AbsorbedForm), with the chunk's matrix operands
+// staged in FRAGMENT ORDER.  Every operand tile is a sequence of 1 KB units of 16
 // rows x 32 contraction indices; in a unit, the 16 bytes at position p belong
 // to matrix-core lane m(p): row m % 16 of the unit's rows, contraction indices
 // 8 (m / 16) .. +7.  One direct-to-LDS load fills one unit (lane i of the load
@@ -1514,23 +1643,21 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
 // gives lane l its operand fragment: neither side computes addresses beyond a
 // per-lane constant and instruction offsets, and a unit read is a 1 KB read in
 // lane order, the fastest LDS read pattern measured (see Swz).
-//   Q, A units (rt, kb): rows 16 rt + r (natural order), m(p) = p.
-//   T units (rt, kb):    rows Chain row(rt, r), m(p) = p.
+//   Q, M units (rt, kb): rows 16 rt + r (natural order), m(p) = p.
+//   W units (sr, kb):    key rows Chain row(sr, r), chunk rows 32 kb + 8 (p / 16)
+//                        .. +7, m(p) = p (W replaces T: absorbed form).
 //   K units (rt, kb):    rows Chain row(rt, r); m(p) = r + 16 g with g = p / 16,
-//                        r = (p % 16) ^ 4 g, which puts both the fragment read
-//                        and the transpose read of K^T on distinct bank groups
-//                        of the plain modulo model (measured: the fragment
-//                        read at about half its lane-order rate, the
-//                        transpose read at two thirds of it; see Swz).
+//                        r = (p % 16) ^ 4 g (measured: the fragment read at
+//                        about half its lane-order rate; see Swz).
 //   V (the dv slice):    row-major; the 16-byte chunks of a row are permuted
 //                        (XOR with 2 (r % 4) for 256-byte rows, 2 ((r / 2) % 2)
 //                        for 128-byte rows), which spreads the transpose read
 //                        of 4 consecutive rows of one column block over the
 //                        banks (without it that read runs 3x slower).
-//   decay record:        [scale exp(G) | exp(G_last - G) | beta | beta exp(G)].
+//   decay record:        [exp(G) | exp(G_last - G) | beta | beta exp(G)].
 // Each wave owns CT tiles of 16 state columns: every operand fragment read
 // from LDS then feeds CT matrix instructions.  The output is computed
-// transposed (O^T = (Q S)^T ... with S^T and D^T as the A operands, whose
+// transposed (O^T = (Q S)^T ... with S^T and X^T as the A operands, whose
 // registers are the B fragments as they stand), so that each lane holds 4
 // consecutive columns of one token row and stores them as one 8-byte write.
 // ---------------------------------------------------------------------------
@@ -1538,7 +1665,7 @@ template <int DK, int NW, int CT>
 __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const int32_t *__restrict__ cu, SlotMap map, int32_t num_seqs, int64_t total_tokens, int32_t hqk, int32_t hv,
-    int32_t dv, const bf16 *__restrict__ tmat, const bf16 *__restrict__ amat, const float *__restrict__ dec,
+    int32_t dv, const bf16 *__restrict__ wmat, const bf16 *__restrict__ mmat, const float *__restrict__ dec,
     const float *state_in, float *state_out, bf16 *__restrict__ o, float scale)
 {
     constexpr int C = 64;
@@ -1552,14 +1679,14 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
     static_assert(DK % 32 == 0, "32-wide contraction steps");
 
     // stage layout (bytes): 1 KB units
-    constexpr int NU_QK = RT * NSK, NU_TA = RT * NSC;
+    constexpr int NU_QK = RT * NSK, NU_W = SR * NSC, NU_M = RT * NSC;
     constexpr int VRB = DVS * 2;                   // bytes per row of the V slice
     constexpr int NU_V = C * VRB / 1024;
     constexpr int OFF_Q = 0;
     constexpr int OFF_K = OFF_Q + NU_QK * 1024;
-    constexpr int OFF_T = OFF_K + NU_QK * 1024;
-    constexpr int OFF_A = OFF_T + NU_TA * 1024;
-    constexpr int OFF_V = OFF_A + NU_TA * 1024;
+    constexpr int OFF_W = OFF_K + NU_QK * 1024;
+    constexpr int OFF_M = OFF_W + NU_W * 1024;
+    constexpr int OFF_V = OFF_M + NU_M * 1024;
     constexpr int OFF_D = OFF_V + NU_V * 1024;
     constexpr int STAGE = OFF_D + 1024;
     static_assert(C * VRB % 1024 == 0 && 4 * C * 4 == 1024, "whole units");
@@ -1637,10 +1764,10 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
     // The stage is filled in rounds of NW units: in round R every wave loads one unit of
     // the same tile (unit (R - first round of the tile) NW + w), so all waves run the same
     // code and each lane's source offsets are computed once.  Rounds: Q, K, T, A, the V
-    // slice, then the decay record (wave 0 only).
-    constexpr int R_Q = NU_QK / NW, R_T = NU_TA / NW, R_V = NU_V / NW;
-    static_assert(NU_QK % NW == 0 && NU_TA % NW == 0 && NU_V % NW == 0, "whole rounds");
-    constexpr int RK0 = R_Q, RT0 = 2 * R_Q, RA0 = RT0 + R_T, RV0 = RA0 + R_T, RD0 = RV0 + R_V;
+    // slice, then the decay record (wave 0 only).  (RT0 and RA0 begin the W and M rounds.)
+    constexpr int R_Q = NU_QK / NW, R_W = NU_W / NW, R_M = NU_M / NW, R_V = NU_V / NW;
+    static_assert(NU_QK % NW == 0 && NU_W % NW == 0 && NU_M % NW == 0 && NU_V % NW == 0, "whole rounds");
+    constexpr int RK0 = R_Q, RT0 = 2 * R_Q, RA0 = RT0 + R_W, RV0 = RA0 + R_M, RD0 = RV0 + R_V;
     constexpr int NR = RD0 + 1;
     const int qk_row = hqk * DK, v_row = hv * dv;
     // (row in the chunk, element column, stage offset of the unit) of this lane's 16
@@ -1653,12 +1780,12 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
             row = R < RK0 ? 16 * rt + r16 : CH::row(rt, r16 ^ g4);
             ecol = 32 * kb + 8 * G;
             blk = (R < RK0 ? OFF_Q : OFF_K) + u * 1024;
-        } else if constexpr (R < RV0) {                // T or A unit (rt, kb)
+        } else if constexpr (R < RV0) {                // W unit (sr, kb) or M unit (rt, kb)
             const int u = (R < RA0 ? R - RT0 : R - RA0) * NW + w;
             const int rt = u / NSC, kb = u % NSC;
             row = R < RA0 ? CH::row(rt, r16) : 16 * rt + r16;
             ecol = 32 * kb + 8 * G;
-            blk = (R < RA0 ? OFF_T : OFF_A) + u * 1024;
+            blk = (R < RA0 ? OFF_W : OFF_M) + u * 1024;
         } else if constexpr (R < RD0) {                // 1 KB of rows of the V slice
             const int u = (R - RV0) * NW + w;
             const int P = u * 64 + lane;                  // physical 16-byte chunk
@@ -1707,8 +1834,8 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
         const char *qb = reinterpret_cast<const char *>(q + ((size_t)t0 * hqk + hq) * DK);
         const char *kb = reinterpret_cast<const char *>(k + ((size_t)t0 * hqk + hq) * DK);
         const char *vb = reinterpret_cast<const char *>(v + ((size_t)t0 * hv + h) * dv + (size_t)s * DVS);
-        const char *tb = reinterpret_cast<const char *>(tmat + (slot * hv + h) * C * C);
-        const char *ab = reinterpret_cast<const char *>(amat + (slot * hv + h) * C * C);
+        const char *tb = reinterpret_cast<const char *>(wmat + (slot * hv + h) * DK * C);
+        const char *ab = reinterpret_cast<const char *>(mmat + (slot * hv + h) * C * C);
         const char *db = reinterpret_cast<const char *>(dec + (slot * hv + h) * 4 * C);
         const bool full = last == C - 1;
         static_for<NR>([&](auto rc) __attribute__((always_inline)) {
@@ -1746,13 +1873,11 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
-    const float inv_scale = 1.f / scale;
 
     // per-lane LDS byte offsets (everything else is an instruction offset)
     const int lin = 16 * lane;                                   // Q, T, A units
     const int kperm = 16 * (16 * G + (r16 ^ g4));                 // K units, fragment read
     const int e = (lane >> 2) & 3, qd = lane & 3;
-    const int ktr = 16 * (16 * qd + 4 * (G ^ qd) + e);            // K units, transpose read
     // V slice, transpose read of column block ct of this wave: rows 8 G + e (+ the
     // tile's first row), logical chunk 2 (CT w + ct) + qd / 2, physical = logical ^ X(row)
     auto vtr = [&](int ct) __attribute__((always_inline)) -> int {
@@ -1812,16 +1937,8 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
         }
 
         stage_hook(std::integral_constant<int, 1>{});
-        // T fragments, then X = beta v - beta exp(G) (K S)
-        bf16x8 ft[NSC][RT];
-#pragma unroll
-        for (int st = 0; st < NSC; ++st)
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                ft[st][rt] = frag(OFF_T + (rt * NSC + st) * 1024 + lin);
-        __builtin_amdgcn_sched_barrier(0);
-        // beta v on this lane's rows CH::row(rt, g4 + i) (the bit cast is of the whole
-        // vector: a bit cast of one element of a vector reads element 0)
+        // X = beta v - beta exp(G) (K S) on this lane's rows CH::row(rt, g4 + i) (the bit
+        // cast is of the whole vector: a bit cast of one element of a vector reads element 0)
         bf16x8 xb[NSC][CT];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
@@ -1836,88 +1953,47 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
             for (int st = 0; st < NSC; ++st)
                 xb[st][ct] = CH::b_frag(t, st);
         }
-
-        // D = T X
-        f32x4 dacc[RT][CT];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-                dacc[rt][ct] = zero4();
-#pragma unroll
-        for (int st = 0; st < NSC; ++st)
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < CT; ++ct)
-                    dacc[rt][ct] = M::mma(ft[st][rt], xb[st][ct], dacc[rt][ct]);
         __builtin_amdgcn_sched_barrier(0);
 
-
         stage_hook(std::integral_constant<int, 2>{});
-        bf16x8 db[NSC][CT], lb[NSC][CT];
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            f32x4 t[RT];
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                t[rt] = dacc[rt][ct];
+        // S <- exp(G_last) S + W X.  W fragments: key rows CH::row(sr, .), chunk rows
+        // 32 st + 8 G + {0..7}, read one key tile ahead of their products.
+        auto load_w = [&](int sr, bf16x8 (&f)[NSC]) __attribute__((always_inline)) {
 #pragma unroll
             for (int st = 0; st < NSC; ++st)
-                db[st][ct] = CH::b_frag(t, st);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                t[rt] *= rec4(1, CH::row(rt, g4));
-#pragma unroll
-            for (int st = 0; st < NSC; ++st)
-                lb[st][ct] = CH::b_frag(t, st);
-        }
-
-        // S <- exp(G_last) S + K^T (diag(lambda) D).  K^T fragments: rows CH::row(sr, .) of
-        // the key index, chunk rows 32 st + 8 G + {0..7} (units rt = 2 st and 2 st + 1),
-        // read one key tile ahead of their products.
-        auto load_kt = [&](int sr, bf16x8 (&f)[NSC]) __attribute__((always_inline)) {
-#pragma unroll
-            for (int st = 0; st < NSC; ++st) {
-                const int base = OFF_K + (sr >> 1) * 1024 + ktr + 8 * (sr & 1);
-                const s16x4 lo = tr4(base + (2 * st) * NSK * 1024);
-                const s16x4 hi = tr4(base + (2 * st + 1) * NSK * 1024);
-                typedef short s16x8 __attribute__((ext_vector_type(8)));
-                const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                f[st] = __builtin_bit_cast(bf16x8, vv);
-            }
+                f[st] = frag(OFF_W + (sr * NSC + st) * 1024 + lin);
         };
-        const float gl = *reinterpret_cast<const float *>(stg + OFF_D + 4 * (C - 1)) * inv_scale;
-        bf16x8 fkt[2][NSC];
-        load_kt(0, fkt[0]);
+        const float gl = *reinterpret_cast<const float *>(stg + OFF_D + 4 * (C - 1));
+        bf16x8 fw[2][NSC];
+        load_w(0, fw[0]);
 #pragma unroll
         for (int sr = 0; sr < SR; ++sr) {
             if (sr + 1 < SR)
-                load_kt(sr + 1, fkt[(sr + 1) & 1]);
+                load_w(sr + 1, fw[(sr + 1) & 1]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 sacc[sr][ct] = sacc[sr][ct] * gl;
 #pragma unroll
                 for (int st = 0; st < NSC; ++st)
-                    sacc[sr][ct] = M::mma(fkt[sr & 1][st], lb[st][ct], sacc[sr][ct]);
+                    sacc[sr][ct] = M::mma(fw[sr & 1][st], xb[st][ct], sacc[sr][ct]);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         stage_hook(std::integral_constant<int, 3>{});
-        // A fragments (A carries the output scale)
-        bf16x8 fa[NSC][RT];
+        // M fragments (M carries the output scale)
+        bf16x8 fm[NSC][RT];
 #pragma unroll
         for (int st = 0; st < NSC; ++st)
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt)
-                fa[st][rt] = frag(OFF_A + (rt * NSC + st) * 1024 + lin);
+                fm[st][rt] = frag(OFF_M + (rt * NSC + st) * 1024 + lin);
 
-        // O^T = scale (Q S)^T diag(exp G) + D^T (scale A)^T: lane l holds token row
-        // 16 rt + l % 16 and the four columns 16 ct + 4 (l / 16) .. +3 of this wave's
+        // O^T = scale (Q S)^T diag(exp G) + X^T M^T: lane l holds token row 16 rt + l % 16
+        // and the four columns 16 ct + 4 (l / 16) .. +3 of this wave's
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-            const float gs = *reinterpret_cast<const float *>(stg + OFF_D + 4 * (16 * rt + r16));
+            const float gs = scale * *reinterpret_cast<const float *>(stg + OFF_D + 4 * (16 * rt + r16));
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
                 qacc[rt][ct] *= gs;
@@ -1928,7 +2004,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
             for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct)
-                    qacc[rt][ct] = M::mma(db[st][ct], fa[st][rt], qacc[rt][ct]);
+                    qacc[rt][ct] = M::mma(xb[st][ct], fm[st][rt], qacc[rt][ct]);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const int r = 16 * rt + r16;
@@ -1983,17 +2059,6 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
 // Launch.
 // ---------------------------------------------------------------------------
 
-// Waves per scan workgroup (16 state columns each): four (64 columns) for bf16
-// io, two when dv = 32 and for fp32 io (whose two stage buffers then still
-// fit in LDS).
-template <typename E>
-static int pick_waves(int dv)
-{
-    if (sizeof(E) == 2 && dv % 64 == 0)
-        return 4;
-    return 2;
-}
-
 template <typename E, int C, int DK, int NW>
 static void launch_scan(const PrefillArgs &p, const SlotMap &map, const E *tmat, const E *amat, const float *dec,
                         const float *sin, float *sout, hipStream_t st)
@@ -2001,7 +2066,7 @@ static void launch_scan(const PrefillArgs &p, const SlotMap &map, const E *tmat,
     const int nv = p.dv / (16 * NW);
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
     const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
-    const ProfEvents ev = prof_events(PROF_SCAN);
+    const ProfEvents ev = prof_events(PROF_SCAN, PROF_SCAN_PLAIN);
     hipExtLaunchKernelGGL((gdn_chunk_scan_kernel<E, C, DK, NW>), dim3((unsigned)blocks), dim3(NW * kWave), 0, st,
                           ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k),
                           static_cast<const E *>(p.v), p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv,
@@ -2009,34 +2074,34 @@ static void launch_scan(const PrefillArgs &p, const SlotMap &map, const E *tmat,
 }
 
 template <int DK, int DVS>
-static void launch_scan_rows(const PrefillArgs &p, const SlotMap &map, const bf16 *tmat, const bf16 *amat,
+static void launch_scan_rows(const PrefillArgs &p, const SlotMap &map, const bf16 *wmat, const bf16 *mmat,
                              const float *dec, const float *sin, float *sout, hipStream_t st)
 {
     const int nv = p.dv / DVS;
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
     const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
-    const ProfEvents ev = prof_events(PROF_SCAN);
-    // three stage buffers where one workgroup per CU is the occupancy anyway (dk = 128)
-    constexpr int NSTAGE = DK >= 128 ? 3 : 2;
+    const ProfEvents ev = prof_events(PROF_SCAN, PROF_SCAN_ROWS);
+    // two stage buffers (with W and M, three of dk = 128 would not fit in LDS)
+    constexpr int NSTAGE = 2;
     hipExtLaunchKernelGGL((gdn_chunk_scan_rows_kernel<bf16, 64, DK, DVS, NSTAGE>), dim3((unsigned)blocks),
                           dim3(kScanThreads), 0, st, ev.start, ev.stop, 0, static_cast<const bf16 *>(p.q),
                           static_cast<const bf16 *>(p.k), static_cast<const bf16 *>(p.v), p.cu_seqlens, map,
-                          p.num_seqs, p.total_tokens, p.hqk, p.hv, p.dv, tmat, amat, dec, sin, sout,
+                          p.num_seqs, p.total_tokens, p.hqk, p.hv, p.dv, wmat, mmat, dec, sin, sout,
                           static_cast<bf16 *>(p.o), p.scale);
 }
 
 template <int DK, int NW, int CT>
-static void launch_scan_bf16(const PrefillArgs &p, const SlotMap &map, const bf16 *tmat, const bf16 *amat,
+static void launch_scan_bf16(const PrefillArgs &p, const SlotMap &map, const bf16 *wmat, const bf16 *mmat,
                              const float *dec, const float *sin, float *sout, hipStream_t st)
 {
     const int nv = p.dv / (16 * CT * NW);
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
     const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
-    const ProfEvents ev = prof_events(PROF_SCAN);
+    const ProfEvents ev = prof_events(PROF_SCAN, PROF_SCAN_WIDE);
     hipExtLaunchKernelGGL((gdn_chunk_scan_bf16_kernel<DK, NW, CT>), dim3((unsigned)blocks), dim3(NW * kWave), 0,
                           st, ev.start, ev.stop, 0, static_cast<const bf16 *>(p.q), static_cast<const bf16 *>(p.k),
                           static_cast<const bf16 *>(p.v), p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv,
-                          p.dv, tmat, amat, dec, sin, sout, static_cast<bf16 *>(p.o), p.scale);
+                          p.dv, wmat, mmat, dec, sin, sout, static_cast<bf16 *>(p.o), p.scale);
 }
 
 // Batches of at most this many sequences are scanned longest first.
@@ -2046,12 +2111,13 @@ template <typename E, int C, int DK>
 static hipError_t launch_prefill_t(const PrefillArgs &p)
 {
     hipStream_t st = static_cast<hipStream_t>(p.stream);
-    // workspace: [chunk table | T matrices | A matrices | decay records]
+    // workspace: [chunk table | T (or W) matrices | A (or M) matrices | decay records]
+    constexpr bool kAbsorbed = AbsorbedForm<E, C>::value;
+    static_assert(kAbsorbed == (std::is_same<E, bf16>::value && C == 64), "matches prefill_absorbed()");
     int32_t *chunk_start = reinterpret_cast<int32_t *>(p.workspace);
     E *tmat = reinterpret_cast<E *>(static_cast<char *>(p.workspace) + p.table_bytes);
-    E *amat = tmat + (size_t)p.max_chunks * p.hv * C * C;
+    E *amat = tmat + (size_t)p.max_chunks * p.hv * (kAbsorbed ? DK : C) * C;
     float *dec = reinterpret_cast<float *>(amat + (size_t)p.max_chunks * p.hv * C * C);
-    const int nw = pick_waves<E>(p.dv);
     // The gated RMSNorm of the output rows, if asked for: in place, after the scans.
     auto finish = [&]() -> hipError_t {
         if (p.norm_z && p.total_tokens > 0) {

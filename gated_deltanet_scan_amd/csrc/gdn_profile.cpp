@@ -18,7 +18,7 @@ namespace {
 
 struct Rec {
     hipEvent_t start = nullptr, stop = nullptr;
-    int32_t kernel = -1;
+    int32_t kernel = -1, variant = -1;
 };
 
 std::atomic<bool> g_on{false};
@@ -28,7 +28,7 @@ size_t g_used = 0;
 
 }  // namespace
 
-ProfEvents prof_events(int32_t kernel)
+ProfEvents prof_events(int32_t kernel, int32_t variant)
 {
     if (!g_on.load(std::memory_order_relaxed))
         return ProfEvents{nullptr, nullptr};
@@ -45,6 +45,7 @@ ProfEvents prof_events(int32_t kernel)
     }
     Rec &r = g_recs[g_used++];
     r.kernel = kernel;
+    r.variant = variant;
     return ProfEvents{r.start, r.stop};
 }
 
@@ -69,7 +70,7 @@ gdn_status gdn_profile_collect(int32_t kernel, int32_t *launches, double *total_
     double sum = 0.0;
     for (size_t i = 0; i < gdn::g_used; ++i) {
         gdn::Rec &r = gdn::g_recs[i];
-        if (r.kernel != kernel)
+        if (r.kernel != kernel && r.variant != kernel)
             continue;
         if (hipEventSynchronize(r.stop) != hipSuccess)
             return GDN_ERR_HIP;

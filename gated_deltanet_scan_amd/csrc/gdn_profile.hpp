@@ -16,6 +16,10 @@ enum ProfKernel : int32_t {
     PROF_NORM = 5,
     PROF_CONV = 6,
     PROF_CONV_STATE = 7,
+    // which chunk-scan kernel a PROF_SCAN launch ran (each such launch also counts as PROF_SCAN)
+    PROF_SCAN_ROWS = 8,    // gdn_chunk_scan_rows_kernel
+    PROF_SCAN_WIDE = 9,    // gdn_chunk_scan_bf16_kernel
+    PROF_SCAN_PLAIN = 10,  // gdn_chunk_scan_kernel
 };
 
 // Start and stop events for one launch of `kernel`: both null while timing is
@@ -24,6 +28,8 @@ enum ProfKernel : int32_t {
 struct ProfEvents {
     hipEvent_t start, stop;
 };
-ProfEvents prof_events(int32_t kernel);
+// `variant` (default: none) names the kernel behind a family identifier such as PROF_SCAN;
+// gdn_profile_collect() of either identifier counts the launch.
+ProfEvents prof_events(int32_t kernel, int32_t variant = -1);
 
 }  // namespace gdn

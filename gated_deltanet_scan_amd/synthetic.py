@@ -99,9 +99,21 @@ def draw_g(gen, shape, law: str) -> torch.Tensor:
     raise KeyError(law)
 
 
+def correlated_unit_keys(gen, T, hqk, dk, noise=0.1):
+    """Highly correlated keys: per query/key head one shared random direction plus
+    N(0, noise^2 / dk) per component, L2-normalised per token (cosine between two keys of
+    a head about 1 / (1 + noise^2))."""
+    shared = _unit_gaussian(gen, (1, hqk, dk))
+    k = shared + noise * torch.randn(T, hqk, dk, generator=gen) / float(dk) ** 0.5
+    return k / k.norm(dim=-1, keepdim=True).clamp_min(1e-12)
+
+
 def make_inputs(lengths, hqk, hv, dk, dv, io_dtype=torch.bfloat16, seed=0, g_law="uniform",
-                s0_std=None, strong_segment=False):
+                s0_std=None, strong_segment=False, key_law="gaussian"):
     """Draw one packed batch on the CPU.
+
+    key_law "gaussian" draws the keys like the queries; "correlated" draws highly
+    correlated keys (correlated_unit_keys).
 
     Returns a dict with q, k [T, HQK, dk] and v [T, HV, dv] in io_dtype;
     g, beta [T, HV] fp32; cu_seqlens [N+1] int32; initial_state
@@ -112,7 +124,12 @@ def make_inputs(lengths, hqk, hv, dk, dv, io_dtype=torch.bfloat16, seed=0, g_law
     T = sum(lengths)
     n = len(lengths)
     q = _unit_gaussian(gen, (T, hqk, dk)).to(io_dtype)
-    k = _unit_gaussian(gen, (T, hqk, dk)).to(io_dtype)
+    if key_law == "correlated":
+        k = correlated_unit_keys(gen, T, hqk, dk).to(io_dtype)
+    elif key_law == "gaussian":
+        k = _unit_gaussian(gen, (T, hqk, dk)).to(io_dtype)
+    else:
+        raise KeyError(key_law)
     v = torch.randn(T, hv, dv, generator=gen).to(io_dtype)
     beta = torch.sigmoid(torch.randn(T, hv, generator=gen)).float()
     g = draw_g(gen, (T, hv), g_law).float()

@@ -2,8 +2,8 @@
  * gdn.h -- C ABI of libgdn, the gfx950 (MI355X) implementation of the gated
  * delta rule used by the Gated DeltaNet linear-attention layers of Qwen3.5.
  *
- * The rule (Qwen3.5-9B architecture page, section Gated DeltaNet; the same
- * step written as a per-token Loop on the NPU page, section "How it works"):
+ * The rule (Qwen3.5-9B architecture page, section Gated DeltaNet; the NPU
+ * page runs the same step token by token, section "How it works"):
  *     S_t = a_t (I - b_t k_t k_t^T) S_{t-1} + b_t k_t v_t^T,   a_t = exp(g_t)
  *     o_t = scale * S_t^T q_t
  * for each value head, with the state S (dk x dv) carried from token to
@@ -85,15 +85,16 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape, int64_t total_tokens,
  * Chunked prefill over a packed batch of variable-length sequences.
  *
  * Defined by the chunkwise-parallel form on the NPU page (section "How it
- * works"): within a chunk of C tokens, with G the cumulative sum of g,
- *   N   = diag(beta) [exp(G_t - G_j) k_t.k_j]_{j<t}
- *   D   = (I + N)^-1 diag(beta) (V - diag(exp G) K S0)
- *   O   = diag(exp G) Q S0 + [exp(G_t - G_j) q_t.k_j]_{j<=t} D
- *   S_T = exp(G_T) S0 + K^T diag(exp(G_T - G)) D
- * and carried from chunk to chunk in order; (I + N)^-1 by forward
- * substitution per chunk, decay exponents masked in log space before exp
- * (Candle pull-request page, section Chunked GatedDeltaNet Scan).  The
- * result equals the token-by-token recurrence up to rounding.
+ * works"): the tokens of a sequence are taken C at a time; within a chunk the
+ * decay is the running sum G of g, the corrections of the chunk's writes are
+ * the solution of one unit lower-triangular system (keys against earlier keys
+ * of the chunk, decayed and scaled by beta), and the state entering the chunk
+ * contributes to every output and to the state leaving it through decayed
+ * products with the chunk's queries and keys.  Chunks are carried one after
+ * the other; the triangular system is solved by forward substitution per chunk,
+ * and decay exponents are masked in log space before exp (Candle pull-request
+ * page, section Chunked GatedDeltaNet Scan).  The result equals the
+ * token-by-token recurrence up to rounding.
  *
  *   q, k           [total_tokens, HQK, dk]  io dtype
  *   v              [total_tokens, HV, dv]   io dtype
@@ -293,8 +294,11 @@ gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, const void *o, const void *
  * gdn_profile_collect() waits for the recorded events of one kernel and
  * returns how many launches were recorded and their summed duration in ms.
  * Kernel identifiers: 0 chunk table and scan order, 1 prep (Gram products and solve),
- * 2 chunk scan (state pass and outputs), 3 decode, 4 snapshot, 5 gated RMSNorm,
- * 6 conv1d, 7 conv state update.
+ * 2 chunk scan (state pass and outputs, any of its kernels), 3 decode, 4 snapshot,
+ * 5 gated RMSNorm, 6 conv1d, 7 conv state update; and which chunk-scan kernel ran
+ * (each of these launches also counts under 2): 8 the row-split scan (few
+ * (sequence, head) pairs, bf16, chunk 64), 9 the whole-head scan (many pairs,
+ * bf16, chunk 64, dk = 128), 10 the general scan (fp32 io or chunk 16).
  * The events are created on first use and kept until the process ends;
  * no device memory is allocated.
  */

@@ -9,11 +9,12 @@ the pages in numpy so that the sequential oracle can be checked against it:
   factor products A_t ... A_{j+1} (b_j k_j v_j^T) plus A_t ... A_1 S_0, every
   dk x dk factor materialised.
 * `chunkwise`: the chunkwise-parallel form of the NPU page (section "How it
-  works"): with G the in-chunk cumulative sum of g,
-      N   = diag(beta) [exp(G_t - G_j) k_t.k_j]_{j<t}
-      D   = (I + N)^-1 diag(beta) (V - diag(exp G) K S0)
-      O   = diag(exp G) Q S0 + [exp(G_t - G_j) q_t.k_j]_{j<=t} D
-      S_T = exp(G_T) S0 + K^T diag(exp(G_T - G)) D
+  works"), in this repository's notation: per chunk, with G the running sum of
+  g, gamma = exp(G), lambda = exp(G_last - G), Gamma = exp(G_last), N the
+  strictly lower matrix of beta_t exp(G_t - G_j) k_t.k_j and A the lower
+  matrix of exp(G_t - G_j) q_t.k_j,
+      D = (I + N)^-1 diag(beta) (V - diag(gamma) K S)
+      O = diag(gamma) Q S + A D,     S <- Gamma S + K^T diag(lambda) D
   with three ways to form (I + N)^-1: forward substitution (the Candle
   pull-request page, section Chunked GatedDeltaNet Scan), exact block doubling
   (D + C)^-1 = D^-1 - D^-1 C D^-1 and the product series

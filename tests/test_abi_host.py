@@ -64,8 +64,15 @@ def test_workspace_size(lib):
     sh = shape()
     T, N = 1000, 3
     max_chunks = -(-T // 64) + N
-    expect = 256 + 2 * max_chunks * 32 * 64 * 64 * 2 + max_chunks * 32 * 4 * 64 * 4
+    # bf16 at chunk 64 (absorbed form): per chunk slot and value head, W (dk x C) and M (C x C)
+    # in bf16 and the decay record (4 C floats)
+    expect = 256 + max_chunks * 32 * (128 * 64 + 64 * 64) * 2 + max_chunks * 32 * 4 * 64 * 4
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), T, N) == expect
+    # fp32 io (direct form): T and A (C x C each)
+    sh32 = gdn.make_shape(2, 4, 32, 32, 16, 0, 1.0)
+    mc = -(-T // 16) + N
+    expect32 = 256 + mc * 4 * 2 * 16 * 16 * 4 + mc * 4 * 4 * 16 * 4
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(sh32), T, N) == expect32
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(shape(d=96)), T, N) == 0     # unsupported
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(shape(hqk=3)), T, N) == 0    # 32 % 3 != 0
     assert lib.gdn_prefill_workspace_bytes(None, T, N) == 0

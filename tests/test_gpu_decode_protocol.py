@@ -38,10 +38,13 @@ def _check_decode(inp, io, label, scale=None):
     eo, es = rel_err(o, o_ref), rel_err(st, S_ref)
     say(label, "max rel err: o %.3e  S %.3e" % (eo, es))
     assert eo <= tol_o and es <= tol_s, (eo, es)
-    # per sequence as well
+    # per sequence, and per (sequence, value head) on the head's own scale
     for i in range(n):
         assert rel_err(o[i], o_ref[i]) <= tol_o
         assert rel_err(st[i], S_ref[i]) <= tol_s
+        for h in range(o.shape[1]):
+            assert rel_err(o[i, h], o_ref[i, h]) <= tol_o, (label, i, h)
+            assert rel_err(st[i, h], S_ref[i, h]) <= tol_s, (label, i, h)
 
 
 def test_decode_64_workload():
@@ -125,7 +128,8 @@ def _slice_tokens(inp, lengths_take, offsets):
 
 def _verify_protocol(w, accepted, label):
     """Packed prefill -> snapshot -> one 16-token verify block per sequence -> restore -> re-feed
-    the accepted prefix.  Checks the verify outputs, the re-fed outputs and the final states."""
+    the accepted prefix.  Checks the prompt outputs, the verify outputs, the re-fed outputs and the
+    final states (per sequence and per value head)."""
     V = w.verify_tokens
     n = len(w.lengths)
     # one draw holds prompt + verify tokens of every sequence; sequences are split below
@@ -171,13 +175,19 @@ def _verify_protocol(w, accepted, label):
     cu_v = [int(x) for x in verify["cu_seqlens"]]
     cu_r = [int(x) for x in refeed["cu_seqlens"]]
     cu_k = [int(x) for x in kept["cu_seqlens"]]
+    op = o_prompt.double().cpu().numpy()
+    cu_p = [int(x) for x in prompt["cu_seqlens"]]
     for i in range(n):
+        # the prompt outputs: the first L tokens of the oracle over prompt + draft
+        ref_prompt = o_draft_ref[starts[i]: starts[i] + w.lengths[i]]
+        assert rel_err(op[cu_p[i]:cu_p[i + 1]], ref_prompt) <= tol_o, "%s seq %d prompt outputs" % (label, i)
+        for h in range(st.shape[1]):
+            assert rel_err(st[i, h], S_kept[i, h]) <= tol_s, "%s seq %d head %d final state" % (label, i, h)
         ref_draft = o_draft_ref[starts[i] + w.lengths[i]: starts[i] + w.lengths[i] + V]
         assert rel_err(ov[cu_v[i]:cu_v[i + 1]], ref_draft) <= tol_o, "%s seq %d verify outputs" % (label, i)
         ref_acc = o_kept[cu_k[i] + w.lengths[i]: cu_k[i + 1]]
         if accepted[i]:
             assert rel_err(orf[cu_r[i]:cu_r[i + 1]], ref_acc) <= tol_o, "%s seq %d re-fed outputs" % (label, i)
-    return o_prompt
 
 
 def test_varlen_verify_rollback_refeed_workload():

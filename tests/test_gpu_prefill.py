@@ -6,8 +6,8 @@ chunk, multi-chunk ragged tails, zero-length sequences, batches without tokens
 (and without sequences), batches at and past
 the 4096-sequence ordering limit, every supported head size and chunk length
 in both io dtypes, the strong-decay (-6.72) segment,
-a weak-decay long-memory stress, in-place prefix reuse and run-to-run
-determinism.
+a weak-decay long-memory stress (also at the full 32k shape), highly
+correlated keys, scale 0, in-place prefix reuse and run-to-run determinism.
 """
 import numpy as np
 import pytest
@@ -19,9 +19,9 @@ from gpu_helpers import check_prefill, gpu_prefill, oracle_prefill, rel_err, say
 pytestmark = pytest.mark.gpu
 
 
-def _case(lengths, hqk, hv, d, io, seed, g_law="uniform", s0_std=0.05, strong=False):
+def _case(lengths, hqk, hv, d, io, seed, g_law="uniform", s0_std=0.05, strong=False, key_law="gaussian"):
     return S.make_inputs(lengths, hqk, hv, d, d, io, seed=seed, g_law=g_law, s0_std=s0_std,
-                         strong_segment=strong)
+                         strong_segment=strong, key_law=key_law)
 
 
 def _run(inp, chunk, io, label, scale=None, host_offsets=True):
@@ -167,9 +167,50 @@ def test_weak_decay_long_memory():
     _run(inp, 64, torch.bfloat16, "weak_decay")
 
 
+def test_weak_decay_at_the_32k_shape():
+    """The 32k prefill shape (one 32768-token sequence, 16 query/key -> 32 value heads, d = 128,
+    initial state N(0, 0.05^2)) with weak decay g ~ -U(0, 0.02): the state remembers thousands
+    of tokens, so rounding on the 512-chunk chain accumulates instead of being forgotten within
+    a chunk as under the workload's strong decay.  Both launch modes."""
+    inp = _case([32768], 16, 32, 128, torch.bfloat16, seed=1013, g_law="weak")
+    for host_offsets in (True, False):
+        _run(inp, 64, torch.bfloat16, "weak_decay_32k", host_offsets=host_offsets)
+
+
+@pytest.mark.parametrize("g_law", ["uniform", "weak"])
+def test_correlated_keys_through_the_solve(g_law):
+    """Highly correlated keys (one shared direction per head plus 10% noise, normalised; the
+    NPU page, section "How it works", warns that real keys are highly correlated and break
+    naive triangular inverses) at the 1k prefill shape: the off-diagonal entries of the
+    chunk's triangular system are near beta, so the fp32 solve and the bf16 inverse carry
+    large, alternating entries.  With the workload's decay law and with weak decay."""
+    inp = _case([1024], 16, 32, 128, torch.bfloat16, seed=1011, g_law=g_law, s0_std=None, strong=True,
+                key_law="correlated")
+    k = inp["k"].double()
+    cos = (k[1:] * k[:-1]).sum(-1)
+    assert float(cos.mean()) > 0.95, "keys are not correlated"
+    _run(inp, 64, torch.bfloat16, "correlated_keys_" + g_law)
+
+
 def test_scale_argument():
     inp = _case([100], 1, 2, 64, torch.float32, seed=25)
     _run(inp, 64, torch.float32, "scale_0.3", scale=0.3)
+
+
+@pytest.mark.parametrize("io,d", [(torch.float32, 64), (torch.bfloat16, 128)])
+def test_scale_zero(io, d):
+    """scale = 0: every output is exactly zero and the state is that of any other scale (the
+    scale multiplies the queries only).  Sequences of several chunks, both launch modes, and
+    for bf16 both scan kernels (8 and 80 (sequence, head) pairs)."""
+    for lengths, hv in (([200, 70], 4), ([130] * 20, 4)):
+        if io == torch.float32 and len(lengths) > 2:
+            continue
+        inp = _case(lengths, 2, hv, d, io, seed=33 + len(lengths))
+        for host_offsets in (True, False):
+            o, St = gpu_prefill(inp, 64, scale=0.0, host_offsets=host_offsets)
+            assert int(torch.count_nonzero(o)) == 0, "scale 0 gave nonzero outputs"
+            o_ref, S_ref = oracle_prefill(inp, scale=0.0)
+            check_prefill(o, St, o_ref, S_ref, inp["cu_seqlens"], io, "scale_0_n%d" % len(lengths))
 
 
 def test_in_place_prefix_reuse_matches_two_calls():
