@@ -1,19 +1,36 @@
 #!/usr/bin/env python3
 """Throughput of the gated delta rule hot path on one MI355X (gfx950).
 
-    python bench.py [--steps K] [--warmup W] [--workload prefill_1k]
+    python bench.py [--steps K] [--warmup W] [--workload varlen_16]
 
-Headline: chunked-prefill tokens/s of one Qwen3.5-9B Gated DeltaNet layer
-(16 query/key heads, 32 value heads, head dim 128, chunk 64; B=1, T=1024,
-bf16 q/k/v, fp32 g/beta/state).  One step = one gdn_prefill_chunked call
-(chunk table, prep, chunk scan) over one batch already resident in HBM.
-Several copies of the batch are rotated so that repeated steps do not run
-out of the 256 MB last-level cache.  The same run also measures the decode
-step (64 sequences, state updated in place, state sets rotated), the long
-32k prefill and the 16-sequence varlen prefill, each with its per-kernel
-durations from HIP events recorded on the library's launch stream; the conv1d
-ahead of the scan and the gated RMSNorm after it, on the 1k and 32k shapes; and
-the fp64 CPU oracle on a bounded sample of the headline workload.
+Headline: the packed variable-length prefill of one Qwen3.5-9B Gated DeltaNet
+layer (16 query/key heads, 32 value heads, head dim 128, chunk 64; 16
+sequences of U{256..8192} tokens, each from its own fp32 initial state; bf16
+q/k/v, fp32 g/beta/state) with the verify protocol of that workload: after the
+prompts, the states are snapshotted, a 16-token draft of every sequence is run
+through the chunked prefill, the states are restored, and the accepted prefix of
+every draft (m ~ U{1..15} tokens) is fed again.  One step = that whole sequence
+of library calls (prefill, snapshot, verify prefill, restore, re-feed prefill)
+over one batch already resident in HBM; `value` counts every token the
+recurrence processes in it (prompts + drafts + re-fed tokens).
+
+The same run measures the 1k and 32k single-sequence prefills, a skewed batch
+(one 32k sequence among 63 short ones), the decode step (64 sequences, state
+updated in place, state sets rotated past the last-level cache), the conv1d
+ahead of the scan and the gated RMSNorm after it, each with per-kernel durations
+from HIP events that the library records on its launch stream, and the fp64 CPU
+oracle on a bounded sample of the headline workload.
+
+Algorithmic work per token and value head (chunk C, head dims dk, dv):
+  flops = 4 C dk HQK/HV (K K^T and Q K^T, shared by a query/key head's value heads)
+        + 2 C (dk + dv) (the two products with the chunk's triangular inverse)
+        + 6 dk dv (the three products with the state) + 2 C dv (the intra-chunk output)
+        = 163,840 at the Qwen3.5-9B shapes;
+  bytes per token = q, k, v read and o written in the io dtype, g and beta in fp32
+        = 24,832 at the Qwen3.5-9B shapes; plus every state read and written once per call.
+Workspace round trips (the chunk matrices written by the prep and read by the scan)
+are not algorithmic: they show up in `traffic`, the HBM bytes that the rocprofv3
+counters measured per launch.
 
 Prints ONE JSON line.
 """
@@ -82,35 +99,25 @@ def esize(dtype):
     return 2 if dtype == torch.bfloat16 else 4
 
 
-def prefill_costs(w, lengths):
-    """Algorithmic bytes and flops per launch of each prefill kernel.
+def flops_per_token_head(w):
+    """Dense-contraction flops per token and value head of the chunked form (a multiply-add is
+    two flops); 163,840 at C = 64, dk = dv = 128, HQK / HV = 1/2."""
+    C, dk, dv = w.chunk, w.dk, w.dv
+    return (4 * C * dk * w.hqk) // w.hv + 2 * C * (dk + dv) + 6 * dk * dv + 2 * C * dv
 
-    Bytes are what the kernel must move between HBM and the chip at least: its inputs
-    read once and its outputs written once.  Flops count the dense contractions only
-    (a multiply-add is two flops): per real token for the scan, per chunk for the prep."""
+
+def bytes_per_token(w):
+    """Algorithmic HBM bytes per token: q, k, v read and o written once, g and beta in fp32."""
     es = esize(w.io_dtype)
-    T = sum(lengths)
-    N = len(lengths)
-    C, dk, dv, hqk, hv = w.chunk, w.dk, w.dv, w.hqk, w.hv
-    E = sum((L + C - 1) // C for L in lengths)
-    qk_bytes = 2 * T * hqk * dk * es
-    gb_bytes = 2 * T * hv * 4
-    ta_bytes = 2 * E * hv * C * C * es + E * hv * 4 * C * 4     # T, A and the decay record
-    s_in = N * hv * dk * dv * 4 if w.s0_std is not None else 0
-    s_out = N * hv * dk * dv * 4
-    prep = {
-        "bytes": qk_bytes + gb_bytes + ta_bytes,
-        # two lower-triangular Gram products per chunk and query/key head, plus the
-        # forward substitution (C^3/3 flops per chunk and value head)
-        "flops": E * hqk * 2 * (C * (C + 1) // 2) * dk * 2 + E * hv * (C ** 3) // 3,
-    }
-    scan = {
-        "bytes": qk_bytes + T * hv * dv * es + gb_bytes + ta_bytes + T * hv * dv * es + s_in + s_out,
-        # [Q;K] S, S update: 6 dk dv; T X and A D: 4 C dv  (per token and value head)
-        "flops": T * hv * (6 * dk * dv + 4 * C * dv),
-    }
-    io_bytes = qk_bytes + 2 * T * hv * dv * es + gb_bytes + s_in + s_out   # what a step must move at least
-    return {"prep": prep, "scan": scan, "io_bytes": io_bytes, "chunks": E}
+    return es * (2 * w.hqk * w.dk + 2 * w.hv * w.dv) + 2 * 4 * w.hv
+
+
+def prefill_costs(w, tokens, calls, seqs):
+    """Algorithmic bytes and flops of `calls` prefill calls that process `tokens` tokens in all,
+    each reading and writing the states of `seqs` sequences once."""
+    state = seqs * w.hv * w.dk * w.dv * 4
+    return {"bytes": bytes_per_token(w) * tokens + 2 * state * calls,
+            "flops": flops_per_token_head(w) * w.hv * tokens}
 
 
 def decode_costs(w):
@@ -126,11 +133,71 @@ def _sync():
     torch.cuda.synchronize()
 
 
-def _clone_inputs(d):
-    return {k: (v.clone() if hasattr(v, "clone") else v) for k, v in d.items()}
+SCAN_VARIANTS = ((8, "gdn_chunk_scan_rows_kernel"), (9, "gdn_chunk_scan_bf16_kernel"), (10, "gdn_chunk_scan_kernel"))
 
 
-def measure_prefill(name, steps, warmup, lengths=None):
+def _kernel_times(steps):
+    """Per-step launches and time of each library kernel recorded since profile_enable."""
+    import gated_deltanet_scan_amd as gdn
+    kern = {}
+    for kid, kname in ((0, "chunk_table"), (1, "prep"), (2, "scan"), (4, "snapshot")):
+        n, tot = gdn.profile_collect(kid)
+        kern[kname] = {"launches_per_step": n / steps, "avg_us": (tot / n * 1e3) if n else None,
+                       "per_step_us": tot * 1e3 / steps}
+    # the scan kernel the library chose (it reports each launch under its kernel's identifier)
+    ran = [(name, gdn.profile_collect(kid)[0]) for kid, name in SCAN_VARIANTS]
+    kern["scan"]["kernel"] = "+".join(name for name, n in ran if n) or None
+    return kern
+
+
+def _timed(fn, steps, warmup):
+    """Wall-clock ms per step of `steps` calls after `warmup` calls (synchronised on both sides),
+    then the per-kernel HIP-event times of a second pass of `steps` calls."""
+    import gated_deltanet_scan_amd as gdn
+    for i in range(warmup):
+        fn(i)
+    _sync()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(i)
+    _sync()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    gdn.profile_enable(True)
+    for i in range(steps):
+        fn(i)
+    _sync()
+    kern = _kernel_times(steps)
+    gdn.profile_enable(False)
+    return ms, kern
+
+
+def _to_dev(x):
+    import torch
+    dev = torch.device("cuda:0")
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def _pack_drafts(w, accepted):
+    """The verify drafts (16 fresh tokens per sequence, drawn from the workload's laws) and the
+    accepted prefixes to re-feed (the first m_n draft tokens of sequence n), packed."""
+    import torch
+    from gated_deltanet_scan_amd import synthetic
+    n = len(w.lengths)
+    V = w.verify_tokens
+    draft = synthetic.make_inputs([V] * n, w.hqk, w.hv, w.dk, w.dv, w.io_dtype, seed=w.seed + 100,
+                                  g_law=w.g_law, s0_std=None)
+    idx = torch.cat([torch.arange(i * V, i * V + m) for i, m in enumerate(accepted)])
+    refeed = {key: draft[key][idx].contiguous() for key in ("q", "k", "v", "g", "beta")}
+    cu = torch.zeros(n + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(accepted, dtype=torch.int64), 0).to(torch.int32)
+    refeed["cu_seqlens"] = cu
+    refeed["initial_state"] = None
+    return draft, refeed
+
+
+def measure_prefill(name, steps, warmup, lengths=None, verify=None):
+    """One prefill workload.  With `verify` (the headline varlen workload), a step is the whole
+    verify protocol: prompt prefill, snapshot, draft prefill, restore, re-feed prefill."""
     import torch
 
     import gated_deltanet_scan_amd as gdn
@@ -138,97 +205,86 @@ def measure_prefill(name, steps, warmup, lengths=None):
     w = synthetic.workload(name)
     lengths = lengths or w.lengths
     x = synthetic.make_workload_inputs(w, lengths=lengths)
-    dev = torch.device("cuda:0")
-    base = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
-    costs = prefill_costs(w, lengths)
-    shape = gdn.make_shape(w.hqk, w.hv, w.dk, w.dv, w.chunk, 1 if w.io_dtype == torch.bfloat16 else 0, 1.0)
-    ws_bytes = gdn.workspace_bytes(shape, sum(lengths), len(lengths))
-    per_set = costs["io_bytes"] + ws_bytes
-    n_sets = int(min(16, max(1, math.ceil(CACHE_DEFEAT_BYTES / per_set))))
+    base = _to_dev(x)
+    N, T = len(lengths), sum(lengths)
+    verify = bool(verify and w.verify_tokens)
+    es = esize(w.io_dtype)
+    ws_bytes = gdn.workspace_bytes(gdn.make_shape(w.hqk, w.hv, w.dk, w.dv, w.chunk,
+                                                  1 if w.io_dtype == torch.bfloat16 else 0, 1.0), T, N)
+    per_set = bytes_per_token(w) * T + ws_bytes
+    n_sets = 1 if verify else int(min(16, max(1, math.ceil(CACHE_DEFEAT_BYTES / per_set))))
     calls = []
     for i in range(n_sets):
-        d = base if i == 0 else _clone_inputs(base)
-        # host copy of the offsets: the library validates them and plans its segments
+        d = base if i == 0 else {k: (v.clone() if hasattr(v, "clone") else v) for k, v in base.items()}
+        # host copy of the offsets: the library validates them and plans its launches
         calls.append(gdn.prepare_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], x["cu_seqlens"],
                                          d["initial_state"], chunk=w.chunk))
-    for i in range(warmup):
-        calls[i % n_sets]()
-    _sync()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        calls[i % n_sets]()
-    _sync()
-    wall = time.perf_counter() - t0
-    ms = wall * 1e3 / steps
+    tokens, n_calls = T, 1
+    if verify:
+        accepted = synthetic.accept_counts(w.seed + 1, N, w.verify_tokens)
+        draft, refeed = _pack_drafts(w, accepted)
+        state = calls[0].result[1]                  # the prompts' final states, updated in place
+        snap = torch.empty_like(state)
+        dd, dr = _to_dev(draft), _to_dev(refeed)
+        ver = gdn.prepare_prefill(dd["q"], dd["k"], dd["v"], dd["g"], dd["beta"], draft["cu_seqlens"], state,
+                                  chunk=w.chunk, final_state=state)
+        ref = gdn.prepare_prefill(dr["q"], dr["k"], dr["v"], dr["g"], dr["beta"], refeed["cu_seqlens"], state,
+                                  chunk=w.chunk, final_state=state)
 
-    # per-kernel durations: HIP events on the launch stream over a second timed pass
-    gdn.profile_enable(True)
-    for i in range(steps):
-        calls[i % n_sets]()
-    _sync()
-    kern = {}
-    for kid, kname in ((0, "chunk_table"), (1, "prep"), (2, "scan")):
-        n, tot = gdn.profile_collect(kid)
-        kern[kname] = {"launches_per_step": n / steps, "avg_us": (tot / n * 1e3) if n else None,
-                       "per_step_us": tot * 1e3 / steps}
-    gdn.profile_enable(False)
-    T = sum(lengths)
-    flops = costs["prep"]["flops"] + costs["scan"]["flops"]
+        def step(i):
+            calls[0]()
+            gdn.state_snapshot(state, snap)
+            ver()
+            gdn.state_snapshot(snap, state)
+            ref()
+        tokens = T + N * w.verify_tokens + sum(accepted)
+        n_calls = 3
+    else:
+        def step(i):
+            calls[i % n_sets]()
+    ms, kern = _timed(step, steps, warmup)
+    costs = prefill_costs(w, tokens, n_calls, N)
     peak = PEAK_BF16_TFLOPS if w.io_dtype == torch.bfloat16 else PEAK_FP32_MFMA_TFLOPS
     out = {
-        "workload": name, "tokens": T, "sequences": len(lengths), "ms_per_step": ms,
-        "tokens_per_s": T / (ms * 1e-3), "rotated_copies": n_sets,
-        "mfma_frac": flops / (ms * 1e-3) / (peak * 1e12),
-        "hbm_frac": costs["io_bytes"] / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "workload": name, "tokens": tokens, "prompt_tokens": T, "sequences": N, "ms_per_step": ms,
+        "tokens_per_s": tokens / (ms * 1e-3), "rotated_copies": n_sets,
+        "algorithmic_flops": costs["flops"], "algorithmic_bytes": costs["bytes"],
+        "mfma_frac": costs["flops"] / (ms * 1e-3) / (peak * 1e12),
+        "hbm_frac": costs["bytes"] / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "kernels": kern,
-        "scan_kernel": scan_kernel_name(w, lengths),
+        "scan_kernel": kern["scan"]["kernel"],
     }
-    # whole-step costs over the kernel's summed launch time (a long or batched prefill is
-    # cut into several launches of each kernel)
-    for kname in ("prep", "scan"):
-        us = kern[kname]["per_step_us"]
-        c = costs[kname]
-        if us:
-            out[kname + "_gbs"] = c["bytes"] / (us * 1e-6) / 1e9
-            out[kname + "_tflops"] = c["flops"] / (us * 1e-6) / 1e12
-    out["_costs"] = costs
-    out["_peak_tflops"] = peak
+    if verify:
+        out["verify"] = {"draft_tokens": N * w.verify_tokens, "refed_tokens": sum(accepted),
+                         "accepted": accepted,
+                         "step": "prefill, snapshot, %d-token draft prefill, restore, re-feed prefill"
+                                 % w.verify_tokens}
+    out["roofline"] = roofline_for(out, costs, peak)
     return out
 
 
-def scan_kernel_name(w, lengths):
-    """Which scan kernel the library runs for this batch (bf16 io, chunk 64: whole-head
-    workgroups for wide batches of 128-dim heads, the row-split kernel otherwise)."""
-    import torch
-    if w.io_dtype == torch.bfloat16 and w.chunk == 64:
-        if w.dv == 128 and len(lengths) * w.hv >= 256:
-            return "gdn_chunk_scan_bf16_kernel"
-        return "gdn_chunk_scan_rows_kernel"
-    return "gdn_chunk_scan_kernel"
-
-
-def roofline_for(pre):
-    """Roofline object of the dominant prefill kernel (the one with the longest average launch)."""
-    kern = pre["kernels"]
-    name = max(("prep", "scan"), key=lambda k: kern[k]["per_step_us"] or 0.0)
-    launches = kern[name]["launches_per_step"]
-    us = kern[name]["avg_us"]
-    # algorithmic cost of one launch: the step's cost over its launches of this kernel
-    c = {k: v / launches for k, v in pre["_costs"][name].items()}
+def roofline_for(pre, costs, peak_tflops):
+    """Roofline object of the scan kernel, the step's dominant kernel: the step's algorithmic
+    bytes (or flops) spread over its scan launches, divided by their average duration."""
+    k = pre["kernels"]["scan"]
+    launches, us = k["launches_per_step"], k["avg_us"]
+    c = {key: v / launches for key, v in costs.items()}
     intensity = c["flops"] / c["bytes"]
-    ridge = pre["_peak_tflops"] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ridge = peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9)
     if intensity < ridge:
         achieved = c["bytes"] / (us * 1e-6) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": achieved / PEAK_HBM_GBS}
     else:
         achieved = c["flops"] / (us * 1e-6) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": pre["_peak_tflops"], "unit": "TFLOP/s",
-                "frac": achieved / pre["_peak_tflops"]}
-    kernel = "gdn_prep_kernel" if name == "prep" else pre["scan_kernel"]
-    roof.update({"traffic": measured_traffic(kernel, pre["workload"]), "kernel": kernel,
-                 "avg_us": us, "algorithmic_bytes": c["bytes"], "algorithmic_flops": c["flops"],
-                 "intensity_flop_per_byte": intensity})
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak_tflops, "unit": "TFLOP/s",
+                "frac": achieved / peak_tflops}
+    kernel = pre["scan_kernel"]
+    roof.update({"traffic": measured_traffic(kernel, pre["workload"]) if kernel and "+" not in kernel else None,
+                 "kernel": kernel, "avg_us": us, "launches_per_step": launches,
+                 "algorithmic_bytes": c["bytes"], "algorithmic_flops": c["flops"],
+                 "intensity_flop_per_byte": intensity,
+                 "mfma_frac_of_kernel": c["flops"] / (us * 1e-6) / (peak_tflops * 1e12)})
     return roof
 
 
@@ -245,7 +301,7 @@ def measure_decode(name, steps, warmup):
     n_sets = int(min(16, max(3, math.ceil(CACHE_DEFEAT_BYTES / costs["bytes"]))))
     calls = []
     for i in range(n_sets):
-        d = base if i == 0 else _clone_inputs(base)
+        d = base if i == 0 else {k: (v.clone() if hasattr(v, "clone") else v) for k, v in base.items()}
         calls.append(gdn.prepare_decode(d["q"], d["k"], d["v"], d["g"], d["beta"], d["initial_state"]))
     for i in range(warmup):
         calls[i % n_sets]()
@@ -355,39 +411,61 @@ def measure_conv(tokens, steps, warmup, hqk=16, hv=32, d=128, width=4):
                          "avg_us": us, "algorithmic_bytes": nbytes}}
 
 
-def cpu_baseline(name, seconds):
+def cpu_baseline(name, seconds, verify=False):
+    """The fp64 oracle as it stands, timed on this host's cores over full passes of the
+    workload (with `verify`, each pass also runs the drafts and the re-fed prefixes from the
+    prompts' final states, as the GPU step does)."""
     import oracle
     from gated_deltanet_scan_amd import synthetic
     w = synthetic.workload(name)
     x = synthetic.make_workload_inputs(w)
     threads = oracle.default_threads()
-    T = w.total_tokens
+    passes = []
+    tokens = w.total_tokens
+    if verify and w.verify_tokens:
+        accepted = synthetic.accept_counts(w.seed + 1, len(w.lengths), w.verify_tokens)
+        draft, refeed = _pack_drafts(w, accepted)
+        tokens += len(w.lengths) * w.verify_tokens + sum(accepted)
+
+    def one_pass():
+        _, st = oracle.gdn_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], x["initial_state"],
+                                   threads=threads)
+        if verify and w.verify_tokens:
+            oracle.gdn_forward(draft["q"], draft["k"], draft["v"], draft["g"], draft["beta"], draft["cu_seqlens"],
+                               st, threads=threads)
+            oracle.gdn_forward(refeed["q"], refeed["k"], refeed["v"], refeed["g"], refeed["beta"],
+                               refeed["cu_seqlens"], st, threads=threads)
     runs = 0
     t0 = time.perf_counter()
     while True:
-        oracle.gdn_forward(x["q"], x["k"], x["v"], x["g"], x["beta"], x["cu_seqlens"], x["initial_state"],
-                           threads=threads)
+        one_pass()
         runs += 1
         wall = time.perf_counter() - t0
         if wall >= seconds or runs >= 1000:
             break
-    return {"value": runs * T / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "%d full passes of %s (%d tokens x %d value heads, fp64 sequential recurrence, "
-                      "%d threads over (sequence, head) items), %.1f s wall" % (runs, name, T, w.hv, threads,
-                                                                                 wall)}
+    what = "prompts, drafts and re-fed prefixes" if verify and w.verify_tokens else "the batch"
+    return {"value": runs * tokens / wall, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full passes of %s over %s (%d tokens x %d value heads per pass, fp64 sequential "
+                      "recurrence, %d threads over (sequence, head) items), %.1f s wall"
+                      % (runs, name, what, tokens, w.hv, threads, wall)}
+
+
+def skewed_lengths():
+    """One 32768-token sequence among 63 sequences of 64 tokens."""
+    return [32768] + [64] * 63
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill_1k")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="varlen_16")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the long and varlen prefill lines")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other prefill, decode, conv and norm lines")
     ap.add_argument("--profile-prefill", action="store_true",
-                    help="run only the headline prefill loop (for rocprofv3 kernel traces and counters)")
+                    help="run only the headline loop (for rocprofv3 kernel traces and counters)")
     ap.add_argument("--profile-decode", action="store_true",
                     help="run only the decode loop (for rocprofv3 kernel traces and counters)")
     ap.add_argument("--profile-norm", action="store_true",
@@ -427,21 +505,28 @@ def main():
         fn = measure_norm if args.profile_norm else measure_conv
         print(json.dumps(fn(32768, args.steps, args.warmup)))
         return
-    print("[bench] prefill %s" % args.workload, file=sys.stderr, flush=True)
-    pre = measure_prefill(args.workload, args.steps, args.warmup)
+    from gated_deltanet_scan_amd import synthetic
+    w = synthetic.workload(args.workload)
+    verify = w.verify_tokens > 0
+    print("[bench] prefill %s%s" % (args.workload, " with the verify protocol" if verify else ""),
+          file=sys.stderr, flush=True)
+    pre = measure_prefill(args.workload, args.steps, args.warmup, verify=verify)
     if args.profile_prefill:
-        print(json.dumps({k: v for k, v in pre.items() if not k.startswith("_")}))
+        print(json.dumps(pre))
         return
-    print("[bench] decode_64", file=sys.stderr, flush=True)
-    dec = measure_decode("decode_64", max(args.steps, 20), args.warmup)
     extra = {}
+    dec = None
     if not args.no_extra:
-        for name in ("prefill_32k", "varlen_16"):
+        print("[bench] decode_64", file=sys.stderr, flush=True)
+        dec = measure_decode("decode_64", max(args.steps, 20), args.warmup)
+        for name in ("prefill_1k", "prefill_32k", "varlen_16"):
             if name == args.workload:
                 continue
             print("[bench] prefill %s" % name, file=sys.stderr, flush=True)
-            r = measure_prefill(name, max(5, min(args.steps, 20)), 2)
-            extra[name] = {k: v for k, v in r.items() if not k.startswith("_")}
+            extra[name] = measure_prefill(name, max(5, min(args.steps, 20)), 2)
+        print("[bench] prefill skewed batch (one 32k sequence among 63 of 64 tokens)", file=sys.stderr, flush=True)
+        extra["skewed_64"] = measure_prefill("prefill_32k", max(5, min(args.steps, 20)), 2, lengths=skewed_lengths())
+        extra["skewed_64"]["workload"] = "skewed_64"
         for tokens in (1024, 32768):
             print("[bench] gated RMSNorm %d tokens" % tokens, file=sys.stderr, flush=True)
             extra["gated_rmsnorm_%d" % tokens] = measure_norm(tokens, max(10, min(args.steps, 50)), 3)
@@ -451,10 +536,12 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+        cpu = cpu_baseline(args.workload, args.cpu_seconds, verify=verify)
 
-    from gated_deltanet_scan_amd import synthetic
-    w = synthetic.workload(args.workload)
+    what = ("%d sequences of U{256..8192} tokens (%d in all) from their own fp32 states, then per sequence a "
+            "%d-token draft from a state snapshot, restore, and re-feed of the accepted prefix"
+            % (len(w.lengths), w.total_tokens, w.verify_tokens)) if verify else \
+        "%d sequence(s), %d tokens" % (len(w.lengths), w.total_tokens)
     line = {
         "metric": METRIC,
         "value": pre["tokens_per_s"],
@@ -468,13 +555,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.io_dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
-        "config": {"workload": "%s: Qwen3.5-9B GDN layer prefill, %d sequence(s), %d tokens, %d QK / %d V heads, "
-                               "dk=dv=%d, chunk %d, bf16 q/k/v, fp32 g/beta/state"
-                               % (args.workload, len(w.lengths), w.total_tokens, w.hqk, w.hv, w.dk, w.chunk),
+        "config": {"workload": "%s: Qwen3.5-9B GDN layer prefill, %s; %d QK / %d V heads, dk=dv=%d, chunk %d, "
+                               "bf16 q/k/v, fp32 g/beta/state" % (args.workload, what, w.hqk, w.hv, w.dk, w.chunk),
                    "global_batch": len(w.lengths), "seq_len": w.total_tokens},
-        "roofline": roofline_for(pre),
+        "roofline": pre["roofline"],
         "cpu_baseline": cpu,
-        "prefill": {k: v for k, v in pre.items() if not k.startswith("_")},
+        "prefill": {k: v for k, v in pre.items() if k != "roofline"},
         "decode": dec,
         "extra": extra,
     }

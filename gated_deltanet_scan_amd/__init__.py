@@ -6,9 +6,9 @@ the seeded synthetic-input generator.
 """
 from .binding import (GdnError, Shape, conv1d_qkv, conv_state_snapshot, decode_step, gated_rmsnorm,
                       header_functions, library_path, load_library, make_shape, prefill_chunked,
-                      prefill_chunked_gated_rmsnorm, prepare_conv1d_qkv, prepare_decode, prepare_gated_rmsnorm,
-                      prepare_prefill, prepare_prefill_gated_rmsnorm, profile_collect, profile_enable,
-                      state_snapshot, version, workspace_bytes)
+                      prefill_chunked_gated_rmsnorm, prepare_conv1d_qkv, prepare_decode,
+                      prepare_gated_rmsnorm, prepare_prefill, prepare_prefill_gated_rmsnorm, profile_collect,
+                      profile_enable, state_snapshot, version, workspace_bytes)
 
 __all__ = ["GdnError", "Shape", "conv1d_qkv", "conv_state_snapshot", "decode_step", "gated_rmsnorm", "header_functions",
            "library_path", "load_library", "make_shape", "prefill_chunked", "prefill_chunked_gated_rmsnorm",

@@ -84,6 +84,14 @@ bool decode_supported(int32_t dk, int32_t dv, int32_t io_dtype)
     return dk == dv && (dk == 32 || dk == 64 || dk == 128);
 }
 
+size_t prefill_slot_bytes(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype)
+{
+    // T and A (C x C io elements each), or W (dk x C) and M (C x C) in the absorbed form,
+    // and the decay record exp(G), exp(G_last - G), beta, beta exp(G) (4 C floats)
+    const size_t first = prefill_absorbed(io_dtype, chunk) ? (size_t)dk : (size_t)chunk;
+    return (size_t)hv * ((first + (size_t)chunk) * (size_t)chunk * io_size(io_dtype) + 4 * (size_t)chunk * sizeof(float));
+}
+
 PrefillWorkspace prefill_workspace(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype, int64_t total_tokens,
                                    int32_t num_seqs)
 {
@@ -96,23 +104,19 @@ PrefillWorkspace prefill_workspace(int32_t hv, int32_t dk, int32_t chunk, int32_
     w.max_chunks = (int32_t)max_chunks;
     // chunk table (num_seqs + 1 entries), then the scan order of the sequences (num_seqs)
     w.table_bytes = ((2 * (size_t)num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
-    // per chunk slot and value head: T and A (C x C io elements each), or W (dk x C) and M
-    // (C x C) in the absorbed form, and the decay record exp(G), exp(G_last - G), beta,
-    // beta exp(G) (4 C floats)
-    const size_t first = prefill_absorbed(io_dtype, chunk) ? (size_t)dk : (size_t)chunk;
-    const size_t mats = (size_t)max_chunks * (size_t)hv * (first + (size_t)chunk) * (size_t)chunk * io_size(io_dtype);
-    const size_t recs = (size_t)max_chunks * (size_t)hv * 4 * (size_t)chunk * sizeof(float);
-    w.total_bytes = w.table_bytes + mats + recs;
+    w.total_bytes = w.table_bytes + (size_t)max_chunks * prefill_slot_bytes(hv, dk, chunk, io_dtype);
     return w;
 }
 
-// Segments keep the T and A matrices plus the q and k rows of one segment
-// (about kSegmentBytes) resident in the last-level cache between the prep and
-// the scan kernels.  Every segment reads and writes the whole batch's states
-// once more, so a batch of many sequences gets segments of at least
-// kStateReuse times its state bytes.
-constexpr size_t kSegmentBytes = 128u << 20;
-constexpr size_t kStateReuse = 32;
+// Segments keep the chunk matrices plus the q and k rows of one segment (about
+// kSegmentBytes) resident in the 256 MB last-level cache between the prep and the scan
+// kernels.  A segment that would hold fewer than kMinSegmentChunks chunks per sequence
+// (many sequences: every segment then re-reads and re-writes all their states, and runs
+// its pairs in rounds of a few chunks) is not worth it: such batches take the single
+// launch over the chunk table, whose scan runs every (sequence, head) chain to its end,
+// longest first.
+constexpr size_t kSegmentBytes = 176u << 20;
+constexpr int64_t kMinSegmentChunks = 32;
 
 int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype,
                             int32_t num_seqs, int32_t max_seq_chunks, int32_t slot_capacity)
@@ -122,18 +126,16 @@ int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, 
     const size_t es = io_size(io_dtype);
     const size_t first = prefill_absorbed(io_dtype, chunk) ? (size_t)dk : (size_t)chunk;
     const size_t per_slot = (size_t)hv * (first + chunk) * chunk * es + (size_t)chunk * 2 * hqk * dk * es;
-    const size_t state_bytes = (size_t)num_seqs * hv * dk * dk * sizeof(float);   // dk == dv
-    const size_t seg_bytes = std::max(kSegmentBytes, kStateReuse * state_bytes);
-    int64_t m = (int64_t)(seg_bytes / per_slot) / num_seqs;
-    m = std::max<int64_t>(m, 1);
-    m = std::min<int64_t>(m, max_seq_chunks);
-    // The workspace is sized for the batch's chunks, not for num_seqs full segments: when it
-    // holds fewer local chunks per sequence than a segment wants (a skewed batch, e.g. one long
-    // sequence among many short ones), segments would be cut short and multiply the launches,
-    // each mostly empty.  Take the single launch over the chunk table instead.
-    if (m > slot_capacity / num_seqs)
+    const int64_t m = (int64_t)(kSegmentBytes / per_slot) / num_seqs;
+    if (m < kMinSegmentChunks && m < max_seq_chunks)
         return 0;
-    return (int32_t)m;
+    // as few segments as the budget allows (one if the batch fits), of balanced length
+    const int64_t nseg = m >= max_seq_chunks ? 1 : (max_seq_chunks + m - 1) / m;
+    const int64_t len = (max_seq_chunks + nseg - 1) / nseg;
+    // a segment takes num_seqs * len slots; the workspace holds ceil(T / C) + N
+    if (len > slot_capacity / num_seqs)
+        return 0;
+    return (int32_t)len;
 }
 
 }  // namespace gdn

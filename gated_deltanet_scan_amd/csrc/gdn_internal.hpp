@@ -96,6 +96,8 @@ bool prefill_supported(int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype);
 bool decode_supported(int32_t dk, int32_t dv, int32_t io_dtype);
 PrefillWorkspace prefill_workspace(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype, int64_t total_tokens,
                                    int32_t num_seqs);
+// Workspace bytes per chunk slot (the chunk matrices and the decay record of every value head).
+size_t prefill_slot_bytes(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype);
 // Segment length (local chunks per sequence) for a batch whose longest sequence has
 // max_seq_chunks chunks; 0 selects the single-launch global mode.
 int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype,

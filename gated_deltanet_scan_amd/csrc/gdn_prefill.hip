@@ -248,10 +248,16 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
 // of the NPU page applied to the block-triangular split, in fp32 on the
 // matrix cores.
 // ---------------------------------------------------------------------------
-constexpr int kPrepWaves = 4;   // waves of a prep workgroup (two workgroups fit a CU)
+// Waves of a prep workgroup: four in the direct form (two workgroups fit a CU); eight in
+// the absorbed form, whose workgroup needs about 94 KB of LDS (one per CU) and whose
+// products with T then give one (value head, block column of T) to each wave.
+template <typename E, int C>
+struct PrepWaves {
+    static constexpr int value = AbsorbedForm<E, C>::value ? 8 : 4;
+};
 
 template <typename E, int C, int DK>
-__global__ __launch_bounds__(kPrepWaves * kWave) void gdn_prep_kernel(
+__global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, SlotMap map, int32_t num_seqs,
     int64_t total_tokens, int32_t hqk, int32_t hv, E *__restrict__ tmat, E *__restrict__ amat,
@@ -274,11 +280,11 @@ __global__ __launch_bounds__(kPrepWaves * kWave) void gdn_prep_kernel(
     constexpr int U1 = ABSORB ? TILE + (TILE > F_BYTES ? TILE : F_BYTES) : (2 * TILE > F_BYTES ? 2 * TILE : F_BYTES);
     constexpr int NCK = TILE / 16;                    // 16-byte chunks of a staged tile
     constexpr int NJ1 = (NCK + 63) / 64;              // 64-lane load jobs per tile
-    constexpr int PW = kPrepWaves, NT = PW * kWave;
+    constexpr int PW = PrepWaves<E, C>::value, NT = PW * kWave;
     constexpr int NJ_PER = (2 * NJ1 + PW - 1) / PW;
     static_assert(DK * ES >= 16 && DK * ES <= 256, "staged rows of 16 .. 256 bytes");
     static_assert(C <= kWave, "one lane per token of a chunk");
-    static_assert(!ABSORB || PW == RT, "absorbed form: one block column of T per wave");
+    static_assert(!ABSORB || PW == RT * HB, "absorbed form: one (head, block column of T) per wave");
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem_qk[U1];
     __shared__ __attribute__((aligned(16))) float Nm[HB * C * LDF];   // N; then A (absorbed form)
@@ -714,8 +720,8 @@ __device__ inline void split_bf16(float x, bf16 &hi, bf16 &lo)
 // Absorbed form of the chunk matrices (see AbsorbedForm), run by the prep after the
 // solve: T (fp32, [HB][C][LDF]) is complete in Tf, K is still staged in Ks (Swz rows),
 // and each wave holds its A tiles (fp32) in akeep, dealt as the Gram tiles were.
-// Wave wv owns block column jb = wv of T: its fp32 values, and those of diag(lambda) T,
-// become hi/lo bf16 operand pairs, and
+// Wave wv owns value head hh = wv / (C / 16) of the pass and block column jb = wv % (C / 16)
+// of its T: the fp32 values, and those of diag(lambda) T, become hi/lo bf16 operand pairs, and
 //   W^T (rows t of block jb, columns i) = (diag(lambda) T)^T K      (two products per step)
 //   M^T (rows j of block jb, columns t) = T^T A^T                   (three: hi hi, hi lo, lo hi)
 // are formed transposed so that each lane stores four consecutive elements of one row
@@ -752,8 +758,9 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
     });
     __syncthreads();
 
-    const int jb = wv, j = 16 * jb + r16;
-    for (int hh = 0; hh < nh; ++hh) {
+    static_assert(PW == RT * HB, "one (head, block column) per wave");
+    const int hh = wv / RT, jb = wv % RT, j = 16 * jb + r16;
+    if (hh < nh) {
         const float *Th = Tf + hh * C * LDF;
         const float *Ah = Am + hh * C * LDF;
         const float gl = Gv[hh][C - 1];
@@ -2162,7 +2169,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
     };
     auto prep = [&](const SlotMap &map, int64_t slots) {
         const ProfEvents ev = prof_events(PROF_PREP);
-        hipExtLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), dim3((unsigned)slots, p.hqk), dim3(kPrepWaves * kWave), 0, st,
+        hipExtLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), dim3((unsigned)slots, p.hqk),
+                              dim3(PrepWaves<E, C>::value * kWave), 0, st,
                               ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k), p.g,
                               p.beta, p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv, tmat, amat, dec,
                               p.scale);
