@@ -61,6 +61,8 @@ def load_library():
         lib.gdn_prefill_workspace_bytes.restype = sz
         lib.gdn_prefill_chunked.argtypes = [SP, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, sz, vp]
         lib.gdn_prefill_chunked.restype = ctypes.c_int
+        lib.gdn_prefill_chunked_noalloc.argtypes = [SP, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, vp]
+        lib.gdn_prefill_chunked_noalloc.restype = ctypes.c_int
         lib.gdn_prefill_chunked_gated_rmsnorm.argtypes = [SP, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, vp,
                                                           ctypes.c_float, vp, vp, sz, vp]
         lib.gdn_prefill_chunked_gated_rmsnorm.restype = ctypes.c_int
@@ -209,6 +211,20 @@ def prefill_chunked(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, sc
     lib, args, keep, dev, out, final_state = _prefill_call(q, k, v, g, beta, cu_seqlens, initial_state, scale,
                                                            chunk, final_state, out, workspace)
     _check(lib, lib.gdn_prefill_chunked(*args, _stream(dev)))
+    return out, final_state
+
+
+def prefill_chunked_noalloc(q, k, v, g, beta, cu_seqlens=None, initial_state=None, *, scale=None, chunk=64,
+                            final_state=None, out=None):
+    """gdn_prefill_chunked_noalloc: the chunked prefill with the library's own device scratch in
+    place of a workspace (the library allocates nothing).  Arguments and result as for
+    prefill_chunked; a batch too large for the scratch raises GdnError (GDN_ERR_WORKSPACE).
+    Calls that overlap in time on one device race on the scratch."""
+    lib, args, keep, dev, out, final_state = _prefill_call(q, k, v, g, beta, cu_seqlens, initial_state, scale,
+                                                           chunk, final_state, out, torch.empty(0, dtype=torch.uint8,
+                                                                                                device=q.device))
+    # (shape, q, k, v, g, beta, cu, N, T, cu_host, s0, final, o) without (workspace, bytes)
+    _check(lib, lib.gdn_prefill_chunked_noalloc(*args[:13], _stream(dev)))
     return out, final_state
 
 

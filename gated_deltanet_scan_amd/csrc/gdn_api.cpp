@@ -160,10 +160,13 @@ struct NormIn {
     float eps;
 };
 
+// own_scratch: the workspace is the library's own device scratch (gdn_prefill_chunked_noalloc),
+// not an argument.
 static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void *k, const void *v, const float *g,
                                const float *beta, const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                                const int32_t *cu_seqlens_host, const float *initial_state, float *final_state, void *o,
-                               void *workspace, size_t workspace_bytes, void *stream, const NormIn *norm)
+                               void *workspace, size_t workspace_bytes, void *stream, const NormIn *norm,
+                               bool own_scratch = false)
 {
     gdn_status st = check_shape(shape);
     if (st != GDN_OK)
@@ -215,9 +218,37 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
         gdn::prefill_workspace(s.num_v_heads, s.dk, s.chunk, s.io_dtype, total_tokens, num_seqs);
     if (ws.total_bytes == 0)
         return fail(GDN_ERR_INVALID_ARG, "batch too large for the chunk table");
-    if (!workspace || workspace_bytes < ws.total_bytes)
+    int32_t slot_capacity = ws.max_chunks;   // chunk slots the workspace holds
+    bool must_segment = false;               // the workspace holds less than the whole batch
+    if (own_scratch) {
+        // The library's scratch: the whole batch when it fits, else segments of the host-known
+        // sequence lengths sized to it.
+        const size_t slot_bytes = gdn::prefill_slot_bytes(s.num_v_heads, s.dk, s.chunk, s.io_dtype);
+        if (ws.total_bytes > gdn::kPrefillScratchBytes) {
+            if (!cu_seqlens_host)
+                return fail(GDN_ERR_WORKSPACE,
+                            "the batch needs %zu bytes of chunk workspace, more than the %zu-byte scratch of "
+                            "gdn_prefill_chunked_noalloc; pass cu_seqlens_host (the batch is then cut into "
+                            "segments) or call gdn_prefill_chunked with a workspace",
+                            ws.total_bytes, gdn::kPrefillScratchBytes);
+            const int64_t cap = ws.table_bytes < gdn::kPrefillScratchBytes
+                                    ? (int64_t)((gdn::kPrefillScratchBytes - ws.table_bytes) / slot_bytes)
+                                    : 0;
+            if (cap < num_seqs)
+                return fail(GDN_ERR_WORKSPACE,
+                            "%d sequences need at least %zu bytes of chunk workspace, more than the %zu-byte "
+                            "scratch of gdn_prefill_chunked_noalloc",
+                            num_seqs, ws.table_bytes + (size_t)num_seqs * slot_bytes, gdn::kPrefillScratchBytes);
+            slot_capacity = (int32_t)cap;
+            must_segment = true;
+        }
+        const hipError_t e = gdn::prefill_scratch(static_cast<hipStream_t>(stream), &workspace, &workspace_bytes);
+        if (e != hipSuccess)
+            return fail(GDN_ERR_HIP, "scratch of gdn_prefill_chunked_noalloc: %s", hipGetErrorString(e));
+    } else if (!workspace || workspace_bytes < ws.total_bytes) {
         return fail(GDN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", ws.total_bytes,
                     workspace ? workspace_bytes : (size_t)0);
+    }
     if (!aligned(workspace, 256))
         return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
 
@@ -228,8 +259,8 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
     const size_t state_bytes = (size_t)num_seqs * s.num_v_heads * s.dk * s.dv * sizeof(float);
     const void *inputs[] = {q, k, v, g, beta, initial_state, workspace, norm ? norm->z : nullptr,
                             norm ? norm->weight : nullptr};
-    const size_t in_bytes[] = {qk_bytes, qk_bytes, v_bytes, gb_bytes, gb_bytes, state_bytes, ws.total_bytes,
-                               v_bytes, (size_t)s.dv * sizeof(float)};
+    const size_t in_bytes[] = {qk_bytes, qk_bytes, v_bytes, gb_bytes, gb_bytes, state_bytes,
+                               std::min(ws.total_bytes, workspace_bytes), v_bytes, (size_t)s.dv * sizeof(float)};
     for (int i = 0; i < 9; ++i) {
         if (overlaps(o, v_bytes, inputs[i], in_bytes[i]))
             return fail(GDN_ERR_INVALID_ARG, "o overlaps an input or the workspace");
@@ -261,7 +292,7 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
     p.final_state = final_state;
     p.o = o;
     p.workspace = workspace;
-    p.max_chunks = ws.max_chunks;
+    p.max_chunks = slot_capacity;
     p.table_bytes = ws.table_bytes;
     p.seg_len = 0;
     p.max_seq_chunks = 0;
@@ -271,7 +302,13 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
             longest = std::max<int64_t>(longest, cu_seqlens_host[n + 1] - cu_seqlens_host[n]);
         p.max_seq_chunks = (int32_t)((longest + s.chunk - 1) / s.chunk);
         p.seg_len = gdn::prefill_segment_len(s.num_qk_heads, s.num_v_heads, s.dk, s.chunk, s.io_dtype, num_seqs,
-                                             p.max_seq_chunks, ws.max_chunks);
+                                             p.max_seq_chunks, slot_capacity);
+        if (must_segment && p.seg_len == 0 && p.max_seq_chunks > 0) {
+            // the scratch holds less than the batch: segments as long as it allows, balanced
+            const int64_t m = slot_capacity / num_seqs;   // >= 1 (checked above)
+            const int64_t nseg = (p.max_seq_chunks + m - 1) / m;
+            p.seg_len = (int32_t)((p.max_seq_chunks + nseg - 1) / nseg);
+        }
         if (p.max_seq_chunks == 0) {   // every sequence empty: one launch passes the states through
             p.seg_len = 1;
             p.max_seq_chunks = 1;
@@ -296,6 +333,15 @@ gdn_status gdn_prefill_chunked(const gdn_shape *shape, const void *q, const void
 {
     return prefill_impl(shape, q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, cu_seqlens_host, initial_state,
                         final_state, o, workspace, workspace_bytes, stream, nullptr);
+}
+
+gdn_status gdn_prefill_chunked_noalloc(const gdn_shape *shape, const void *q, const void *k, const void *v,
+                                       const float *g, const float *beta, const int32_t *cu_seqlens, int32_t num_seqs,
+                                       int64_t total_tokens, const int32_t *cu_seqlens_host, const float *initial_state,
+                                       float *final_state, void *o, void *stream)
+{
+    return prefill_impl(shape, q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, cu_seqlens_host, initial_state,
+                        final_state, o, nullptr, 0, stream, nullptr, true);
 }
 
 gdn_status gdn_prefill_chunked_gated_rmsnorm(const gdn_shape *shape, const void *q, const void *k, const void *v,

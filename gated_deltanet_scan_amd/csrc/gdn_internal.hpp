@@ -92,6 +92,13 @@ struct PrefillWorkspace {
     size_t total_bytes;
 };
 
+// Bytes of the library's own device scratch behind gdn_prefill_chunked_noalloc (one copy per
+// device, held until the process ends).
+constexpr size_t kPrefillScratchBytes = size_t(64) << 20;
+// Device address of that scratch on the device of `stream` (the null stream: the current
+// device), looked up once per device.
+hipError_t prefill_scratch(hipStream_t stream, void **ptr, size_t *bytes);
+
 bool prefill_supported(int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype);
 bool decode_supported(int32_t dk, int32_t dv, int32_t io_dtype);
 PrefillWorkspace prefill_workspace(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype, int64_t total_tokens,

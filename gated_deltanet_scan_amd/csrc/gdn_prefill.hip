@@ -39,6 +39,8 @@
 #include "gdn_internal.hpp"
 #include "gdn_profile.hpp"
 
+#include <mutex>
+
 namespace gdn {
 
 // ---------------------------------------------------------------------------
@@ -2207,6 +2209,52 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
         prep(map, p.max_chunks);
     scan(map, p.initial_state, p.final_state);
     return finish();
+}
+
+// The library's own device scratch behind gdn_prefill_chunked_noalloc: one copy per device,
+// held until the process ends.  In host code `scratch` names a host-side stand-in, not a
+// device address: the kernels are given the address that hipGetSymbolAddress returns for
+// the device, looked up once per device with that device current.
+__device__ __align__(256) unsigned char scratch[kPrefillScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+void *g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t prefill_scratch(hipStream_t stream, void **ptr, size_t *bytes)
+{
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess)
+            return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess)
+                e = e2;
+        }
+        if (e != hipSuccess)
+            return e;
+        if (!p)
+            return hipErrorInvalidSymbol;
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    *bytes = kPrefillScratchBytes;
+    return hipSuccess;
 }
 
 hipError_t launch_prefill(const PrefillArgs &p)

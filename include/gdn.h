@@ -125,6 +125,37 @@ gdn_status gdn_prefill_chunked(const gdn_shape *shape,
                                void *o, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gdn_prefill_chunked without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It allocates nothing: its chunk workspace
+ * is the library's own device scratch of 64 MiB (67,108,864 bytes), one copy
+ * per device, allocated when the library's code is loaded on that device and
+ * held until the process ends.  Every other argument, the output and the
+ * result are those of gdn_prefill_chunked.
+ *
+ * Limit.  A batch whose chunk workspace (gdn_prefill_workspace_bytes) fits the
+ * scratch runs as with gdn_prefill_chunked.  A larger one needs
+ * cu_seqlens_host: it is then run in segments of local chunks sized to the
+ * scratch, which fails with GDN_ERR_WORKSPACE (and touches nothing) when even
+ * one chunk per sequence does not fit (at the Qwen3.5-9B shapes, 32 value
+ * heads of d = 128: 819,200 bytes per chunk slot, i.e. about 80 sequences).
+ * Without cu_seqlens_host a larger batch fails with GDN_ERR_WORKSPACE.
+ *
+ * Sharing.  All calls on one device use the same scratch and leave their
+ * contents in it (nothing has to be cleared: the calls overwrite what they
+ * read).  Calls that overlap in time on one device -- on two streams, or from
+ * two threads without ordering -- RACE on the scratch and give wrong results;
+ * the caller must order them (for example, one stream per device).
+ */
+gdn_status gdn_prefill_chunked_noalloc(const gdn_shape *shape,
+                                       const void *q, const void *k, const void *v,
+                                       const float *g, const float *beta,
+                                       const int32_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                                       const int32_t *cu_seqlens_host,
+                                       const float *initial_state, float *final_state,
+                                       void *o, void *stream);
+
+/*
  * One decode step: one new token for each of `num_seqs` independent
  * sequences, state updated IN PLACE.  Defined by the one-token matrix form
  * on the NPU page (section "How it works"): with d = exp(g) and

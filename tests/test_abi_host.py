@@ -233,3 +233,30 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(4, 1, 32)
     with pytest.raises(ValueError):
         gdn.prefill_chunked(x, x, torch.zeros(4, 2, 32), torch.zeros(4, 2), torch.zeros(4, 2))
+
+
+def test_noalloc_prefill_rejects_batches_beyond_its_scratch(lib):
+    """gdn_prefill_chunked_noalloc refuses, on the host and before any device call, a batch whose
+    chunk workspace exceeds its 64 MiB scratch when no host offsets are given, and a batch of
+    more sequences than the scratch has chunk slots even with them (GDN_ERR_WORKSPACE); and it
+    checks its other arguments as gdn_prefill_chunked does."""
+    sh = shape()
+    T = 12000                                   # 190 chunk slots of 819,200 bytes: 155 MB
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), T, 2) > (64 << 20)
+    rc = lib.gdn_prefill_chunked_noalloc(ctypes.byref(sh), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6),
+                                         2, T, None, fake(7), fake(8), fake(9), None)
+    assert rc == binding.GDN_ERR_WORKSPACE
+    assert b"scratch" in lib.gdn_last_error()
+    N = 120                                     # more sequences than its 81 chunk slots
+    cu = np.arange(0, 70 * (N + 1), 70, dtype=np.int32)
+    rc = lib.gdn_prefill_chunked_noalloc(ctypes.byref(sh), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6),
+                                         N, int(cu[-1]), cu.ctypes.data_as(ctypes.c_void_p), fake(7), fake(8),
+                                         fake(9), None)
+    assert rc == binding.GDN_ERR_WORKSPACE
+    # argument errors come first, as for the workspace entry point
+    rc = lib.gdn_prefill_chunked_noalloc(ctypes.byref(shape(d=96)), fake(1), fake(2), fake(3), fake(4), fake(5),
+                                         fake(6), 1, 128, None, fake(7), fake(8), fake(9), None)
+    assert rc == binding.GDN_ERR_UNSUPPORTED
+    rc = lib.gdn_prefill_chunked_noalloc(ctypes.byref(sh), ctypes.c_void_p(0x7f0000000008), fake(2), fake(3),
+                                         fake(4), fake(5), fake(6), 1, 128, None, fake(7), fake(8), fake(9), None)
+    assert rc == binding.GDN_ERR_INVALID_ARG
