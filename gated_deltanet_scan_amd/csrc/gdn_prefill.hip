@@ -162,6 +162,19 @@ __device__ inline size_t slot_of(const SlotMap &m, int n, int c)
     return (size_t)n * m.seg_len + (c - m.seg_first);
 }
 
+// Block index -> (item, member) such that the `members` workgroups of one item run on
+// one XCD, dispatched back to back: the 8 XCDs take workgroups round-robin (block b on
+// XCD b % 8), so an item's members take blocks 8 apart.  Used so that the workgroups
+// that read the same q and k rows (the value heads of a query/key group, and the
+// column slices of each) share one XCD's L2.  A grid of ceil(items / 8) * 8 * members
+// blocks covers every (item, member) once.
+__device__ inline void xcd_group(int bid, int members, int &item, int &member)
+{
+    const int k = bid >> 3;
+    member = k % members;
+    item = (k / members) * 8 + (bid & 7);
+}
+
 // Byte layout of a staged tile with rows of RB bytes: row r holds its 16-byte
 // chunk j at position j ^ perm(r).  perm is injective over 16 consecutive rows
 // of one 256-byte line and moves 4 consecutive rows by even amounts, so that
@@ -223,8 +236,9 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
                                 f32x4 (&akeep)[NKEEP][HB], int nh, int wv, int lane, bf16 *wout, bf16 *mout);
 
 // ---------------------------------------------------------------------------
-// Prep kernel.  One workgroup per (chunk slot, query/key head); writes, for
-// every value head h of the group,
+// Prep kernel.  One workgroup per (chunk slot, query/key head), or per (chunk
+// slot, value head) in the absorbed form; writes, for every value head h of the
+// workgroup,
 //   tmat[slot][h] = (I + N)^-1   (C x C, row-major, unit lower triangular)
 //   amat[slot][h] = scale [exp(G_t - G_j) q_t.k_j]_{j<=t}  (C x C, zero above)
 //   dec[slot][h]  = [exp(G) | exp(G_last - G) | beta | beta exp(G)]
@@ -250,12 +264,11 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
 // of the NPU page applied to the block-triangular split, in fp32 on the
 // matrix cores.
 // ---------------------------------------------------------------------------
-// Waves of a prep workgroup: four in the direct form (two workgroups fit a CU); eight in
-// the absorbed form, whose workgroup needs about 94 KB of LDS (one per CU) and whose
-// products with T then give one (value head, block column of T) to each wave.
+// Waves of a prep workgroup: four, with one block column of T per wave in the products of
+// the absorbed form.
 template <typename E, int C>
 struct PrepWaves {
-    static constexpr int value = AbsorbedForm<E, C>::value ? 8 : 4;
+    static constexpr int value = 4;
 };
 
 template <typename E, int C, int DK>
@@ -263,12 +276,16 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
     const E *__restrict__ q, const E *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, SlotMap map, int32_t num_seqs,
     int64_t total_tokens, int32_t hqk, int32_t hv, E *__restrict__ tmat, E *__restrict__ amat,
-    float *__restrict__ dec, float scale)
+    float *__restrict__ dec, float scale, int32_t nslots)
 {
     constexpr int ES = (int)sizeof(E);
     constexpr int LDF = C + 4;      // fp32 C x C rows
     constexpr int RT = C / 16;      // 16-row blocks
-    constexpr int HB = 2;           // value heads per pass
+    // value heads per workgroup pass: the two of a query/key group share its Gram products
+    // (direct form, two workgroups of about 74 KB per CU); in the absorbed form, whose pass
+    // keeps k and T alive together, one value head per workgroup (about 53 KB, three per CU;
+    // the grid runs over value heads and each computes its group's Gram products)
+    constexpr int HB = AbsorbedForm<E, C>::value ? 1 : 2;
     constexpr int VN = Vec16<E>::n;
     typedef typename Vec16<E>::type V16;
     typedef typename MmaFor<E, DK>::type MK;
@@ -299,22 +316,41 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
         (__attribute__((address_space(3))) unsigned char *)smem_qk;
 
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int hq = blockIdx.y;
+    const int group = hv / hqk;
+    // chunk slot, query/key head, first value head and number of value heads of this
+    // workgroup.  One value head per workgroup: a 1-D grid over (slot, query/key head)
+    // items whose value heads share an XCD (their q and k rows then meet in its L2).
+    int sidx, hq, hfirst, nheads;
+    if constexpr (HB == 1) {
+        int item, member;
+        xcd_group(blockIdx.x, group, item, member);
+        if (item >= nslots * hqk)
+            return;
+        sidx = item / hqk;
+        hq = item - sidx * hqk;
+        hfirst = hq * group + member;
+        nheads = 1;
+    } else {
+        sidx = blockIdx.x;
+        hq = blockIdx.y;
+        hfirst = hq * group;
+        nheads = group;
+    }
     int n, c;
     size_t slot;
     if (map.chunk_start) {
-        const int32_t e = blockIdx.x;
+        const int32_t e = sidx;
         if (e >= map.chunk_start[num_seqs])
             return;
         n = find_sequence(map.chunk_start, num_seqs, e);
         c = e - map.chunk_start[n];
         slot = e;
     } else {
-        n = blockIdx.x / map.seg_len;
-        c = map.seg_first + (int)(blockIdx.x - n * map.seg_len);
+        n = sidx / map.seg_len;
+        c = map.seg_first + (int)(sidx - n * map.seg_len);
         if (n >= num_seqs || c >= seq_chunks(map, cu, n, total_tokens, C))
             return;
-        slot = blockIdx.x;
+        slot = sidx;
     }
     int64_t a, b;
     seq_range(cu, n, total_tokens, a, b);
@@ -343,9 +379,8 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
     };
 
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const int group = hv / hqk;
-    for (int hb = 0; hb < group; hb += HB) {
-        const int nh = min(HB, group - hb);
+    for (int hb = 0; hb < nheads; hb += HB) {
+        const int nh = min(HB, nheads - hb);
         // g and beta of the pass's value heads, one token per lane, in every wave (issued
         // before the q, k rows); padding tokens carry g = 0, beta = 0
         float gv[HB], bv[HB];
@@ -354,7 +389,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
             gv[hh] = 0.f;
             bv[hh] = 0.f;
             if (hh < nh && lane < len) {
-                const int h = hq * group + hb + hh;
+                const int h = hfirst + hb + hh;
                 gv[hh] = g[(size_t)(t0 + lane) * hv + h];
                 bv[hh] = beta[(size_t)(t0 + lane) * hv + h];
             }
@@ -376,7 +411,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
             }
         }
         if (wv < nh && lane < C) {
-            const int h = hq * group + hb + wv;
+            const int h = hfirst + hb + wv;
             const float G = wv == 0 ? Gr[0] : Gr[HB - 1];
             const float Glast = __shfl(G, C - 1, kWave);
             float *rec = dec + (slot * hv + h) * 4 * C;
@@ -429,7 +464,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
                 for (int hh = 0; hh < HB; ++hh) {
                     if (hh >= nh)
                         break;
-                    const int h = hq * group + hb + hh;
+                    const int h = hfirst + hb + hh;
                     const float gt = Gw[wv][hh][t], bt = Bw[wv][hh][t];
                     const f32x4 gj = *reinterpret_cast<const f32x4 *>(&Gw[wv][hh][j0]);
                     f32x4 nv, av;
@@ -451,7 +486,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
 #pragma unroll
                 for (int hh = 0; hh < HB; ++hh)
                     if (hh < nh)
-                        store4(amat + (slot * hv + hq * group + hb + hh) * C * C + t * C + j0, 0.f, 0.f, 0.f, 0.f);
+                        store4(amat + (slot * hv + hfirst + hb + hh) * C * C + t * C + j0, 0.f, 0.f, 0.f, 0.f);
             }
           });
         };
@@ -537,8 +572,8 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
 
         if constexpr (ABSORB) {
             absorb_products<C, DK, PW, HB, NKEEP>(Ks, Tf, Nm, Gw[wv], akeep, nh, wv, lane,
-                                                  tmat + (slot * hv + hq * group + hb) * DK * C,
-                                                  amat + (slot * hv + hq * group + hb) * C * C);
+                                                  tmat + (slot * hv + hfirst + hb) * DK * C,
+                                                  amat + (slot * hv + hfirst + hb) * C * C);
             __syncthreads();
             continue;
         }
@@ -547,7 +582,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
             const int hh = idx / (C * C / VN);
             const int rem = (idx - hh * (C * C / VN)) * VN;
             const int t = rem / C, j0 = rem - (rem / C) * C;
-            const int h = hq * group + hb + hh;
+            const int h = hfirst + hb + hh;
             V16 tv;
 #pragma unroll
             for (int e4 = 0; e4 < VN; e4 += 4) {
@@ -592,9 +627,10 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
 // element j % 4 of input lane j / 4's read for each of the 4 rows); with fp32
 // every lane reads its single element.
 //
-// Block index -> work: the 8 XCDs take workgroups round-robin, so the dv
-// slices of one (sequence, head) are placed on one XCD (shared Q, K, T, A
-// reads then hit the same L2).
+// Block index -> work (xcd_group): the value heads of one (sequence, query/key
+// head) and all their dv slices are placed on one XCD, so that their shared Q
+// and K reads (and a head's W and M, read by each of its slices) hit the same
+// L2.
 // ---------------------------------------------------------------------------
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -900,10 +936,13 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_kernel(
     const int r16 = lane & 15, g4 = 4 * (lane >> 4);
     const int nv = dv / DVS;
     const int pairs = num_seqs * hv;
-    const int bid = blockIdx.x;
-    const int j8 = bid >> 3;
-    const int pair = (j8 / nv) * 8 + (bid & 7);
-    const int s = j8 % nv;
+    // item = (sequence rank, query/key head); its members are the group's value heads
+    // times their column slices
+    const int group = hv / hqk;
+    int item, member;
+    xcd_group(blockIdx.x, group * nv, item, member);
+    const int pair = item * group + member / nv;
+    const int s = member % nv;
     if (pair >= pairs)
         return;
     const int n = ranked_sequence(map, pair / hv), h = pair - (pair / hv) * hv;
@@ -1343,10 +1382,13 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     const int lw = wave - kWaves;                    // loader index
     const int nv = dv / DVS;
     const int pairs = num_seqs * hv;
-    const int bid = blockIdx.x;
-    const int j8 = bid >> 3;
-    const int pair = (j8 / nv) * 8 + (bid & 7);
-    const int s = j8 % nv;
+    // item = (sequence rank, query/key head); its members are the group's value heads
+    // times their column slices
+    const int group = hv / hqk;
+    int item, member;
+    xcd_group(blockIdx.x, group * nv, item, member);
+    const int pair = item * group + member / nv;
+    const int s = member % nv;
     if (pair >= pairs)
         return;
     const int n = ranked_sequence(map, pair / hv), h = pair - (pair / hv) * hv;
@@ -1717,10 +1759,13 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
     const int r16 = lane & 15, G = lane >> 4, g4 = 4 * G;
     const int nv = dv / DVS;
     const int pairs = num_seqs * hv;
-    const int bid = blockIdx.x;
-    const int j8 = bid >> 3;
-    const int pair = (j8 / nv) * 8 + (bid & 7);
-    const int s = j8 % nv;
+    // item = (sequence rank, query/key head); its members are the group's value heads
+    // times their column slices
+    const int group = hv / hqk;
+    int item, member;
+    xcd_group(blockIdx.x, group * nv, item, member);
+    const int pair = item * group + member / nv;
+    const int s = member % nv;
     if (pair >= pairs)
         return;
     const int n = ranked_sequence(map, pair / hv), h = pair - (pair / hv) * hv;
@@ -2074,7 +2119,8 @@ static void launch_scan(const PrefillArgs &p, const SlotMap &map, const E *tmat,
 {
     const int nv = p.dv / (16 * NW);
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
-    const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
+    const int64_t items = (int64_t)p.num_seqs * p.hqk;                 // (sequence, query/key head)
+    const int64_t blocks = ((items + 7) / 8) * 8 * (p.hv / p.hqk) * nv;
     const ProfEvents ev = prof_events(PROF_SCAN, PROF_SCAN_PLAIN);
     hipExtLaunchKernelGGL((gdn_chunk_scan_kernel<E, C, DK, NW>), dim3((unsigned)blocks), dim3(NW * kWave), 0, st,
                           ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k),
@@ -2088,7 +2134,8 @@ static void launch_scan_rows(const PrefillArgs &p, const SlotMap &map, const bf1
 {
     const int nv = p.dv / DVS;
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
-    const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
+    const int64_t items = (int64_t)p.num_seqs * p.hqk;                 // (sequence, query/key head)
+    const int64_t blocks = ((items + 7) / 8) * 8 * (p.hv / p.hqk) * nv;
     const ProfEvents ev = prof_events(PROF_SCAN, PROF_SCAN_ROWS);
     // two stage buffers (with W and M, three of dk = 128 would not fit in LDS)
     constexpr int NSTAGE = 2;
@@ -2105,7 +2152,8 @@ static void launch_scan_bf16(const PrefillArgs &p, const SlotMap &map, const bf1
 {
     const int nv = p.dv / (16 * CT * NW);
     const int64_t pairs = (int64_t)p.num_seqs * p.hv;
-    const int64_t blocks = ((pairs + 7) / 8) * 8 * nv;
+    const int64_t items = (int64_t)p.num_seqs * p.hqk;                 // (sequence, query/key head)
+    const int64_t blocks = ((items + 7) / 8) * 8 * (p.hv / p.hqk) * nv;
     const ProfEvents ev = prof_events(PROF_SCAN, PROF_SCAN_WIDE);
     hipExtLaunchKernelGGL((gdn_chunk_scan_bf16_kernel<DK, NW, CT>), dim3((unsigned)blocks), dim3(NW * kWave), 0,
                           st, ev.start, ev.stop, 0, static_cast<const bf16 *>(p.q), static_cast<const bf16 *>(p.k),
@@ -2171,11 +2219,17 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
     };
     auto prep = [&](const SlotMap &map, int64_t slots) {
         const ProfEvents ev = prof_events(PROF_PREP);
-        hipExtLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), dim3((unsigned)slots, p.hqk),
+        // grid: (chunk slot, query/key head); in the absorbed form (one value head per
+        // workgroup) 1-D, ceil(slots * HQK / 8) * 8 * group blocks (xcd_group)
+        const int64_t items = slots * p.hqk;
+        const dim3 grid = AbsorbedForm<E, C>::value
+                              ? dim3((unsigned)(((items + 7) / 8) * 8 * (p.hv / p.hqk)))
+                              : dim3((unsigned)slots, (unsigned)p.hqk);
+        hipExtLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), grid,
                               dim3(PrepWaves<E, C>::value * kWave), 0, st,
                               ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k), p.g,
                               p.beta, p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv, tmat, amat, dec,
-                              p.scale);
+                              p.scale, (int32_t)slots);
     };
 
     // Longest sequences first in the scans (their chains of chunk steps bound the time).
