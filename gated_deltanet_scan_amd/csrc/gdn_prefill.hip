@@ -232,7 +232,7 @@ struct AbsorbedForm {
 };
 
 template <int C, int DK, int PW, int HB, int NKEEP>
-__device__ void absorb_products(const unsigned char *Ks, const float *Tf, float *Am, const float (*Gv)[C],
+__device__ void absorb_products(const unsigned char *Ks, const float *Tf, float *Am, float (*Gv)[C],
                                 f32x4 (&akeep)[NKEEP][HB], int nh, int wv, int lane, bf16 *wout, bf16 *mout);
 
 // ---------------------------------------------------------------------------
@@ -746,6 +746,14 @@ struct KtOperand<float, MC, MK, S> {
     }
 };
 
+// Orders this wave's LDS accesses before and after it (lanes of one wave).
+__device__ inline void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Round x to bf16 (hi) and the remainder to bf16 (lo): hi + lo carries about 16
 // significant bits, and products of hi/lo pairs accumulated in fp32 give sums that
 // cancel accurately.
@@ -763,19 +771,24 @@ __device__ inline void split_bf16(float x, bf16 &hi, bf16 &lo)
 //   W^T (rows t of block jb, columns i) = (diag(lambda) T)^T K      (two products per step)
 //   M^T (rows j of block jb, columns t) = T^T A^T                   (three: hi hi, hi lo, lo hi)
 // are formed transposed so that each lane stores four consecutive elements of one row
-// of W or M.  M is zero above its diagonal blocks, written as such.
+// of W or M.  M is zero above its diagonal blocks, written as such.  A goes to the N region
+// (which the solve no longer reads) as a hi and a lo bf16 matrix, C rows of C elements in
+// the Swz chunk order, so that each operand fragment of A^T is one 16-byte read.
 template <int C, int DK, int PW, int HB, int NKEEP>
-__device__ void absorb_products(const unsigned char *Ks, const float *Tf, float *Am, const float (*Gv)[C],
+__device__ void absorb_products(const unsigned char *Ks, const float *Tf, float *Am, float (*Gv)[C],
                                 f32x4 (&akeep)[NKEEP][HB], int nh, int wv, int lane, bf16 *wout, bf16 *mout)
 {
     constexpr int LDF = C + 4, RT = C / 16, NS = C / 32;
     typedef Mma<bf16> M;
     typedef KtOperand<bf16, M, MmaBf16K16, Swz<DK * 2>> KT;
+    typedef Swz<C * 2> SA;
     static_assert(C % 32 == 0 && DK % 16 == 0, "32-wide chunk steps, 16-row key tiles");
+    static_assert(HB * 2 * C * C * 2 <= HB * C * LDF * 4, "hi and lo A fit the N region");
     const int r16 = lane & 15, G = lane >> 4;
+    unsigned char *const Ab = reinterpret_cast<unsigned char *>(Am);   // [HB][hi | lo][C rows of 2 C bytes]
 
-    // A (fp32) into the N region, which the solve no longer reads; tiles above the
-    // diagonal as zeros (the deal of the Gram tiles decides which wave writes what)
+    // A as hi/lo bf16 into the N region; tiles above the diagonal as zeros (the deal of the
+    // Gram tiles decides which wave writes what)
     static_for<RT * RT>([&](auto pc) {
         constexpr int P = decltype(pc)::value;
         constexpr int tr = P / RT, tc = P % RT;
@@ -791,34 +804,52 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
             f32x4 v = zero4();
             if constexpr (lower)
                 v = akeep[idx / PW][hh];
-            *reinterpret_cast<f32x4 *>(Am + (hh * C + t) * LDF + j0) = v;
+            bf16x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                bf16 h0, l0;
+                split_bf16(v[e], h0, l0);
+                hi[e] = h0;
+                lo[e] = l0;
+            }
+            unsigned char *base = Ab + hh * 2 * C * C * 2;
+            *reinterpret_cast<bf16x4 *>(base + SA::off(t, 2 * j0)) = hi;
+            *reinterpret_cast<bf16x4 *>(base + C * C * 2 + SA::off(t, 2 * j0)) = lo;
         }
     });
     __syncthreads();
 
-    static_assert(PW == RT * HB, "one (head, block column) per wave");
     const int hh = wv / RT, jb = wv % RT, j = 16 * jb + r16;
     if (hh < nh) {
         const float *Th = Tf + hh * C * LDF;
-        const float *Ah = Am + hh * C * LDF;
-        const float gl = Gv[hh][C - 1];
+        const unsigned char *Ahi = Ab + hh * 2 * C * C * 2, *Alo = Ahi + C * C * 2;
+        // lambda_m = exp(G_last - G_m) over this wave's own copy of G (read back by itself)
+        {
+            const float lam = expf(Gv[hh][C - 1] - Gv[hh][lane & (C - 1)]);
+            wave_lds_sync();
+            if (lane < C)
+                Gv[hh][lane] = lam;
+            wave_lds_sync();
+        }
         // column j of T (zero above the diagonal blocks) and of diag(lambda) T, contraction
         // rows 32 s + 8 G + {0..7}, as hi/lo pairs
         bf16x8 thi[NS], tlo[NS], lhi[NS], llo[NS];
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
+            const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&Gv[hh][32 * st + 8 * G]);
+            const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&Gv[hh][32 * st + 8 * G + 4]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int m = 32 * st + 8 * G + e;
                 const float tv = ((m >> 4) >= jb) ? Th[m * LDF + j] : 0.f;
-                const float lv = tv * expf(gl - Gv[hh][m]);
-                bf16 h0, l0, h1, l1;
-                split_bf16(tv, h0, l0);
-                split_bf16(lv, h1, l1);
+                const float lv = tv * (e < 4 ? l0[e] : l1[e - 4]);
+                bf16 h0, lo0, h1, lo1;
+                split_bf16(tv, h0, lo0);
+                split_bf16(lv, h1, lo1);
                 thi[st][e] = h0;
-                tlo[st][e] = l0;
+                tlo[st][e] = lo0;
                 lhi[st][e] = h1;
-                llo[st][e] = l1;
+                llo[st][e] = lo1;
             }
         }
         // W^T tiles (rows t of block jb, columns i of key block it): lane stores
@@ -844,20 +875,9 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
             if (tt >= jb) {
 #pragma unroll
                 for (int st = 0; st < NS; ++st) {
-                    const float *ar = Ah + (16 * tt + r16) * LDF + 32 * st + 8 * G;
-                    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(ar);
-                    const f32x4 a1 = *reinterpret_cast<const f32x4 *>(ar + 4);
-                    bf16x8 ahi, alo;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        bf16 h, l;
-                        split_bf16(a0[e], h, l);
-                        ahi[e] = h;
-                        alo[e] = l;
-                        split_bf16(a1[e], h, l);
-                        ahi[e + 4] = h;
-                        alo[e + 4] = l;
-                    }
+                    const int off = SA::off(16 * tt + r16, 64 * st + 16 * G);
+                    const bf16x8 ahi = *reinterpret_cast<const bf16x8 *>(Ahi + off);
+                    const bf16x8 alo = *reinterpret_cast<const bf16x8 *>(Alo + off);
                     acc = M::mma(thi[st], ahi, acc);
                     acc = M::mma(thi[st], alo, acc);
                     acc = M::mma(tlo[st], ahi, acc);
@@ -868,12 +888,6 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
     }
 }
 
-__device__ inline void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 template <typename E, int C, int DK, int NW>
 __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_kernel(
@@ -1341,15 +1355,19 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     static_assert(C <= kWave, "one lane per token of a chunk");
     static_assert(DVS % 16 == 0 && DK % 16 == 0 && C % 16 == 0, "16x16 tiles");
 
-    // stage buffer layout (bytes) and the 1 KB direct-to-LDS load jobs that fill it:
-    // Q, K (C x DK), W (DK x C), M (C x C), the V slice (C x DVS) and the decay record
+    // Stage buffers (bytes) and the 1 KB direct-to-LDS load jobs that fill them.  A chunk is
+    // staged in two parts: part A, Q, K (C x DK) and the V slice (C x DVS), read only before
+    // the step's first barrier; part B, W (DK x C), M (C x C) and the decay record, read
+    // through the step.  Part A has NSTAGE buffers (it can be refilled two chunks ahead once
+    // the step has passed its first barrier), part B two.
     constexpr int OFF_Q = 0;
     constexpr int OFF_K = OFF_Q + C * DK * ES;
-    constexpr int OFF_W = OFF_K + C * DK * ES;
+    constexpr int OFF_V = OFF_K + C * DK * ES;
+    constexpr int STAGE_A = OFF_V + C * DVS * ES;
+    constexpr int OFF_W = 0;
     constexpr int OFF_M = OFF_W + DK * C * ES;
-    constexpr int OFF_V = OFF_M + C * C * ES;
-    constexpr int OFF_D = OFF_V + C * DVS * ES;
-    constexpr int STAGE = OFF_D + 4 * C * 4;
+    constexpr int OFF_D = OFF_M + C * C * ES;
+    constexpr int STAGE_B = OFF_D + 4 * C * 4;
     constexpr int NCK_QK = C * DK * ES / 16;   // 16-byte chunks per tile
     constexpr int NCK_W = DK * C * ES / 16;
     constexpr int NCK_M = C * C * ES / 16;
@@ -1362,21 +1380,24 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     constexpr int NJ_D = (NCK_D + 63) / 64;
     constexpr int J_W = 2 * NJ_QK, J_M = J_W + NJ_W, J_V = J_M + NJ_M, J_D = J_V + NJ_V;
     constexpr int NJ = J_D + NJ_D;
-    static_assert(STAGE % 16 == 0 && OFF_D % 16 == 0, "16-byte aligned stage blocks");
+    static_assert(STAGE_A % 1024 == 0 && STAGE_B % 16 == 0 && OFF_D % 16 == 0, "16-byte aligned stage blocks");
     static_assert(AbsorbedForm<E, C>::value, "the row-split scan reads the absorbed form");
 
-    // NSTAGE stage buffers: the loaders fill chunk c + NSTAGE - 1 while the compute waves
-    // work on chunk c
-    static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three stage buffers");
-    static_assert(NSTAGE * STAGE + DVS * LDC * ES + DVS * LDK * ES <= 163840,
+    // While the compute waves work on chunk c, the loaders fill part B of chunk c + 1 and
+    // part A of chunk c + NSTAGE - 1.
+    static_assert(NSTAGE == 2 || NSTAGE == 3, "two or three part-A buffers");
+    static_assert(NSTAGE * STAGE_A + 2 * STAGE_B + DVS * LDC * ES + DVS * LDK * ES <= 163840,
                   "stage buffers and exchange tiles must fit the 160 KB of LDS");
-    __shared__ __attribute__((aligned(1024))) unsigned char stage_mem[NSTAGE * STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char stage_a[NSTAGE * STAGE_A];
+    __shared__ __attribute__((aligned(1024))) unsigned char stage_b[2 * STAGE_B];
     __shared__ __attribute__((aligned(16))) E Xt[DVS * LDC];
     __shared__ __attribute__((aligned(16))) E St[DVS * LDK];
 
     // the stage buffers as LDS addresses (the direct loads write LDS by address)
-    __attribute__((address_space(3))) unsigned char *const lds_stage =
-        (__attribute__((address_space(3))) unsigned char *)stage_mem;
+    __attribute__((address_space(3))) unsigned char *const lds_a =
+        (__attribute__((address_space(3))) unsigned char *)stage_a;
+    __attribute__((address_space(3))) unsigned char *const lds_b =
+        (__attribute__((address_space(3))) unsigned char *)stage_b;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const bool loader = wave >= kWaves;              // waves 4..7 stage chunks, 0..3 compute
     const int lw = wave - kWaves;                    // loader index
@@ -1433,7 +1454,8 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         }
     }
 
-    // ---- loaders: chunk c straight into stage buffer c % NSTAGE (direct-to-LDS loads) ----
+    // ---- loaders: part A of chunk c into buffer c % NSTAGE of stage_a, part B into buffer
+    //      c % 2 of stage_b (direct-to-LDS loads) ----
     // Job J (of NJ) moves 1 KB of the stage with one load: lane i writes the 16 bytes at
     // 16 i of the job's block.  Loader lw runs jobs lw, lw + 4, ...; which tile and rows a
     // job covers is fixed at compile time (one code path per loader), and all loads of a
@@ -1471,10 +1493,13 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
             return min((J - J_D) * 64 + lane, NCK_D - 1) * 4;   // floats
         }
     };
-    // Stage chunk c.  Rows past the chunk's last real row are loaded from it.
-    auto issue_jobs = [&](auto wc, int c) __attribute__((always_inline)) {
+    // Stage part PART (0: A, 1: B) of chunk c.  Rows past the chunk's last real row are
+    // loaded from it.
+    auto issue_jobs = [&](auto wc, auto partc, int c) __attribute__((always_inline)) {
         constexpr int W = decltype(wc)::value;
-        __attribute__((address_space(3))) unsigned char *stg = lds_stage + (c % NSTAGE) * STAGE;
+        constexpr int PART = decltype(partc)::value;
+        __attribute__((address_space(3))) unsigned char *stg =
+            PART == 0 ? lds_a + (c % NSTAGE) * STAGE_A : lds_b + (c & 1) * STAGE_B;
         const int64_t t0 = a + (int64_t)c * C;
         const int last = (int)min<int64_t>(C, b - t0) - 1;   // >= 0 for every chunk of the sequence
         const size_t slot = slot_begin + (size_t)(c - c_begin);
@@ -1486,7 +1511,8 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         const E *db = reinterpret_cast<const E *>(dec + (slot * hv + h) * 4 * C);
         static_for<NJ_PER>([&](auto uc) {
             constexpr int J = W + decltype(uc)::value * kWaves;
-            if constexpr (J < NJ) {
+            constexpr bool in_a = J < J_W || (J >= J_V && J < J_D);   // Q, K, V
+            if constexpr (J < NJ && in_a == (PART == 0)) {
                 constexpr std::integral_constant<int, J> jc{};
                 const E *base;
                 int off = job_off(jc, min(job_row(jc), last));
@@ -1522,9 +1548,10 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         }
     };
     // ---- compute waves: one chunk step on stage buffer `cur` (barrier B1 inside) ----
-    auto step = [&](int cur, int64_t t0, int len) __attribute__((always_inline)) {
-        const unsigned char *stg = stage_mem + cur * STAGE;
-        const float *Gs = reinterpret_cast<const float *>(stg + OFF_D);   // exp(G)
+    auto step = [&](int c, int64_t t0, int len) __attribute__((always_inline)) {
+        const unsigned char *stg = stage_a + (c % NSTAGE) * STAGE_A;     // Q, K, V
+        const unsigned char *stb = stage_b + (c & 1) * STAGE_B;          // W, M, record
+        const float *Gs = reinterpret_cast<const float *>(stb + OFF_D);   // exp(G)
         const float *Bet = Gs + 2 * C;                                     // beta
         const float *BGam = Gs + 3 * C;                                    // beta exp(G)
 
@@ -1580,7 +1607,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
                 const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
 #pragma unroll
                 for (int k0 = 0; k0 < C; k0 += MC::kStep) {
-                    const auto am = staged_frag<MC, SC, E>(stg + OFF_M, rt * 16 + r, k0 + kk);
+                    const auto am = staged_frag<MC, SC, E>(stb + OFF_M, rt * 16 + r, k0 + kk);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
                         oacc[u][ct] = MC::mma(MC::load(Xt + (ct * 16 + r) * LDC + k0 + kk), am, oacc[u][ct]);
@@ -1607,7 +1634,7 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
                 const int r = lane & 15, kk = (lane >> 4) * MC::kPerLane;
 #pragma unroll
                 for (int k0 = 0; k0 < C; k0 += MC::kStep) {
-                    const auto aw = staged_frag<MC, SC, E>(stg + OFF_W, sr * 16 + r, k0 + kk);
+                    const auto aw = staged_frag<MC, SC, E>(stb + OFF_W, sr * 16 + r, k0 + kk);
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct)
                         sacc[u][ct] = MC::mma(aw, MC::load(Xt + (ct * 16 + r) * LDC + k0 + kk), sacc[u][ct]);
@@ -1620,27 +1647,39 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
         }
     };
 
-    // ---- pipeline: while the compute waves work on chunk c (stage c % NSTAGE), the
-    //      loaders stage chunk c + NSTAGE - 1.  The direct loads are not tracked by the
-    //      compiler's LDS dependences: before the barrier that ends a step, each loader
-    //      waits until its loads of chunk c + 1 have landed, leaving those of a later chunk
-    //      in flight (the counter retires loads in issue order).  The loaders take bare
-    //      barriers: a fenced one would first wait for all their loads. ----
-    // wait for all of this loader's loads but those of one chunk (jobs W, W + 4, ... < NJ)
-    auto wait_all_but_one_chunk = [&](auto wc) __attribute__((always_inline)) {
+    // ---- pipeline: while the compute waves work on chunk c, the loaders stage part B of
+    //      chunk c + 1 and then part A of chunk c + NSTAGE - 1 (part A of chunk c is dead
+    //      once the step passes its first barrier, part B of chunk c - 1 once the previous
+    //      step ended).  The direct loads are not tracked by the compiler's LDS dependences:
+    //      before the barrier that ends a step, each loader waits until every load of chunk
+    //      c + 1 has landed, leaving only its part-A loads of chunk c + 2 in flight (the
+    //      counter retires loads in issue order).  The loaders take bare barriers: a fenced
+    //      one would first wait for all their loads. ----
+    // wait for all of this loader's loads but its part-A jobs of one chunk (jobs W, W + 4, ...)
+    auto wait_all_but_part_a = [&](auto wc) __attribute__((always_inline)) {
         constexpr int W = decltype(wc)::value;
-        constexpr int cnt = W < NJ ? (NJ - W + kWaves - 1) / kWaves : 0;
+        constexpr int cnt = [] {
+            int n = 0;
+            for (int J = W; J < NJ; J += kWaves)
+                n += (J < J_W || (J >= J_V && J < J_D)) ? 1 : 0;
+            return n;
+        }();
         static_assert(cnt < 64, "vmcnt holds at most 63");
         __builtin_amdgcn_s_waitcnt((cnt & 15) | ((cnt >> 4) << 14) | 0x0f70);   // vmcnt(cnt) only
         asm volatile("" ::: "memory");
     };
-    constexpr int AHEAD = NSTAGE - 1;
+    constexpr std::integral_constant<int, 0> part_a{};
+    constexpr std::integral_constant<int, 1> part_b{};
+    constexpr int AHEAD = NSTAGE - 1;   // chunks of lead of part A
     if (loader) {
-        by_loader([&](auto wc) { issue_jobs(wc, c_begin); });
+        by_loader([&](auto wc) {
+            issue_jobs(wc, part_a, c_begin);
+            issue_jobs(wc, part_b, c_begin);
+        });
         if (AHEAD == 2 && c_begin + 1 < c_end)
             by_loader([&](auto wc) {
-                issue_jobs(wc, c_begin + 1);
-                wait_all_but_one_chunk(wc);
+                issue_jobs(wc, part_a, c_begin + 1);
+                wait_all_but_part_a(wc);
             });
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -1651,18 +1690,20 @@ __global__ __launch_bounds__(kScanThreads) void gdn_chunk_scan_rows_kernel(
     }
     for (int c = c_begin; c < c_end; ++c) {
         if (loader) {
+            if (c + 1 < c_end)
+                by_loader([&](auto wc) { issue_jobs(wc, part_b, c + 1); });
             if (c + AHEAD < c_end)
-                by_loader([&](auto wc) { issue_jobs(wc, c + AHEAD); });
+                by_loader([&](auto wc) { issue_jobs(wc, part_a, c + AHEAD); });
             // B1 of the compute waves: the loaders publish nothing there
             __builtin_amdgcn_s_barrier();
             if (AHEAD == 2 && c + 2 < c_end)
-                by_loader([&](auto wc) { wait_all_but_one_chunk(wc); });
+                by_loader([&](auto wc) { wait_all_but_part_a(wc); });
             else
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();   // end of step: chunk c + 1 is staged
         } else {
             const int64_t ct0 = a + (int64_t)c * C;
-            step(c % NSTAGE, ct0, (int)min<int64_t>(C, b - ct0));
+            step(c, ct0, (int)min<int64_t>(C, b - ct0));
             __syncthreads();   // end of step: St is complete
         }
     }
@@ -2137,8 +2178,9 @@ static void launch_scan_rows(const PrefillArgs &p, const SlotMap &map, const bf1
     const int64_t items = (int64_t)p.num_seqs * p.hqk;                 // (sequence, query/key head)
     const int64_t blocks = ((items + 7) / 8) * 8 * (p.hv / p.hqk) * nv;
     const ProfEvents ev = prof_events(PROF_SCAN, PROF_SCAN_ROWS);
-    // two stage buffers (with W and M, three of dk = 128 would not fit in LDS)
-    constexpr int NSTAGE = 2;
+    // part-A (Q, K, V) buffers: three where one workgroup per CU is the occupancy anyway
+    // (dk = 128), two for smaller dk (two workgroups per CU)
+    constexpr int NSTAGE = DK >= 128 ? 3 : 2;
     hipExtLaunchKernelGGL((gdn_chunk_scan_rows_kernel<bf16, 64, DK, DVS, NSTAGE>), dim3((unsigned)blocks),
                           dim3(kScanThreads), 0, st, ev.start, ev.stop, 0, static_cast<const bf16 *>(p.q),
                           static_cast<const bf16 *>(p.k), static_cast<const bf16 *>(p.v), p.cu_seqlens, map,
