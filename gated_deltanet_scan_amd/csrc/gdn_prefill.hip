@@ -770,8 +770,9 @@ __device__ inline void split_bf16(float x, bf16 &hi, bf16 &lo)
 // of its T: the fp32 values, and those of diag(lambda) T, become hi/lo bf16 operand pairs, and
 //   W^T (rows t of block jb, columns i) = (diag(lambda) T)^T K      (two products per step)
 //   M^T (rows j of block jb, columns t) = T^T A^T                   (three: hi hi, hi lo, lo hi)
-// are formed transposed so that each lane stores four consecutive elements of one row
-// of W or M.  M is zero above its diagonal blocks, written as such.  A goes to the N region
+// are formed transposed (each lane holds four consecutive elements of one row of W or M)
+// and written out as whole rows through LDS.  M is zero above its diagonal blocks, written
+// as such.  A goes to the N region
 // (which the solve no longer reads) as a hi and a lo bf16 matrix, C rows of C elements in
 // the Swz chunk order, so that each operand fragment of A^T is one 16-byte read.
 template <int C, int DK, int PW, int HB, int NKEEP>
@@ -782,6 +783,7 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
     typedef Mma<bf16> M;
     typedef KtOperand<bf16, M, MmaBf16K16, Swz<DK * 2>> KT;
     typedef Swz<C * 2> SA;
+    constexpr int TILE_BYTES = C * DK * 2;   // the staged k rows (T follows them)
     static_assert(C % 32 == 0 && DK % 16 == 0, "32-wide chunk steps, 16-row key tiles");
     static_assert(HB * 2 * C * C * 2 <= HB * C * LDF * 4, "hi and lo A fit the N region");
     const int r16 = lane & 15, G = lane >> 4;
@@ -820,6 +822,7 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
     __syncthreads();
 
     const int hh = wv / RT, jb = wv % RT, j = 16 * jb + r16;
+    f32x4 wres[DK / 16], mres[RT];
     if (hh < nh) {
         const float *Th = Tf + hh * C * LDF;
         const unsigned char *Ahi = Ab + hh * 2 * C * C * 2, *Alo = Ahi + C * C * 2;
@@ -852,9 +855,8 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
                 llo[st][e] = lo1;
             }
         }
-        // W^T tiles (rows t of block jb, columns i of key block it): lane stores
+        // W^T tiles (rows t of block jb, columns i of key block it): lane holds
         // W[16 it + l % 16][16 jb + 4 G .. + 3]
-        bf16 *wh = wout + (size_t)hh * DK * C;
 #pragma unroll
         for (int it = 0; it < DK / 16; ++it) {
             f32x4 acc = zero4();
@@ -864,11 +866,10 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
                 acc = M::mma(lhi[st], kf, acc);
                 acc = M::mma(llo[st], kf, acc);
             }
-            store4(wh + (16 * it + r16) * C + 16 * jb + 4 * G, acc[0], acc[1], acc[2], acc[3]);
+            wres[it] = acc;
         }
-        // M^T tiles (rows j of block jb, columns t of block tt): lane stores
+        // M^T tiles (rows j of block jb, columns t of block tt): lane holds
         // M[16 tt + l % 16][16 jb + 4 G .. + 3]; zero for tt < jb
-        bf16 *mh = mout + (size_t)hh * C * C;
 #pragma unroll
         for (int tt = 0; tt < RT; ++tt) {
             f32x4 acc = zero4();
@@ -883,7 +884,40 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
                     acc = M::mma(tlo[st], ahi, acc);
                 }
             }
-            store4(mh + (16 * tt + r16) * C + 16 * jb + 4 * G, acc[0], acc[1], acc[2], acc[3]);
+            mres[tt] = acc;
+        }
+    }
+    // W and M to global memory as whole rows: through LDS (K, T and A are dead once every
+    // wave has passed the barrier), rows padded to 2 C + 16 bytes so that the 16 rows of a
+    // tile fall on distinct banks, then 16-byte stores of consecutive lanes along each row
+    __syncthreads();
+    constexpr int LDW = C + 8;   // padded row, elements
+    static_assert(DK * LDW * 2 <= TILE_BYTES + HB * C * LDF * 4, "W rows fit the k and T regions");
+    static_assert(HB * C * LDW * 2 <= HB * C * LDF * 4, "M rows fit the N region");
+    bf16 *Wl = reinterpret_cast<bf16 *>(const_cast<unsigned char *>(Ks));   // [DK][LDW], over k and T
+    bf16 *Ml = reinterpret_cast<bf16 *>(Am);                                // [C][LDW], over A
+    if (hh < nh) {
+#pragma unroll
+        for (int it = 0; it < DK / 16; ++it)
+            *reinterpret_cast<bf16x4 *>(Wl + (16 * it + r16) * LDW + 16 * jb + 4 * G) =
+                bf16x4{(bf16)wres[it][0], (bf16)wres[it][1], (bf16)wres[it][2], (bf16)wres[it][3]};
+#pragma unroll
+        for (int tt = 0; tt < RT; ++tt)
+            *reinterpret_cast<bf16x4 *>(Ml + (16 * tt + r16) * LDW + 16 * jb + 4 * G) =
+                bf16x4{(bf16)mres[tt][0], (bf16)mres[tt][1], (bf16)mres[tt][2], (bf16)mres[tt][3]};
+    }
+    __syncthreads();
+    static_assert(HB == 1, "one value head per pass in the absorbed form");
+    if (nh > 0) {
+        constexpr int CPR = C * 2 / 16;   // 16-byte pieces per row
+        for (int idx = wv * kWave + lane; idx < (DK + C) * CPR; idx += PW * kWave) {
+            const int row = idx / CPR, q = idx - (idx / CPR) * CPR;
+            if (row < DK)
+                *reinterpret_cast<bf16x8 *>(wout + row * C + q * 8) =
+                    *reinterpret_cast<const bf16x8 *>(Wl + row * LDW + q * 8);
+            else
+                *reinterpret_cast<bf16x8 *>(mout + (row - DK) * C + q * 8) =
+                    *reinterpret_cast<const bf16x8 *>(Ml + (row - DK) * LDW + q * 8);
         }
     }
 }
