@@ -8,10 +8,10 @@ from .binding import (GdnError, Shape, conv1d_qkv, conv_state_snapshot, decode_s
                       header_functions, library_path, load_library, make_shape, prefill_chunked,
                       prefill_chunked_gated_rmsnorm, prefill_chunked_noalloc, prepare_conv1d_qkv, prepare_decode,
                       prepare_gated_rmsnorm, prepare_prefill, prepare_prefill_gated_rmsnorm, profile_collect,
-                      profile_enable, state_snapshot, version, workspace_bytes)
+                      profile_enable, state_snapshot, version, workspace_bytes, workspace_bytes_for)
 
 __all__ = ["GdnError", "Shape", "conv1d_qkv", "conv_state_snapshot", "decode_step", "gated_rmsnorm", "header_functions",
            "library_path", "load_library", "make_shape", "prefill_chunked", "prefill_chunked_gated_rmsnorm", "prefill_chunked_noalloc",
            "prepare_conv1d_qkv", "prepare_decode", "prepare_prefill_gated_rmsnorm",
            "prepare_gated_rmsnorm", "prepare_prefill", "profile_collect", "profile_enable", "state_snapshot", "version",
-           "workspace_bytes"]
+           "workspace_bytes", "workspace_bytes_for"]

@@ -59,6 +59,8 @@ def load_library():
         SP = ctypes.POINTER(Shape)
         lib.gdn_prefill_workspace_bytes.argtypes = [SP, i64, i32]
         lib.gdn_prefill_workspace_bytes.restype = sz
+        lib.gdn_prefill_workspace_bytes_for.argtypes = [SP, vp, i32]
+        lib.gdn_prefill_workspace_bytes_for.restype = sz
         lib.gdn_prefill_chunked.argtypes = [SP, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, vp, sz, vp]
         lib.gdn_prefill_chunked.restype = ctypes.c_int
         lib.gdn_prefill_chunked_noalloc.argtypes = [SP, vp, vp, vp, vp, vp, vp, i32, i64, vp, vp, vp, vp, vp]
@@ -139,6 +141,15 @@ def workspace_bytes(shape: Shape, total_tokens: int, num_seqs: int) -> int:
                                                           int(num_seqs)))
 
 
+def workspace_bytes_for(shape: Shape, cu_seqlens_host) -> int:
+    """Workspace bytes the prefill uses for a batch whose offsets are known on the host."""
+    arr = torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    if arr.device.type != "cpu" or arr.dim() != 1 or arr.shape[0] < 1:
+        raise ValueError("cu_seqlens_host must be a 1-D host sequence of num_seqs + 1 offsets")
+    return int(load_library().gdn_prefill_workspace_bytes_for(ctypes.byref(shape), ctypes.c_void_p(arr.data_ptr()),
+                                                              int(arr.shape[0] - 1)))
+
+
 def _prefill_call(q, k, v, g, beta, cu_seqlens, initial_state, scale, chunk, final_state, out, workspace):
     """Validate and marshal the arguments of gdn_prefill_chunked; returns (lib, args, keep, out, final)."""
     lib = load_library()
@@ -188,6 +199,8 @@ def _prefill_call(q, k, v, g, beta, cu_seqlens, initial_state, scale, chunk, fin
     if need == 0 and n > 0:
         raise GdnError(GDN_ERR_UNSUPPORTED, "no prefill kernel for dk=%d dv=%d chunk=%d %s" % (dk, dv, chunk, io))
     if workspace is None:
+        if cu_host is not None:   # the plan for these lengths may need less (segments)
+            need = workspace_bytes_for(shape, cu_host) or need
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, dev, 1)
     host_arr = None if cu_host is None else cu_host.numpy()

@@ -153,6 +153,35 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape, int64_t total_tokens,
         .total_bytes;
 }
 
+size_t gdn_prefill_workspace_bytes_for(const gdn_shape *shape, const int32_t *cu_seqlens_host, int32_t num_seqs)
+{
+    if (!cu_seqlens_host || num_seqs < 0 || check_shape(shape) != GDN_OK)
+        return 0;
+    const gdn_shape &s = *shape;
+    if (!gdn::prefill_supported(s.dk, s.dv, s.chunk, s.io_dtype) || cu_seqlens_host[0] != 0)
+        return 0;
+    int64_t longest = 0;
+    for (int32_t n = 0; n < num_seqs; ++n) {
+        const int64_t len = (int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n];
+        if (len < 0)
+            return 0;
+        longest = std::max(longest, len);
+    }
+    const int64_t total = cu_seqlens_host[num_seqs];
+    const gdn::PrefillWorkspace ws = gdn::prefill_workspace(s.num_v_heads, s.dk, s.chunk, s.io_dtype, total, num_seqs);
+    if (ws.total_bytes == 0 || num_seqs == 0)
+        return ws.total_bytes;
+    // the plan gdn_prefill_chunked takes for these lengths with the whole-batch workspace:
+    // segments use num_seqs * seg_len chunk slots, the single launch all of them
+    const int32_t seg_len = gdn::prefill_segment_len(s.num_qk_heads, s.num_v_heads, s.dk, s.chunk, s.io_dtype,
+                                                     num_seqs, (int32_t)((longest + s.chunk - 1) / s.chunk),
+                                                     ws.max_chunks);
+    if (seg_len <= 0)
+        return ws.total_bytes;
+    return ws.table_bytes +
+           (size_t)num_seqs * seg_len * gdn::prefill_slot_bytes(s.num_v_heads, s.dk, s.chunk, s.io_dtype);
+}
+
 // The gated RMSNorm applied to the prefill's output rows (gdn_prefill_chunked_gated_rmsnorm).
 struct NormIn {
     const void *z;
@@ -220,34 +249,30 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
         return fail(GDN_ERR_INVALID_ARG, "batch too large for the chunk table");
     int32_t slot_capacity = ws.max_chunks;   // chunk slots the workspace holds
     bool must_segment = false;               // the workspace holds less than the whole batch
-    if (own_scratch) {
-        // The library's scratch: the whole batch when it fits, else segments of the host-known
-        // sequence lengths sized to it.
+    const size_t avail = own_scratch ? gdn::kPrefillScratchBytes : (workspace ? workspace_bytes : 0);
+    if (!own_scratch && !workspace)
+        return fail(GDN_ERR_WORKSPACE, "workspace needs %zu bytes, got none", ws.total_bytes);
+    if (ws.total_bytes > avail) {
+        // Less than the whole batch: segments of the host-known sequence lengths sized to it.
+        const char *what = own_scratch ? "the scratch of gdn_prefill_chunked_noalloc" : "the workspace";
+        if (!cu_seqlens_host)
+            return fail(GDN_ERR_WORKSPACE,
+                        "the batch needs %zu bytes of chunk workspace and %s holds %zu; pass cu_seqlens_host "
+                        "(the batch is then cut into segments that fit)",
+                        ws.total_bytes, what, avail);
         const size_t slot_bytes = gdn::prefill_slot_bytes(s.num_v_heads, s.dk, s.chunk, s.io_dtype);
-        if (ws.total_bytes > gdn::kPrefillScratchBytes) {
-            if (!cu_seqlens_host)
-                return fail(GDN_ERR_WORKSPACE,
-                            "the batch needs %zu bytes of chunk workspace, more than the %zu-byte scratch of "
-                            "gdn_prefill_chunked_noalloc; pass cu_seqlens_host (the batch is then cut into "
-                            "segments) or call gdn_prefill_chunked with a workspace",
-                            ws.total_bytes, gdn::kPrefillScratchBytes);
-            const int64_t cap = ws.table_bytes < gdn::kPrefillScratchBytes
-                                    ? (int64_t)((gdn::kPrefillScratchBytes - ws.table_bytes) / slot_bytes)
-                                    : 0;
-            if (cap < num_seqs)
-                return fail(GDN_ERR_WORKSPACE,
-                            "%d sequences need at least %zu bytes of chunk workspace, more than the %zu-byte "
-                            "scratch of gdn_prefill_chunked_noalloc",
-                            num_seqs, ws.table_bytes + (size_t)num_seqs * slot_bytes, gdn::kPrefillScratchBytes);
-            slot_capacity = (int32_t)cap;
-            must_segment = true;
-        }
+        const int64_t cap = ws.table_bytes < avail ? (int64_t)((avail - ws.table_bytes) / slot_bytes) : 0;
+        if (cap < num_seqs)
+            return fail(GDN_ERR_WORKSPACE,
+                        "%d sequences need at least %zu bytes of chunk workspace (one chunk each); %s holds %zu",
+                        num_seqs, ws.table_bytes + (size_t)num_seqs * slot_bytes, what, avail);
+        slot_capacity = (int32_t)cap;
+        must_segment = true;
+    }
+    if (own_scratch) {
         const hipError_t e = gdn::prefill_scratch(static_cast<hipStream_t>(stream), &workspace, &workspace_bytes);
         if (e != hipSuccess)
             return fail(GDN_ERR_HIP, "scratch of gdn_prefill_chunked_noalloc: %s", hipGetErrorString(e));
-    } else if (!workspace || workspace_bytes < ws.total_bytes) {
-        return fail(GDN_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", ws.total_bytes,
-                    workspace ? workspace_bytes : (size_t)0);
     }
     if (!aligned(workspace, 256))
         return fail(GDN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
@@ -304,7 +329,7 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
         p.seg_len = gdn::prefill_segment_len(s.num_qk_heads, s.num_v_heads, s.dk, s.chunk, s.io_dtype, num_seqs,
                                              p.max_seq_chunks, slot_capacity);
         if (must_segment && p.seg_len == 0 && p.max_seq_chunks > 0) {
-            // the scratch holds less than the batch: segments as long as it allows, balanced
+            // the workspace holds less than the batch: segments as long as it allows, balanced
             const int64_t m = slot_capacity / num_seqs;   // >= 1 (checked above)
             const int64_t nseg = (p.max_seq_chunks + m - 1) / m;
             p.seg_len = (int32_t)((p.max_seq_chunks + nseg - 1) / nseg);

@@ -55,7 +55,7 @@ typedef enum gdn_status {
     GDN_OK = 0,
     GDN_ERR_INVALID_ARG = 1,  /* null pointer, bad size, misalignment, bad cu_seqlens (host copy) */
     GDN_ERR_UNSUPPORTED = 2,  /* a valid request this build has no kernel for */
-    GDN_ERR_WORKSPACE = 3,    /* workspace missing or smaller than gdn_prefill_workspace_bytes() */
+    GDN_ERR_WORKSPACE = 3,    /* workspace missing or too small for the batch */
     GDN_ERR_HIP = 4           /* the HIP runtime refused a launch; see gdn_last_error() */
 } gdn_status;
 
@@ -80,6 +80,19 @@ typedef struct gdn_shape {
  * unsupported or invalid shape.
  */
 size_t gdn_prefill_workspace_bytes(const gdn_shape *shape, int64_t total_tokens, int32_t num_seqs);
+
+/*
+ * Bytes of device scratch that gdn_prefill_chunked actually uses for the batch
+ * whose host offsets are `cu_seqlens_host` ([num_seqs + 1], as for
+ * gdn_prefill_chunked), when it is given those offsets: at most
+ * gdn_prefill_workspace_bytes().  Long sequences are run in segments of local
+ * chunks (a segment's chunk matrices stay in the last-level cache between the
+ * prep and the scan), and a segment needs slots for its own chunks only: for
+ * one 32768-token sequence at 32 value heads of d = 128, about 105 MB instead
+ * of 420 MB.  Returns 0 for an unsupported shape or invalid offsets (negative
+ * lengths, cu_seqlens_host[0] != 0).  Pure host computation.
+ */
+size_t gdn_prefill_workspace_bytes_for(const gdn_shape *shape, const int32_t *cu_seqlens_host, int32_t num_seqs);
 
 /*
  * Chunked prefill over a packed batch of variable-length sequences.
@@ -113,8 +126,16 @@ size_t gdn_prefill_workspace_bytes(const gdn_shape *shape, int64_t total_tokens,
  *                  (in-place prefix reuse), must not overlap anything else
  *   o              [total_tokens, HV, dv] io dtype out; must not overlap
  *                  any input
- *   workspace      device scratch of at least gdn_prefill_workspace_bytes()
- *                  bytes, 256-byte aligned; contents on entry are ignored.
+ *   workspace      device scratch, 256-byte aligned; contents on entry are
+ *                  ignored.  gdn_prefill_workspace_bytes() bytes always
+ *                  suffice.  With cu_seqlens_host, less is accepted: the
+ *                  batch is then run in segments of local chunks sized to
+ *                  the workspace (gdn_prefill_workspace_bytes_for() gives the
+ *                  size of the plan taken with the whole-batch workspace), and
+ *                  the call fails with GDN_ERR_WORKSPACE, touching nothing,
+ *                  when the workspace cannot hold one chunk of every sequence.
+ *                  Without cu_seqlens_host a smaller workspace fails with
+ *                  GDN_ERR_WORKSPACE.  The results do not depend on the plan.
  */
 gdn_status gdn_prefill_chunked(const gdn_shape *shape,
                                const void *q, const void *k, const void *v,

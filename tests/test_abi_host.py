@@ -78,6 +78,47 @@ def test_workspace_size(lib):
     assert lib.gdn_prefill_workspace_bytes(None, T, N) == 0
 
 
+def test_workspace_size_for_host_lengths(lib):
+    """gdn_prefill_workspace_bytes_for: the slots of the segment plan for host-known lengths."""
+    sh = shape()
+    slot = 32 * ((128 + 64) * 64 * 2 + 4 * 64 * 4)          # 819,200 bytes
+    cu = np.array([0, 32768], dtype=np.int32)                # 512 chunks: four segments of 128
+    got = lib.gdn_prefill_workspace_bytes_for(ctypes.byref(sh), cu.ctypes.data_as(ctypes.c_void_p), 1)
+    assert got == 256 + 128 * slot
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), 32768, 1) == 256 + 513 * slot
+    assert gdn.workspace_bytes_for(sh, cu) == got
+    # 16 sequences of up to 8192 tokens: single launch over the chunk table, every slot
+    from gated_deltanet_scan_amd import synthetic
+    lengths = synthetic.varlen_lengths(1004)
+    cu16 = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    assert gdn.workspace_bytes_for(sh, cu16) == lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), int(cu16[-1]), 16)
+    # a short batch: one segment as long as its longest sequence
+    cu3 = np.array([0, 333, 666, 1000], dtype=np.int32)
+    assert gdn.workspace_bytes_for(sh, cu3) == 256 + 3 * 6 * slot
+    # invalid offsets or shapes
+    for bad in ([5, 100], [0, 100, 50]):
+        arr = np.array(bad, dtype=np.int32)
+        assert lib.gdn_prefill_workspace_bytes_for(ctypes.byref(sh), arr.ctypes.data_as(ctypes.c_void_p),
+                                                   len(bad) - 1) == 0
+    assert lib.gdn_prefill_workspace_bytes_for(ctypes.byref(sh), None, 1) == 0
+    assert lib.gdn_prefill_workspace_bytes_for(ctypes.byref(shape(d=96)), cu.ctypes.data_as(ctypes.c_void_p), 1) == 0
+
+
+def test_prefill_refuses_a_workspace_without_a_chunk_per_sequence(lib):
+    """A workspace below the whole batch is cut into segments only with host offsets, and only
+    if it holds one chunk of every sequence; otherwise GDN_ERR_WORKSPACE before any launch."""
+    sh = shape()
+    slot = 32 * ((128 + 64) * 64 * 2 + 4 * 64 * 4)
+    N, T = 4, 4000
+    cu = np.linspace(0, T, N + 1).astype(np.int32)
+    assert prefill(lib, sh, T=T, N=N, cu_host=cu, ws_bytes=256 + N * slot - 1) == binding.GDN_ERR_WORKSPACE
+    assert b"one chunk each" in lib.gdn_last_error()
+    rc = lib.gdn_prefill_chunked(ctypes.byref(sh), fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), N, T, None,
+                                 fake(7), fake(8), fake(9), fake(10), 256 + 10 * slot, None)
+    assert rc == binding.GDN_ERR_WORKSPACE
+    assert b"cu_seqlens_host" in lib.gdn_last_error()
+
+
 def test_prefill_rejects_bad_shapes(lib):
     assert lib.gdn_prefill_chunked(None, *([None] * 5), None, 1, 1, None, None, None, None, None, 0, None) == 1
     assert prefill(lib, shape(hqk=3)) == binding.GDN_ERR_INVALID_ARG

@@ -261,3 +261,63 @@ def test_chunk_length_does_not_change_the_answer():
     o64, s64 = gpu_prefill(inp, 64)
     assert rel_err(o16.double().cpu(), o64.double().cpu()) < 1e-4
     assert rel_err(s16.double().cpu(), s64.double().cpu()) < 1e-4
+
+
+def test_workspace_smaller_than_the_batch():
+    """With host offsets a workspace smaller than gdn_prefill_workspace_bytes() is accepted: the
+    batch runs in segments sized to it.  The whole-batch workspace, the size of the plan
+    (gdn_prefill_workspace_bytes_for) and a workspace of 5 chunk slots per sequence give the
+    same bits (per-chunk arithmetic does not depend on the plan; the state is carried in fp32
+    between segments), and agree with the oracle."""
+    import gated_deltanet_scan_amd as gdn
+    from gated_deltanet_scan_amd import binding
+    lengths = [3000, 700, 1500, 64]
+    inp = _case(lengths, 2, 4, 128, torch.bfloat16, seed=31)
+    d = {key: (val.cuda() if isinstance(val, torch.Tensor) else val) for key, val in inp.items()}
+    cu = inp["cu_seqlens"].cpu()
+    sh = binding.make_shape(2, 4, 128, 128, 64, binding.GDN_DTYPE_BF16, 128 ** -0.5)
+    full = gdn.workspace_bytes(sh, int(cu[-1]), len(lengths))
+    plan = gdn.workspace_bytes_for(sh, cu)
+    slot = 4 * ((128 + 64) * 64 * 2 + 4 * 64 * 4)
+    tight = 256 + len(lengths) * 5 * slot
+    assert tight < plan <= full, (tight, plan, full)
+    runs = []
+    for nbytes in (full, plan, tight):
+        say("workspace", nbytes, "bytes of", full)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        o, st = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["initial_state"], chunk=64,
+                                    workspace=ws)
+        torch.cuda.synchronize()
+        runs.append((o, st))
+    for o, st in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(st, runs[0][1])
+    o_ref, s_ref = oracle_prefill(inp)
+    check_prefill(runs[2][0], runs[2][1], o_ref, s_ref, inp["cu_seqlens"], torch.bfloat16, "tight_workspace")
+    # one slot short of a chunk per sequence: refused, outputs untouched
+    ws = torch.empty(256 + len(lengths) * slot - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(gdn.GdnError):
+        gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["initial_state"], chunk=64,
+                            workspace=ws)
+
+
+def test_planned_workspace_at_the_32k_shape():
+    """prefill_32k with the workspace of its plan (128-chunk segments, about a quarter of the
+    whole-batch size) gives the bits of the whole-batch workspace."""
+    import gated_deltanet_scan_amd as gdn
+    from gated_deltanet_scan_amd import binding
+    w = S.workload("prefill_32k")
+    inp = S.make_workload_inputs(w)
+    d = {key: (val.cuda() if isinstance(val, torch.Tensor) else val) for key, val in inp.items()}
+    cu = inp["cu_seqlens"].cpu()
+    sh = binding.make_shape(w.hqk, w.hv, w.dk, w.dv, w.chunk, binding.GDN_DTYPE_BF16, w.dk ** -0.5)
+    full = gdn.workspace_bytes(sh, int(cu[-1]), 1)
+    plan = gdn.workspace_bytes_for(sh, cu)
+    say("prefill_32k workspace", plan, "of", full)
+    assert plan < full // 3
+    runs = []
+    for nbytes in (full, plan):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        runs.append(gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], cu, d["initial_state"],
+                                        chunk=w.chunk, workspace=ws))
+        torch.cuda.synchronize()
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
