@@ -298,10 +298,15 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
     // whose products with T still read k)
     constexpr int U1 = ABSORB ? TILE + (TILE > F_BYTES ? TILE : F_BYTES) : (2 * TILE > F_BYTES ? 2 * TILE : F_BYTES);
     constexpr int NCK = TILE / 16;                    // 16-byte chunks of a staged tile
-    constexpr int NJ1 = (NCK + 63) / 64;              // 64-lane load jobs per tile
+    constexpr int NJ1 = NCK / 64;                     // 64-lane load jobs (1 KB) per tile
     constexpr int PW = PrepWaves<E, C>::value, NT = PW * kWave;
     constexpr int NJ_PER = (2 * NJ1 + PW - 1) / PW;
-    static_assert(DK * ES >= 16 && DK * ES <= 256, "staged rows of 16 .. 256 bytes");
+    constexpr int RB = DK * ES;                       // bytes of a staged row
+    constexpr int RPJ = 1024 / RB;                    // rows per load job
+    constexpr int KPAT = 16 / RPJ;                    // jobs per period of the row permutation
+    static_assert(RB >= 64 && RB <= 256, "staged rows of 64 .. 256 bytes");
+    static_assert(NCK % 64 == 0 && NJ1 % KPAT == 0 && PW % KPAT == 0,
+                  "whole jobs; every job of a wave has the same lane pattern");
     static_assert(C <= kWave, "one lane per token of a chunk");
     static_assert(!ABSORB || PW == RT * HB, "absorbed form: one (head, block column of T) per wave");
 
@@ -357,28 +362,43 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
     const int64_t t0 = a + (int64_t)c * C;
     const int len = (int)min<int64_t>(C, b - t0);   // >= 1
 
-    // q and k rows of the chunk into LDS.  Job J moves 1 KB: lane i writes the 16 bytes
-    // at 16 i of the job's block, the source chunk is the Swz image of that position.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    // q and k rows of the chunk into LDS.  Job idx of a tile moves 1 KB: lane i writes the 16
+    // bytes at 16 i of the job's block, i.e. row r = RPJ idx + i / (RB / 16) of the tile, chunk
+    // position i % (RB / 16), whose source is chunk (position ^ perm(r)) of that token row
+    // (Swz).  perm has period 16 in r, and the jobs of this wave all start at rows
+    // = RPJ (wv % KPAT) modulo 16, so one lane offset serves all of them; the rest of a job's
+    // offset (16 rows per period) is uniform and goes into the scalar base.  In a ragged chunk
+    // rows past its end repeat its last row.
     auto issue_qk = [&]() __attribute__((always_inline)) {
-        const E *kb = k + ((size_t)t0 * hqk + hq) * DK;
-        const E *qb = q + ((size_t)t0 * hqk + hq) * DK;
+        const uint32_t rowb = (uint32_t)hqk * DK * ES;      // bytes between tokens of one head
+        const char *kb = reinterpret_cast<const char *>(k + ((size_t)t0 * hqk + hq) * DK);
+        const char *qb = reinterpret_cast<const char *>(q + ((size_t)t0 * hqk + hq) * DK);
+        const int lr = lane / (RB / 16), lpos = lane % (RB / 16);
+        const int r_in = RPJ * (wv % KPAT) + lr;            // row within the period of perm
+        const uint32_t chunk_off = (uint32_t)((lpos ^ SK::perm(r_in)) * 16);
+        const uint32_t lane_off = (uint32_t)r_in * rowb + chunk_off;
+        const bool ragged = len < C;
 #pragma unroll
         for (int u = 0; u < NJ_PER; ++u) {
-            const int J = wave + u * PW;
+            const int J = wv + u * PW;
             if (J < 2 * NJ1) {
                 const int idx = J % NJ1;
-                const int P = min(idx * 64 + lane, NCK - 1);
-                const int r = P / (DK * ES / 16), pos = P % (DK * ES / 16);
-                const E *src = (J >= NJ1 ? qb : kb) + (size_t)min(r, len - 1) * hqk * DK + (pos ^ SK::perm(r)) * VN;
-                if (idx * 64 + lane < NCK)
-                    __builtin_amdgcn_global_load_lds(
-                        (const __attribute__((address_space(1))) void *)src,
-                        (__attribute__((address_space(3))) void *)(lds_qk + (J >= NJ1 ? TILE : 0) + idx * 1024), 16, 0, 0);
+                const char *base = J >= NJ1 ? qb : kb;
+                uint32_t off;
+                if (!ragged) {
+                    base += (size_t)(idx / KPAT) * 16 * rowb;
+                    off = lane_off;
+                } else {
+                    off = (uint32_t)min(RPJ * idx + lr, len - 1) * rowb + chunk_off;
+                }
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(base + off),
+                    (__attribute__((address_space(3))) void *)(lds_qk + (J >= NJ1 ? TILE : 0) + idx * 1024), 16, 0, 0);
             }
         }
     };
 
-    const int wv = __builtin_amdgcn_readfirstlane(wave);
     for (int hb = 0; hb < nheads; hb += HB) {
         const int nh = min(HB, nheads - hb);
         // g and beta of the pass's value heads, one token per lane, in every wave (issued
@@ -389,9 +409,9 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
             gv[hh] = 0.f;
             bv[hh] = 0.f;
             if (hh < nh && lane < len) {
-                const int h = hfirst + hb + hh;
-                gv[hh] = g[(size_t)(t0 + lane) * hv + h];
-                bv[hh] = beta[(size_t)(t0 + lane) * hv + h];
+                const size_t at = (size_t)t0 * hv + hfirst + hb + hh;   // uniform base, lane offset
+                gv[hh] = (g + at)[lane * hv];
+                bv[hh] = (beta + at)[lane * hv];
             }
         }
         issue_qk();
@@ -466,15 +486,23 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
                         break;
                     const int h = hfirst + hb + hh;
                     const float gt = Gw[wv][hh][t], bt = Bw[wv][hh][t];
+                    const float st = t < len ? scale : 0.f;   // rows past the chunk's end: A = 0
                     const f32x4 gj = *reinterpret_cast<const f32x4 *>(&Gw[wv][hh][j0]);
                     f32x4 nv, av;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        // exp(G_t - G_j) only for j <= t, where the exponent is <= 0 (log-space mask)
+                        // exp(G_t - G_j) only for j <= t, where the exponent is <= 0 (log-space
+                        // mask); below the diagonal tiles every j < t
                         const int j = j0 + e;
-                        const float ed = (j <= t) ? __expf(gt - gj[e]) : 0.f;
-                        nv[e] = (j < t) ? bt * ed * kk[e] : 0.f;
-                        av[e] = (t < len) ? scale * ed * qk[e] : 0.f;
+                        float ed;
+                        if constexpr (tc < tr) {
+                            ed = __expf(gt - gj[e]);
+                            nv[e] = bt * ed * kk[e];
+                        } else {
+                            ed = (j <= t) ? __expf(gt - gj[e]) : 0.f;
+                            nv[e] = (j < t) ? bt * ed * kk[e] : 0.f;
+                        }
+                        av[e] = st * ed * qk[e];
                     }
                     *reinterpret_cast<f32x4 *>(Nm + (hh * C + t) * LDF + j0) = nv;
                     if constexpr (ABSORB)
@@ -909,16 +937,21 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
     __syncthreads();
     static_assert(HB == 1, "one value head per pass in the absorbed form");
     if (nh > 0) {
-        constexpr int CPR = C * 2 / 16;   // 16-byte pieces per row
-        for (int idx = wv * kWave + lane; idx < (DK + C) * CPR; idx += PW * kWave) {
-            const int row = idx / CPR, q = idx - (idx / CPR) * CPR;
-            if (row < DK)
-                *reinterpret_cast<bf16x8 *>(wout + row * C + q * 8) =
-                    *reinterpret_cast<const bf16x8 *>(Wl + row * LDW + q * 8);
-            else
-                *reinterpret_cast<bf16x8 *>(mout + (row - DK) * C + q * 8) =
-                    *reinterpret_cast<const bf16x8 *>(Ml + (row - DK) * LDW + q * 8);
-        }
+        constexpr int CPR = C * 2 / 16;              // 16-byte pieces per row
+        constexpr int RPI = PW * kWave / CPR;        // rows per pass of the workgroup
+        static_assert(DK % RPI == 0 && C % RPI == 0, "whole passes over W and M");
+        const int r0 = wv * (kWave / CPR) + lane / CPR, qp = lane % CPR;
+        char *wb = reinterpret_cast<char *>(wout), *mb = reinterpret_cast<char *>(mout);
+        static_for<DK / RPI>([&](auto ic) {
+            const int row = decltype(ic)::value * RPI + r0;
+            *reinterpret_cast<bf16x8 *>(wb + (uint32_t)(row * C + qp * 8) * 2u) =
+                *reinterpret_cast<const bf16x8 *>(Wl + row * LDW + qp * 8);
+        });
+        static_for<C / RPI>([&](auto ic) {
+            const int row = decltype(ic)::value * RPI + r0;
+            *reinterpret_cast<bf16x8 *>(mb + (uint32_t)(row * C + qp * 8) * 2u) =
+                *reinterpret_cast<const bf16x8 *>(Ml + row * LDW + qp * 8);
+        });
     }
 }
 
