@@ -317,6 +317,9 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
     const unsigned char *Ks = smem_qk;                  // staged k rows
     const unsigned char *Qs = smem_qk + TILE;           // staged q rows
     float *Tf = reinterpret_cast<float *>(smem_qk + (ABSORB ? TILE : 0));   // [HB][C][LDF], after the Gram products
+    // element (row t, column j) of a head's T: row-major, or column-major in the absorbed form
+    // (whose products read T by columns)
+    auto tix = [](int t, int j) __attribute__((always_inline)) { return ABSORB ? j * LDF + t : t * LDF + j; };
     __attribute__((address_space(3))) unsigned char *const lds_qk =
         (__attribute__((address_space(3))) unsigned char *)smem_qk;
 
@@ -529,7 +532,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
             const int bb = lane >> 4, j = lane & 15;
             if (bb < RT) {
                 const float *Nb = Nm + (wave * C + bb * 16) * LDF + bb * 16;
-                float *Tb = Tf + (wave * C + bb * 16) * LDF + bb * 16;
+                float *Tb = Tf + wave * C * LDF + tix(bb * 16, bb * 16);
                 float x[16];
 #pragma unroll
                 for (int t = 0; t < 16; ++t) {
@@ -539,9 +542,15 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
                         s -= Nb[t * LDF + u] * x[u];
                     x[t] = s;
                 }
+                if constexpr (ABSORB) {   // column j of the block: 16 consecutive floats
 #pragma unroll
-                for (int t = 0; t < 16; ++t)
-                    Tb[t * LDF + j] = x[t];
+                    for (int t = 0; t < 16; t += 4)
+                        *reinterpret_cast<f32x4 *>(Tb + j * LDF + t) = f32x4{x[t], x[t + 1], x[t + 2], x[t + 3]};
+                } else {
+#pragma unroll
+                    for (int t = 0; t < 16; ++t)
+                        Tb[t * LDF + j] = x[t];
+                }
             }
         }
         __syncthreads();
@@ -569,9 +578,13 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
                     if (BP != bp)
                         return;
                     f32x4 tb[RT];
+                    if constexpr (ABSORB) {
+                        tb[BP] = *reinterpret_cast<const f32x4 *>(Th + tix(BP * 16 + g4, BP * 16 + r16));
+                    } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        tb[BP][i] = Th[(BP * 16 + g4 + i) * LDF + BP * 16 + r16];
+                        for (int i = 0; i < 4; ++i)
+                            tb[BP][i] = Th[tix(BP * 16 + g4 + i, BP * 16 + r16)];
+                    }
                     static_for<RT - 1 - BP>([&](auto dc) {
                         constexpr int B = BP + 1 + decltype(dc)::value;
                         f32x4 y = zero4();
@@ -582,15 +595,25 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
                             for (int st = 0; st < 4; ++st)
                                 y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], tb[M][st], y, 0, 0, 0);
                         });
-                        const f32x4 dv = *reinterpret_cast<const f32x4 *>(Th + (B * 16 + r16) * LDF + B * 16 + g4);
+                        f32x4 dv;   // row r16 of D_B, columns g4 .. g4 + 3
+                        if constexpr (ABSORB) {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                dv[i] = Th[tix(B * 16 + r16, B * 16 + g4 + i)];
+                        } else {
+                            dv = *reinterpret_cast<const f32x4 *>(Th + tix(B * 16 + r16, B * 16 + g4));
+                        }
                         f32x4 t = zero4();
 #pragma unroll
                         for (int st = 0; st < 4; ++st)
                             t = __builtin_amdgcn_mfma_f32_16x16x4f32(dv[st], y[st], t, 0, 0, 0);
+                        tb[B] = -t;
+                        if constexpr (ABSORB) {
+                            *reinterpret_cast<f32x4 *>(Th + tix(B * 16 + g4, BP * 16 + r16)) = tb[B];
+                        } else {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            tb[B][i] = -t[i];
-                            Th[(B * 16 + g4 + i) * LDF + BP * 16 + r16] = -t[i];
+                            for (int i = 0; i < 4; ++i)
+                                Th[tix(B * 16 + g4 + i, BP * 16 + r16)] = tb[B][i];
                         }
                     });
                 });
@@ -791,8 +814,20 @@ __device__ inline void split_bf16(float x, bf16 &hi, bf16 &lo)
     lo = (bf16)(x - (float)hi);
 }
 
+// split_bf16 of two values at once, as packed pairs (value 0 in the low half): one
+// two-value conversion for the hi pair, one for the remainders.  Returns {hi, lo}.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ inline u32x2 split_bf16x2(float x0, float x1)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+    const f32x2 r = {x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u)};
+    return u32x2{h, __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2))};
+}
+
 // Absorbed form of the chunk matrices (see AbsorbedForm), run by the prep after the
-// solve: T (fp32, [HB][C][LDF]) is complete in Tf, K is still staged in Ks (Swz rows),
+// solve: T (fp32, [HB][C][LDF], column j at j LDF) is complete in Tf, K is still staged in Ks (Swz rows),
 // and each wave holds its A tiles (fp32) in akeep, dealt as the Gram tiles were.
 // Wave wv owns value head hh = wv / (C / 16) of the pass and block column jb = wv % (C / 16)
 // of its T: the fp32 values, and those of diag(lambda) T, become hi/lo bf16 operand pairs, and
@@ -834,17 +869,10 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
             f32x4 v = zero4();
             if constexpr (lower)
                 v = akeep[idx / PW][hh];
-            bf16x4 hi, lo;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bf16 h0, l0;
-                split_bf16(v[e], h0, l0);
-                hi[e] = h0;
-                lo[e] = l0;
-            }
+            const u32x2 p0 = split_bf16x2(v[0], v[1]), p1 = split_bf16x2(v[2], v[3]);
             unsigned char *base = Ab + hh * 2 * C * C * 2;
-            *reinterpret_cast<bf16x4 *>(base + SA::off(t, 2 * j0)) = hi;
-            *reinterpret_cast<bf16x4 *>(base + C * C * 2 + SA::off(t, 2 * j0)) = lo;
+            *reinterpret_cast<u32x2 *>(base + SA::off(t, 2 * j0)) = u32x2{p0[0], p1[0]};
+            *reinterpret_cast<u32x2 *>(base + C * C * 2 + SA::off(t, 2 * j0)) = u32x2{p0[1], p1[1]};
         }
     });
     __syncthreads();
@@ -856,7 +884,7 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
         const unsigned char *Ahi = Ab + hh * 2 * C * C * 2, *Alo = Ahi + C * C * 2;
         // lambda_m = exp(G_last - G_m) over this wave's own copy of G (read back by itself)
         {
-            const float lam = expf(Gv[hh][C - 1] - Gv[hh][lane & (C - 1)]);
+            const float lam = __expf(Gv[hh][C - 1] - Gv[hh][lane & (C - 1)]);
             wave_lds_sync();
             if (lane < C)
                 Gv[hh][lane] = lam;
@@ -865,23 +893,34 @@ __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float 
         // column j of T (zero above the diagonal blocks) and of diag(lambda) T, contraction
         // rows 32 s + 8 G + {0..7}, as hi/lo pairs
         bf16x8 thi[NS], tlo[NS], lhi[NS], llo[NS];
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
             const f32x4 l0 = *reinterpret_cast<const f32x4 *>(&Gv[hh][32 * st + 8 * G]);
             const f32x4 l1 = *reinterpret_cast<const f32x4 *>(&Gv[hh][32 * st + 8 * G + 4]);
+            // rows 32 st + 8 G .. + 7 of column j (consecutive in Tf); rows above the diagonal
+            // blocks hold stale data and are cleared by a mask (the reads stay unconditional)
+            const uint32_t keep = ((2 * st + (G >> 1)) >= jb) ? 0xffffffffu : 0u;
+            const u32x4 m0 = __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4 *>(Th + j * LDF + 32 * st + 8 * G)) & keep;
+            const u32x4 m1 = __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4 *>(Th + j * LDF + 32 * st + 8 * G + 4)) & keep;
+            const f32x4 t0 = __builtin_bit_cast(f32x4, m0), t1 = __builtin_bit_cast(f32x4, m1);
+            const f32x4 v0 = t0 * l0, v1 = t1 * l1;
+            u32x4 th, tl, lh, ll;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int m = 32 * st + 8 * G + e;
-                const float tv = ((m >> 4) >= jb) ? Th[m * LDF + j] : 0.f;
-                const float lv = tv * (e < 4 ? l0[e] : l1[e - 4]);
-                bf16 h0, lo0, h1, lo1;
-                split_bf16(tv, h0, lo0);
-                split_bf16(lv, h1, lo1);
-                thi[st][e] = h0;
-                tlo[st][e] = lo0;
-                lhi[st][e] = h1;
-                llo[st][e] = lo1;
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 &tq = q < 2 ? t0 : t1;
+                const f32x4 &vq = q < 2 ? v0 : v1;
+                const u32x2 a = split_bf16x2(tq[2 * (q & 1)], tq[2 * (q & 1) + 1]);
+                const u32x2 b = split_bf16x2(vq[2 * (q & 1)], vq[2 * (q & 1) + 1]);
+                th[q] = a[0];
+                tl[q] = a[1];
+                lh[q] = b[0];
+                ll[q] = b[1];
             }
+            thi[st] = __builtin_bit_cast(bf16x8, th);
+            tlo[st] = __builtin_bit_cast(bf16x8, tl);
+            lhi[st] = __builtin_bit_cast(bf16x8, lh);
+            llo[st] = __builtin_bit_cast(bf16x8, ll);
         }
         // W^T tiles (rows t of block jb, columns i of key block it): lane holds
         // W[16 it + l % 16][16 jb + 4 G .. + 3]
