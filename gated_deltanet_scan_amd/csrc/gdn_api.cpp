@@ -322,9 +322,15 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
     p.seg_len = 0;
     p.max_seq_chunks = 0;
     if (cu_seqlens_host) {
-        int64_t longest = 0;
-        for (int32_t n = 0; n < num_seqs; ++n)
-            longest = std::max<int64_t>(longest, cu_seqlens_host[n + 1] - cu_seqlens_host[n]);
+        int64_t longest = 0, prev_chunks = INT64_MAX;
+        p.ordered = true;
+        for (int32_t n = 0; n < num_seqs; ++n) {
+            const int64_t len = cu_seqlens_host[n + 1] - cu_seqlens_host[n];
+            const int64_t chunks = (len + s.chunk - 1) / s.chunk;
+            longest = std::max<int64_t>(longest, len);
+            p.ordered = p.ordered && chunks <= prev_chunks;
+            prev_chunks = chunks;
+        }
         p.max_seq_chunks = (int32_t)((longest + s.chunk - 1) / s.chunk);
         p.seg_len = gdn::prefill_segment_len(s.num_qk_heads, s.num_v_heads, s.dk, s.chunk, s.io_dtype, num_seqs,
                                              p.max_seq_chunks, slot_capacity);

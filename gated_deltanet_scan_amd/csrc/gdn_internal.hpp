@@ -24,6 +24,8 @@ struct PrefillArgs {
     size_t table_bytes;    // bytes of the chunk table and sequence order at the start of the workspace
     int32_t seg_len;       // > 0: segment mode, local chunks per sequence per segment (0: global mode)
     int32_t max_seq_chunks;  // segment mode: chunks of the longest sequence
+    bool ordered;            // host offsets show chunk counts that never increase along the batch
+                             // (the scans' longest-first order is then the batch order)
     // optional gated RMSNorm of the output rows (o then holds y): gate, weight and eps
     const void *norm_z;
     const float *norm_weight;

@@ -2380,9 +2380,10 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
                               p.scale, (int32_t)slots);
     };
 
-    // Longest sequences first in the scans (their chains of chunk steps bound the time).
+    // Longest sequences first in the scans (their chains of chunk steps bound the time),
+    // unless the host offsets show the batch in that order already.
     const int32_t *order = nullptr;
-    if (p.num_seqs > 1 && p.num_seqs <= kMaxOrderedSeqs) {
+    if (p.num_seqs > 1 && p.num_seqs <= kMaxOrderedSeqs && !p.ordered) {
         int32_t *ord = chunk_start + p.num_seqs + 1;   // after the chunk table
         const ProfEvents ev = prof_events(PROF_CHUNK_TABLE);
         hipExtLaunchKernelGGL(gdn_seq_order_kernel, dim3((unsigned)((p.num_seqs + kThreads - 1) / kThreads)),

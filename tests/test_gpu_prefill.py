@@ -321,3 +321,16 @@ def test_planned_workspace_at_the_32k_shape():
                                         chunk=w.chunk, workspace=ws))
         torch.cuda.synchronize()
     assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+
+
+@pytest.mark.parametrize("hv", [4, 32])
+def test_batch_already_longest_first(hv):
+    """Host offsets whose chunk counts never increase along the batch: the scans take the batch
+    order as it stands (no ordering launch).  Same bits as with device offsets (ordered on the
+    device), and parity with the oracle; with 32 value heads the whole-head scan runs."""
+    lengths = [700, 300, 300, 65, 64, 1, 0]
+    inp = _case(lengths, hv // 2, hv, 128, torch.bfloat16, seed=33)
+    o_h, s_h = gpu_prefill(inp, 64, host_offsets=True)
+    o_d, s_d = gpu_prefill(inp, 64, host_offsets=False)
+    assert torch.equal(o_h, o_d) and torch.equal(s_h, s_d)
+    _run(inp, 64, torch.bfloat16, "longest_first_hv%d" % hv)
