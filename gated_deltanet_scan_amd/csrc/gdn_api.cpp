@@ -10,6 +10,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <vector>
 
 namespace {
 
@@ -136,6 +138,38 @@ int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, 
     if (len > slot_capacity / num_seqs)
         return 0;
     return (int32_t)len;
+}
+
+// A batch whose longest sequences would bound a whole-head scan (each of its workgroups runs
+// one (sequence, head) chain, about 3 us per chunk step when its CU is to itself, about 4 us
+// when the chip is busy) runs them in the row-split scan instead (about 1.2 us per step, eight
+// workgroups per pair, so at most 256 / (8 HV) sequences in one round of the chip), then the
+// rest in the whole-head scan.  The split is taken when its modelled time is under 80% of the
+// single kernel's.
+int32_t prefill_long_ranks(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype, const int64_t *chunks_desc,
+                           int32_t num_seqs)
+{
+    if (!prefill_absorbed(io_dtype, chunk) || dk != 128 || num_seqs < 2 || (int64_t)num_seqs * hv <= 64)
+        return 0;
+    constexpr double kRowStep = 1.2, kWholeChain = 3.0, kWholeBusy = 4.0, kCUs = 256.0;
+    const int32_t kmax = std::min<int32_t>(num_seqs - 1, std::max<int32_t>(1, 256 / (8 * hv)));
+    std::vector<double> tail(num_seqs + 1, 0.0);   // chunks of ranks >= r
+    for (int32_t r = num_seqs - 1; r >= 0; --r)
+        tail[r] = tail[r + 1] + (double)chunks_desc[r];
+    auto whole = [&](int32_t r) {   // whole-head scan of ranks >= r
+        return std::max(chunks_desc[r] * kWholeChain, tail[r] * hv * kWholeBusy / kCUs);
+    };
+    const double single = whole(0);
+    int32_t best = 0;
+    double best_t = 0.8 * single;
+    for (int32_t k = 1; k <= kmax; ++k) {
+        const double t = chunks_desc[0] * kRowStep + whole(k);
+        if (t < best_t) {
+            best_t = t;
+            best = k;
+        }
+    }
+    return best;
 }
 
 }  // namespace gdn
@@ -332,6 +366,13 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
             prev_chunks = chunks;
         }
         p.max_seq_chunks = (int32_t)((longest + s.chunk - 1) / s.chunk);
+        {
+            std::vector<int64_t> chunks(num_seqs);
+            for (int32_t n = 0; n < num_seqs; ++n)
+                chunks[n] = (cu_seqlens_host[n + 1] - cu_seqlens_host[n] + s.chunk - 1) / s.chunk;
+            std::sort(chunks.begin(), chunks.end(), std::greater<int64_t>());
+            p.long_ranks = gdn::prefill_long_ranks(s.num_v_heads, s.dk, s.chunk, s.io_dtype, chunks.data(), num_seqs);
+        }
         p.seg_len = gdn::prefill_segment_len(s.num_qk_heads, s.num_v_heads, s.dk, s.chunk, s.io_dtype, num_seqs,
                                              p.max_seq_chunks, slot_capacity);
         if (must_segment && p.seg_len == 0 && p.max_seq_chunks > 0) {

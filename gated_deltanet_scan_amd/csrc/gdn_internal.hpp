@@ -26,6 +26,8 @@ struct PrefillArgs {
     int32_t max_seq_chunks;  // segment mode: chunks of the longest sequence
     bool ordered;            // host offsets show chunk counts that never increase along the batch
                              // (the scans' longest-first order is then the batch order)
+    int32_t long_ranks;      // > 0: the first long_ranks ranks (longest sequences) are scanned by
+                             // the row-split kernel, the rest by the whole-head kernel
     // optional gated RMSNorm of the output rows (o then holds y): gate, weight and eps
     const void *norm_z;
     const float *norm_weight;
@@ -109,6 +111,10 @@ PrefillWorkspace prefill_workspace(int32_t hv, int32_t dk, int32_t chunk, int32_
 size_t prefill_slot_bytes(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype);
 // Segment length (local chunks per sequence) for a batch whose longest sequence has
 // max_seq_chunks chunks; 0 selects the single-launch global mode.
+// Number of longest sequences to scan apart from the rest (0: one scan kernel for the batch);
+// chunks_desc: the chunk counts of the batch, longest first.
+int32_t prefill_long_ranks(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype, const int64_t *chunks_desc,
+                           int32_t num_seqs);
 int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype,
                             int32_t num_seqs, int32_t max_seq_chunks, int32_t slot_capacity);
 

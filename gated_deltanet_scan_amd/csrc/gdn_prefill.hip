@@ -140,10 +140,16 @@ struct SlotMap {
     int32_t seg_first;           // first local chunk index of this launch
     int32_t seg_len;             // local chunks per sequence in this launch
     const int32_t *seq_order;    // scan kernels: the sequence of rank r is seq_order[r]; NULL: r
+    int32_t rank0;               // scan kernels: first rank of this launch (its ranks: rank0 + i)
+    int32_t ranks;               // scan launches: number of ranks (sequences) this launch covers
 };
 
-// Sequence of the scan work item with sequence rank r.
-__device__ inline int ranked_sequence(const SlotMap &m, int r) { return m.seq_order ? m.seq_order[r] : r; }
+// Sequence of the scan work item with rank index i of its launch.
+__device__ inline int ranked_sequence(const SlotMap &m, int i)
+{
+    const int r = m.rank0 + i;
+    return m.seq_order ? m.seq_order[r] : r;
+}
 
 // Number of chunks of sequence n (consistent with the clamping of the chunk table).
 __device__ inline int seq_chunks(const SlotMap &m, const int32_t *cu, int n, int64_t total_tokens, int chunk)
@@ -2265,13 +2271,12 @@ static void launch_scan(const PrefillArgs &p, const SlotMap &map, const E *tmat,
                         const float *sin, float *sout, hipStream_t st)
 {
     const int nv = p.dv / (16 * NW);
-    const int64_t pairs = (int64_t)p.num_seqs * p.hv;
-    const int64_t items = (int64_t)p.num_seqs * p.hqk;                 // (sequence, query/key head)
+    const int64_t items = (int64_t)map.ranks * p.hqk;                  // (sequence, query/key head)
     const int64_t blocks = ((items + 7) / 8) * 8 * (p.hv / p.hqk) * nv;
     const ProfEvents ev = prof_events(PROF_SCAN, PROF_SCAN_PLAIN);
     hipExtLaunchKernelGGL((gdn_chunk_scan_kernel<E, C, DK, NW>), dim3((unsigned)blocks), dim3(NW * kWave), 0, st,
                           ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k),
-                          static_cast<const E *>(p.v), p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv,
+                          static_cast<const E *>(p.v), p.cu_seqlens, map, map.ranks, p.total_tokens, p.hqk, p.hv,
                           p.dv, tmat, amat, dec, sin, sout, static_cast<E *>(p.o), p.scale);
 }
 
@@ -2280,8 +2285,7 @@ static void launch_scan_rows(const PrefillArgs &p, const SlotMap &map, const bf1
                              const float *dec, const float *sin, float *sout, hipStream_t st)
 {
     const int nv = p.dv / DVS;
-    const int64_t pairs = (int64_t)p.num_seqs * p.hv;
-    const int64_t items = (int64_t)p.num_seqs * p.hqk;                 // (sequence, query/key head)
+    const int64_t items = (int64_t)map.ranks * p.hqk;                  // (sequence, query/key head)
     const int64_t blocks = ((items + 7) / 8) * 8 * (p.hv / p.hqk) * nv;
     const ProfEvents ev = prof_events(PROF_SCAN, PROF_SCAN_ROWS);
     // part-A (Q, K, V) buffers: three where one workgroup per CU is the occupancy anyway
@@ -2290,7 +2294,7 @@ static void launch_scan_rows(const PrefillArgs &p, const SlotMap &map, const bf1
     hipExtLaunchKernelGGL((gdn_chunk_scan_rows_kernel<bf16, 64, DK, DVS, NSTAGE>), dim3((unsigned)blocks),
                           dim3(kScanThreads), 0, st, ev.start, ev.stop, 0, static_cast<const bf16 *>(p.q),
                           static_cast<const bf16 *>(p.k), static_cast<const bf16 *>(p.v), p.cu_seqlens, map,
-                          p.num_seqs, p.total_tokens, p.hqk, p.hv, p.dv, wmat, mmat, dec, sin, sout,
+                          map.ranks, p.total_tokens, p.hqk, p.hv, p.dv, wmat, mmat, dec, sin, sout,
                           static_cast<bf16 *>(p.o), p.scale);
 }
 
@@ -2299,13 +2303,12 @@ static void launch_scan_bf16(const PrefillArgs &p, const SlotMap &map, const bf1
                              const float *dec, const float *sin, float *sout, hipStream_t st)
 {
     const int nv = p.dv / (16 * CT * NW);
-    const int64_t pairs = (int64_t)p.num_seqs * p.hv;
-    const int64_t items = (int64_t)p.num_seqs * p.hqk;                 // (sequence, query/key head)
+    const int64_t items = (int64_t)map.ranks * p.hqk;                  // (sequence, query/key head)
     const int64_t blocks = ((items + 7) / 8) * 8 * (p.hv / p.hqk) * nv;
     const ProfEvents ev = prof_events(PROF_SCAN, PROF_SCAN_WIDE);
     hipExtLaunchKernelGGL((gdn_chunk_scan_bf16_kernel<DK, NW, CT>), dim3((unsigned)blocks), dim3(NW * kWave), 0,
                           st, ev.start, ev.stop, 0, static_cast<const bf16 *>(p.q), static_cast<const bf16 *>(p.k),
-                          static_cast<const bf16 *>(p.v), p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv,
+                          static_cast<const bf16 *>(p.v), p.cu_seqlens, map, map.ranks, p.total_tokens, p.hqk, p.hv,
                           p.dv, wmat, mmat, dec, sin, sout, static_cast<bf16 *>(p.o), p.scale);
 }
 
@@ -2355,6 +2358,18 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
             // crossover: 64 pairs (1024-token sequences, 16 chunk steps).
             const int64_t pairs = (int64_t)p.num_seqs * p.hv;
             if constexpr (DK == 128) {
+                if (p.long_ranks > 0 && p.long_ranks < p.num_seqs) {
+                    // Mixed batch (host offsets: a few sequences whose chains would bound a
+                    // whole-head scan): its longest sequences (the first ranks) in the
+                    // row-split scan, the rest in the whole-head scan.
+                    SlotMap lm = map, rm = map;
+                    lm.ranks = p.long_ranks;
+                    rm.rank0 = map.rank0 + p.long_ranks;
+                    rm.ranks = map.ranks - p.long_ranks;
+                    launch_scan_rows<DK, 16>(p, lm, tmat, amat, dec, sin, sout, st);
+                    launch_scan_bf16<DK, 8, 1>(p, rm, tmat, amat, dec, sin, sout, st);
+                    return;
+                }
                 if (pairs > 64) {
                     launch_scan_bf16<DK, 8, 1>(p, map, tmat, amat, dec, sin, sout, st);
                     return;
@@ -2395,7 +2410,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
     if (p.seg_len > 0) {
         // Segment mode: local chunks [s0, s0 + seg_len) of every sequence per step.
         for (int32_t s0 = 0; s0 < p.max_seq_chunks; s0 += p.seg_len) {
-            const SlotMap map{nullptr, s0, p.seg_len, order};
+            const SlotMap map{nullptr, s0, p.seg_len, order, 0, p.num_seqs};
             prep(map, (int64_t)p.num_seqs * p.seg_len);
             scan(map, s0 == 0 ? p.initial_state : p.final_state, p.final_state);
         }
@@ -2407,7 +2422,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
         hipExtLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
                               p.cu_seqlens, p.num_seqs, p.total_tokens, (int32_t)C, p.max_chunks, chunk_start);
     }
-    const SlotMap map{chunk_start, 0, INT32_MAX, order};
+    const SlotMap map{chunk_start, 0, INT32_MAX, order, 0, p.num_seqs};
     if (p.max_chunks > 0)
         prep(map, p.max_chunks);
     scan(map, p.initial_state, p.final_state);

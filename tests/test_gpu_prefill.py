@@ -334,3 +334,13 @@ def test_batch_already_longest_first(hv):
     o_d, s_d = gpu_prefill(inp, 64, host_offsets=False)
     assert torch.equal(o_h, o_d) and torch.equal(s_h, s_d)
     _run(inp, 64, torch.bfloat16, "longest_first_hv%d" % hv)
+
+
+@pytest.mark.parametrize("host_offsets", [True, False])
+def test_skewed_batch(host_offsets):
+    """One long sequence among short ones.  With host offsets its chains run in the row-split
+    scan and the short sequences in the whole-head scan (two launches over disjoint ranks);
+    with device offsets everything runs in the whole-head scan.  Both against the oracle."""
+    lengths = [8192] + [64] * 20 + [37, 0]
+    _run(_case(lengths, 16, 32, 128, torch.bfloat16, seed=35), 64, torch.bfloat16, "skewed",
+         host_offsets=host_offsets)
