@@ -60,6 +60,7 @@ KERNEL_SOURCES = {
     "gdn_chunk_scan_rows_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_chunk_scan_bf16_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_chunk_scan_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
+    "gdn_chunk_scan_tform_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_prep_kernel": ("gated_deltanet_scan_amd/csrc/gdn_prefill.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_decode_kernel": ("gated_deltanet_scan_amd/csrc/gdn_decode.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
     "gdn_gated_rmsnorm_kernel": ("gated_deltanet_scan_amd/csrc/gdn_norm.hip", "gated_deltanet_scan_amd/csrc/gdn_device.hpp"),
@@ -133,7 +134,8 @@ def _sync():
     torch.cuda.synchronize()
 
 
-SCAN_VARIANTS = ((8, "gdn_chunk_scan_rows_kernel"), (9, "gdn_chunk_scan_bf16_kernel"), (10, "gdn_chunk_scan_kernel"))
+SCAN_VARIANTS = ((8, "gdn_chunk_scan_rows_kernel"), (9, "gdn_chunk_scan_bf16_kernel"), (10, "gdn_chunk_scan_kernel"),
+                 (11, "gdn_chunk_scan_tform_kernel"))
 
 
 def _kernel_times(steps):

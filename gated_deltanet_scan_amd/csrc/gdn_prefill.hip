@@ -221,6 +221,78 @@ __device__ inline typename M::frag staged_frag(const unsigned char *base, int ro
     return M::load(reinterpret_cast<const E *>(base + S::off(row, col * (int)sizeof(E))));
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident chains of products.  Three products of the chunk step
+// take their B operand from the accumulator tiles of an earlier product:
+// [Q;K] S (S from the S update), T X and A D (X and D from the products
+// before them), K^T (lambda D).  An accumulator tile gives lane l column
+// l % 16 and rows 4 (l / 16) + {0..3}; a B fragment wants column l % 16 and
+// kPerLane contraction indices per lane group.  Chain<M> (M = the consuming
+// instruction) makes the two agree without moving data:
+//   row(t, r)     the matrix row that the PRODUCER computes in row r of its
+//                 output tile t (it reads that row of its own A operand);
+//   b_frag(t, s)  the consumer's B fragment of contraction step s, taken from
+//                 the accumulator tiles as they stand;
+//   a_col(s, l)   first contraction index of lane l's A fragment at step s.
+// ---------------------------------------------------------------------------
+template <typename M>
+struct Chain;
+
+// 16x16x32 bf16: tiles 2s and 2s+1 hold, in lane group g, the contraction
+// indices 32 s + 8 g + {0..3} and 32 s + 8 g + {4..7}.
+template <>
+struct Chain<Mma<bf16>> {
+    __device__ static inline int row(int t, int r) { return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3); }
+    __device__ static inline int a_col(int s, int lane) { return 32 * s + 8 * (lane >> 4); }
+    __device__ static inline bf16x8 b_frag(const f32x4 *t, int s)
+    {
+        const f32x4 a = t[2 * s], b = t[2 * s + 1];
+        return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3], (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+    }
+};
+
+// 16x16x16 bf16: tile s holds the indices 16 s + 4 g + {0..3} as it stands.
+template <>
+struct Chain<MmaBf16K16> {
+    __device__ static inline int row(int t, int r) { return 16 * t + r; }
+    __device__ static inline int a_col(int s, int lane) { return 16 * s + 4 * (lane >> 4); }
+    __device__ static inline bf16x4 b_frag(const f32x4 *t, int s)
+    {
+        const f32x4 a = t[s];
+        return bf16x4{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
+    }
+};
+
+// 16x16x4 fp32: step s = 4 t + i uses slot i of tile t, i.e. in lane group g
+// the index 16 t + 4 g + i.
+template <>
+struct Chain<Mma<float>> {
+    __device__ static inline int row(int t, int r) { return 16 * t + r; }
+    __device__ static inline int a_col(int s, int lane) { return 16 * (s >> 2) + 4 * (lane >> 4) + (s & 3); }
+    __device__ static inline float b_frag(const f32x4 *t, int s) { return t[s >> 2][s & 3]; }
+};
+
+// Round x to bf16 (hi) and the remainder to bf16 (lo): hi + lo carries about 16
+// significant bits, and products of hi/lo pairs accumulated in fp32 give sums that
+// cancel accurately.
+__device__ inline void split_bf16(float x, bf16 &hi, bf16 &lo)
+{
+    hi = (bf16)x;
+    lo = (bf16)(x - (float)hi);
+}
+
+// split_bf16 of two values at once, as packed pairs (value 0 in the low half): one
+// two-value conversion for the hi pair, one for the remainders.  Returns {hi, lo}.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ inline u32x2 split_bf16x2(float x0, float x1)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
+    const f32x2 r = {x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u)};
+    return u32x2{h, __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2))};
+}
+
 // Which form the chunk matrices take for io type E and chunk C.  Direct form
 // (fp32 io, chunk 16): T = (I + N)^-1 and A, and the scan forms D = T X.
 // Absorbed form (bf16 io, chunk 64): the products with T are taken in the
@@ -236,6 +308,23 @@ template <typename E, int C>
 struct AbsorbedForm {
     static constexpr bool value = sizeof(E) == 2 && C == 64;
 };
+
+// What the prep writes per (chunk, value head):
+//   kPrepDirect    T and A (fp32 io, chunk 16; the scan forms D = T X)
+//   kPrepAbsorbed  W and M (bf16 io, chunk 64; row-split and whole-head scans)
+//   kPrepTForm     T alone, as hi/lo bf16 pairs (bf16 io, chunk 64, dk 128; the T-form
+//                  whole-head scan forms A from its staged q and k and takes Y = T X with
+//                  the hi/lo pairs, so the cancelling sums of T's columns stay fp32-accurate)
+// and the decay record.  T-form record: [G | exp(G_last - G) | beta | beta exp(G)] (the scan
+// masks exp(G_t - G_j) in log space itself); the others: [exp(G) | ... ].
+enum PrepForm { kPrepDirect = 0, kPrepAbsorbed = 1, kPrepTForm = 2 };
+
+// T in the T form: 6 units of 16 rows x 32 columns per bf16 matrix (hi, then lo), the
+// units of T's row tiles rt (rows Chain<Mma<bf16>>::row(rt, .)) and column halves st with
+// st <= rt / 2 (the other two are zero: T is lower triangular); unit u(rt, st) holds at
+// its 16-byte position p the row Chain row(rt, p % 16), columns 32 st + 8 (p / 16) .. +7.
+constexpr int kTUnits = 6;
+__host__ __device__ constexpr int tform_unit(int rt, int st) { return rt < 2 ? rt : 2 + 2 * (rt - 2) + st; }
 
 template <int C, int DK, int PW, int HB, int NKEEP>
 __device__ void absorb_products(const unsigned char *Ks, const float *Tf, float *Am, float (*Gv)[C],
@@ -277,7 +366,7 @@ struct PrepWaves {
     static constexpr int value = 4;
 };
 
-template <typename E, int C, int DK>
+template <typename E, int C, int DK, int FORM>
 __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_kernel(
     const E *__restrict__ q, const E *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta, const int32_t *__restrict__ cu, SlotMap map, int32_t num_seqs,
@@ -292,21 +381,30 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
     // keeps k and T alive together, one value head per workgroup (about 53 KB, three per CU;
     // the grid runs over value heads and each computes its group's Gram products)
     constexpr int HB = AbsorbedForm<E, C>::value ? 1 : 2;
+    static_assert((FORM != kPrepDirect) == AbsorbedForm<E, C>::value, "form of the io type and chunk");
+    static_assert(FORM != kPrepTForm || DK == 128, "T form: dk 128");
+    constexpr bool TFORM = FORM == kPrepTForm;   // k rows only, K K^T only, T out
     constexpr int VN = Vec16<E>::n;
     typedef typename Vec16<E>::type V16;
     typedef typename MmaFor<E, DK>::type MK;
     typedef Swz<DK * ES> SK;
     // bf16 io at chunk 64: the products with T are taken here (absorbed form, see absorb_products)
-    constexpr bool ABSORB = AbsorbedForm<E, C>::value;
+    constexpr bool ABSORB = FORM == kPrepAbsorbed;
+    constexpr bool COLT = FORM != kPrepDirect;   // T kept column-major in LDS
     constexpr int TILE = C * DK * ES;                 // bytes of the staged q (or k) rows
     constexpr int F_BYTES = HB * C * LDF * (int)sizeof(float);
     // k, q rows, then T of HB heads: over both (direct form), or over q only (absorbed form,
     // whose products with T still read k)
-    constexpr int U1 = ABSORB ? TILE + (TILE > F_BYTES ? TILE : F_BYTES) : (2 * TILE > F_BYTES ? 2 * TILE : F_BYTES);
+    // (T form: k rows only, and T over them once the Gram products are done: about 36 KB,
+    // four workgroups per CU)
+    constexpr int U1 = TFORM   ? (TILE > F_BYTES ? TILE : F_BYTES)
+                       : COLT ? TILE + (TILE > F_BYTES ? TILE : F_BYTES)
+                              : (2 * TILE > F_BYTES ? 2 * TILE : F_BYTES);
     constexpr int NCK = TILE / 16;                    // 16-byte chunks of a staged tile
     constexpr int NJ1 = NCK / 64;                     // 64-lane load jobs (1 KB) per tile
     constexpr int PW = PrepWaves<E, C>::value, NT = PW * kWave;
-    constexpr int NJ_PER = (2 * NJ1 + PW - 1) / PW;
+    constexpr int NJOBS = TFORM ? NJ1 : 2 * NJ1;       // the T form stages k only
+    constexpr int NJ_PER = (NJOBS + PW - 1) / PW;
     constexpr int RB = DK * ES;                       // bytes of a staged row
     constexpr int RPJ = 1024 / RB;                    // rows per load job
     constexpr int KPAT = 16 / RPJ;                    // jobs per period of the row permutation
@@ -323,9 +421,9 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
     const unsigned char *Ks = smem_qk;                  // staged k rows
     const unsigned char *Qs = smem_qk + TILE;           // staged q rows
     float *Tf = reinterpret_cast<float *>(smem_qk + (ABSORB ? TILE : 0));   // [HB][C][LDF], after the Gram products
-    // element (row t, column j) of a head's T: row-major, or column-major in the absorbed form
-    // (whose products read T by columns)
-    auto tix = [](int t, int j) __attribute__((always_inline)) { return ABSORB ? j * LDF + t : t * LDF + j; };
+    // element (row t, column j) of a head's T: row-major, or column-major in the absorbed and
+    // T forms (whose products and unit writes read T by columns)
+    auto tix = [](int t, int j) __attribute__((always_inline)) { return COLT ? j * LDF + t : t * LDF + j; };
     __attribute__((address_space(3))) unsigned char *const lds_qk =
         (__attribute__((address_space(3))) unsigned char *)smem_qk;
 
@@ -391,7 +489,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
 #pragma unroll
         for (int u = 0; u < NJ_PER; ++u) {
             const int J = wv + u * PW;
-            if (J < 2 * NJ1) {
+            if (J < NJOBS) {
                 const int idx = J % NJ1;
                 const char *base = J >= NJ1 ? qb : kb;
                 uint32_t off;
@@ -445,7 +543,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
             const float Glast = __shfl(G, C - 1, kWave);
             float *rec = dec + (slot * hv + h) * 4 * C;
             const float eg = expf(G);
-            rec[lane] = eg;
+            rec[lane] = TFORM ? G : eg;
             rec[C + lane] = expf(Glast - G);
             rec[2 * C + lane] = wv == 0 ? bv[0] : bv[HB - 1];
             rec[3 * C + lane] = (wv == 0 ? bv[0] : bv[HB - 1]) * eg;
@@ -481,13 +579,15 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
                 for (int st = 0; st < NS; ++st) {
                     fj[st] = staged_frag<MK, SK, E>(Ks, tc * 16 + r16, st * MK::kStep + kq);
                     fkt[st] = staged_frag<MK, SK, E>(Ks, tr * 16 + r16, st * MK::kStep + kq);
-                    fqt[st] = staged_frag<MK, SK, E>(Qs, tr * 16 + r16, st * MK::kStep + kq);
+                    if constexpr (!TFORM)
+                        fqt[st] = staged_frag<MK, SK, E>(Qs, tr * 16 + r16, st * MK::kStep + kq);
                 }
                 f32x4 kk = zero4(), qk = zero4();
 #pragma unroll
                 for (int st = 0; st < NS; ++st) {
                     kk = MK::mma(fj[st], fkt[st], kk);
-                    qk = MK::mma(fj[st], fqt[st], qk);
+                    if constexpr (!TFORM)
+                        qk = MK::mma(fj[st], fqt[st], qk);
                 }
 #pragma unroll
                 for (int hh = 0; hh < HB; ++hh) {
@@ -516,10 +616,10 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
                     *reinterpret_cast<f32x4 *>(Nm + (hh * C + t) * LDF + j0) = nv;
                     if constexpr (ABSORB)
                         akeep[idx / PW][hh] = av;
-                    else
+                    else if constexpr (!TFORM)
                         store4(amat + (slot * hv + h) * C * C + t * C + j0, av[0], av[1], av[2], av[3]);
                 }
-            } else if constexpr (!ABSORB) {
+            } else if constexpr (FORM == kPrepDirect) {
 #pragma unroll
                 for (int hh = 0; hh < HB; ++hh)
                     if (hh < nh)
@@ -548,7 +648,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
                         s -= Nb[t * LDF + u] * x[u];
                     x[t] = s;
                 }
-                if constexpr (ABSORB) {   // column j of the block: 16 consecutive floats
+                if constexpr (COLT) {   // column j of the block: 16 consecutive floats
 #pragma unroll
                     for (int t = 0; t < 16; t += 4)
                         *reinterpret_cast<f32x4 *>(Tb + j * LDF + t) = f32x4{x[t], x[t + 1], x[t + 2], x[t + 3]};
@@ -584,7 +684,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
                     if (BP != bp)
                         return;
                     f32x4 tb[RT];
-                    if constexpr (ABSORB) {
+                    if constexpr (COLT) {
                         tb[BP] = *reinterpret_cast<const f32x4 *>(Th + tix(BP * 16 + g4, BP * 16 + r16));
                     } else {
 #pragma unroll
@@ -602,7 +702,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
                                 y = __builtin_amdgcn_mfma_f32_16x16x4f32(av[st], tb[M][st], y, 0, 0, 0);
                         });
                         f32x4 dv;   // row r16 of D_B, columns g4 .. g4 + 3
-                        if constexpr (ABSORB) {
+                        if constexpr (COLT) {
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
                                 dv[i] = Th[tix(B * 16 + r16, B * 16 + g4 + i)];
@@ -614,7 +714,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
                         for (int st = 0; st < 4; ++st)
                             t = __builtin_amdgcn_mfma_f32_16x16x4f32(dv[st], y[st], t, 0, 0, 0);
                         tb[B] = -t;
-                        if constexpr (ABSORB) {
+                        if constexpr (COLT) {
                             *reinterpret_cast<f32x4 *>(Th + tix(B * 16 + g4, BP * 16 + r16)) = tb[B];
                         } else {
 #pragma unroll
@@ -627,6 +727,34 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
             __syncthreads();
         }
 
+        if constexpr (TFORM) {
+            // T as hi/lo fragment units (see tform_unit): task = (unit, position); the 8
+            // columns of a row come from the column-major T, with the blocks above the
+            // diagonal (stale LDS) cleared
+            static_assert(HB == 1 && RT == 4, "one value head, chunk 64");
+            bf16 *tout = tmat + (slot * hv + hfirst + hb) * (2 * kTUnits * 512);
+            for (int task = tid; task < kTUnits * kWave; task += NT) {
+                const int u = task / kWave, pos = task % kWave;
+                const int rt = u < 2 ? u : 2 + (u - 2) / 2, st = u < 2 ? 0 : (u - 2) % 2;
+                const int t = Chain<Mma<bf16>>::row(rt, pos % 16), j0 = 32 * st + 8 * (pos / 16);
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    v[e] = ((j0 + e) >> 4) <= (t >> 4) ? Tf[tix(t, j0 + e)] : 0.f;
+                typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+                u32x4 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const u32x2 pr = split_bf16x2(v[2 * e], v[2 * e + 1]);
+                    hi[e] = pr[0];
+                    lo[e] = pr[1];
+                }
+                *reinterpret_cast<u32x4 *>(tout + u * 512 + pos * 8) = hi;
+                *reinterpret_cast<u32x4 *>(tout + (kTUnits + u) * 512 + pos * 8) = lo;
+            }
+            __syncthreads();
+            continue;
+        }
         if constexpr (ABSORB) {
             absorb_products<C, DK, PW, HB, NKEEP>(Ks, Tf, Nm, Gw[wv], akeep, nh, wv, lane,
                                                   tmat + (slot * hv + hfirst + hb) * DK * C,
@@ -712,57 +840,6 @@ struct SwzChain {
     __device__ static inline int off(int r, int b) { return r * RB + ((((b >> 4) ^ perm(r)) << 4) | (b & 15)); }
 };
 
-// ---------------------------------------------------------------------------
-// Register-resident chains of products.  Three products of the chunk step
-// take their B operand from the accumulator tiles of an earlier product:
-// [Q;K] S (S from the S update), T X and A D (X and D from the products
-// before them), K^T (lambda D).  An accumulator tile gives lane l column
-// l % 16 and rows 4 (l / 16) + {0..3}; a B fragment wants column l % 16 and
-// kPerLane contraction indices per lane group.  Chain<M> (M = the consuming
-// instruction) makes the two agree without moving data:
-//   row(t, r)     the matrix row that the PRODUCER computes in row r of its
-//                 output tile t (it reads that row of its own A operand);
-//   b_frag(t, s)  the consumer's B fragment of contraction step s, taken from
-//                 the accumulator tiles as they stand;
-//   a_col(s, l)   first contraction index of lane l's A fragment at step s.
-// ---------------------------------------------------------------------------
-template <typename M>
-struct Chain;
-
-// 16x16x32 bf16: tiles 2s and 2s+1 hold, in lane group g, the contraction
-// indices 32 s + 8 g + {0..3} and 32 s + 8 g + {4..7}.
-template <>
-struct Chain<Mma<bf16>> {
-    __device__ static inline int row(int t, int r) { return 32 * (t >> 1) + 8 * (r >> 2) + 4 * (t & 1) + (r & 3); }
-    __device__ static inline int a_col(int s, int lane) { return 32 * s + 8 * (lane >> 4); }
-    __device__ static inline bf16x8 b_frag(const f32x4 *t, int s)
-    {
-        const f32x4 a = t[2 * s], b = t[2 * s + 1];
-        return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3], (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
-    }
-};
-
-// 16x16x16 bf16: tile s holds the indices 16 s + 4 g + {0..3} as it stands.
-template <>
-struct Chain<MmaBf16K16> {
-    __device__ static inline int row(int t, int r) { return 16 * t + r; }
-    __device__ static inline int a_col(int s, int lane) { return 16 * s + 4 * (lane >> 4); }
-    __device__ static inline bf16x4 b_frag(const f32x4 *t, int s)
-    {
-        const f32x4 a = t[s];
-        return bf16x4{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3]};
-    }
-};
-
-// 16x16x4 fp32: step s = 4 t + i uses slot i of tile t, i.e. in lane group g
-// the index 16 t + 4 g + i.
-template <>
-struct Chain<Mma<float>> {
-    __device__ static inline int row(int t, int r) { return 16 * t + r; }
-    __device__ static inline int a_col(int s, int lane) { return 16 * (s >> 2) + 4 * (lane >> 4) + (s & 3); }
-    __device__ static inline float b_frag(const f32x4 *t, int s) { return t[s >> 2][s & 3]; }
-};
-
 // A operand of the S update: K^T, output rows = key indices in the order
 // Chain<MK>::row(sr, .), contraction over chunk rows in the order of
 // Chain<MC> (MK, MC: the instructions of the key and chunk contractions).
@@ -809,27 +886,6 @@ __device__ inline void wave_lds_sync()
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Round x to bf16 (hi) and the remainder to bf16 (lo): hi + lo carries about 16
-// significant bits, and products of hi/lo pairs accumulated in fp32 give sums that
-// cancel accurately.
-__device__ inline void split_bf16(float x, bf16 &hi, bf16 &lo)
-{
-    hi = (bf16)x;
-    lo = (bf16)(x - (float)hi);
-}
-
-// split_bf16 of two values at once, as packed pairs (value 0 in the low half): one
-// two-value conversion for the hi pair, one for the remainders.  Returns {hi, lo}.
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ inline u32x2 split_bf16x2(float x0, float x1)
-{
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x0, x1}, bf16x2));
-    const f32x2 r = {x0 - __uint_as_float(h << 16), x1 - __uint_as_float(h & 0xffff0000u)};
-    return u32x2{h, __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2))};
 }
 
 // Absorbed form of the chunk matrices (see AbsorbedForm), run by the prep after the
@@ -2263,6 +2319,452 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Whole-head scan of the T form (bf16 io, chunk 64, dk = dv = 128; see PrepForm): one
+// workgroup of 8 waves per (sequence, value head), each wave owning 16 state columns held in
+// matrix-core accumulators, as in gdn_chunk_scan_bf16_kernel.  The prep hands over T as hi/lo
+// bf16 units and the decay record; per chunk the step computes
+//   A   = scale exp(G_t - G_j) q_t.k_j for j <= t: 12 tiles of 16 query rows by 16 key rows
+//         (key rows in Chain order), dealt to the waves round-robin and formed inside the
+//         [Q;K] S products from the same fragments, then left in LDS as a hi and a lo matrix
+//   X   = beta v - beta exp(G) (K S)
+//   Y   = T X = T_hi X + T_lo X
+//   S  <- exp(G_last) S + K^T (lambda Y)_hi + K^T (lambda Y)_lo
+//   O   = scale exp(G) Q S + A_hi Y_hi + A_hi Y_lo + A_lo Y_hi
+// Every product that meets T, Y or A takes hi/lo pairs of the fp32 values, so the cancelling
+// sums of T's alternating columns (correlated keys) are carried at about 16 significant bits;
+// q, k, X and S enter as bf16.  K^T comes from the K units with the LDS transpose read: for
+// the contraction rows 32 st + 8 g + {0..7} and key rows Chain row(sr, .), input lane
+// (e, quarter) of a 16-lane group reads 4 keys of chunk row 32 st + 8 g + e (+ 4).
+// ---------------------------------------------------------------------------
+template <int DK, int NW>
+__global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
+    const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
+    const int32_t *__restrict__ cu, SlotMap map, int32_t num_seqs, int64_t total_tokens, int32_t hqk, int32_t hv,
+    int32_t dv, const bf16 *__restrict__ tmat, const float *__restrict__ dec, const float *state_in,
+    float *state_out, bf16 *__restrict__ o, float scale)
+{
+    constexpr int C = 64;
+    constexpr int WC = 16;                        // columns per wave
+    constexpr int DVS = WC * NW;                  // columns per workgroup
+    constexpr int NT = NW * kWave;
+    constexpr int RT = C / 16, SR = DK / 16;
+    constexpr int NSK = DK / 32, NSC = C / 32;
+    typedef Mma<bf16> M;
+    typedef Chain<M> CH;
+    static_assert(DK == 128 && DVS == 128, "whole heads of 128 columns");
+
+    // stage layout (bytes): 1 KB units
+    constexpr int NU_QK = RT * NSK, NU_T = 2 * kTUnits;
+    constexpr int VRB = DVS * 2;                   // bytes per row of the V slice
+    constexpr int NU_V = C * VRB / 1024;
+    constexpr int OFF_Q = 0;
+    constexpr int OFF_K = OFF_Q + NU_QK * 1024;
+    constexpr int OFF_T = OFF_K + NU_QK * 1024;
+    constexpr int OFF_V = OFF_T + NU_T * 1024;
+    constexpr int OFF_D = OFF_V + NU_V * 1024;
+    constexpr int STAGE = OFF_D + 1024;
+    constexpr int AB = C * C * 2;                  // bytes of one bf16 A matrix
+    typedef Swz<C * 2> SA;
+    static_assert(C * VRB % 1024 == 0 && 4 * C * 4 == 1024 && VRB == 256, "whole units, 256-byte V rows");
+
+    __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char abuf[2 * AB];   // A hi, A lo (rows t, SA order)
+    auto stage_ptr = [&](auto bufc) __attribute__((always_inline)) -> unsigned char * {
+        return decltype(bufc)::value ? stage1 : stage0;
+    };
+    auto stage_lds = [&](auto bufc) __attribute__((always_inline)) {
+        return (__attribute__((address_space(3))) unsigned char *)(decltype(bufc)::value ? stage1 : stage0);
+    };
+
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+    const int r16 = lane & 15, G = lane >> 4, g4 = 4 * G;
+    const int nv = dv / DVS;
+    const int pairs = num_seqs * hv;
+    const int group = hv / hqk;
+    int item, member;
+    xcd_group(blockIdx.x, group * nv, item, member);
+    const int pair = item * group + member / nv;
+    const int s = member % nv;
+    if (pair >= pairs)
+        return;
+    const int n = ranked_sequence(map, pair / hv), h = pair - (pair / hv) * hv;
+    const int hq = h / (hv / hqk);
+    int64_t a, b;
+    seq_range(cu, n, total_tokens, a, b);
+    const int nch = seq_chunks(map, cu, n, total_tokens, C);
+    const int c_begin = map.seg_first;
+    const int c_end = min(nch, map.seg_first + map.seg_len);
+    const int col0 = s * DVS + WC * w;                  // first state / output column of this wave
+    const size_t state_base = (size_t)(n * hv + h) * DK * dv;
+    if (c_begin >= c_end) {
+        if (c_begin == 0 && state_in != state_out) {
+            for (int i = tid; i < DK * DVS; i += NT) {
+                const size_t off = state_base + (size_t)(i / DVS) * dv + s * DVS + (i % DVS);
+                state_out[off] = state_in ? state_in[off] : 0.f;
+            }
+        }
+        return;
+    }
+
+    // ---- state columns in accumulators: tile sr, slot i holds key row CH::row(sr, g4 + i),
+    //      column col0 + l % 16 ----
+    f32x4 sacc[SR];
+#pragma unroll
+    for (int sr = 0; sr < SR; ++sr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            sacc[sr][i] = state_in ? state_in[state_base + (size_t)CH::row(sr, g4 + i) * dv + col0 + r16] : 0.f;
+
+    // ---- staging (as in gdn_chunk_scan_bf16_kernel; T units are contiguous 1 KB blocks) ----
+    const size_t slot0 = slot_of(map, n, 0);
+    constexpr int R_Q = NU_QK / NW, R_T = (NU_T + NW - 1) / NW, R_V = NU_V / NW;
+    static_assert(NU_QK % NW == 0 && NU_V % NW == 0, "whole rounds");
+    constexpr int RK0 = R_Q, RT0 = 2 * R_Q, RV0 = RT0 + R_T, RD0 = RV0 + R_V;
+    constexpr int NR = RD0 + 1;
+    const int qk_row = hqk * DK, v_row = hv * dv;
+    auto round_src = [&](auto rc, int &row, int &ecol, int &blk) __attribute__((always_inline)) {
+        constexpr int R = decltype(rc)::value;
+        if constexpr (R < RT0) {                       // Q or K unit (rt, kb)
+            const int u = (R < RK0 ? R : R - RK0) * NW + w;
+            const int rt = u / NSK, kb = u % NSK;
+            row = R < RK0 ? 16 * rt + r16 : CH::row(rt, r16 ^ g4);
+            ecol = 32 * kb + 8 * G;
+            blk = (R < RK0 ? OFF_Q : OFF_K) + u * 1024;
+        } else if constexpr (R < RV0) {                // T unit (hi units, then lo)
+            const int u = min((R - RT0) * NW + w, NU_T - 1);
+            row = u;
+            ecol = 8 * lane;
+            blk = OFF_T + u * 1024;
+        } else if constexpr (R < RD0) {                // 1 KB of rows of the V slice
+            const int u = (R - RV0) * NW + w;
+            const int P = u * 64 + lane;
+            row = P / (VRB / 16);
+            const int j = (P % (VRB / 16)) ^ (2 * (row & 3));
+            ecol = j * 8;
+            blk = OFF_V + u * 1024;
+        } else {                                       // decay record, 4 floats per lane
+            row = 0;
+            ecol = lane * 4;
+            blk = OFF_D;
+        }
+    };
+    auto round_bytes = [&](auto rc, int row, int ecol) __attribute__((always_inline)) -> uint32_t {
+        constexpr int R = decltype(rc)::value;
+        if constexpr (R < RT0)
+            return (uint32_t)(row * qk_row + ecol) * 2u;
+        else if constexpr (R < RV0)
+            return (uint32_t)(row * 512 + ecol) * 2u;
+        else if constexpr (R < RD0)
+            return (uint32_t)(row * v_row + ecol) * 2u;
+        else
+            return (uint32_t)ecol * 4u;
+    };
+    uint32_t loff[NR];
+    int lblk[NR];
+    static_for<NR>([&](auto rc) __attribute__((always_inline)) {
+        int row, ecol, blk;
+        round_src(rc, row, ecol, blk);
+        loff[decltype(rc)::value] = round_bytes(rc, row, ecol);
+        lblk[decltype(rc)::value] = blk;
+    });
+    auto issue_rounds = [&](auto bufc, int c, auto loc, auto hic) __attribute__((always_inline)) {
+        constexpr int LO = decltype(loc)::value, HI = decltype(hic)::value;
+        __attribute__((address_space(3))) unsigned char *stg = stage_lds(bufc);
+        const int64_t t0 = a + (int64_t)c * C;
+        const int last = (int)min<int64_t>(C, b - t0) - 1;
+        const size_t slot = slot0 + c;
+        const char *qb = reinterpret_cast<const char *>(q + ((size_t)t0 * hqk + hq) * DK);
+        const char *kb = reinterpret_cast<const char *>(k + ((size_t)t0 * hqk + hq) * DK);
+        const char *vb = reinterpret_cast<const char *>(v + ((size_t)t0 * hv + h) * dv + (size_t)s * DVS);
+        const char *tb = reinterpret_cast<const char *>(tmat + (slot * hv + h) * (NU_T * 512));
+        const char *db = reinterpret_cast<const char *>(dec + (slot * hv + h) * 4 * C);
+        const bool full = last == C - 1;
+        static_for<NR>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int R = decltype(rc)::value;
+            if constexpr (R < LO || R >= HI)
+                return;
+            uint32_t off = loff[R];
+            if constexpr (R < RT0 || (R >= RV0 && R < RD0)) {
+                if (!full) {   // ragged last chunk: rows past its end repeat its last row
+                    int row, ecol, blk;
+                    round_src(rc, row, ecol, blk);
+                    off = round_bytes(rc, min(row, last), ecol);
+                }
+            }
+            const char *base = R < RK0 ? qb : R < RT0 ? kb : R < RV0 ? tb : R < RD0 ? vb : db;
+            const bool on = R < RT0 || (R >= RV0 && R < RD0) ? true
+                            : R < RV0 ? (R - RT0) * NW + w < NU_T : w == 0;
+            if (on)
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(base + off),
+                                                 (__attribute__((address_space(3))) void *)(stg + lblk[R]), 16, 0,
+                                                 0);
+        });
+    };
+    auto issue_stage = [&](auto bufc, int c) __attribute__((always_inline)) {
+        issue_rounds(bufc, c, std::integral_constant<int, 0>{}, std::integral_constant<int, NR>{});
+    };
+    constexpr int kPartEnd[4] = {RT0, RV0, RD0, NR};
+    auto stage_part = [&](auto bufc, int c, auto pc) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value;
+        issue_rounds(bufc, c, std::integral_constant<int, P == 0 ? 0 : kPartEnd[P == 0 ? 0 : P - 1]>{},
+                     std::integral_constant<int, kPartEnd[P]>{});
+    };
+    auto stage_done = [&]() __attribute__((always_inline)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+
+    // per-lane LDS byte offsets
+    const int lin = 16 * lane;                                   // Q, T units
+    const int kperm = 16 * (16 * G + (r16 ^ g4));                 // K units, fragment read
+    const int e = (lane >> 2) & 3, qd = lane & 3;
+    const int vtro = (8 * G + e) * VRB + 16 * ((2 * w + (qd >> 1)) ^ (2 * e)) + 8 * (qd & 1);
+    // K^T transpose read: position of (chunk row 4 g + e of a unit, key quarter qd)
+    const int ktpos = 16 * (16 * qd + ((g4 + e) ^ (4 * qd)));
+
+    // A tiles: tile index -> (query row tile tr, key tile tc in Chain order)
+    constexpr int NA = 12;
+    auto a_tile = [](int idx, int &tr, int &tc) __attribute__((always_inline)) {
+        tr = idx < 4 ? idx / 2 : 2 + (idx - 4) / 4;
+        tc = idx < 4 ? idx % 2 : (idx - 4) % 4;
+    };
+    constexpr int NA_W = (NA + NW - 1) / NW;                     // tiles per wave, at most
+    // the wave index as a scalar: the per-wave branches around matrix instructions must be
+    // scalar branches (a matrix instruction runs for the whole wave whatever the exec mask,
+    // so an exec-masked branch would let every wave run every tile's product)
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+
+    auto step = [&](auto bufc, int64_t t0, int len, auto &&stage_hook) __attribute__((always_inline)) {
+        const unsigned char *stg = stage_ptr(bufc);
+        auto frag = [&](int off) __attribute__((always_inline)) {
+            return *reinterpret_cast<const bf16x8 *>(stg + off);
+        };
+        auto rec4 = [&](int arr, int row0) __attribute__((always_inline)) {
+            return *reinterpret_cast<const f32x4 *>(stg + OFF_D + 4 * (arr * C + row0));
+        };
+        auto rec1 = [&](int arr, int row) __attribute__((always_inline)) {
+            return *reinterpret_cast<const float *>(stg + OFF_D + 4 * (arr * C + row));
+        };
+        auto tr4 = [&](int off) __attribute__((always_inline)) {
+            return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(stage_lds(bufc) + off));
+        };
+
+        // ---- [Q;K] S, and this wave's A tiles from the same fragments ----
+        stage_hook(std::integral_constant<int, 0>{});
+        bf16x8 sb[NSK];
+#pragma unroll
+        for (int st = 0; st < NSK; ++st)
+            sb[st] = CH::b_frag(sacc, st);
+        f32x4 qacc[RT], xacc[RT], aacc[NA_W];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            qacc[rt] = zero4();
+            xacc[rt] = zero4();
+        }
+#pragma unroll
+        for (int i = 0; i < NA_W; ++i)
+            aacc[i] = zero4();
+#pragma unroll
+        for (int st = 0; st < NSK; ++st) {
+            bf16x8 fq[RT], fk[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                fq[rt] = frag(OFF_Q + (rt * NSK + st) * 1024 + lin);
+                fk[rt] = frag(OFF_K + (rt * NSK + st) * 1024 + kperm);
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                qacc[rt] = M::mma(sb[st], fq[rt], qacc[rt]);
+                xacc[rt] = M::mma(fk[rt], sb[st], xacc[rt]);
+            }
+            // A^T tile (key rows CH::row(tc, .), query rows 16 tr + .) = K_tc . Q_tr
+            static_for<NW>([&](auto wc) __attribute__((always_inline)) {
+                constexpr int W = decltype(wc)::value;
+                if (W != wu)
+                    return;
+                static_for<NA_W>([&](auto ic) __attribute__((always_inline)) {
+                    constexpr int I = decltype(ic)::value, IDX = W + I * NW;
+                    if constexpr (IDX < NA) {
+                        constexpr int TR = IDX < 4 ? IDX / 2 : 2 + (IDX - 4) / 4;
+                        constexpr int TC = IDX < 4 ? IDX % 2 : (IDX - 4) % 4;
+                        aacc[I] = M::mma(fk[TC], fq[TR], aacc[I]);
+                    }
+                });
+            });
+        }
+        // A: lane holds query row t = 16 tr + l % 16 and the 4 consecutive keys j0 .. j0 + 3,
+        // j0 = CH::row(tc, 4 g); exp(G_t - G_j) is formed only for j <= t (log-space mask)
+        static_for<NA_W>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int I = decltype(ic)::value;
+            const int idx = wu + I * NW;
+            if (idx < NA) {
+                int tr, tc;
+                a_tile(idx, tr, tc);
+                const int t = 16 * tr + r16, j0 = CH::row(tc, g4);
+                const float gt = rec1(0, t);
+                const f32x4 gj = rec4(0, j0);
+                f32x4 av;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    av[i] = (j0 + i <= t) ? scale * __expf(gt - gj[i]) * aacc[I][i] : 0.f;
+                const u32x2 p0 = split_bf16x2(av[0], av[1]), p1 = split_bf16x2(av[2], av[3]);
+                const int off = SA::off(t, 2 * j0);
+                *reinterpret_cast<u32x2 *>(abuf + off) = u32x2{p0[0], p1[0]};
+                *reinterpret_cast<u32x2 *>(abuf + AB + off) = u32x2{p0[1], p1[1]};
+            }
+        });
+
+        stage_hook(std::integral_constant<int, 1>{});
+        // X = beta v - beta exp(G) (K S) on this lane's rows CH::row(rt, g4 + i)
+        bf16x8 xb[NSC];
+        {
+            f32x4 t[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                const bf16x4 vv = __builtin_bit_cast(bf16x4, tr4(OFF_V + CH::row(rt, 0) * VRB + vtro));
+                const f32x4 vf = {(float)vv[0], (float)vv[1], (float)vv[2], (float)vv[3]};
+                t[rt] = rec4(2, CH::row(rt, g4)) * vf - rec4(3, CH::row(rt, g4)) * xacc[rt];
+            }
+#pragma unroll
+            for (int st = 0; st < NSC; ++st)
+                xb[st] = CH::b_frag(t, st);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        stage_hook(std::integral_constant<int, 2>{});
+        // Y = T_hi X + T_lo X (rows CH::row(rt, .)); T is zero in units (rt < 2, st = 1)
+        f32x4 yacc[RT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            yacc[rt] = zero4();
+#pragma unroll
+            for (int st = 0; st < NSC; ++st) {
+                if (rt < 2 && st == 1)
+                    continue;
+                const int u = tform_unit(rt, st);
+                const bf16x8 th = frag(OFF_T + u * 1024 + lin), tl = frag(OFF_T + (kTUnits + u) * 1024 + lin);
+                yacc[rt] = M::mma(th, xb[st], yacc[rt]);
+                yacc[rt] = M::mma(tl, xb[st], yacc[rt]);
+            }
+        }
+        // hi/lo B fragments of Y and of lambda Y (contraction rows 32 st + 8 g + {0..7})
+        bf16x8 yh[NSC], yl[NSC], dh[NSC], dl[NSC];
+        {
+            f32x4 ly[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                ly[rt] = rec4(1, CH::row(rt, g4)) * yacc[rt];
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+            for (int st = 0; st < NSC; ++st) {
+                u32x4 a0, a1, b0, b1;
+#pragma unroll
+                for (int hlf = 0; hlf < 2; ++hlf)
+#pragma unroll
+                    for (int pr = 0; pr < 2; ++pr) {
+                        const f32x4 &ty = yacc[2 * st + hlf], &tl = ly[2 * st + hlf];
+                        const u32x2 sy = split_bf16x2(ty[2 * pr], ty[2 * pr + 1]);
+                        const u32x2 sl = split_bf16x2(tl[2 * pr], tl[2 * pr + 1]);
+                        a0[2 * hlf + pr] = sy[0];
+                        a1[2 * hlf + pr] = sy[1];
+                        b0[2 * hlf + pr] = sl[0];
+                        b1[2 * hlf + pr] = sl[1];
+                    }
+                yh[st] = __builtin_bit_cast(bf16x8, a0);
+                yl[st] = __builtin_bit_cast(bf16x8, a1);
+                dh[st] = __builtin_bit_cast(bf16x8, b0);
+                dl[st] = __builtin_bit_cast(bf16x8, b1);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        stage_hook(std::integral_constant<int, 3>{});
+        // S <- exp(G_last) S + K^T (lambda Y)_hi + K^T (lambda Y)_lo
+        const float gl = __expf(rec1(0, C - 1));
+#pragma unroll
+        for (int sr = 0; sr < SR; ++sr) {
+            sacc[sr] = sacc[sr] * gl;
+#pragma unroll
+            for (int st = 0; st < NSC; ++st) {
+                const int u0 = OFF_K + ((2 * st) * NSK + (sr >> 1)) * 1024 + ktpos + 8 * (sr & 1);
+                const s16x4 k0 = tr4(u0), k1 = tr4(u0 + NSK * 1024);
+                typedef short s16x8 __attribute__((ext_vector_type(8)));
+                const bf16x8 kt = __builtin_bit_cast(bf16x8, s16x8{k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]});
+                sacc[sr] = M::mma(kt, dh[st], sacc[sr]);
+                sacc[sr] = M::mma(kt, dl[st], sacc[sr]);
+            }
+        }
+
+        // every wave's A tiles are in LDS (an LDS-only barrier: the next chunk's staging
+        // loads stay in flight)
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        // O^T = scale (Q S)^T diag(exp G) + Y^T A^T: lane l holds token row 16 rt + l % 16 and
+        // the four columns 4 (l / 16) .. +3 of this wave's
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const float gs = scale * __expf(rec1(0, 16 * rt + r16));
+            qacc[rt] *= gs;
+#pragma unroll
+            for (int st = 0; st < NSC; ++st) {
+                if (rt < 2 && st == 1)
+                    continue;
+                const int off = SA::off(16 * rt + r16, 64 * st + 16 * G);
+                const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(abuf + off);
+                const bf16x8 al = *reinterpret_cast<const bf16x8 *>(abuf + AB + off);
+                qacc[rt] = M::mma(yh[st], ah, qacc[rt]);
+                qacc[rt] = M::mma(yl[st], ah, qacc[rt]);
+                qacc[rt] = M::mma(yh[st], al, qacc[rt]);
+            }
+        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+            const int r = 16 * rt + r16;
+            if (r < len) {
+                bf16 *orow = o + ((size_t)(t0 + r) * hv + h) * dv + col0 + g4;
+                *reinterpret_cast<bf16x4 *>(orow) =
+                    bf16x4{(bf16)qacc[rt][0], (bf16)qacc[rt][1], (bf16)qacc[rt][2], (bf16)qacc[rt][3]};
+            }
+        }
+    };
+
+    // ---- pipeline: buffers alternate from buffer 0; the end-of-step barrier also keeps the
+    //      next step's A tiles from overwriting the ones still being read ----
+    const std::integral_constant<int, 0> buf0;
+    const std::integral_constant<int, 1> buf1;
+    issue_stage(buf0, c_begin);
+    stage_done();
+    for (int c = c_begin;;) {
+        bool more = c + 1 < c_end;
+        int64_t t0 = a + (int64_t)c * C;
+        step(buf0, t0, (int)min<int64_t>(C, b - t0), [&](auto pc) __attribute__((always_inline)) {
+            if (more)
+                stage_part(buf1, c + 1, pc);
+        });
+        stage_done();
+        if (++c >= c_end)
+            break;
+        more = c + 1 < c_end;
+        t0 = a + (int64_t)c * C;
+        step(buf1, t0, (int)min<int64_t>(C, b - t0), [&](auto pc) __attribute__((always_inline)) {
+            if (more)
+                stage_part(buf0, c + 1, pc);
+        });
+        stage_done();
+        if (++c >= c_end)
+            break;
+    }
+
+    // ---- final state ----
+#pragma unroll
+    for (int sr = 0; sr < SR; ++sr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            state_out[state_base + (size_t)CH::row(sr, g4 + i) * dv + col0 + r16] = sacc[sr][i];
+}
+
+// ---------------------------------------------------------------------------
 // Launch.
 // ---------------------------------------------------------------------------
 
@@ -2312,6 +2814,20 @@ static void launch_scan_bf16(const PrefillArgs &p, const SlotMap &map, const bf1
                           p.dv, wmat, mmat, dec, sin, sout, static_cast<bf16 *>(p.o), p.scale);
 }
 
+template <int DK, int NW>
+static void launch_scan_tform(const PrefillArgs &p, const SlotMap &map, const bf16 *tmat, const float *dec,
+                              const float *sin, float *sout, hipStream_t st)
+{
+    const int nv = p.dv / (16 * NW);
+    const int64_t items = (int64_t)map.ranks * p.hqk;                  // (sequence, query/key head)
+    const int64_t blocks = ((items + 7) / 8) * 8 * (p.hv / p.hqk) * nv;
+    const ProfEvents ev = prof_events(PROF_SCAN, PROF_SCAN_TFORM);
+    hipExtLaunchKernelGGL((gdn_chunk_scan_tform_kernel<DK, NW>), dim3((unsigned)blocks), dim3(NW * kWave), 0, st,
+                          ev.start, ev.stop, 0, static_cast<const bf16 *>(p.q), static_cast<const bf16 *>(p.k),
+                          static_cast<const bf16 *>(p.v), p.cu_seqlens, map, map.ranks, p.total_tokens, p.hqk, p.hv,
+                          p.dv, tmat, dec, sin, sout, static_cast<bf16 *>(p.o), p.scale);
+}
+
 // Batches of at most this many sequences are scanned longest first.
 constexpr int32_t kMaxOrderedSeqs = 4096;
 
@@ -2347,6 +2863,10 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
         return hipGetLastError();
     };
 
+    // Whole-head batches (many (sequence, head) pairs, no split by length) take the T form:
+    // the prep writes T alone and the whole-head scan forms A and Y = T X itself.
+    const bool mixed = p.long_ranks > 0 && p.long_ranks < p.num_seqs;
+    const bool tform = kAbsorbed && DK == 128 && (int64_t)p.num_seqs * p.hv > 64 && !mixed;
     auto scan = [&](const SlotMap &map, const float *sin, float *sout) {
         if constexpr (std::is_same<E, bf16>::value && C == 64) {
             // 32 columns per wave; a whole 128-column head per workgroup when the batch
@@ -2358,7 +2878,11 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
             // crossover: 64 pairs (1024-token sequences, 16 chunk steps).
             const int64_t pairs = (int64_t)p.num_seqs * p.hv;
             if constexpr (DK == 128) {
-                if (p.long_ranks > 0 && p.long_ranks < p.num_seqs) {
+                if (tform) {
+                    launch_scan_tform<DK, 8>(p, map, tmat, dec, sin, sout, st);
+                    return;
+                }
+                if (mixed) {
                     // Mixed batch (host offsets: a few sequences whose chains would bound a
                     // whole-head scan): its longest sequences (the first ranks) in the
                     // row-split scan, the rest in the whole-head scan.
@@ -2388,11 +2912,23 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
         const dim3 grid = AbsorbedForm<E, C>::value
                               ? dim3((unsigned)(((items + 7) / 8) * 8 * (p.hv / p.hqk)))
                               : dim3((unsigned)slots, (unsigned)p.hqk);
-        hipExtLaunchKernelGGL((gdn_prep_kernel<E, C, DK>), grid,
-                              dim3(PrepWaves<E, C>::value * kWave), 0, st,
-                              ev.start, ev.stop, 0, static_cast<const E *>(p.q), static_cast<const E *>(p.k), p.g,
-                              p.beta, p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv, tmat, amat, dec,
-                              p.scale, (int32_t)slots);
+        auto go = [&](auto kern) {
+            hipExtLaunchKernelGGL(kern, grid, dim3(PrepWaves<E, C>::value * kWave), 0, st, ev.start, ev.stop, 0,
+                                  static_cast<const E *>(p.q), static_cast<const E *>(p.k), p.g, p.beta,
+                                  p.cu_seqlens, map, p.num_seqs, p.total_tokens, p.hqk, p.hv, tmat, amat, dec,
+                                  p.scale, (int32_t)slots);
+        };
+        if constexpr (!kAbsorbed) {
+            go(gdn_prep_kernel<E, C, DK, kPrepDirect>);
+        } else {
+            if constexpr (DK == 128) {
+                if (tform) {
+                    go(gdn_prep_kernel<E, C, DK, kPrepTForm>);
+                    return;
+                }
+            }
+            go(gdn_prep_kernel<E, C, DK, kPrepAbsorbed>);
+        }
     };
 
     // Longest sequences first in the scans (their chains of chunk steps bound the time),

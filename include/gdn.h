@@ -350,7 +350,9 @@ gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, const void *o, const void *
  * 5 gated RMSNorm, 6 conv1d, 7 conv state update; and which chunk-scan kernel ran
  * (each of these launches also counts under 2): 8 the row-split scan (few
  * (sequence, head) pairs, bf16, chunk 64), 9 the whole-head scan (many pairs,
- * bf16, chunk 64, dk = 128), 10 the general scan (fp32 io or chunk 16).
+ * bf16, chunk 64, dk = 128, in a batch split by length), 10 the general scan (fp32 io
+ * or chunk 16), 11 the whole-head scan of the T form (many pairs, bf16, chunk 64,
+ * dk = 128).
  * The events are created on first use and kept until the process ends;
  * no device memory is allocated.
  */
