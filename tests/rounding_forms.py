@@ -10,6 +10,9 @@ decayed query-key matrix carrying the output scale:
              (operands rounded: S, W', U, D, lambda D, A)
   absorbed:  W = K^T lambda T,  M = A T  (formed without rounding),
              O = scale gamma Q S + M X,  S <- Gamma S + W X   (operands rounded: S, X, W, M)
+  tform:     Y = T X with T as a hi/lo bf16 pair,  S <- Gamma S + K^T (lambda Y) with lambda Y
+             as a hi/lo pair,  O = scale gamma Q S + A Y with A and Y as hi/lo pairs (the
+             lo x lo product dropped)              (operands rounded: S, X; T, lambda Y, A, Y split)
 Every product accumulates in fp32; T comes from an fp64 inverse (the solve is not what is
 compared here).
 """
@@ -19,6 +22,11 @@ import torch
 
 def _bf(x):
     return x.to(torch.bfloat16).to(torch.float32)
+
+
+def _split(x):
+    hi = _bf(x)
+    return hi, _bf(x - hi)
 
 
 def run(q, k, v, g, beta, form, chunk=64, scale=None):
@@ -45,6 +53,16 @@ def run(q, k, v, g, beta, form, chunk=64, scale=None):
         gam, lam = torch.exp(G).float(), torch.exp(G[-1] - G).float()
         Gam = float(torch.exp(G[-1]))
         Sb = _bf(S)
+        if form == "tform":
+            X = _bf(b[:, None] * V - (b * gam)[:, None] * (K @ Sb))
+            Th, Tl = _split(Tm)
+            Y = Th @ X + Tl @ X
+            Dh, Dl = _split(lam[:, None] * Y)
+            Ah, Al = _split(A)
+            Yh, Yl = _split(Y)
+            o[c0:c1] = scale * gam[:, None] * (Q @ Sb) + Ah @ Yh + Ah @ Yl + Al @ Yh
+            S = Gam * S + K.T @ Dh + K.T @ Dl
+            continue
         if form == "absorbed":
             W = (K.T * lam[None, :]) @ Tm
             M = A @ Tm
