@@ -43,16 +43,52 @@
 
 namespace gdn {
 
+// Order in which the scan kernels take the sequences: by decreasing length
+// (ties by index), so that the workgroups of the longest chains of chunk steps
+// are dispatched first and the short ones fill the compute units they free.
+// order[rank] = n; the ranks form a permutation, so every entry is written
+// once.  Quadratic in the number of sequences (used for small batches only).
+__device__ inline void rank_sequence(const int32_t *__restrict__ cu, int32_t num_seqs, int64_t total_tokens,
+                                     int32_t *__restrict__ order, int n)
+{
+    if (n >= num_seqs)
+        return;
+    auto length = [&](int m) {
+        const int64_t a = min<int64_t>(max<int64_t>(cu[m], 0), total_tokens);
+        const int64_t b = min<int64_t>(max<int64_t>(cu[m + 1], a), total_tokens);
+        return b - a;
+    };
+    const int64_t len = length(n);
+    int rank = 0;
+    for (int m = 0; m < num_seqs; ++m) {
+        const int64_t lm = length(m);
+        rank += (lm > len || (lm == len && m < n)) ? 1 : 0;
+    }
+    order[rank] = n;
+}
+
+__global__ __launch_bounds__(kThreads) void gdn_seq_order_kernel(const int32_t *__restrict__ cu, int32_t num_seqs,
+                                                               int64_t total_tokens, int32_t *__restrict__ order)
+{
+    rank_sequence(cu, num_seqs, total_tokens, order, blockIdx.x * kThreads + threadIdx.x);
+}
+
 // ---------------------------------------------------------------------------
 // Chunk table: chunk_start[n] = sum_{m<n} ceil(L_m / C), clamped to
 // max_chunks; chunk_start[num_seqs] = total number of chunks.  Offsets are
 // clamped to [0, total_tokens] so that invalid input cannot send later
-// kernels out of bounds.  One workgroup.
+// kernels out of bounds.  Workgroup 0 builds the table; with `order` given, the
+// grid has one thread per sequence and also ranks them (gdn_seq_order_kernel's
+// work in the same launch).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void gdn_chunk_table_kernel(
     const int32_t *__restrict__ cu, int32_t num_seqs, int64_t total_tokens, int32_t chunk,
-    int32_t max_chunks, int32_t *__restrict__ chunk_start)
+    int32_t max_chunks, int32_t *__restrict__ chunk_start, int32_t *__restrict__ order)
 {
+    if (order)
+        rank_sequence(cu, num_seqs, total_tokens, order, blockIdx.x * kThreads + threadIdx.x);
+    if (blockIdx.x != 0)
+        return;
     __shared__ int64_t wave_tot[kWaves];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     int64_t carry = 0;
@@ -87,31 +123,6 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_table_kernel(
     }
     if (tid == 0)
         chunk_start[num_seqs] = (int32_t)min<int64_t>(carry, max_chunks);
-}
-
-// Order in which the scan kernels take the sequences: by decreasing length
-// (ties by index), so that the workgroups of the longest chains of chunk steps
-// are dispatched first and the short ones fill the compute units they free.
-// order[rank] = n; the ranks form a permutation, so every entry is written
-// once.  Quadratic in the number of sequences (used for small batches only).
-__global__ __launch_bounds__(kThreads) void gdn_seq_order_kernel(const int32_t *__restrict__ cu, int32_t num_seqs,
-                                                               int64_t total_tokens, int32_t *__restrict__ order)
-{
-    const int n = blockIdx.x * kThreads + threadIdx.x;
-    if (n >= num_seqs)
-        return;
-    auto length = [&](int m) {
-        const int64_t a = min<int64_t>(max<int64_t>(cu[m], 0), total_tokens);
-        const int64_t b = min<int64_t>(max<int64_t>(cu[m + 1], a), total_tokens);
-        return b - a;
-    };
-    const int64_t len = length(n);
-    int rank = 0;
-    for (int m = 0; m < num_seqs; ++m) {
-        const int64_t lm = length(m);
-        rank += (lm > len || (lm == len && m < n)) ? 1 : 0;
-    }
-    order[rank] = n;
 }
 
 // Sequence that owns chunk entry e: chunk_start[n] <= e < chunk_start[n+1].
@@ -2932,18 +2943,19 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
     };
 
     // Longest sequences first in the scans (their chains of chunk steps bound the time),
-    // unless the host offsets show the batch in that order already.
-    const int32_t *order = nullptr;
-    if (p.num_seqs > 1 && p.num_seqs <= kMaxOrderedSeqs && !p.ordered) {
-        int32_t *ord = chunk_start + p.num_seqs + 1;   // after the chunk table
-        const ProfEvents ev = prof_events(PROF_CHUNK_TABLE);
-        hipExtLaunchKernelGGL(gdn_seq_order_kernel, dim3((unsigned)((p.num_seqs + kThreads - 1) / kThreads)),
-                              dim3(kThreads), 0, st, ev.start, ev.stop, 0, p.cu_seqlens, p.num_seqs, p.total_tokens,
-                              ord);
-        order = ord;
-    }
+    // unless the host offsets show the batch in that order already.  In the single launch
+    // over the chunk table the ranking runs in the table's launch.
+    int32_t *order = nullptr;
+    if (p.num_seqs > 1 && p.num_seqs <= kMaxOrderedSeqs && !p.ordered)
+        order = chunk_start + p.num_seqs + 1;   // after the chunk table
+    const unsigned rank_blocks = (unsigned)((p.num_seqs + kThreads - 1) / kThreads);
 
     if (p.seg_len > 0) {
+        if (order) {
+            const ProfEvents ev = prof_events(PROF_CHUNK_TABLE);
+            hipExtLaunchKernelGGL(gdn_seq_order_kernel, dim3(rank_blocks), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
+                                  p.cu_seqlens, p.num_seqs, p.total_tokens, order);
+        }
         // Segment mode: local chunks [s0, s0 + seg_len) of every sequence per step.
         for (int32_t s0 = 0; s0 < p.max_seq_chunks; s0 += p.seg_len) {
             const SlotMap map{nullptr, s0, p.seg_len, order, 0, p.num_seqs};
@@ -2955,8 +2967,9 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
 
     {
         const ProfEvents ev = prof_events(PROF_CHUNK_TABLE);
-        hipExtLaunchKernelGGL(gdn_chunk_table_kernel, dim3(1), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
-                              p.cu_seqlens, p.num_seqs, p.total_tokens, (int32_t)C, p.max_chunks, chunk_start);
+        hipExtLaunchKernelGGL(gdn_chunk_table_kernel, dim3(order ? rank_blocks : 1u), dim3(kThreads), 0, st, ev.start,
+                              ev.stop, 0, p.cu_seqlens, p.num_seqs, p.total_tokens, (int32_t)C, p.max_chunks,
+                              chunk_start, order);
     }
     const SlotMap map{chunk_start, 0, INT32_MAX, order, 0, p.num_seqs};
     if (p.max_chunks > 0)
