@@ -329,7 +329,6 @@ struct AbsorbedForm {
 // and the decay record.  T-form record: [G | exp(G_last - G) | beta | beta exp(G)] (the scan
 // masks exp(G_t - G_j) in log space itself); the others: [exp(G) | ... ].
 enum PrepForm { kPrepDirect = 0, kPrepAbsorbed = 1, kPrepTForm = 2 };
-
 // T in the T form: 6 units of 16 rows x 32 columns per bf16 matrix (hi, then lo), the
 // units of T's row tiles rt (rows Chain<Mma<bf16>>::row(rt, .)) and column halves st with
 // st <= rt / 2 (the other two are zero: T is lower triangular); unit u(rt, st) holds at
@@ -2346,6 +2345,10 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_bf16_kernel(
 // q, k, X and S enter as bf16.  K^T comes from the K units with the LDS transpose read: for
 // the contraction rows 32 st + 8 g + {0..7} and key rows Chain row(sr, .), input lane
 // (e, quarter) of a 16-lane group reads 4 keys of chunk row 32 st + 8 g + e (+ 4).
+// The output leaves through LDS: each wave holds 16 columns of the chunk's 64 rows, which
+// written straight out would be 32-byte pieces of each row (partial-line writes, about a
+// sixth of the kernel's time on a long batch); the waves write their pieces into one bf16
+// row buffer, and after the barrier that ends the step each wave stores 8 whole rows.
 // ---------------------------------------------------------------------------
 template <int DK, int NW>
 __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
@@ -2375,12 +2378,17 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
     constexpr int OFF_D = OFF_V + NU_V * 1024;
     constexpr int STAGE = OFF_D + 1024;
     constexpr int AB = C * C * 2;                  // bytes of one bf16 A matrix
-    typedef Swz<C * 2> SA;
     static_assert(C * VRB % 1024 == 0 && 4 * C * 4 == 1024 && VRB == 256, "whole units, 256-byte V rows");
 
     __shared__ __attribute__((aligned(1024))) unsigned char stage0[STAGE];
     __shared__ __attribute__((aligned(1024))) unsigned char stage1[STAGE];
-    __shared__ __attribute__((aligned(1024))) unsigned char abuf[2 * AB];   // A hi, A lo (rows t, SA order)
+    // A hi, A lo, each in 1 KB fragment units: unit 2 rt + st holds at 16-byte position p the
+    // query row 16 rt + p % 16, keys 32 st + 8 (p / 16) .. +7
+    __shared__ __attribute__((aligned(1024))) unsigned char abuf[2 * AB];
+    // the chunk's output rows (bf16, rows of ORB bytes): each wave writes its 16 columns, and
+    // after the barrier that ends the step each wave stores 8 whole rows (full-line writes)
+    constexpr int ORB = DVS * 2 + 16;
+    __shared__ __attribute__((aligned(16))) unsigned char obuf[C * ORB];
     auto stage_ptr = [&](auto bufc) __attribute__((always_inline)) -> unsigned char * {
         return decltype(bufc)::value ? stage1 : stage0;
     };
@@ -2546,8 +2554,26 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
     // so an exec-masked branch would let every wave run every tile's product)
     const int wu = __builtin_amdgcn_readfirstlane(w);
 
-    auto step = [&](auto bufc, int64_t t0, int len, auto &&stage_hook) __attribute__((always_inline)) {
+    // the previous chunk's output rows, from obuf to o: rows 8 w .. 8 w + 7 of this wave, lane l
+    // moving 16 bytes of row 8 w + 4 u + l / 16 (u = 0, 1); rows past the chunk's end skipped
+    const uint32_t olane = (uint32_t)(lane >> 4) * (uint32_t)(hv * dv) + (uint32_t)(8 * (lane & 15));
+    int64_t t0c = 0;
+    int lenc = 0;
+    auto store_rows = [&]() __attribute__((always_inline)) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        bf16 *ob = o + ((size_t)t0c * hv + h) * dv + (size_t)s * DVS;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int r = 8 * wu + 4 * u + (lane >> 4);
+            const u32x4 v4 = *reinterpret_cast<const u32x4 *>(obuf + r * ORB + 16 * (lane & 15));
+            if (r < lenc)
+                *reinterpret_cast<u32x4 *>(ob + (size_t)(8 * wu + 4 * u) * hv * dv + olane) = v4;
+        }
+    };
+
+    auto step = [&](auto bufc, int64_t t0, int len, bool carried, auto &&stage_hook) __attribute__((always_inline)) {
         const unsigned char *stg = stage_ptr(bufc);
+        unsigned char *abw = abuf;
         auto frag = [&](int off) __attribute__((always_inline)) {
             return *reinterpret_cast<const bf16x8 *>(stg + off);
         };
@@ -2562,8 +2588,11 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
                 (__attribute__((address_space(3))) s16x4 *)(stage_lds(bufc) + off));
         };
 
-        // ---- [Q;K] S, and this wave's A tiles from the same fragments ----
+        // ---- the previous chunk's output rows (obuf was filled before the last barrier) ----
         stage_hook(std::integral_constant<int, 0>{});
+        if (carried)
+            store_rows();
+        // ---- [Q;K] S, and this wave's A tiles from the same fragments ----
         bf16x8 sb[NSK];
 #pragma unroll
         for (int st = 0; st < NSK; ++st)
@@ -2621,9 +2650,11 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
                 for (int i = 0; i < 4; ++i)
                     av[i] = (j0 + i <= t) ? scale * __expf(gt - gj[i]) * aacc[I][i] : 0.f;
                 const u32x2 p0 = split_bf16x2(av[0], av[1]), p1 = split_bf16x2(av[2], av[3]);
-                const int off = SA::off(t, 2 * j0);
-                *reinterpret_cast<u32x2 *>(abuf + off) = u32x2{p0[0], p1[0]};
-                *reinterpret_cast<u32x2 *>(abuf + AB + off) = u32x2{p0[1], p1[1]};
+                // keys j0 .. j0 + 3 = 32 (tc / 2) + 8 g + 4 (tc % 2) + {0..3}: unit (tr, tc / 2),
+                // position r16 + 16 g, half tc % 2
+                const int off = (2 * tr + (tc >> 1)) * 1024 + 16 * lane + 8 * (tc & 1);
+                *reinterpret_cast<u32x2 *>(abw + off) = u32x2{p0[0], p1[0]};
+                *reinterpret_cast<u32x2 *>(abw + AB + off) = u32x2{p0[1], p1[1]};
             }
         });
 
@@ -2708,40 +2739,45 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
             }
         }
 
-        // every wave's A tiles are in LDS (an LDS-only barrier: the next chunk's staging
-        // loads stay in flight)
+        // every wave's A tiles are in LDS, and every wave has stored the previous chunk's rows
+        // from obuf (an LDS-only barrier: the next chunk's staging loads stay in flight)
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        // O^T = scale (Q S)^T diag(exp G) + Y^T A^T: lane l holds token row 16 rt + l % 16 and
-        // the four columns 4 (l / 16) .. +3 of this wave's
+        // O^T = scale (Q S)^T diag(exp G) + Y^T A^T: lane l holds token row 16 rt + l % 16 and the
+        // four columns 4 (l / 16) .. +3 of this wave's.  Key half 0 meets all four row tiles,
+        // half 1 the last two (the others are zero): the fragments of a half are read together
+        // and the row tiles' products interleaved.
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const float gs = scale * __expf(rec1(0, 16 * rt + r16));
-            qacc[rt] *= gs;
+        for (int rt = 0; rt < RT; ++rt)
+            qacc[rt] *= scale * __expf(rec1(0, 16 * rt + r16));
+        static_for<NSC>([&](auto sc) __attribute__((always_inline)) {
+            constexpr int ST = decltype(sc)::value, R0 = ST == 0 ? 0 : 2;
+            bf16x8 ah[RT], al[RT];
 #pragma unroll
-            for (int st = 0; st < NSC; ++st) {
-                if (rt < 2 && st == 1)
-                    continue;
-                const int off = SA::off(16 * rt + r16, 64 * st + 16 * G);
-                const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(abuf + off);
-                const bf16x8 al = *reinterpret_cast<const bf16x8 *>(abuf + AB + off);
-                qacc[rt] = M::mma(yh[st], ah, qacc[rt]);
-                qacc[rt] = M::mma(yl[st], ah, qacc[rt]);
-                qacc[rt] = M::mma(yh[st], al, qacc[rt]);
+            for (int rt = R0; rt < RT; ++rt) {
+                const int off = (2 * rt + ST) * 1024 + 16 * lane;
+                ah[rt] = *reinterpret_cast<const bf16x8 *>(abuf + off);
+                al[rt] = *reinterpret_cast<const bf16x8 *>(abuf + AB + off);
             }
-        }
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-            const int r = 16 * rt + r16;
-            if (r < len) {
-                bf16 *orow = o + ((size_t)(t0 + r) * hv + h) * dv + col0 + g4;
-                *reinterpret_cast<bf16x4 *>(orow) =
-                    bf16x4{(bf16)qacc[rt][0], (bf16)qacc[rt][1], (bf16)qacc[rt][2], (bf16)qacc[rt][3]};
-            }
-        }
+            for (int rt = R0; rt < RT; ++rt)
+                qacc[rt] = M::mma(yh[ST], ah[rt], qacc[rt]);
+#pragma unroll
+            for (int rt = R0; rt < RT; ++rt)
+                qacc[rt] = M::mma(yl[ST], ah[rt], qacc[rt]);
+#pragma unroll
+            for (int rt = R0; rt < RT; ++rt)
+                qacc[rt] = M::mma(yh[ST], al[rt], qacc[rt]);
+        });
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            *reinterpret_cast<bf16x4 *>(obuf + (16 * rt + r16) * ORB + 2 * (WC * wu + g4)) =
+                bf16x4{(bf16)qacc[rt][0], (bf16)qacc[rt][1], (bf16)qacc[rt][2], (bf16)qacc[rt][3]};
+        t0c = t0;
+        lenc = len;
     };
 
-    // ---- pipeline: buffers alternate from buffer 0; the end-of-step barrier also keeps the
-    //      next step's A tiles from overwriting the ones still being read ----
+    // ---- pipeline: buffers alternate from buffer 0; the barrier that ends a step also
+    //      publishes its output rows in obuf to the next step ----
     const std::integral_constant<int, 0> buf0;
     const std::integral_constant<int, 1> buf1;
     issue_stage(buf0, c_begin);
@@ -2749,22 +2785,26 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
     for (int c = c_begin;;) {
         bool more = c + 1 < c_end;
         int64_t t0 = a + (int64_t)c * C;
-        step(buf0, t0, (int)min<int64_t>(C, b - t0), [&](auto pc) __attribute__((always_inline)) {
+        step(buf0, t0, (int)min<int64_t>(C, b - t0), c != c_begin, [&](auto pc) __attribute__((always_inline)) {
             if (more)
                 stage_part(buf1, c + 1, pc);
         });
         stage_done();
-        if (++c >= c_end)
+        if (++c >= c_end) {
+            store_rows();
             break;
+        }
         more = c + 1 < c_end;
         t0 = a + (int64_t)c * C;
-        step(buf1, t0, (int)min<int64_t>(C, b - t0), [&](auto pc) __attribute__((always_inline)) {
+        step(buf1, t0, (int)min<int64_t>(C, b - t0), true, [&](auto pc) __attribute__((always_inline)) {
             if (more)
                 stage_part(buf0, c + 1, pc);
         });
         stage_done();
-        if (++c >= c_end)
+        if (++c >= c_end) {
+            store_rows();
             break;
+        }
     }
 
     // ---- final state ----
