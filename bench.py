@@ -142,7 +142,7 @@ def _kernel_times(steps):
     """Per-step launches and time of each library kernel recorded since profile_enable."""
     import gated_deltanet_scan_amd as gdn
     kern = {}
-    for kid, kname in ((0, "chunk_table"), (1, "prep"), (2, "scan"), (4, "snapshot")):
+    for kid, kname in ((0, "chunk_table"), (1, "prep"), (2, "scan"), (12, "short"), (4, "snapshot")):
         n, tot = gdn.profile_collect(kid)
         kern[kname] = {"launches_per_step": n / steps, "avg_us": (tot / n * 1e3) if n else None,
                        "per_step_us": tot * 1e3 / steps}
@@ -261,13 +261,19 @@ def measure_prefill(name, steps, warmup, lengths=None, verify=None):
                          "accepted": accepted,
                          "step": "prefill, snapshot, %d-token draft prefill, restore, re-feed prefill"
                                  % w.verify_tokens}
-    out["roofline"] = roofline_for(out, costs, peak)
+    scan_costs = costs
+    if verify and kern["short"]["launches_per_step"]:
+        # the draft and re-feed calls ran the token-recurrent kernel (every sequence of each at
+        # most 8 tokens), so the scan launches did the prompts' work alone
+        scan_costs = prefill_costs(w, T, 1, N)
+    out["roofline"] = roofline_for(out, scan_costs, peak)
     return out
 
 
 def roofline_for(pre, costs, peak_tflops):
-    """Roofline object of the scan kernel, the step's dominant kernel: the step's algorithmic
-    bytes (or flops) spread over its scan launches, divided by their average duration."""
+    """Roofline object of the scan kernel, the step's dominant kernel: the algorithmic bytes (or
+    flops) of the calls its launches served, spread over those launches, divided by their
+    average duration."""
     k = pre["kernels"]["scan"]
     launches, us = k["launches_per_step"], k["avg_us"]
     c = {key: v / launches for key, v in costs.items()}

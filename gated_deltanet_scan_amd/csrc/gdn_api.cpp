@@ -355,6 +355,7 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
     p.table_bytes = ws.table_bytes;
     p.seg_len = 0;
     p.max_seq_chunks = 0;
+    p.max_len = -1;
     if (cu_seqlens_host) {
         int64_t longest = 0, prev_chunks = INT64_MAX;
         p.ordered = true;
@@ -366,6 +367,7 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
             prev_chunks = chunks;
         }
         p.max_seq_chunks = (int32_t)((longest + s.chunk - 1) / s.chunk);
+        p.max_len = (int32_t)longest;
         {
             std::vector<int64_t> chunks(num_seqs);
             for (int32_t n = 0; n < num_seqs; ++n)

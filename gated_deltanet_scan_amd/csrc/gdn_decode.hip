@@ -143,6 +143,168 @@ hipError_t launch_decode(const DecodeArgs &p)
 }
 
 // ---------------------------------------------------------------------------
+// Prefill of a batch of short sequences (each at most kShortPrefillTokens tokens): the
+// one-token step above, token by token, with the state slices held in registers for the
+// whole sequence.  This is the recurrence of the NPU page's per-token loop (section "How
+// it works") rather than its chunkwise form: for a sequence shorter than one chunk the
+// chunkwise form's per-chunk matrices cost a second launch (the prep) and a chunk step of
+// work for a handful of tokens, while here the state is read once and written once and the
+// batch is one launch.
+//
+// One workgroup per (sequence, value head), one wave per 32-column slice as in the decode
+// kernel.  The sequence's k and q rows (of its query/key head), its v rows, g and beta are
+// staged in LDS first (16-byte loads spread over the workgroup); the token loop then reads
+// only LDS and registers.  Sequence bounds are clamped to [0, total_tokens] and the staged
+// length to kShortPrefillTokens, so inconsistent offsets cannot send an access out of
+// bounds.
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+__global__ __launch_bounds__(D / kDecodeCols * kWave) void gdn_short_prefill_kernel(
+    const E *__restrict__ q, const E *__restrict__ k, const E *__restrict__ v, const float *__restrict__ g,
+    const float *__restrict__ beta, const int32_t *__restrict__ cu, int64_t total_tokens,
+    const float *state_in, float *state_out, E *__restrict__ o, int32_t hqk, int32_t hv, float scale)
+{
+    constexpr int NS = D / kDecodeCols;   // waves: column slices per state
+    constexpr int NT = NS * kWave;
+    constexpr int RG = 8;                 // row groups per wave
+    constexpr int RPL = D / RG;           // rows per lane
+    constexpr int L = kShortPrefillTokens;
+    constexpr int VN = Vec16<E>::n;
+    constexpr int VPR = D / VN;           // 16-byte vectors per row
+    typedef typename Vec16<E>::type V16;
+    static_assert(D % kDecodeCols == 0 && D % VN == 0, "lane layout");
+
+    __shared__ __attribute__((aligned(16))) E ks[L][D];
+    __shared__ __attribute__((aligned(16))) E qs[L][D];
+    __shared__ __attribute__((aligned(16))) E vs[L][D];
+    __shared__ float gs[L], bs[L];
+
+    const int pair = blockIdx.x;   // n * hv + h
+    const int n = pair / hv, h = pair - n * hv;
+    const int hq = h / (hv / hqk);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int64_t a = min<int64_t>(max<int64_t>(cu[n], 0), total_tokens);
+    const int64_t b = min<int64_t>(max<int64_t>(cu[n + 1], a), total_tokens);
+    const int len = (int)min<int64_t>(b - a, L);
+
+    for (int i = tid; i < len * VPR; i += NT) {
+        const int t = i / VPR, c = (i - t * VPR) * VN;
+        const size_t tok = (size_t)(a + t);
+        *reinterpret_cast<V16 *>(&ks[t][c]) = *reinterpret_cast<const V16 *>(k + (tok * hqk + hq) * D + c);
+        *reinterpret_cast<V16 *>(&qs[t][c]) = *reinterpret_cast<const V16 *>(q + (tok * hqk + hq) * D + c);
+        *reinterpret_cast<V16 *>(&vs[t][c]) = *reinterpret_cast<const V16 *>(v + (tok * hv + h) * D + c);
+    }
+    for (int t = tid; t < len; t += NT) {
+        gs[t] = g[(size_t)(a + t) * hv + h];
+        bs[t] = beta[(size_t)(a + t) * hv + h];
+    }
+
+    // lane (rg, cg): columns col .. col + 3 of rows rg * RPL .. rg * RPL + RPL - 1
+    const int rg = lane / 8, cg = lane % 8;
+    const int col = wave * kDecodeCols + 4 * cg;
+    const size_t sbase = (size_t)pair * D * D + (size_t)(rg * RPL) * D + col;
+    f32x4 s[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+        s[i] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + sbase + (size_t)i * D) : zero4();
+    __syncthreads();
+
+    for (int t = 0; t < len; ++t) {
+        float kr[RPL], qr[RPL];
+        if constexpr (RPL % VN == 0) {
+#pragma unroll
+            for (int c = 0; c < RPL / VN; ++c) {
+                const V16 kv = *reinterpret_cast<const V16 *>(&ks[t][rg * RPL + c * VN]);
+                const V16 qv = *reinterpret_cast<const V16 *>(&qs[t][rg * RPL + c * VN]);
+#pragma unroll
+                for (int e = 0; e < VN; ++e) {
+                    kr[c * VN + e] = to_f32(kv[e]);
+                    qr[c * VN + e] = to_f32(qv[e]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                kr[i] = to_f32(ks[t][rg * RPL + i]);
+                qr[i] = to_f32(qs[t][rg * RPL + i]);
+            }
+        }
+        const float alpha = expf(gs[t]);
+        const float bt = bs[t];
+        float vv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            vv[e] = to_f32(vs[t][col + e]);
+
+        f32x4 a4 = zero4(), b4 = zero4();
+        float qk = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            a4 += kr[i] * s[i];
+            b4 += qr[i] * s[i];
+            qk += qr[i] * kr[i];
+        }
+#pragma unroll
+        for (int m = 8; m < kWave; m <<= 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a4[e] += __shfl_xor(a4[e], m, kWave);
+                b4[e] += __shfl_xor(b4[e], m, kWave);
+            }
+            qk += __shfl_xor(qk, m, kWave);
+        }
+        f32x4 d4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            d4[e] = bt * (vv[e] - alpha * a4[e]);
+        if (rg == 0) {
+            E *op = o + ((size_t)(a + t) * hv + h) * D + col;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                op[e] = (E)(scale * (alpha * b4[e] + qk * d4[e]));
+        }
+#pragma unroll
+        for (int i = 0; i < RPL; ++i)
+            s[i] = alpha * s[i] + kr[i] * d4;
+    }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+        *reinterpret_cast<f32x4 *>(state_out + sbase + (size_t)i * D) = s[i];
+}
+
+template <typename E, int D>
+static hipError_t launch_short_prefill_t(const PrefillArgs &p)
+{
+    const int64_t blocks = (int64_t)p.num_seqs * p.hv;
+    if (blocks > 0) {
+        hipStream_t st = static_cast<hipStream_t>(p.stream);
+        const ProfEvents ev = prof_events(PROF_SHORT);
+        hipExtLaunchKernelGGL((gdn_short_prefill_kernel<E, D>), dim3((unsigned)blocks),
+                              dim3(D / kDecodeCols * kWave), 0, st, ev.start, ev.stop, 0,
+                              static_cast<const E *>(p.q), static_cast<const E *>(p.k),
+                              static_cast<const E *>(p.v), p.g, p.beta, p.cu_seqlens, p.total_tokens,
+                              p.initial_state, p.final_state, static_cast<E *>(p.o), p.hqk, p.hv, p.scale);
+    }
+    return hipGetLastError();
+}
+
+bool short_prefill_supported(int32_t dk, int32_t dv)
+{
+    return dk == dv && (dk == 32 || dk == 64 || dk == 128);
+}
+
+hipError_t launch_short_prefill(const PrefillArgs &p)
+{
+    const bool bf = p.io_dtype == 1;
+    switch (p.dk) {
+    case 32: return bf ? launch_short_prefill_t<bf16, 32>(p) : launch_short_prefill_t<float, 32>(p);
+    case 64: return bf ? launch_short_prefill_t<bf16, 64>(p) : launch_short_prefill_t<float, 64>(p);
+    case 128: return bf ? launch_short_prefill_t<bf16, 128>(p) : launch_short_prefill_t<float, 128>(p);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Snapshot: dst[dst_rows[i]] = src[src_rows[i]] for whole per-sequence states.
 // Grid (num_rows, parts of 2048 16-byte vectors).  Out-of-range row indices
 // are skipped so that device index arrays can never send a copy out of

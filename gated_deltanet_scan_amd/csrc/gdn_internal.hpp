@@ -28,6 +28,7 @@ struct PrefillArgs {
                              // (the scans' longest-first order is then the batch order)
     int32_t long_ranks;      // > 0: the first long_ranks ranks (longest sequences) are scanned by
                              // the row-split kernel, the rest by the whole-head kernel
+    int32_t max_len;         // tokens of the longest sequence (host offsets), -1 if unknown
     // optional gated RMSNorm of the output rows (o then holds y): gate, weight and eps
     const void *norm_z;
     const float *norm_weight;
@@ -120,6 +121,14 @@ int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, 
 
 hipError_t launch_prefill(const PrefillArgs &p);
 hipError_t launch_decode(const DecodeArgs &p);
+// Batches whose sequences are all at most this many tokens long (known from host offsets) take
+// the token-recurrent prefill: one launch, no chunk matrices.  Measured against prep + chunk
+// scan at dk = dv = 128, 32 value heads, 1-32 sequences: 2-2.5x faster at 4 tokens, even at
+// 16, slower at 32 (its token steps are a chain of dependent vector products and reductions,
+// about 1 us each).
+constexpr int32_t kShortPrefillTokens = 8;
+bool short_prefill_supported(int32_t dk, int32_t dv);
+hipError_t launch_short_prefill(const PrefillArgs &p);
 hipError_t launch_snapshot(const SnapshotArgs &p);
 hipError_t launch_norm(const NormArgs &p);
 hipError_t launch_conv(const ConvArgs &p);

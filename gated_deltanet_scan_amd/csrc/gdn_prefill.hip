@@ -2884,6 +2884,28 @@ static void launch_scan_tform(const PrefillArgs &p, const SlotMap &map, const bf
 // Batches of at most this many sequences are scanned longest first.
 constexpr int32_t kMaxOrderedSeqs = 4096;
 
+// The gated RMSNorm of a prefill's output rows, if asked for: in place, after the scans.
+static hipError_t launch_prefill_norm(const PrefillArgs &p)
+{
+    if (p.norm_z && p.total_tokens > 0) {
+        NormArgs n{};
+        n.hv = p.hv;
+        n.dv = p.dv;
+        n.io_dtype = p.io_dtype;
+        n.o = p.o;
+        n.z = p.norm_z;
+        n.weight = p.norm_weight;
+        n.y = p.o;
+        n.tokens = p.total_tokens;
+        n.eps = p.norm_eps;
+        n.stream = p.stream;
+        const hipError_t e = launch_norm(n);
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipGetLastError();
+}
+
 template <typename E, int C, int DK>
 static hipError_t launch_prefill_t(const PrefillArgs &p)
 {
@@ -2896,25 +2918,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
     E *amat = tmat + (size_t)p.max_chunks * p.hv * (kAbsorbed ? DK : C) * C;
     float *dec = reinterpret_cast<float *>(amat + (size_t)p.max_chunks * p.hv * C * C);
     // The gated RMSNorm of the output rows, if asked for: in place, after the scans.
-    auto finish = [&]() -> hipError_t {
-        if (p.norm_z && p.total_tokens > 0) {
-            NormArgs n{};
-            n.hv = p.hv;
-            n.dv = p.dv;
-            n.io_dtype = p.io_dtype;
-            n.o = p.o;
-            n.z = p.norm_z;
-            n.weight = p.norm_weight;
-            n.y = p.o;
-            n.tokens = p.total_tokens;
-            n.eps = p.norm_eps;
-            n.stream = p.stream;
-            const hipError_t e = launch_norm(n);
-            if (e != hipSuccess)
-                return e;
-        }
-        return hipGetLastError();
-    };
+    auto finish = [&]() -> hipError_t { return launch_prefill_norm(p); };
 
     // Whole-head batches (many (sequence, head) pairs, no split by length) take the T form:
     // the prep writes T alone and the whole-head scan forms A and Y = T X itself.
@@ -3068,6 +3072,14 @@ hipError_t prefill_scratch(hipStream_t stream, void **ptr, size_t *bytes)
 
 hipError_t launch_prefill(const PrefillArgs &p)
 {
+    // Every sequence at most kShortPrefillTokens long (known from host offsets): one
+    // token-recurrent launch, no chunk matrices; then the norm, if asked for.
+    if (p.max_len >= 0 && p.max_len <= kShortPrefillTokens && short_prefill_supported(p.dk, p.dv)) {
+        const hipError_t e = launch_short_prefill(p);
+        if (e != hipSuccess)
+            return e;
+        return launch_prefill_norm(p);
+    }
     const bool bf = p.io_dtype == 1;
 #define GDN_PREFILL_CASE(E_, C_, D_)                 \
     if (p.chunk == C_ && p.dk == D_)                 \

@@ -21,6 +21,7 @@ enum ProfKernel : int32_t {
     PROF_SCAN_WIDE = 9,    // gdn_chunk_scan_bf16_kernel
     PROF_SCAN_PLAIN = 10,  // gdn_chunk_scan_kernel
     PROF_SCAN_TFORM = 11,  // gdn_chunk_scan_tform_kernel
+    PROF_SHORT = 12,       // gdn_short_prefill_kernel (token-recurrent prefill of short sequences)
 };
 
 // Start and stop events for one launch of `kernel`: both null while timing is

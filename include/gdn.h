@@ -121,6 +121,10 @@ size_t gdn_prefill_workspace_bytes_for(const gdn_shape *shape, const int32_t *cu
  *                  is validated and the call fails with GDN_ERR_INVALID_ARG
  *                  on a violation.  Without it, invalid device offsets give
  *                  unspecified results but never out-of-bounds accesses.
+ *                  When it shows every sequence at most 8 tokens long (and
+ *                  dk = dv), the call runs the token-by-token recurrence
+ *                  instead (the decode step's form, one launch, the workspace
+ *                  untouched): same results up to rounding.
  *   initial_state  [num_seqs, HV, dk, dv] fp32, or NULL for zeros
  *   final_state    [num_seqs, HV, dk, dv] fp32 out; MAY alias initial_state
  *                  (in-place prefix reuse), must not overlap anything else
@@ -352,7 +356,8 @@ gdn_status gdn_gated_rmsnorm(const gdn_shape *shape, const void *o, const void *
  * (sequence, head) pairs, bf16, chunk 64), 9 the whole-head scan (many pairs,
  * bf16, chunk 64, dk = 128, in a batch split by length), 10 the general scan (fp32 io
  * or chunk 16), 11 the whole-head scan of the T form (many pairs, bf16, chunk 64,
- * dk = 128).
+ * dk = 128); 12 the token-recurrent prefill of short sequences (every sequence at most
+ * 8 tokens, known from cu_seqlens_host).
  * The events are created on first use and kept until the process ends;
  * no device memory is allocated.
  */

@@ -126,10 +126,12 @@ def _slice_tokens(inp, lengths_take, offsets):
     return out
 
 
-def _verify_protocol(w, accepted, label):
+def _verify_protocol(w, accepted, label, host_offsets=False):
     """Packed prefill -> snapshot -> one 16-token verify block per sequence -> restore -> re-feed
     the accepted prefix.  Checks the prompt outputs, the verify outputs, the re-fed outputs and the
-    final states (per sequence and per value head)."""
+    final states (per sequence and per value head).  With host offsets, a re-feed of at most 8
+    tokens per sequence takes the token-recurrent prefill; the other calls, and every call with
+    device offsets, the chunked kernels."""
     V = w.verify_tokens
     n = len(w.lengths)
     # one draw holds prompt + verify tokens of every sequence; sequences are split below
@@ -144,21 +146,22 @@ def _verify_protocol(w, accepted, label):
     say(label, "prompt prefill", sum(w.lengths), "tokens")
     dev_p = to_dev(prompt)
     state = dev_p["initial_state"].clone()
+    cu_of = lambda part, dev: part["cu_seqlens"] if host_offsets else dev["cu_seqlens"]
     o_prompt, _ = gdn.prefill_chunked(dev_p["q"], dev_p["k"], dev_p["v"], dev_p["g"], dev_p["beta"],
-                                      dev_p["cu_seqlens"], state, final_state=state)
+                                      cu_of(prompt, dev_p), state, final_state=state)
     snap = torch.empty_like(state)
     say(label, "snapshot")
     gdn.state_snapshot(state, snap)
     say(label, "verify block")
     dev_v = to_dev(verify)
     o_verify, _ = gdn.prefill_chunked(dev_v["q"], dev_v["k"], dev_v["v"], dev_v["g"], dev_v["beta"],
-                                      dev_v["cu_seqlens"], state, final_state=state)
+                                      cu_of(verify, dev_v), state, final_state=state)
     say(label, "restore")
     gdn.state_snapshot(snap, state)
     say(label, "re-feed", accepted)
     dev_r = to_dev(refeed)
     o_refeed, _ = gdn.prefill_chunked(dev_r["q"], dev_r["k"], dev_r["v"], dev_r["g"], dev_r["beta"],
-                                      dev_r["cu_seqlens"], state, final_state=state)
+                                      cu_of(refeed, dev_r), state, final_state=state)
     torch.cuda.synchronize()
 
     # oracle: prompt + accepted tokens in one pass per sequence
@@ -190,13 +193,15 @@ def _verify_protocol(w, accepted, label):
             assert rel_err(orf[cu_r[i]:cu_r[i + 1]], ref_acc) <= tol_o, "%s seq %d re-fed outputs" % (label, i)
 
 
-def test_varlen_verify_rollback_refeed_workload():
+@pytest.mark.parametrize("host_offsets", [False, True])
+def test_varlen_verify_rollback_refeed_workload(host_offsets):
     w = S.workload("varlen_16")
     accepted = S.accept_counts(w.seed + 1, len(w.lengths), w.verify_tokens)
-    _verify_protocol(w, accepted, "varlen_16_protocol")
+    _verify_protocol(w, accepted, "varlen_16_protocol", host_offsets=host_offsets)
 
 
-def test_verify_protocol_accept_none_and_all():
+@pytest.mark.parametrize("host_offsets", [False, True])
+def test_verify_protocol_accept_none_and_all(host_offsets):
     w = S.Workload("small_protocol", [300, 64, 17], 2, 4, 128, 128, 64, torch.bfloat16, "uniform", 0.05, 330,
                    verify_tokens=16)
-    _verify_protocol(w, [0, 16, 7], "protocol_edges")
+    _verify_protocol(w, [0, 16, 7], "protocol_edges", host_offsets=host_offsets)

@@ -8,6 +8,9 @@ the 4096-sequence ordering limit, every supported head size and chunk length
 in both io dtypes, the strong-decay (-6.72) segment,
 a weak-decay long-memory stress (also at the full 32k shape), highly
 correlated keys, scale 0, in-place prefix reuse and run-to-run determinism.
+With host offsets, a batch whose sequences are all at most 8 tokens long takes the
+token-recurrent path instead (tests/test_gpu_short_prefill.py); the device-offset runs
+keep the chunked kernels covered at those lengths.
 """
 import numpy as np
 import pytest
@@ -57,10 +60,14 @@ def test_varlen_16_workload(host_offsets):
     _run(S.make_workload_inputs(w), w.chunk, w.io_dtype, "varlen_16", host_offsets=host_offsets)
 
 
+@pytest.mark.parametrize("host_offsets", [True, False])
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 127, 128, 129])
 @pytest.mark.parametrize("io,d,chunk", [(torch.float32, 32, 16), (torch.bfloat16, 128, 64)])
-def test_lengths_around_the_chunk(T, io, d, chunk):
-    _run(_case([T], 1, 2, d, io, seed=100 + T), chunk, io, "len%d_d%d_c%d" % (T, d, chunk))
+def test_lengths_around_the_chunk(T, io, d, chunk, host_offsets):
+    """With host offsets the length 1 takes the token-recurrent path; with device offsets every
+    length runs the chunked kernels."""
+    _run(_case([T], 1, 2, d, io, seed=100 + T), chunk, io, "len%d_d%d_c%d" % (T, d, chunk),
+         host_offsets=host_offsets)
 
 
 @pytest.mark.parametrize("host_offsets", [True, False])
