@@ -310,7 +310,9 @@ hipError_t launch_short_prefill(const PrefillArgs &p)
 // are skipped so that device index arrays can never send a copy out of
 // bounds.
 // ---------------------------------------------------------------------------
-constexpr int kSnapVecsPerThread = 8;
+// 16-byte vectors per thread, all loaded before any is stored: 16 (256 bytes in flight per
+// thread) copies the 32 MB of a 16-sequence, 32-head batch in 11.3 us; 8: 17.4 us; 32: 12.8 us.
+constexpr int kSnapVecsPerThread = 16;
 
 __global__ __launch_bounds__(kThreads) void gdn_snapshot_kernel(
     const float *__restrict__ src, const int32_t *__restrict__ src_rows, int32_t src_cap,
