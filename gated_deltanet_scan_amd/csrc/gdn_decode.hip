@@ -48,10 +48,12 @@ __global__ __launch_bounds__(kThreads) void gdn_decode_kernel(
     const int col = slice * kDecodeCols + 4 * cg;
     float *S = state + (size_t)pair * D * D + (size_t)(rg * RPL) * D + col;
 
+    // the state: ordinary loads, non-temporal stores (measured at decode_64: 44.7 us per launch;
+    // 47.0 with non-temporal loads as well, 52.4 with neither)
     f32x4 s[RPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i)
-        s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)i * D));
+        s[i] = *reinterpret_cast<const f32x4 *>(S + (size_t)i * D);
 
     // this lane's rows of k and q
     float kr[RPL], qr[RPL];
