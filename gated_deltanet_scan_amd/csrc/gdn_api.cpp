@@ -71,8 +71,8 @@ bool prefill_supported(int32_t dk, int32_t dv, int32_t chunk, int32_t io_dtype)
 {
     if (dk != dv)
         return false;
-    if (io_dtype == GDN_DTYPE_F32 && dk > 64)
-        return false;
+    if (io_dtype == GDN_DTYPE_F32 && dk == 128)   // the token-recurrent kernel (no chunked one)
+        return chunk == 16 || chunk == 64;
     if (chunk == 64)
         return dk == 32 || dk == 64 || dk == 128;
     if (chunk == 16)
@@ -238,7 +238,7 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
     if (!gdn::prefill_supported(s.dk, s.dv, s.chunk, s.io_dtype))
         return fail(GDN_ERR_UNSUPPORTED,
                     "no prefill kernel for dk=%d dv=%d chunk=%d io_dtype=%d (dk == dv in {32,64,128}, "
-                    "chunk 64, or chunk 16 with dk <= 64; fp32 io needs dk <= 64)",
+                    "chunk 64, or chunk 16 with dk <= 64 (fp32 io: also dk = 128))",
                     s.dk, s.dv, s.chunk, s.io_dtype);
     if (num_seqs < 0 || total_tokens < 0)
         return fail(GDN_ERR_INVALID_ARG, "negative num_seqs (%d) or total_tokens (%lld)", num_seqs,

@@ -155,10 +155,11 @@ hipError_t launch_decode(const DecodeArgs &p)
 //
 // One workgroup per (sequence, value head), one wave per 32-column slice as in the decode
 // kernel.  The sequence's k and q rows (of its query/key head), its v rows, g and beta are
-// staged in LDS first (16-byte loads spread over the workgroup); the token loop then reads
-// only LDS and registers.  Sequence bounds are clamped to [0, total_tokens] and the staged
-// length to kShortPrefillTokens, so inconsistent offsets cannot send an access out of
-// bounds.
+// staged in LDS kShortPrefillTokens tokens at a time (16-byte loads spread over the
+// workgroup); the token loop then reads only LDS and registers.  Sequences longer than one
+// block (fp32 io at dk = 128, which has no chunked kernel, takes this path at any length)
+// run block after block with the state kept in registers.  Sequence bounds are clamped to
+// [0, total_tokens], so inconsistent offsets cannot send an access out of bounds.
 // ---------------------------------------------------------------------------
 template <typename E, int D>
 __global__ __launch_bounds__(D / kDecodeCols * kWave) void gdn_short_prefill_kernel(
@@ -185,10 +186,22 @@ __global__ __launch_bounds__(D / kDecodeCols * kWave) void gdn_short_prefill_ker
     const int n = pair / hv, h = pair - n * hv;
     const int hq = h / (hv / hqk);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int64_t a = min<int64_t>(max<int64_t>(cu[n], 0), total_tokens);
-    const int64_t b = min<int64_t>(max<int64_t>(cu[n + 1], a), total_tokens);
-    const int len = (int)min<int64_t>(b - a, L);
+    const int64_t a0 = min<int64_t>(max<int64_t>(cu[n], 0), total_tokens);
+    const int64_t b = min<int64_t>(max<int64_t>(cu[n + 1], a0), total_tokens);
 
+    // lane (rg, cg): columns col .. col + 3 of rows rg * RPL .. rg * RPL + RPL - 1
+    const int rg = lane / 8, cg = lane % 8;
+    const int col = wave * kDecodeCols + 4 * cg;
+    const size_t sbase = (size_t)pair * D * D + (size_t)(rg * RPL) * D + col;
+    f32x4 s[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i)
+        s[i] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + sbase + (size_t)i * D) : zero4();
+
+    for (int64_t a = a0; a < b; a += L) {
+    const int len = (int)min<int64_t>(b - a, L);
+    if (a != a0)
+        __syncthreads();   // every wave is done with the previous block's staged tokens
     for (int i = tid; i < len * VPR; i += NT) {
         const int t = i / VPR, c = (i - t * VPR) * VN;
         const size_t tok = (size_t)(a + t);
@@ -200,15 +213,6 @@ __global__ __launch_bounds__(D / kDecodeCols * kWave) void gdn_short_prefill_ker
         gs[t] = g[(size_t)(a + t) * hv + h];
         bs[t] = beta[(size_t)(a + t) * hv + h];
     }
-
-    // lane (rg, cg): columns col .. col + 3 of rows rg * RPL .. rg * RPL + RPL - 1
-    const int rg = lane / 8, cg = lane % 8;
-    const int col = wave * kDecodeCols + 4 * cg;
-    const size_t sbase = (size_t)pair * D * D + (size_t)(rg * RPL) * D + col;
-    f32x4 s[RPL];
-#pragma unroll
-    for (int i = 0; i < RPL; ++i)
-        s[i] = state_in ? *reinterpret_cast<const f32x4 *>(state_in + sbase + (size_t)i * D) : zero4();
     __syncthreads();
 
     for (int t = 0; t < len; ++t) {
@@ -268,6 +272,7 @@ __global__ __launch_bounds__(D / kDecodeCols * kWave) void gdn_short_prefill_ker
 #pragma unroll
         for (int i = 0; i < RPL; ++i)
             s[i] = alpha * s[i] + kr[i] * d4;
+    }
     }
 #pragma unroll
     for (int i = 0; i < RPL; ++i)

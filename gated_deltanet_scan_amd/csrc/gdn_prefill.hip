@@ -3072,9 +3072,12 @@ hipError_t prefill_scratch(hipStream_t stream, void **ptr, size_t *bytes)
 
 hipError_t launch_prefill(const PrefillArgs &p)
 {
-    // Every sequence at most kShortPrefillTokens long (known from host offsets): one
-    // token-recurrent launch, no chunk matrices; then the norm, if asked for.
-    if (p.max_len >= 0 && p.max_len <= kShortPrefillTokens && short_prefill_supported(p.dk, p.dv)) {
+    // Every sequence at most kShortPrefillTokens long (known from host offsets), or fp32 io at
+    // dk = 128 (no chunked kernel): one token-recurrent launch, no chunk matrices; then the
+    // norm, if asked for.
+    const bool short_batch = p.max_len >= 0 && p.max_len <= kShortPrefillTokens;
+    const bool fp32_wide = p.io_dtype == 0 && p.dk == 128;
+    if ((short_batch || fp32_wide) && short_prefill_supported(p.dk, p.dv)) {
         const hipError_t e = launch_short_prefill(p);
         if (e != hipSuccess)
             return e;

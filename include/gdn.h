@@ -38,8 +38,9 @@
  *           every buffer untouched.  gdn_last_error() gives a message for
  *           the calling thread's last failure.
  * Sizes.    Supported head dimensions: dk == dv in {32, 64, 128}; chunk
- *           length in {16, 64} (chunk 16 only with dk <= 64).  Anything else
- *           returns GDN_ERR_UNSUPPORTED.
+ *           length in {16, 64} (chunk 16 only with dk <= 64, except fp32 io at
+ *           dk = 128, whose prefill runs the token-by-token recurrence at either
+ *           chunk length).  Anything else returns GDN_ERR_UNSUPPORTED.
  */
 #ifndef GDN_H
 #define GDN_H
@@ -124,7 +125,9 @@ size_t gdn_prefill_workspace_bytes_for(const gdn_shape *shape, const int32_t *cu
  *                  When it shows every sequence at most 8 tokens long (and
  *                  dk = dv), the call runs the token-by-token recurrence
  *                  instead (the decode step's form, one launch, the workspace
- *                  untouched): same results up to rounding.
+ *                  untouched): same results up to rounding.  fp32 io at
+ *                  dk = 128 always runs that recurrence (there is no chunked
+ *                  kernel for it; its time grows with the longest sequence).
  *   initial_state  [num_seqs, HV, dk, dv] fp32, or NULL for zeros
  *   final_state    [num_seqs, HV, dk, dv] fp32 out; MAY alias initial_state
  *                  (in-place prefix reuse), must not overlap anything else

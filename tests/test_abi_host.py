@@ -126,7 +126,10 @@ def test_prefill_rejects_bad_shapes(lib):
     assert prefill(lib, shape(d=96)) == binding.GDN_ERR_UNSUPPORTED
     assert prefill(lib, shape(chunk=32)) == binding.GDN_ERR_UNSUPPORTED
     assert prefill(lib, shape(d=128, chunk=16)) == binding.GDN_ERR_UNSUPPORTED
-    assert prefill(lib, shape(d=128, io=F32)) == binding.GDN_ERR_UNSUPPORTED
+    # fp32 io at dk = 128 is served (token-recurrent kernel): past the shape check, a misaligned
+    # q is the first error (argument checks come before any device work)
+    assert prefill(lib, shape(d=128, io=F32), q=ctypes.c_void_p(fake(1).value + 4)) == binding.GDN_ERR_INVALID_ARG
+    assert b"aligned" in lib.gdn_last_error()
     assert prefill(lib, shape(io=7)) == binding.GDN_ERR_INVALID_ARG
     assert prefill(lib, shape(scale=float("nan"))) == binding.GDN_ERR_INVALID_ARG
 

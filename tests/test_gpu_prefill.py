@@ -74,8 +74,8 @@ def test_lengths_around_the_chunk(T, io, d, chunk, host_offsets):
 @pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("d,chunk", [(32, 16), (64, 16), (32, 64), (64, 64), (128, 64)])
 def test_every_kernel_instance(io, d, chunk, host_offsets):
-    if io == torch.float32 and d > 64:
-        pytest.skip("fp32 io is built for dk <= 64")
+    """Every (io dtype, head size, chunk) instance; fp32 io at dk = 128 runs the token-recurrent
+    kernel at any length."""
     lengths = [3 * chunk + 5, chunk, 1, 2 * chunk - 1]
     _run(_case(lengths, 2, 4, d, io, seed=7 * d + chunk), chunk, io, "inst_d%d_c%d" % (d, chunk),
          host_offsets=host_offsets)

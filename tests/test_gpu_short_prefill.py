@@ -3,7 +3,7 @@ are all at most 8 tokens long, with host offsets) against the fp64 oracle.
 
 The library takes this path when cu_seqlens_host shows every sequence at most 8 tokens
 long: one launch (profile identifier 12) and no prep or chunk scan.  Cases: every head size
-in both io dtypes (fp32 at dk <= 64, as the chunked path), lengths 0 .. 8 with a
+in both io dtypes, lengths 0 .. 8 with a
 zero-length sequence, the limit itself (8 tokens: recurrent; 9: chunked), no initial state,
 in-place prefix reuse, a short verify block at the Qwen3.5-9B shape (16 sequences of 8
 tokens, 16 QK / 32 V heads, dk = dv = 128, bf16) and the gated RMSNorm after it.  Bars as
@@ -54,8 +54,6 @@ def _run(inp, io, label, chunk=64, initial_state="from_inputs", inplace=False):
 @pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("d", [32, 64, 128])
 def test_short_batch_every_head_size(io, d):
-    if io == torch.float32 and d > 64:
-        pytest.skip("fp32 io prefill is built for dk <= 64")
     inp = S.make_inputs([5, 0, 8, 1, 7, 3], 2, 4, d, d, io, seed=900 + d, s0_std=0.05)
     counts = _run(inp, io, "short_d%d" % d)
     assert counts[PROF_SHORT] == 1 and counts[PROF_PREP] == 0 and counts[PROF_SCAN] == 0, counts
@@ -117,3 +115,20 @@ def test_gated_rmsnorm_after_the_recurrent_path():
     tol_o, tol_s = TOL[torch.bfloat16]
     assert short_launches == 1 and norm_launches == 1
     assert ey <= tol_o and es <= tol_s, (ey, es)
+
+
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_fp32_at_dk_128_any_length(chunk):
+    """fp32 io at dk = dv = 128 has no chunked kernel: every call runs the token-recurrent
+    kernel, block of 8 tokens after block, whatever the lengths (here up to 300 tokens, with
+    and without host offsets)."""
+    inp = S.make_inputs([300, 1, 0, 17, 64], 2, 4, 128, 128, torch.float32, seed=971 + chunk, s0_std=0.05)
+    counts = _run(inp, torch.float32, "fp32_d128_c%d" % chunk, chunk=chunk)
+    assert counts[PROF_SHORT] == 1 and counts[PROF_PREP] == 0 and counts[PROF_SCAN] == 0, counts
+    d = to_dev(inp)
+    say("fp32_d128 device offsets")
+    o, St = gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["initial_state"],
+                                chunk=chunk)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(inp)
+    check_prefill(o, St, o_ref, S_ref, inp["cu_seqlens"], torch.float32, "fp32_d128_device_offsets")
