@@ -326,9 +326,11 @@ struct AbsorbedForm {
 //   kPrepTForm     T alone, as hi/lo bf16 pairs (bf16 io, chunk 64, dk 128; the T-form
 //                  whole-head scan forms A from its staged q and k and takes Y = T X with
 //                  the hi/lo pairs, so the cancelling sums of T's columns stay fp32-accurate)
-// and the decay record.  T-form record: [G | exp(G_last - G) | beta | beta exp(G)] (the scan
-// masks exp(G_t - G_j) in log space itself); the others: [exp(G) | ... ].
+// and the decay record.  T-form record: [G log2(e) | exp(G_last - G) | beta | beta exp(G)]
+// (the scan forms its decays as powers of two and masks exp(G_t - G_j) in log space
+// itself); the others: [exp(G) | ... ].
 enum PrepForm { kPrepDirect = 0, kPrepAbsorbed = 1, kPrepTForm = 2 };
+constexpr float kLog2E = 1.44269504088896340736f;   // log2(e)
 // T in the T form: 6 units of 16 rows x 32 columns per bf16 matrix (hi, then lo), the
 // units of T's row tiles rt (rows Chain<Mma<bf16>>::row(rt, .)) and column halves st with
 // st <= rt / 2 (the other two are zero: T is lower triangular); unit u(rt, st) holds at
@@ -553,7 +555,7 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
             const float Glast = __shfl(G, C - 1, kWave);
             float *rec = dec + (slot * hv + h) * 4 * C;
             const float eg = expf(G);
-            rec[lane] = TFORM ? G : eg;
+            rec[lane] = TFORM ? G * kLog2E : eg;
             rec[C + lane] = expf(Glast - G);
             rec[2 * C + lane] = wv == 0 ? bv[0] : bv[HB - 1];
             rec[3 * C + lane] = (wv == 0 ? bv[0] : bv[HB - 1]) * eg;
@@ -2558,6 +2560,8 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
     // so an exec-masked branch would let every wave run every tile's product)
     const int wu = __builtin_amdgcn_readfirstlane(w);
 
+    // the output scale as a power of two, added to the record's G log2(e)
+    const float log2_scale = __log2f(scale);
     // the previous chunk's output rows, from obuf to o: rows 8 w .. 8 w + 7 of this wave, lane l
     // moving 16 bytes of row 8 w + 4 u + l / 16 (u = 0, 1); rows past the chunk's end skipped
     const uint32_t olane = (uint32_t)(lane >> 4) * (uint32_t)(hv * dv) + (uint32_t)(8 * (lane & 15));
@@ -2647,12 +2651,12 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
                 int tr, tc;
                 a_tile(idx, tr, tc);
                 const int t = 16 * tr + r16, j0 = CH::row(tc, g4);
-                const float gt = rec1(0, t);
+                const float gt = rec1(0, t) + log2_scale;
                 const f32x4 gj = rec4(0, j0);
                 f32x4 av;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    av[i] = (j0 + i <= t) ? scale * __expf(gt - gj[i]) * aacc[I][i] : 0.f;
+                    av[i] = (j0 + i <= t) ? __builtin_amdgcn_exp2f(gt - gj[i]) * aacc[I][i] : 0.f;
                 const u32x2 p0 = split_bf16x2(av[0], av[1]), p1 = split_bf16x2(av[2], av[3]);
                 // keys j0 .. j0 + 3 = 32 (tc / 2) + 8 g + 4 (tc % 2) + {0..3}: unit (tr, tc / 2),
                 // position r16 + 16 g, half tc % 2
@@ -2726,7 +2730,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
 
         stage_hook(std::integral_constant<int, 1>{});
         // S <- exp(G_last) S + K^T (lambda Y)_hi + K^T (lambda Y)_lo
-        const float gl = __expf(rec1(0, C - 1));
+        const float gl = __builtin_amdgcn_exp2f(rec1(0, C - 1));
 #pragma unroll
         for (int sr = 0; sr < SR; ++sr) {
             sacc[sr] = sacc[sr] * gl;
@@ -2750,7 +2754,7 @@ __global__ __launch_bounds__(NW * kWave) void gdn_chunk_scan_tform_kernel(
         // and the row tiles' products interleaved.
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-            qacc[rt] *= scale * __expf(rec1(0, 16 * rt + r16));
+            qacc[rt] *= __builtin_amdgcn_exp2f(rec1(0, 16 * rt + r16) + log2_scale);
         static_for<NSC>([&](auto sc) __attribute__((always_inline)) {
             constexpr int ST = decltype(sc)::value, R0 = ST == 0 ? 0 : 2;
             bf16x8 ah[RT], al[RT];
