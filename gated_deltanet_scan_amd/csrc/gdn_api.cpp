@@ -104,8 +104,9 @@ PrefillWorkspace prefill_workspace(int32_t hv, int32_t dk, int32_t chunk, int32_
     if (max_chunks > INT32_MAX)
         return w;
     w.max_chunks = (int32_t)max_chunks;
-    // chunk table (num_seqs + 1 entries), then the scan order of the sequences (num_seqs)
-    w.table_bytes = ((2 * (size_t)num_seqs + 1) * sizeof(int32_t) + 255) / 256 * 256;
+    // chunk table (num_seqs + 1 entries), the scan order of the sequences (num_seqs), then
+    // (8-byte aligned) the first token and length of every chunk slot
+    w.table_bytes = (prefill_slot_info_offset(num_seqs) + (size_t)max_chunks * 2 * sizeof(int32_t) + 255) / 256 * 256;
     w.total_bytes = w.table_bytes + (size_t)max_chunks * prefill_slot_bytes(hv, dk, chunk, io_dtype);
     return w;
 }

@@ -8,6 +8,13 @@
 
 namespace gdn {
 
+// Byte offset in the workspace of the per-slot (first token, length) pairs, after the chunk
+// table (num_seqs + 1 entries) and the scan order (num_seqs entries).
+inline size_t prefill_slot_info_offset(int32_t num_seqs)
+{
+    return ((2 * (size_t)num_seqs + 1) * sizeof(int32_t) + 7) / 8 * 8;
+}
+
 struct PrefillArgs {
     int32_t hqk, hv, dk, dv, chunk, io_dtype;
     float scale;
@@ -21,7 +28,7 @@ struct PrefillArgs {
     void *o;
     void *workspace;
     int32_t max_chunks;    // chunk slots the workspace holds (upper bound on the chunks of the batch)
-    size_t table_bytes;    // bytes of the chunk table and sequence order at the start of the workspace
+    size_t table_bytes;    // bytes of the chunk table, sequence order and slot entries at the start of the workspace
     int32_t seg_len;       // > 0: segment mode, local chunks per sequence per segment (0: global mode)
     int32_t max_seq_chunks;  // segment mode: chunks of the longest sequence
     bool ordered;            // host offsets show chunk counts that never increase along the batch

@@ -39,6 +39,7 @@
 #include "gdn_internal.hpp"
 #include "gdn_profile.hpp"
 
+#include <algorithm>
 #include <mutex>
 
 namespace gdn {
@@ -79,25 +80,37 @@ __global__ __launch_bounds__(kThreads) void gdn_seq_order_kernel(const int32_t *
 // clamped to [0, total_tokens] so that invalid input cannot send later
 // kernels out of bounds.  Workgroup 0 builds the table; with `order` given, the
 // grid has one thread per sequence and also ranks them (gdn_seq_order_kernel's
-// work in the same launch).
+// work in the same launch).  With `slot_info` given, workgroup i also writes
+// the entries of slots [i K, (i + 1) K) (K = kSlotsPerTableBlock, slots below
+// max_chunks): the chunk's first token and its length, length 0 past the
+// batch's chunks.  The prep then finds its chunk with one load instead of a
+// search of the table.
 // ---------------------------------------------------------------------------
+constexpr int32_t kSlotsPerTableBlock = 2048;
+
 __global__ __launch_bounds__(kThreads) void gdn_chunk_table_kernel(
     const int32_t *__restrict__ cu, int32_t num_seqs, int64_t total_tokens, int32_t chunk,
-    int32_t max_chunks, int32_t *__restrict__ chunk_start, int32_t *__restrict__ order)
+    int32_t max_chunks, int32_t *__restrict__ chunk_start, int32_t *__restrict__ order,
+    int2 *__restrict__ slot_info)
 {
     if (order)
         rank_sequence(cu, num_seqs, total_tokens, order, blockIdx.x * kThreads + threadIdx.x);
-    if (blockIdx.x != 0)
+    const int64_t lo = (int64_t)blockIdx.x * kSlotsPerTableBlock;
+    const int64_t hi = min<int64_t>(lo + kSlotsPerTableBlock, max_chunks);
+    const bool info = slot_info && lo < hi;
+    if (blockIdx.x != 0 && !info)
         return;
     __shared__ int64_t wave_tot[kWaves];
+    // this block of sequences: first slot (kThreads + 1 entries), first token, end token
+    __shared__ int64_t s_first[kThreads + 1], s_a[kThreads], s_b[kThreads];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     int64_t carry = 0;
     for (int32_t base = 0; base < num_seqs; base += kThreads) {
         const int32_t n = base + tid;
-        int64_t cnt = 0;
+        int64_t cnt = 0, a = 0, b = 0;
         if (n < num_seqs) {
-            const int64_t a = min<int64_t>(max<int64_t>(cu[n], 0), total_tokens);
-            const int64_t b = min<int64_t>(max<int64_t>(cu[n + 1], a), total_tokens);
+            a = min<int64_t>(max<int64_t>(cu[n], 0), total_tokens);
+            b = min<int64_t>(max<int64_t>(cu[n + 1], a), total_tokens);
             cnt = (b - a + chunk - 1) / chunk;
         }
         int64_t incl = cnt;
@@ -113,16 +126,47 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_table_kernel(
         int64_t before = carry;
         for (int w = 0; w < wave; ++w)
             before += wave_tot[w];
-        if (n < num_seqs)
-            chunk_start[n] = (int32_t)min<int64_t>(before + incl - cnt, max_chunks);
+        const int64_t first = before + incl - cnt;
+        if (n < num_seqs && blockIdx.x == 0)
+            chunk_start[n] = (int32_t)min<int64_t>(first, max_chunks);
         int64_t block = 0;
         for (int w = 0; w < kWaves; ++w)
             block += wave_tot[w];
+        if (info) {
+            // the slots of this block's sequences that fall among this workgroup's: each
+            // thread takes slots in turn and finds the owning sequence in LDS (the last one
+            // whose first slot is at most the slot: empty sequences own none)
+            const int nb = min(kThreads, num_seqs - base);
+            if (tid < nb) {
+                s_first[tid] = first;
+                s_a[tid] = a;
+                s_b[tid] = b;
+            }
+            if (tid == 0)
+                s_first[nb] = carry + block;
+            __syncthreads();
+            const int64_t e_end = min<int64_t>(hi, carry + block);
+            for (int64_t e = max<int64_t>(lo, carry) + tid; e < e_end; e += kThreads) {
+                int m0 = 0, m1 = nb;
+                while (m1 - m0 > 1) {
+                    const int mid = (m0 + m1) >> 1;
+                    if (s_first[mid] <= e)
+                        m0 = mid;
+                    else
+                        m1 = mid;
+                }
+                const int64_t t0 = s_a[m0] + (e - s_first[m0]) * chunk;
+                slot_info[e] = make_int2((int)t0, (int)min<int64_t>(chunk, s_b[m0] - t0));
+            }
+        }
         carry += block;
         __syncthreads();
     }
-    if (tid == 0)
+    if (blockIdx.x == 0 && tid == 0)
         chunk_start[num_seqs] = (int32_t)min<int64_t>(carry, max_chunks);
+    if (info)
+        for (int64_t e = max<int64_t>(carry, lo) + tid; e < hi; e += kThreads)
+            slot_info[e] = make_int2(0, 0);
 }
 
 // Sequence that owns chunk entry e: chunk_start[n] <= e < chunk_start[n+1].
@@ -153,6 +197,7 @@ struct SlotMap {
     const int32_t *seq_order;    // scan kernels: the sequence of rank r is seq_order[r]; NULL: r
     int32_t rank0;               // scan kernels: first rank of this launch (its ranks: rank0 + i)
     int32_t ranks;               // scan launches: number of ranks (sequences) this launch covers
+    const int2 *slot_info;       // global mode, prep: per slot, its chunk's first token and length
 };
 
 // Sequence of the scan work item with rank index i of its launch.
@@ -460,26 +505,39 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
         hfirst = hq * group;
         nheads = group;
     }
-    int n, c;
+    int64_t t0;
+    int len;
     size_t slot;
-    if (map.chunk_start) {
-        const int32_t e = sidx;
-        if (e >= map.chunk_start[num_seqs])
+    if (map.slot_info) {
+        // the table launch's entry for this slot (length 0: past the batch), read as one
+        // 64-bit load so that the first token is not fetched only after the length test
+        const uint64_t si = *reinterpret_cast<const uint64_t *>(map.slot_info + sidx);
+        len = (int)(uint32_t)(si >> 32);
+        if (len <= 0)
             return;
-        n = find_sequence(map.chunk_start, num_seqs, e);
-        c = e - map.chunk_start[n];
-        slot = e;
-    } else {
-        n = sidx / map.seg_len;
-        c = map.seg_first + (int)(sidx - n * map.seg_len);
-        if (n >= num_seqs || c >= seq_chunks(map, cu, n, total_tokens, C))
-            return;
+        t0 = (int)(uint32_t)si;
         slot = sidx;
+    } else {
+        int n, c;
+        if (map.chunk_start) {
+            const int32_t e = sidx;
+            if (e >= map.chunk_start[num_seqs])
+                return;
+            n = find_sequence(map.chunk_start, num_seqs, e);
+            c = e - map.chunk_start[n];
+            slot = e;
+        } else {
+            n = sidx / map.seg_len;
+            c = map.seg_first + (int)(sidx - n * map.seg_len);
+            if (n >= num_seqs || c >= seq_chunks(map, cu, n, total_tokens, C))
+                return;
+            slot = sidx;
+        }
+        int64_t a, b;
+        seq_range(cu, n, total_tokens, a, b);
+        t0 = a + (int64_t)c * C;
+        len = (int)min<int64_t>(C, b - t0);   // >= 1
     }
-    int64_t a, b;
-    seq_range(cu, n, total_tokens, a, b);
-    const int64_t t0 = a + (int64_t)c * C;
-    const int len = (int)min<int64_t>(C, b - t0);   // >= 1
 
     const int wv = __builtin_amdgcn_readfirstlane(wave);
     // q and k rows of the chunk into LDS.  Job idx of a tile moves 1 KB: lane i writes the 16
@@ -3015,13 +3073,16 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
         return finish();
     }
 
+    int2 *slot_info = reinterpret_cast<int2 *>(static_cast<char *>(p.workspace) + prefill_slot_info_offset(p.num_seqs));
     {
         const ProfEvents ev = prof_events(PROF_CHUNK_TABLE);
-        hipExtLaunchKernelGGL(gdn_chunk_table_kernel, dim3(order ? rank_blocks : 1u), dim3(kThreads), 0, st, ev.start,
-                              ev.stop, 0, p.cu_seqlens, p.num_seqs, p.total_tokens, (int32_t)C, p.max_chunks,
-                              chunk_start, order);
+        const unsigned info_blocks = (unsigned)((p.max_chunks + kSlotsPerTableBlock - 1) / kSlotsPerTableBlock);
+        const unsigned blocks = std::max(std::max(order ? rank_blocks : 1u, info_blocks), 1u);
+        hipExtLaunchKernelGGL(gdn_chunk_table_kernel, dim3(blocks), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
+                              p.cu_seqlens, p.num_seqs, p.total_tokens, (int32_t)C, p.max_chunks, chunk_start, order,
+                              slot_info);
     }
-    const SlotMap map{chunk_start, 0, INT32_MAX, order, 0, p.num_seqs};
+    const SlotMap map{chunk_start, 0, INT32_MAX, order, 0, p.num_seqs, slot_info};
     if (p.max_chunks > 0)
         prep(map, p.max_chunks);
     scan(map, p.initial_state, p.final_state);

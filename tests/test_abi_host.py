@@ -60,18 +60,25 @@ def test_status_strings_and_version(lib):
     assert lib.gdn_version() >= 100
 
 
+def table_bytes(num_seqs, max_chunks):
+    """The workspace's table region: chunk table (N + 1 int32), scan order (N int32), then,
+    8-byte aligned, a (first token, length) int32 pair per chunk slot; 256-byte aligned."""
+    head = -(-(2 * num_seqs + 1) * 4 // 8) * 8
+    return -(-(head + 8 * max_chunks) // 256) * 256
+
+
 def test_workspace_size(lib):
     sh = shape()
     T, N = 1000, 3
     max_chunks = -(-T // 64) + N
     # bf16 at chunk 64 (absorbed form): per chunk slot and value head, W (dk x C) and M (C x C)
     # in bf16 and the decay record (4 C floats)
-    expect = 256 + max_chunks * 32 * (128 * 64 + 64 * 64) * 2 + max_chunks * 32 * 4 * 64 * 4
+    expect = table_bytes(N, max_chunks) + max_chunks * 32 * (128 * 64 + 64 * 64) * 2 + max_chunks * 32 * 4 * 64 * 4
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), T, N) == expect
     # fp32 io (direct form): T and A (C x C each)
     sh32 = gdn.make_shape(2, 4, 32, 32, 16, 0, 1.0)
     mc = -(-T // 16) + N
-    expect32 = 256 + mc * 4 * 2 * 16 * 16 * 4 + mc * 4 * 4 * 16 * 4
+    expect32 = table_bytes(N, mc) + mc * 4 * 2 * 16 * 16 * 4 + mc * 4 * 4 * 16 * 4
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(sh32), T, N) == expect32
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(shape(d=96)), T, N) == 0     # unsupported
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(shape(hqk=3)), T, N) == 0    # 32 % 3 != 0
@@ -84,8 +91,8 @@ def test_workspace_size_for_host_lengths(lib):
     slot = 32 * ((128 + 64) * 64 * 2 + 4 * 64 * 4)          # 819,200 bytes
     cu = np.array([0, 32768], dtype=np.int32)                # 512 chunks: four segments of 128
     got = lib.gdn_prefill_workspace_bytes_for(ctypes.byref(sh), cu.ctypes.data_as(ctypes.c_void_p), 1)
-    assert got == 256 + 128 * slot
-    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), 32768, 1) == 256 + 513 * slot
+    assert got == table_bytes(1, 513) + 128 * slot
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), 32768, 1) == table_bytes(1, 513) + 513 * slot
     assert gdn.workspace_bytes_for(sh, cu) == got
     # 16 sequences of up to 8192 tokens: single launch over the chunk table, every slot
     from gated_deltanet_scan_amd import synthetic
@@ -94,7 +101,7 @@ def test_workspace_size_for_host_lengths(lib):
     assert gdn.workspace_bytes_for(sh, cu16) == lib.gdn_prefill_workspace_bytes(ctypes.byref(sh), int(cu16[-1]), 16)
     # a short batch: one segment as long as its longest sequence
     cu3 = np.array([0, 333, 666, 1000], dtype=np.int32)
-    assert gdn.workspace_bytes_for(sh, cu3) == 256 + 3 * 6 * slot
+    assert gdn.workspace_bytes_for(sh, cu3) == table_bytes(3, -(-1000 // 64) + 3) + 3 * 6 * slot
     # invalid offsets or shapes
     for bad in ([5, 100], [0, 100, 50]):
         arr = np.array(bad, dtype=np.int32)
