@@ -18,15 +18,20 @@
 // state is carried from chunk to chunk in order, the work inside a chunk is
 // batched products: Candle pull-request page, section Chunked GatedDeltaNet
 // Scan).  Kernels:
-//   gdn_chunk_table_kernel  chunk offsets of every sequence (integer scan)
-//   gdn_prep_kernel         per (chunk, query/key head): K K^T and Q K^T on
-//                           the matrix cores; per value head of the group:
-//                           G, log-space-masked exp(G_t - G_j), N, the unit
-//                           lower-triangular T = (I + N)^-1, A = decayed Q K^T
-//                           times the output scale
-//   gdn_chunk_scan_kernel   per (sequence, value head, dv-slice): for each
-//                           chunk, [Q;K] S, X = diag(beta)(V - diag(exp G) K S),
-//                           D = T X, O = diag(exp G) Q S + A D, S update.
+//   gdn_chunk_table_kernel  chunk offsets of every sequence (integer scan), the
+//                           longest-first order, each slot's first token and length
+//   gdn_seq_order_kernel    the longest-first order alone (segment mode)
+//   gdn_prep_kernel         per chunk: K K^T (and Q K^T) on the matrix cores; per
+//                           value head: G, log-space-masked exp(G_t - G_j), N, the
+//                           unit lower-triangular T = (I + N)^-1, then one of the
+//                           forms of PrepForm (T and A; W and M; T alone as hi/lo)
+//   gdn_chunk_scan_kernel   direct form (fp32 io, chunk 16): per (sequence, value
+//                           head, dv-slice), for each chunk, [Q;K] S,
+//                           X = diag(beta)(V - diag(exp G) K S), D = T X,
+//                           O = diag(exp G) Q S + A D, S update
+//   gdn_chunk_scan_rows_kernel   absorbed form, 16-column slices (few pairs)
+//   gdn_chunk_scan_bf16_kernel   absorbed form, whole heads (split batches)
+//   gdn_chunk_scan_tform_kernel  T form, whole heads (many pairs)
 //
 // Where the chunks' T and A live.  Global mode: one slot per chunk of the
 // batch, slot = chunk_start[n] + c.  Segment mode (the host knows the
@@ -2972,7 +2977,8 @@ template <typename E, int C, int DK>
 static hipError_t launch_prefill_t(const PrefillArgs &p)
 {
     hipStream_t st = static_cast<hipStream_t>(p.stream);
-    // workspace: [chunk table | T (or W) matrices | A (or M) matrices | decay records]
+    // workspace: [chunk table, scan order, slot entries | T (or W) matrices | A (or M) matrices |
+    // decay records]
     constexpr bool kAbsorbed = AbsorbedForm<E, C>::value;
     static_assert(kAbsorbed == (std::is_same<E, bf16>::value && C == 64), "matches prefill_absorbed()");
     int32_t *chunk_start = reinterpret_cast<int32_t *>(p.workspace);
