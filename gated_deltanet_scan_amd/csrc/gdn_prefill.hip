@@ -174,20 +174,6 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_table_kernel(
             slot_info[e] = make_int2(0, 0);
 }
 
-// Sequence that owns chunk entry e: chunk_start[n] <= e < chunk_start[n+1].
-__device__ inline int find_sequence(const int32_t *chunk_start, int32_t num_seqs, int32_t e)
-{
-    int lo = 0, hi = num_seqs;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (chunk_start[mid] <= e)
-            lo = mid;
-        else
-            hi = mid;
-    }
-    return lo;
-}
-
 __device__ inline void seq_range(const int32_t *cu, int n, int64_t total_tokens, int64_t &a, int64_t &b)
 {
     a = min<int64_t>(max<int64_t>(cu[n], 0), total_tokens);
@@ -203,6 +189,7 @@ struct SlotMap {
     int32_t rank0;               // scan kernels: first rank of this launch (its ranks: rank0 + i)
     int32_t ranks;               // scan launches: number of ranks (sequences) this launch covers
     const int2 *slot_info;       // global mode, prep: per slot, its chunk's first token and length
+                                 // (the prep's only source in global mode)
 };
 
 // Sequence of the scan work item with rank index i of its launch.
@@ -522,22 +509,12 @@ __global__ __launch_bounds__((PrepWaves<E, C>::value * kWave)) void gdn_prep_ker
             return;
         t0 = (int)(uint32_t)si;
         slot = sidx;
-    } else {
-        int n, c;
-        if (map.chunk_start) {
-            const int32_t e = sidx;
-            if (e >= map.chunk_start[num_seqs])
-                return;
-            n = find_sequence(map.chunk_start, num_seqs, e);
-            c = e - map.chunk_start[n];
-            slot = e;
-        } else {
-            n = sidx / map.seg_len;
-            c = map.seg_first + (int)(sidx - n * map.seg_len);
-            if (n >= num_seqs || c >= seq_chunks(map, cu, n, total_tokens, C))
-                return;
-            slot = sidx;
-        }
+    } else {   // segment mode
+        const int n = sidx / map.seg_len;
+        const int c = map.seg_first + (int)(sidx - n * map.seg_len);
+        if (n >= num_seqs || c >= seq_chunks(map, cu, n, total_tokens, C))
+            return;
+        slot = sidx;
         int64_t a, b;
         seq_range(cu, n, total_tokens, a, b);
         t0 = a + (int64_t)c * C;
