@@ -32,6 +32,11 @@ Workspace round trips (the chunk matrices written by the prep and read by the sc
 are not algorithmic: they show up in `traffic`, the HBM bytes that the rocprofv3
 counters measured per launch.
 
+Warm-up: the first few dozen steps of a run are slower while the GPU's clocks
+ramp up (varlen_16, 30 timed steps: 1.166 ms per step after 3 untimed steps,
+1.108 after 20, 1.082 after 60, 1.088 after 120), so the default is 60 untimed
+steps before the timed ones.
+
 Prints ONE JSON line.
 """
 import argparse
@@ -466,8 +471,8 @@ def skewed_lengths():
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--workload", default="varlen_16")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -531,16 +536,16 @@ def main():
             if name == args.workload:
                 continue
             print("[bench] prefill %s" % name, file=sys.stderr, flush=True)
-            extra[name] = measure_prefill(name, max(5, min(args.steps, 20)), 2)
+            extra[name] = measure_prefill(name, max(5, min(args.steps, 20)), 10)
         print("[bench] prefill skewed batch (one 32k sequence among 63 of 64 tokens)", file=sys.stderr, flush=True)
-        extra["skewed_64"] = measure_prefill("prefill_32k", max(5, min(args.steps, 20)), 2, lengths=skewed_lengths())
+        extra["skewed_64"] = measure_prefill("prefill_32k", max(5, min(args.steps, 20)), 10, lengths=skewed_lengths())
         extra["skewed_64"]["workload"] = "skewed_64"
         for tokens in (1024, 32768):
             print("[bench] gated RMSNorm %d tokens" % tokens, file=sys.stderr, flush=True)
-            extra["gated_rmsnorm_%d" % tokens] = measure_norm(tokens, max(10, min(args.steps, 50)), 3)
+            extra["gated_rmsnorm_%d" % tokens] = measure_norm(tokens, max(10, min(args.steps, 50)), 10)
         for tokens in (1024, 32768):
             print("[bench] conv1d %d tokens" % tokens, file=sys.stderr, flush=True)
-            extra["conv1d_qkv_%d" % tokens] = measure_conv(tokens, max(10, min(args.steps, 50)), 3)
+            extra["conv1d_qkv_%d" % tokens] = measure_conv(tokens, max(10, min(args.steps, 50)), 10)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
