@@ -92,6 +92,19 @@ def test_wide_slices_many_sequences(nseq):
              "wide_n%d" % nseq, host_offsets=host_offsets)
 
 
+@pytest.mark.parametrize("hqk,hv,nseq", [(8, 8, 10), (4, 16, 6), (2, 16, 5), (1, 4, 2)])
+def test_query_key_groups(hqk, hv, nseq):
+    """1, 4 and 8 value heads per query/key head (the other cases use 2): the prep deals a
+    group's value heads to one XCD and forms the group's Gram products per value head, and the
+    scans read the group's q and k rows.  Whole-head scan (80-96 pairs) and row-split scan (8
+    pairs), sequences of several chunks with ragged ends, both launch modes."""
+    gen = torch.Generator().manual_seed(hqk * 100 + hv)
+    lengths = [int(x) for x in torch.randint(1, 300, (nseq,), generator=gen)]
+    inp = _case(lengths, hqk, hv, 128, torch.bfloat16, seed=40 + hv + hqk)
+    for host_offsets in (True, False):
+        _run(inp, 64, torch.bfloat16, "groups_%d_%d" % (hqk, hv), host_offsets=host_offsets)
+
+
 @pytest.mark.parametrize("nseq", [4096, 4100])
 def test_batches_at_and_past_the_ordering_limit(nseq):
     """Up to 4096 sequences a ranking kernel orders the batch so that the scans start the
