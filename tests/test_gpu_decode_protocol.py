@@ -70,6 +70,14 @@ def test_decode_large_batch_and_empty_batch():
     assert o.shape[0] == 0 and torch.equal(state.cpu(), inp["initial_state"])
 
 
+@pytest.mark.parametrize("hqk,hv", [(4, 16), (1, 8), (8, 8)])
+def test_decode_query_key_groups(hqk, hv):
+    """4, 8 and 1 value heads per query/key head (the cases above use 1 and 2): each value
+    head's wave reads its group's query and key rows."""
+    _check_decode(_decode_inputs(6, hqk, hv, 128, torch.bfloat16, seed=320 + hv + hqk), torch.bfloat16,
+                  "decode_groups_%d_%d" % (hqk, hv))
+
+
 def test_decode_strong_decay_and_scale():
     inp = _decode_inputs(3, 1, 2, 128, torch.bfloat16, seed=310)
     inp["g"][:] = S.STRONG_DECAY

@@ -59,6 +59,14 @@ def test_short_batch_every_head_size(io, d):
     assert counts[PROF_SHORT] == 1 and counts[PROF_PREP] == 0 and counts[PROF_SCAN] == 0, counts
 
 
+@pytest.mark.parametrize("hqk,hv", [(4, 16), (1, 8), (8, 8)])
+def test_short_batch_query_key_groups(hqk, hv):
+    """4, 8 and 1 value heads per query/key head on the token-recurrent path."""
+    inp = S.make_inputs([8, 3, 0, 6], hqk, hv, 128, 128, torch.bfloat16, seed=910 + hv + hqk, s0_std=0.05)
+    counts = _run(inp, torch.bfloat16, "short_groups_%d_%d" % (hqk, hv))
+    assert counts[PROF_SHORT] == 1 and counts[PROF_PREP] == 0, counts
+
+
 @pytest.mark.parametrize("longest,recurrent", [(8, True), (9, False)])
 def test_limit_of_the_recurrent_path(longest, recurrent):
     inp = S.make_inputs([longest, 7, 2], 2, 4, 128, 128, torch.bfloat16, seed=930 + longest, s0_std=0.05)
