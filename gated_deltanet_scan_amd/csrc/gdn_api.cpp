@@ -141,6 +141,27 @@ int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, 
     return (int32_t)len;
 }
 
+// Windows: a batch whose longest sequences take the row-split scan keeps, as segments do, the
+// chunk matrices of one window resident in the last-level cache between the prep and the scans.
+// Unlike segments, a window's chunk table gives slots only to the chunks that fall in it, so the
+// short sequences (done in the first window) cost no slots in the later ones, and the whole-batch
+// workspace holds every window.  The budget is the long ranks' slots: the first window also
+// holds the short sequences' chunks.
+int32_t prefill_window_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype, int32_t long_ranks,
+                           int32_t max_seq_chunks)
+{
+    if (long_ranks <= 0 || max_seq_chunks <= 0)
+        return 0;
+    const size_t es = io_size(io_dtype);
+    const size_t first = prefill_absorbed(io_dtype, chunk) ? (size_t)dk : (size_t)chunk;
+    const size_t per_slot = (size_t)hv * (first + chunk) * chunk * es + (size_t)chunk * 2 * hqk * dk * es;
+    const int64_t m = (int64_t)(kSegmentBytes / per_slot) / long_ranks;
+    if (m >= max_seq_chunks || m < kMinSegmentChunks)
+        return 0;
+    const int64_t nwin = (max_seq_chunks + m - 1) / m;
+    return (int32_t)((max_seq_chunks + nwin - 1) / nwin);
+}
+
 // A batch whose longest sequences would bound a whole-head scan (each of its workgroups runs
 // one (sequence, head) chain, about 3 us per chunk step when its CU is to itself, about 4 us
 // when the chip is busy) runs them in the row-split scan instead (about 1.2 us per step, eight
@@ -357,6 +378,10 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
     p.seg_len = 0;
     p.max_seq_chunks = 0;
     p.max_len = -1;
+    p.win_len = 0;
+    p.win_slots = nullptr;
+    p.rest_chunks = -1;
+    std::vector<int64_t> win_slots;   // chunk slots of each window (host offsets, windows only)
     if (cu_seqlens_host) {
         int64_t longest = 0, prev_chunks = INT64_MAX;
         p.ordered = true;
@@ -375,6 +400,8 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
                 chunks[n] = (cu_seqlens_host[n + 1] - cu_seqlens_host[n] + s.chunk - 1) / s.chunk;
             std::sort(chunks.begin(), chunks.end(), std::greater<int64_t>());
             p.long_ranks = gdn::prefill_long_ranks(s.num_v_heads, s.dk, s.chunk, s.io_dtype, chunks.data(), num_seqs);
+            if (p.long_ranks > 0)
+                p.rest_chunks = (int32_t)chunks[p.long_ranks];
         }
         p.seg_len = gdn::prefill_segment_len(s.num_qk_heads, s.num_v_heads, s.dk, s.chunk, s.io_dtype, num_seqs,
                                              p.max_seq_chunks, slot_capacity);
@@ -383,6 +410,21 @@ static gdn_status prefill_impl(const gdn_shape *shape, const void *q, const void
             const int64_t m = slot_capacity / num_seqs;   // >= 1 (checked above)
             const int64_t nseg = (p.max_seq_chunks + m - 1) / m;
             p.seg_len = (int32_t)((p.max_seq_chunks + nseg - 1) / nseg);
+        }
+        if (p.seg_len == 0 && p.long_ranks > 0) {
+            p.win_len = gdn::prefill_window_len(s.num_qk_heads, s.num_v_heads, s.dk, s.chunk, s.io_dtype,
+                                                p.long_ranks, p.max_seq_chunks);
+            if (p.win_len > 0) {
+                // window j holds local chunks [j L, (j + 1) L) of every sequence
+                const int64_t L = p.win_len;
+                win_slots.assign((p.max_seq_chunks + L - 1) / L, 0);
+                for (int32_t n = 0; n < num_seqs; ++n) {
+                    const int64_t c = ((int64_t)cu_seqlens_host[n + 1] - cu_seqlens_host[n] + s.chunk - 1) / s.chunk;
+                    for (size_t j = 0; (int64_t)j * L < c; ++j)
+                        win_slots[j] += std::min<int64_t>(L, c - (int64_t)j * L);
+                }
+                p.win_slots = win_slots.data();
+            }
         }
         if (p.max_seq_chunks == 0) {   // every sequence empty: one launch passes the states through
             p.seg_len = 1;

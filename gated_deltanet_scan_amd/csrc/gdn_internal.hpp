@@ -36,6 +36,10 @@ struct PrefillArgs {
     int32_t long_ranks;      // > 0: the first long_ranks ranks (longest sequences) are scanned by
                              // the row-split kernel, the rest by the whole-head kernel
     int32_t max_len;         // tokens of the longest sequence (host offsets), -1 if unknown
+    int32_t win_len;         // > 0 (global mode, long_ranks > 0): the batch is run in windows of
+                             // win_len local chunks of every sequence, one chunk table per window
+    const int64_t *win_slots;  // host array: chunk slots of window j (ceil(max_seq_chunks / win_len))
+    int32_t rest_chunks;     // chunks of the longest sequence past the first long_ranks ranks, -1 if unknown
     // optional gated RMSNorm of the output rows (o then holds y): gate, weight and eps
     const void *norm_z;
     const float *norm_weight;
@@ -117,14 +121,18 @@ PrefillWorkspace prefill_workspace(int32_t hv, int32_t dk, int32_t chunk, int32_
                                    int32_t num_seqs);
 // Workspace bytes per chunk slot (the chunk matrices and the decay record of every value head).
 size_t prefill_slot_bytes(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype);
-// Segment length (local chunks per sequence) for a batch whose longest sequence has
-// max_seq_chunks chunks; 0 selects the single-launch global mode.
 // Number of longest sequences to scan apart from the rest (0: one scan kernel for the batch);
 // chunks_desc: the chunk counts of the batch, longest first.
 int32_t prefill_long_ranks(int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype, const int64_t *chunks_desc,
                            int32_t num_seqs);
+// Segment length (local chunks per sequence) for a batch whose longest sequence has
+// max_seq_chunks chunks; 0 selects the single-launch global mode.
 int32_t prefill_segment_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype,
                             int32_t num_seqs, int32_t max_seq_chunks, int32_t slot_capacity);
+// Window length (local chunks of every sequence per window) of a global-mode batch whose first
+// long_ranks ranks take the row-split scan; 0: one window.
+int32_t prefill_window_len(int32_t hqk, int32_t hv, int32_t dk, int32_t chunk, int32_t io_dtype, int32_t long_ranks,
+                           int32_t max_seq_chunks);
 
 hipError_t launch_prefill(const PrefillArgs &p);
 hipError_t launch_decode(const DecodeArgs &p);

@@ -34,7 +34,10 @@
 //   gdn_chunk_scan_tform_kernel  T form, whole heads (many pairs)
 //
 // Where the chunks' T and A live.  Global mode: one slot per chunk of the
-// batch, slot = chunk_start[n] + c.  Segment mode (the host knows the
+// batch, slot = chunk_start[n] + c; or, for a batch whose longest sequences
+// take the row-split scan, windows of W local chunks [w0, w0 + W) of every
+// sequence, each with a chunk table of its own over the chunks that fall in it,
+// slot = chunk_start[n] + (c - w0).  Segment mode (the host knows the
 // sequence lengths): the launch is split into segments of M local chunk
 // indices [s0, s0 + M) of every sequence, slot = n * M + (c - s0); prep and
 // scan run per segment, the state is carried in final_state between
@@ -81,7 +84,10 @@ __global__ __launch_bounds__(kThreads) void gdn_seq_order_kernel(const int32_t *
 
 // ---------------------------------------------------------------------------
 // Chunk table: chunk_start[n] = sum_{m<n} ceil(L_m / C), clamped to
-// max_chunks; chunk_start[num_seqs] = total number of chunks.  Offsets are
+// max_chunks; chunk_start[num_seqs] = total number of chunks.  Over a window
+// of local chunks [win_first, win_first + win_len) a sequence counts only
+// its chunks in the window, and a slot's entry is that of local chunk
+// win_first + (slot - chunk_start[n]).  Offsets are
 // clamped to [0, total_tokens] so that invalid input cannot send later
 // kernels out of bounds.  Workgroup 0 builds the table; with `order` given, the
 // grid has one thread per sequence and also ranks them (gdn_seq_order_kernel's
@@ -96,7 +102,7 @@ constexpr int32_t kSlotsPerTableBlock = 2048;
 __global__ __launch_bounds__(kThreads) void gdn_chunk_table_kernel(
     const int32_t *__restrict__ cu, int32_t num_seqs, int64_t total_tokens, int32_t chunk,
     int32_t max_chunks, int32_t *__restrict__ chunk_start, int32_t *__restrict__ order,
-    int2 *__restrict__ slot_info)
+    int2 *__restrict__ slot_info, int32_t win_first, int32_t win_len)
 {
     if (order)
         rank_sequence(cu, num_seqs, total_tokens, order, blockIdx.x * kThreads + threadIdx.x);
@@ -116,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_table_kernel(
         if (n < num_seqs) {
             a = min<int64_t>(max<int64_t>(cu[n], 0), total_tokens);
             b = min<int64_t>(max<int64_t>(cu[n + 1], a), total_tokens);
-            cnt = (b - a + chunk - 1) / chunk;
+            cnt = min<int64_t>(max<int64_t>((b - a + chunk - 1) / chunk - win_first, 0), win_len);
         }
         int64_t incl = cnt;
 #pragma unroll
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void gdn_chunk_table_kernel(
                     else
                         m1 = mid;
                 }
-                const int64_t t0 = s_a[m0] + (e - s_first[m0]) * chunk;
+                const int64_t t0 = s_a[m0] + (win_first + e - s_first[m0]) * chunk;
                 slot_info[e] = make_int2((int)t0, (int)min<int64_t>(chunk, s_b[m0] - t0));
             }
         }
@@ -183,7 +189,7 @@ __device__ inline void seq_range(const int32_t *cu, int n, int64_t total_tokens,
 // Placement of chunk slots in the workspace (see the file header).
 struct SlotMap {
     const int32_t *chunk_start;  // global mode: per-sequence first slot; NULL in segment mode
-    int32_t seg_first;           // first local chunk index of this launch
+    int32_t seg_first;           // first local chunk index of this launch (segment or window)
     int32_t seg_len;             // local chunks per sequence in this launch
     const int32_t *seq_order;    // scan kernels: the sequence of rank r is seq_order[r]; NULL: r
     int32_t rank0;               // scan kernels: first rank of this launch (its ranks: rank0 + i)
@@ -199,11 +205,12 @@ __device__ inline int ranked_sequence(const SlotMap &m, int i)
     return m.seq_order ? m.seq_order[r] : r;
 }
 
-// Number of chunks of sequence n (consistent with the clamping of the chunk table).
+// Number of chunks of sequence n (consistent with the clamping of the chunk table; in a window,
+// the chunks up to the window's end).
 __device__ inline int seq_chunks(const SlotMap &m, const int32_t *cu, int n, int64_t total_tokens, int chunk)
 {
     if (m.chunk_start)
-        return m.chunk_start[n + 1] - m.chunk_start[n];
+        return m.seg_first + (m.chunk_start[n + 1] - m.chunk_start[n]);
     int64_t a, b;
     seq_range(cu, n, total_tokens, a, b);
     return (int)((b - a + chunk - 1) / chunk);
@@ -212,7 +219,7 @@ __device__ inline int seq_chunks(const SlotMap &m, const int32_t *cu, int n, int
 __device__ inline size_t slot_of(const SlotMap &m, int n, int c)
 {
     if (m.chunk_start)
-        return (size_t)m.chunk_start[n] + c;
+        return (size_t)((int64_t)m.chunk_start[n] + (c - m.seg_first));
     return (size_t)n * m.seg_len + (c - m.seg_first);
 }
 
@@ -2988,12 +2995,14 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
                     // Mixed batch (host offsets: a few sequences whose chains would bound a
                     // whole-head scan): its longest sequences (the first ranks) in the
                     // row-split scan, the rest in the whole-head scan.
+                    // (In segments or windows past the rest's chunks only the first.)
                     SlotMap lm = map, rm = map;
                     lm.ranks = p.long_ranks;
                     rm.rank0 = map.rank0 + p.long_ranks;
                     rm.ranks = map.ranks - p.long_ranks;
                     launch_scan_rows<DK, 16>(p, lm, tmat, amat, dec, sin, sout, st);
-                    launch_scan_bf16<DK, 8, 1>(p, rm, tmat, amat, dec, sin, sout, st);
+                    if (p.rest_chunks < 0 || map.seg_first < p.rest_chunks || map.seg_first == 0)
+                        launch_scan_bf16<DK, 8, 1>(p, rm, tmat, amat, dec, sin, sout, st);
                     return;
                 }
                 if (pairs > 64) {
@@ -3057,18 +3066,29 @@ static hipError_t launch_prefill_t(const PrefillArgs &p)
     }
 
     int2 *slot_info = reinterpret_cast<int2 *>(static_cast<char *>(p.workspace) + prefill_slot_info_offset(p.num_seqs));
-    {
-        const ProfEvents ev = prof_events(PROF_CHUNK_TABLE);
-        const unsigned info_blocks = (unsigned)((p.max_chunks + kSlotsPerTableBlock - 1) / kSlotsPerTableBlock);
-        const unsigned blocks = std::max(std::max(order ? rank_blocks : 1u, info_blocks), 1u);
-        hipExtLaunchKernelGGL(gdn_chunk_table_kernel, dim3(blocks), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
-                              p.cu_seqlens, p.num_seqs, p.total_tokens, (int32_t)C, p.max_chunks, chunk_start, order,
-                              slot_info);
+    // One window over every chunk, or (host offsets, long ranks) windows of win_len local chunks
+    // of every sequence, with win_slots[j] slots each: table, prep and scans per window, the
+    // state carried in final_state between windows.
+    const bool windows = p.win_len > 0 && p.win_slots;
+    const int32_t win = windows ? p.win_len : INT32_MAX;
+    for (int32_t w0 = 0, j = 0;; w0 += win, ++j) {
+        const int32_t slots = windows ? (int32_t)p.win_slots[j] : p.max_chunks;
+        {
+            const ProfEvents ev = prof_events(PROF_CHUNK_TABLE);
+            const unsigned info_blocks = (unsigned)((slots + kSlotsPerTableBlock - 1) / kSlotsPerTableBlock);
+            int32_t *const rank = w0 == 0 ? order : nullptr;   // the order stays for later windows
+            const unsigned blocks = std::max(std::max(rank ? rank_blocks : 1u, info_blocks), 1u);
+            hipExtLaunchKernelGGL(gdn_chunk_table_kernel, dim3(blocks), dim3(kThreads), 0, st, ev.start, ev.stop, 0,
+                                  p.cu_seqlens, p.num_seqs, p.total_tokens, (int32_t)C, slots, chunk_start, rank,
+                                  slot_info, w0, win);
+        }
+        const SlotMap map{chunk_start, w0, win, order, 0, p.num_seqs, slot_info};
+        if (slots > 0)
+            prep(map, slots);
+        scan(map, w0 == 0 ? p.initial_state : p.final_state, p.final_state);
+        if (!windows || w0 + win >= p.max_seq_chunks)
+            break;
     }
-    const SlotMap map{chunk_start, 0, INT32_MAX, order, 0, p.num_seqs, slot_info};
-    if (p.max_chunks > 0)
-        prep(map, p.max_chunks);
-    scan(map, p.initial_state, p.final_state);
     return finish();
 }
 

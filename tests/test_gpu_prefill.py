@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 import torch
 
+import gated_deltanet_scan_amd as gdn
 from gated_deltanet_scan_amd import synthetic as S
 from gpu_helpers import check_prefill, gpu_prefill, oracle_prefill, rel_err, say
 
@@ -364,3 +365,25 @@ def test_skewed_batch(host_offsets):
     lengths = [8192] + [64] * 20 + [37, 0]
     _run(_case(lengths, 16, 32, 128, torch.bfloat16, seed=35), 64, torch.bfloat16, "skewed",
          host_offsets=host_offsets)
+
+
+def test_skewed_batch_windows():
+    """A long sequence whose row-split chain spans several windows of local chunks, each with a
+    chunk table of its own; a second sequence reaches past the first window, the rest (one
+    chunk or none) end in it.  At this shape (16 QK / 32 V heads, dk = dv = 128, bf16) the
+    375-chunk sequence takes windows of 125 chunks: three table launches and three row-split
+    scans, and the whole-head scan of the other sequences in the two windows that hold their
+    chunks (the third holds none).  Against the oracle, states and outputs."""
+    import gated_deltanet_scan_amd as gdn
+    lengths = [24000, 9000] + [64] * 20 + [37, 0, 1]
+    inp = _case(lengths, 16, 32, 128, torch.bfloat16, seed=36)
+    gdn.profile_enable(True)
+    try:
+        eo, es = _run(inp, 64, torch.bfloat16, "skewed_windows")
+        torch.cuda.synchronize()
+        counts = {kid: gdn.profile_collect(kid)[0] for kid in (0, 8, 9)}
+    finally:
+        gdn.profile_enable(False)
+    say("skewed_windows", "launches: chunk table %d, row-split scan %d, whole-head scan %d"
+        % (counts[0], counts[8], counts[9]))
+    assert counts == {0: 3, 8: 3, 9: 2}, counts
