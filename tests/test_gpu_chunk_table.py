@@ -9,7 +9,8 @@ integers themselves, exactly, against a host computation of the same definitions
 batches cover one and several blocks of 256 sequences, one and several table workgroups of
 2048 slots, zero-length sequences, ragged last chunks and slots past the batch's chunks.
 The workspace is filled with a stale byte pattern first, so that an entry left unwritten
-shows.
+shows.  A last case checks the table that a windowed call (host offsets, a long sequence in
+the row-split scan, windows of local chunks) leaves behind: its last window's.
 """
 import numpy as np
 import pytest
@@ -76,3 +77,36 @@ def test_table_order_and_slot_entries(case):
     bad = np.nonzero(np.any(got_slots != slots, axis=1))[0]
     assert bad.size == 0, "slot entries differ at %s: got %s, expected %s" % (
         bad[:5].tolist(), got_slots[bad[:5]].tolist(), slots[bad[:5]].tolist())
+
+
+def test_last_window_table():
+    """Windows: one chunk table per window of local chunks [w0, w0 + W), counting only the
+    chunks in it.  At 16 QK / 32 V heads, dk = dv = 128, bf16, the 375-chunk sequence below
+    takes windows of W = 125 chunks (three launches, checked by the parity case of the same
+    batch), so after the call the workspace holds the last window's table (w0 = 250): the
+    125 slots of the long sequence's last 125 chunks, every other sequence empty, and the
+    longest-first order written by the first window's launch."""
+    lengths = [24000, 9000] + [64] * 20 + [37, 0, 1]
+    N, T = len(lengths), int(sum(lengths))
+    inp = S.make_inputs(lengths, 16, 32, 128, 128, torch.bfloat16, seed=91, s0_std=None)
+    shape = gdn.make_shape(16, 32, 128, 128, C, 1, 128 ** -0.5)
+    need = gdn.workspace_bytes(shape, T, N)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    d = to_dev(inp)
+    say("chunk_table", "windows", "N=%d" % N, "T=%d" % T, "workspace %d bytes" % need)
+    gdn.prefill_chunked(d["q"], d["k"], d["v"], d["g"], d["beta"], inp["cu_seqlens"].cpu(), None, chunk=C,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    W, w0 = 125, 250
+    counts = [min(max(-(-n // C) - w0, 0), W) for n in lengths]
+    table = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    order = np.array(sorted(range(N), key=lambda n: (-lengths[n], n)), dtype=np.int32)
+    slots = np.array([(w0 * C + e * C, min(C, lengths[0] - (w0 + e) * C)) for e in range(table[-1])],
+                     dtype=np.int32)
+    raw = ws[:4 * (2 * N + 1) + 8 + 8 * len(slots)].cpu().numpy()
+    ints = raw[:4 * (2 * N + 1)].view(np.int32)
+    off = (4 * (2 * N + 1) + 7) // 8 * 8
+    got = raw[off:off + 8 * len(slots)].view(np.int32).reshape(-1, 2)
+    np.testing.assert_array_equal(ints[:N + 1], table)
+    np.testing.assert_array_equal(ints[N + 1:2 * N + 1], order)
+    np.testing.assert_array_equal(got, slots)
