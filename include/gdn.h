@@ -128,6 +128,10 @@ size_t gdn_prefill_workspace_bytes_for(const gdn_shape *shape, const int32_t *cu
  *                  untouched): same results up to rounding.  fp32 io at
  *                  dk = 128 always runs that recurrence (there is no chunked
  *                  kernel for it; its time grows with the longest sequence).
+ *                  With it the library also plans the chunked launches from
+ *                  the lengths (segments or windows of local chunks, a split
+ *                  of the longest sequences into the row-split scan); the
+ *                  results do not depend on the plan beyond rounding.
  *   initial_state  [num_seqs, HV, dk, dv] fp32, or NULL for zeros
  *   final_state    [num_seqs, HV, dk, dv] fp32 out; MAY alias initial_state
  *                  (in-place prefix reuse), must not overlap anything else
