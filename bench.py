@@ -518,6 +518,16 @@ def main():
         fn = measure_norm if args.profile_norm else measure_conv
         print(json.dumps(fn(32768, args.steps, args.warmup)))
         return
+    if args.workload == "skewed_64":
+        # the skewed batch alone (prefill_32k's shapes, one 32k sequence among 63 of 64 tokens)
+        if not args.profile_prefill:
+            print("--workload skewed_64 goes with --profile-prefill", file=sys.stderr)
+            sys.exit(2)
+        print("[bench] prefill skewed batch (one 32k sequence among 63 of 64 tokens)", file=sys.stderr, flush=True)
+        pre = measure_prefill("prefill_32k", args.steps, args.warmup, lengths=skewed_lengths())
+        pre["workload"] = "skewed_64"
+        print(json.dumps(pre))
+        return
     from gated_deltanet_scan_amd import synthetic
     w = synthetic.workload(args.workload)
     verify = w.verify_tokens > 0
